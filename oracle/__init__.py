@@ -1,0 +1,253 @@
+"""CPU oracle for one MoE layer (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg
+may import this package. The product library never loads it; the two share no code.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, FP32, sequential sums, built without
+fast-math and with floating-point contraction off). This module only builds and loads it
+and marshals numpy arrays. Each wrapper names the page passage its C function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+ERR_IDX_RANGE, ERR_IDX_DUP, ERR_NONFINITE, ERR_SEQLENS = 1, 2, 4, 8
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-shared", "-fPIC", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.orc_router_logits.argtypes = [P, P, P, I64, I32, I32, I32, P]
+        L.orc_router_logits.restype = None
+        L.orc_route_from_logits.argtypes = [P, P, I64, I32, I32, P, P, P, P]
+        L.orc_route_from_logits.restype = I32
+        L.orc_replay_check.argtypes = [P, P, I64, I32, I32]
+        L.orc_replay_check.restype = I32
+        L.orc_permute.argtypes = [P, I64, I32, I32, P, P, P, P]
+        L.orc_permute.restype = I32
+        L.orc_seq_counts.argtypes = [P, I64, I32, I32, P, I32, P]
+        L.orc_seq_counts.restype = I32
+        L.orc_weighted_counts.argtypes = [P, P, I64, I32, I32, P]
+        L.orc_weighted_counts.restype = I32
+        L.orc_gather.argtypes = [P, P, I64, I32, I32, I32, P]
+        L.orc_gather.restype = None
+        L.orc_expert_ffn.argtypes = [P, P, I64, I32, I32, P, P, I32, P, P]
+        L.orc_expert_ffn.restype = None
+        L.orc_combine.argtypes = [P, P, P, I64, I32, I32, I32, P]
+        L.orc_combine.restype = None
+        L.orc_round_bf16.argtypes = [P, P, I64]
+        L.orc_round_bf16.restype = None
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = I32
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _dt(dtype: str) -> int:
+    return 1 if dtype == "bf16" else 0
+
+
+def _store_dtype(dtype: str):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().orc_round_bf16(_p(a), _p(out), a.size)
+    return out
+
+
+def router_logits(x, w_router, bias, dtype: str) -> np.ndarray:
+    """Router logits (fixed-K FP32 projection, plus optional bias). "0 train-infer
+    mismatch ...", "The router: matching expert ids and weights"."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    x = np.ascontiguousarray(x)
+    w_router = np.ascontiguousarray(w_router)
+    bias = _c(bias, np.float32)
+    out = np.empty((T, E), dtype=np.float32)
+    lib().orc_router_logits(_p(x), _p(w_router), _p(bias), T, d, E, _dt(dtype), _p(out))
+    return out
+
+
+def route_from_logits(logits, k: int, token_mult=None, want_probs: bool = False):
+    """FP32 softmax, top-k (logit desc, id asc), left-to-right renormalisation and
+    multiplicity-weighted probability mass. Returns (idx, w, prob_mass, err[, probs])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    q = _c(token_mult, np.int32)
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    mass = np.empty(E, dtype=np.float32)
+    probs = np.empty((T, E), dtype=np.float32) if want_probs else None
+    err = lib().orc_route_from_logits(_p(logits), _p(q), T, E, k, _p(idx), _p(w),
+                                      _p(probs), _p(mass))
+    if err < 0:
+        raise ValueError("bad route dimensions")
+    if want_probs:
+        return idx, w, mass, err, probs
+    return idx, w, mass, err
+
+
+def replay_check(idx, w, E: int) -> int:
+    """Validation of replayed ids/weights ("Total Router Recall")."""
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T, k = idx.shape
+    return lib().orc_replay_check(_p(idx), _p(w), T, E, k)
+
+
+def permute(idx, E: int):
+    """Histogram, exclusive offsets, stable counting sort. Returns
+    (counts, offsets, perm, inv, err)."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    perm = np.full(T * k, -1, dtype=np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    err = lib().orc_permute(_p(idx), T, k, E, _p(counts), _p(offsets), _p(perm), _p(inv))
+    return counts, offsets, perm, inv, err
+
+
+def seq_counts(idx, E: int, cu_seqlens):
+    idx = _c(idx, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    T, k = idx.shape
+    S = len(cu) - 1
+    out = np.zeros((S, E), dtype=np.int32)
+    err = lib().orc_seq_counts(_p(idx), T, k, E, _p(cu), S, _p(out))
+    return out, err
+
+
+def weighted_counts(idx, E: int, token_mult=None):
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    q = _c(token_mult, np.int32)
+    out = np.empty(E, dtype=np.int64)
+    err = lib().orc_weighted_counts(_p(idx), _p(q), T, k, E, _p(out))
+    return out, err
+
+
+def gather(x, perm, k: int, n_rows: Optional[int] = None) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    perm = _c(perm, np.int32)
+    n = len(perm) if n_rows is None else n_rows
+    d = x.shape[1]
+    out = np.empty((n, d), dtype=x.dtype)
+    lib().orc_gather(_p(x), _p(perm), n, k, d, 1 if x.dtype == np.uint16 else 0, _p(out))
+    return out
+
+
+def expert_ffn(xrows, rowexp, w13, w2, dtype: str):
+    """SwiGLU expert FFN per row: FP32 gate/up sums, one rounding of h, FP32 down sum.
+    Returns (h, y)."""
+    xrows = np.ascontiguousarray(xrows)
+    rowexp = _c(rowexp, np.int32)
+    n, d = xrows.shape
+    I = w13.shape[1] // 2
+    h = np.empty((n, I), dtype=_store_dtype(dtype))
+    y = np.empty((n, d), dtype=np.float32)
+    lib().orc_expert_ffn(_p(xrows), _p(rowexp), n, d, I, _p(np.ascontiguousarray(w13)),
+                         _p(np.ascontiguousarray(w2)), _dt(dtype), _p(h), _p(y))
+    return h, y
+
+
+def combine(y, inv, w, dtype: str):
+    """Slot-order FP32 weighted sum, rounded once to the output dtype."""
+    y = _c(y, np.float32)
+    inv = _c(inv, np.int32)
+    w = _c(w, np.float32)
+    T, k = w.shape
+    d = y.shape[1]
+    out = np.empty((T, d), dtype=_store_dtype(dtype))
+    lib().orc_combine(_p(y), _p(inv), _p(w), T, k, d, _dt(dtype), _p(out))
+    return out
+
+
+def forward(L, logits: Optional[np.ndarray] = None, S_stats: bool = True) -> dict:
+    """All stages for a small layer ``L`` (a ``workloads.Layer``). In router mode the
+    discrete decisions are taken from ``logits`` when given (the logits exported by the
+    implementation under test), else from the oracle's own logits."""
+    res = {}
+    err = 0
+    if L.mode == "router":
+        own = router_logits(L.x, L.w_router, L.logit_bias, L.dtype)
+        res["logits"] = own
+        use = own if logits is None else logits
+        idx, w, mass, e = route_from_logits(use, L.k, L.token_mult)
+        res["prob_mass"] = mass
+        err |= e
+    else:
+        idx, w = L.idx_in, L.w_in
+        err |= replay_check(idx, w, L.E)
+    res["idx"], res["w"] = np.ascontiguousarray(idx), np.ascontiguousarray(w)
+    counts, offsets, perm, inv, e = permute(idx, L.E)
+    err |= e
+    res.update(counts=counts, offsets=offsets, perm=perm, inv=inv)
+    if S_stats:
+        res["weighted_counts"], e = weighted_counts(idx, L.E, L.token_mult)
+        err |= e
+        if L.cu_seqlens is not None:
+            res["seq_counts"], e = seq_counts(idx, L.E, L.cu_seqlens)
+            err |= e
+    x_perm = gather(L.x, perm, L.k)
+    res["x_perm"] = x_perm
+    rowexp = np.repeat(np.arange(L.E, dtype=np.int32), counts)
+    h, y = expert_ffn(x_perm, rowexp, L.w13, L.w2, L.dtype)
+    res["h"], res["y"] = h, y
+    res["out"] = combine(y, inv, w, L.dtype)
+    res["err"] = err
+    return res
+
+
+def forward_tokens(L, tokens, idx, w):
+    """Expert FFN + combine for a subset of tokens, given their routing rows. Returns
+    (h[len(tokens),k,I], y[len(tokens),k,d], out[len(tokens),d])."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    k = L.k
+    sel_idx = np.ascontiguousarray(idx[tokens], dtype=np.int32)
+    sel_w = np.ascontiguousarray(w[tokens], dtype=np.float32)
+    xr = np.ascontiguousarray(np.repeat(L.x[tokens], k, axis=0))
+    h, y = expert_ffn(xr, sel_idx.reshape(-1), L.w13, L.w2, L.dtype)
+    inv = np.arange(len(tokens) * k, dtype=np.int32)
+    out = combine(y, inv, sel_w, L.dtype)
+    n = len(tokens)
+    return h.reshape(n, k, -1), y.reshape(n, k, -1), out

@@ -1,0 +1,336 @@
+/*
+ * moe_oracle.c -- plain, slow, CPU reference for one MoE layer's routing, dispatch,
+ * grouped SwiGLU experts, combine and load statistics.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or calls this
+ * file; only the test suite, the smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Every floating-point step is FP32 (the precision the pages fix for router softmax,
+ * routing weights and the expert accumulators), evaluated in one written-out sequential
+ * order, built with -ffp-contract=off and without fast-math so no step is fused or
+ * reordered. OpenMP is used only across independent rows: each result is computed by
+ * one thread in the same order whatever the thread count.
+ *
+ * Sources (page title, section):
+ *  [MM]  "0 train-infer mismatch for Open-weight MoE RL in Open-source code",
+ *        "Matrix multiplication: the same reduction along K".
+ *  [SW]  same page, "SwiGLU: rounding after the multiply".
+ *  [RT]  same page, "Mixture-of-experts layers" / "The router: matching expert ids and
+ *        weights".
+ *  [EX]  same page, "The experts: keeping the route weight inside the accumulator" and
+ *        "Sharding the experts" (slot-order FP32 accumulation, rounded once).
+ *  [TRR] same page, "Total Router Recall" (replayed ids as ints + normalized FP32
+ *        weights, used as given) and "Hash and learned expert routing" (weights, ids and
+ *        slot order preserved through the expert forward).
+ *  [SEL] same page, "Selecting sparse-attention positions" (lower position wins ties;
+ *        adopted for expert ties).
+ *  [RP]  "RoutePack: Expert Placement and Attention-Aware Data Packing for MoE
+ *        Reinforcement Learning", Sec. 2.1 "Routing replay" eq. (1) (per-sample
+ *        per-expert assignment counts) and Sec. 3.3 (aggregate expert load L_e).
+ *  [HA]  "HARTS: Efficient Agentic Reinforcement Learning for Hybrid-Attention Models
+ *        over Arbitrary Rollout Trees", Sec. 3 "MoE semantics without expert expansion"
+ *        eq. (20) (multiplicity q_c weights mass and counts) and Sec. 4 "MoE execution
+ *        and objectives" (no-token-drop: each row routed, dispatched, computed and
+ *        combined once).
+ *
+ * Data types: dt = 0 means float32 arrays, dt = 1 means bfloat16 stored as uint16.
+ * All pins of these functions live in the CPU test suite; no function is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_ERR_IDX_RANGE 1
+#define ORC_ERR_IDX_DUP 2
+#define ORC_ERR_NONFINITE 4
+#define ORC_ERR_SEQLENS 8
+
+/* bfloat16 <-> float32. Widening is exact; narrowing rounds to nearest, ties to even. */
+static float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u); /* NaN */
+    uint32_t keep_lsb = (u >> 16) & 1u;
+    u = u + 0x7fffu + keep_lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static float orc_load(const void *p, int64_t i, int dt) {
+    return dt ? orc_bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+}
+
+static void orc_store(void *p, int64_t i, float v, int dt) {
+    if (dt) ((uint16_t *)p)[i] = orc_f32_to_bf16(v);
+    else ((float *)p)[i] = v;
+}
+
+int orc_version(void) { return 1; }
+
+/* Exposed for the test suite: the bf16 narrowing used at every rounding point. */
+void orc_round_bf16(const float *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(in[i]);
+}
+
+/* [MM], [RT]: router logits l[t,e] = sum_c x[t,c] * w_router[e,c] (+ bias[e]).
+ * One FP32 accumulator per logit, c increasing: the K order never depends on T. */
+void orc_router_logits(const void *x, const void *w_router, const float *bias, int64_t T,
+                       int d, int E, int dt, float *logits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            float acc = 0.0f;
+            for (int c = 0; c < d; ++c) {
+                float prod = orc_load(x, t * (int64_t)d + c, dt) *
+                             orc_load(w_router, (int64_t)e * d + c, dt);
+                acc = acc + prod;
+            }
+            logits[t * (int64_t)E + e] = bias ? acc + bias[e] : acc;
+        }
+    }
+}
+
+/* Does expert a rank before expert b? Larger logit first; equal logits: lower id [SEL]. */
+static int orc_ranks_before(float la, int a, float lb, int b) {
+    if (la > lb) return 1;
+    if (la < lb) return 0;
+    return a < b;
+}
+
+/* [RT] + [HA]: FP32 softmax over all E logits, top-k, left-to-right renormalisation.
+ *  - selection: the k experts that come first in the order (logit desc, id asc); slot j
+ *    holds the j-th of them ("sorted by probability"; selection keyed on the FP32 logit,
+ *    which orders the probabilities the same way);
+ *  - p_e = exp(l_e - m) / Z with m = the largest logit and Z = sum over e ascending;
+ *  - s = ((p_0 + p_1) + ...) over the selected slots, w_j = p_j / s;
+ *  - prob_mass[e] = sum over t ascending of q_t * p[t,e] (q_t = 1 when q is NULL).
+ * probs (optional, [T,E]) receives p. Returns error bits (non-finite logit). */
+int orc_route_from_logits(const float *logits, const int32_t *q, int64_t T, int E, int k,
+                          int32_t *idx, float *w, float *probs, float *prob_mass) {
+    int err = 0;
+    if (E > 256 || k < 1 || k > E) return -1;
+    float *p_all = probs;
+    int own = 0;
+    if (prob_mass && !p_all) {
+        p_all = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+        own = 1;
+    }
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * (int64_t)E;
+        int32_t sel[256];
+        unsigned char taken[256];
+        memset(taken, 0, sizeof(taken));
+        for (int e = 0; e < E; ++e)
+            if (!isfinite(l[e])) err |= ORC_ERR_NONFINITE;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || orc_ranks_before(l[e], e, l[best], best)) best = e;
+            }
+            sel[j] = best;
+            taken[best] = 1;
+        }
+        float m = l[sel[0]];
+        float z[256];
+        float Z = 0.0f;
+        for (int e = 0; e < E; ++e) {
+            z[e] = expf(l[e] - m);
+            Z = Z + z[e];
+        }
+        float p[256];
+        for (int e = 0; e < E; ++e) p[e] = z[e] / Z;
+        float s = p[sel[0]];
+        for (int j = 1; j < k; ++j) s = s + p[sel[j]];
+        for (int j = 0; j < k; ++j) {
+            idx[t * k + j] = sel[j];
+            w[t * k + j] = p[sel[j]] / s;
+        }
+        if (p_all)
+            for (int e = 0; e < E; ++e) p_all[t * (int64_t)E + e] = p[e];
+    }
+    if (prob_mass) {
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < E; ++e) {
+            float acc = 0.0f;
+            for (int64_t t = 0; t < T; ++t) {
+                float qt = q ? (float)q[t] : 1.0f;
+                acc = acc + qt * p_all[t * (int64_t)E + e];
+            }
+            prob_mass[e] = acc;
+        }
+    }
+    if (own) free(p_all);
+    return err;
+}
+
+/* [TRR]: replayed ids and weights are used as given. The only work is validation:
+ * every id in [0,E), no id twice in a row, every weight finite. Returns error bits. */
+int orc_replay_check(const int32_t *idx, const float *w, int64_t T, int E, int k) {
+    int err = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            if (e < 0 || e >= E) err |= ORC_ERR_IDX_RANGE;
+            if (!isfinite(w[t * k + j])) err |= ORC_ERR_NONFINITE;
+            for (int i = 0; i < j; ++i)
+                if (idx[t * k + i] == e) err |= ORC_ERR_IDX_DUP;
+        }
+    }
+    return err;
+}
+
+/* [RP] eq. (1) / Sec. 3.3 and [HA] Sec. 4: expert histogram, exclusive offsets and a
+ * stable counting sort of the flat assignments a = t*k + j by expert.
+ *   counts[e]    = #{a : idx[a] == e}
+ *   offsets[0]=0, offsets[e+1] = offsets[e] + counts[e]
+ *   perm[p] = a, inv[a] = p, where segment e holds its assignments in increasing a.
+ * Out-of-range ids raise ORC_ERR_IDX_RANGE and are left out. Returns error bits. */
+int orc_permute(const int32_t *idx, int64_t T, int k, int E, int32_t *counts,
+                int32_t *offsets, int32_t *perm, int32_t *inv) {
+    int err = 0;
+    int64_t A = T * k;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < A; ++a) {
+        int32_t e = idx[a];
+        if (e < 0 || e >= E) { err |= ORC_ERR_IDX_RANGE; continue; }
+        counts[e] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t a = 0; a < A; ++a) {
+        int32_t e = idx[a];
+        if (e < 0 || e >= E) { inv[a] = -1; continue; }
+        int32_t p = cursor[e]++;
+        perm[p] = (int32_t)a;
+        inv[a] = p;
+    }
+    free(cursor);
+    return err;
+}
+
+/* [RP] eq. (1): per-sequence counts a_{s,e} over the tokens [cu[s], cu[s+1]) of a packed
+ * microbatch. cu must start at 0, end at T and never decrease (else ORC_ERR_SEQLENS). */
+int orc_seq_counts(const int32_t *idx, int64_t T, int k, int E, const int32_t *cu, int S,
+                   int32_t *seq_counts) {
+    if (cu[0] != 0 || cu[S] != T) return ORC_ERR_SEQLENS;
+    for (int s = 0; s < S; ++s)
+        if (cu[s + 1] < cu[s]) return ORC_ERR_SEQLENS;
+    memset(seq_counts, 0, sizeof(int32_t) * (size_t)S * (size_t)E);
+    int err = 0;
+    for (int s = 0; s < S; ++s) {
+        for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+            for (int j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                if (e < 0 || e >= E) { err |= ORC_ERR_IDX_RANGE; continue; }
+                seq_counts[(int64_t)s * E + e] += 1;
+            }
+        }
+    }
+    return err;
+}
+
+/* [HA] eq. (20): multiplicity-weighted assignment counts sum_t q_t [e in idx[t]]. */
+int orc_weighted_counts(const int32_t *idx, const int32_t *q, int64_t T, int k, int E,
+                        int64_t *wc) {
+    int err = 0;
+    for (int e = 0; e < E; ++e) wc[e] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            if (e < 0 || e >= E) { err |= ORC_ERR_IDX_RANGE; continue; }
+            wc[e] += q ? (int64_t)q[t] : 1;
+        }
+    }
+    return err;
+}
+
+/* [RP] Introduction (dispatch): x_perm[p,:] = x[perm[p] / k, :], an exact copy. */
+void orc_gather(const void *x, const int32_t *perm, int64_t n_rows, int k, int d, int dt,
+                void *x_perm) {
+    size_t es = dt ? 2 : 4;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < n_rows; ++p) {
+        int64_t t = perm[p] / k;
+        memcpy((char *)x_perm + (size_t)p * d * es, (const char *)x + (size_t)t * d * es,
+               (size_t)d * es);
+    }
+}
+
+/* [MM], [SW], [EX]: one expert's SwiGLU FFN for each row r with its expert rowexp[r]:
+ *   g_i = sum_c xr[c] w13[e,i,c],  u_i = sum_c xr[c] w13[e,I+i,c]  (FP32, c ascending)
+ *   h_i = silu(g_i) * u_i in FP32, silu(g) = g / (1 + exp(-g)); rounded once to the
+ *         storage dtype (bf16 for dt=1, unchanged for dt=0)
+ *   y_o = sum_i h_i w2[e,o,i] (FP32, i ascending), kept in FP32.
+ * h (dtype dt, [n,I]) and y (float, [n,d]) are outputs. */
+void orc_expert_ffn(const void *xr, const int32_t *rowexp, int64_t n, int d, int I,
+                    const void *w13, const void *w2, int dt, void *h, float *y) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t e = rowexp[r];
+        float *hr = (float *)malloc(sizeof(float) * (size_t)I);
+        for (int i = 0; i < I; ++i) {
+            float g = 0.0f, u = 0.0f;
+            for (int c = 0; c < d; ++c) {
+                float xv = orc_load(xr, r * (int64_t)d + c, dt);
+                g = g + xv * orc_load(w13, (e * 2 * I + i) * (int64_t)d + c, dt);
+                u = u + xv * orc_load(w13, (e * 2 * I + I + i) * (int64_t)d + c, dt);
+            }
+            float silu = g / (1.0f + expf(-g));
+            float hv = silu * u;
+            orc_store(h, r * (int64_t)I + i, hv, dt);
+            hr[i] = orc_load(h, r * (int64_t)I + i, dt);
+        }
+        for (int o = 0; o < d; ++o) {
+            float acc = 0.0f;
+            for (int i = 0; i < I; ++i)
+                acc = acc + hr[i] * orc_load(w2, (e * d + o) * (int64_t)I + i, dt);
+            y[r * (int64_t)d + o] = acc;
+        }
+        free(hr);
+    }
+}
+
+/* [EX], [RT]: out[t,o] = round_out( ((0 + w_0 Y_0) + w_1 Y_1) + ... ) over the slots in
+ * slot order, every product and sum in FP32, one final rounding (bf16 for dt=1). Y_j is
+ * row inv[t*k+j] of y (the expert output of assignment (t,j)). */
+void orc_combine(const float *y, const int32_t *inv, const float *w, int64_t T, int k,
+                 int d, int dt, void *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int o = 0; o < d; ++o) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                float prod = w[t * k + j] * y[(int64_t)inv[t * k + j] * d + o];
+                acc = acc + prod;
+            }
+            orc_store(out, t * (int64_t)d + o, acc, dt);
+        }
+    }
+}
+
+int orc_num_threads(void) {
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
