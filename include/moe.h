@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path: deterministic no-drop
+ * top-k routing or routing replay, stable dispatch into expert-contiguous rows, grouped
+ * SwiGLU expert GEMMs, the slot-order weighted combine, and per-expert load statistics.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers the caller owns (e.g. torch tensors). The
+ *    library only borrows them until the work it enqueued has run. It never allocates,
+ *    never frees, never synchronises the host, and enqueues everything on `stream`
+ *    (a hipStream_t; NULL = the null stream).
+ *  - Layouts are row-major and dense. bf16 tensors hold bfloat16 bit patterns (uint16).
+ *    Weight layouts follow the Linear convention [out, in]: w_router[E,d],
+ *    w13[E,2I,d] (gate rows 0..I-1 then up rows I..2I-1), w2[E,d,I].
+ *  - Host-checkable errors (null required pointer, bad sizes or dtype, small workspace)
+ *    return a status and enqueue nothing. Data errors found on the device (bad replay
+ *    ids, non-finite logits/weights, bad cu_seqlens) are OR-ed into the caller's int32
+ *    *d_err (device memory; the library never clears it, the caller zeroes it before the
+ *    first call). When *d_err != 0 the outputs are unspecified, but every kernel stays
+ *    inside its buffers. d_err may be NULL (no report).
+ *  - Determinism: every output is bitwise identical from run to run. Every per-token
+ *    output row (topk_idx, topk_w, x_perm/h/y rows reached through inv, out) is bitwise
+ *    independent of T, of the other tokens and of the launch shape (tile_m), because
+ *    every reduction has one fixed order that nothing but the reduced length decides.
+ *  - Reentrant; no global mutable state. No C++ exception crosses this boundary.
+ *
+ * Sources (page title, section):
+ *  [MM]  "0 train-infer mismatch for Open-weight MoE RL in Open-source code",
+ *        "Matrix multiplication: the same reduction along K" (fixed-K products).
+ *  [SW]  same page, "SwiGLU: rounding after the multiply".
+ *  [RT]  same page, "The router: matching expert ids and weights".
+ *  [EX]  same page, "The experts: keeping the route weight inside the accumulator" and
+ *        "Sharding the experts".
+ *  [TRR] same page, "Total Router Recall"; "Hash and learned expert routing".
+ *  [SEL] same page, "Selecting sparse-attention positions" (lower position wins ties).
+ *  [RP]  "RoutePack: Expert Placement and Attention-Aware Data Packing for MoE
+ *        Reinforcement Learning", Sec. 2.1 eq. (1), Sec. 3.3.
+ *  [HA]  "HARTS: Efficient Agentic Reinforcement Learning for Hybrid-Attention Models
+ *        over Arbitrary Rollout Trees", eq. (20) and "MoE execution and objectives".
+ */
+#ifndef MOE_LAYER_ROUTING_AMD_MOE_H
+#define MOE_LAYER_ROUTING_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_E_NULLPTR = 1,   /* a required pointer is NULL */
+    MOE_E_SHAPE = 2,     /* a size is outside the supported range */
+    MOE_E_DTYPE = 3,     /* dtype is not MOE_F32 or MOE_BF16 */
+    MOE_E_WORKSPACE = 4, /* workspace NULL or smaller than moe_workspace_size() */
+    MOE_E_LAUNCH = 5     /* the HIP runtime rejected a launch or an event record */
+} moe_status;
+
+/* bits OR-ed into *d_err by device-side checks */
+enum {
+    MOE_DERR_IDX_RANGE = 1, /* an expert id outside [0, E) */
+    MOE_DERR_IDX_DUP = 2,   /* the same expert twice in one token's replayed row */
+    MOE_DERR_NONFINITE = 4, /* a NaN/Inf router logit or replayed weight */
+    MOE_DERR_SEQLENS = 8    /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_S = T */
+};
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem sizes. Supported: 0 <= T, T*k < 2^31; 1 <= E <= 256; 1 <= k <= min(E, 8);
+ * 64 <= d <= 16384 and 64 <= inter <= 16384, both multiples of 64.
+ * dtype is the storage type of x, w_router, w13, w2, x_perm, h and out; logits,
+ * probabilities, routing weights, y and all accumulators are FP32.
+ * tile_m: 0 selects the grouped-GEMM token-tile height automatically; 16, 32, 64 or 128
+ * forces it. Results are bitwise identical for every value (launch shape only). */
+typedef struct moe_dims {
+    int64_t T;
+    int32_t d;
+    int32_t E;
+    int32_t k;
+    int32_t inter;
+    int32_t dtype;
+    int32_t tile_m;
+} moe_dims;
+
+/* Bytes of device workspace any entry point needs for `dims` (the largest of them; it
+ * serves moe_forward as well). Pure host function; returns 0 for invalid dims. The
+ * workspace holds small per-block partials and tile lists, never a full activation. */
+size_t moe_workspace_size(const moe_dims *dims);
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(moe_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/* Router [MM][RT][SEL][HA].
+ *   logits[t,e] = sum_c x[t,c] w_router[e,c] (+ logit_bias[e]): FP32 accumulation over c
+ *     in one fixed order for every T (no M-dependent split of K);
+ *   probabilities p[t,:] = FP32 softmax over all E logits (shifted by the largest);
+ *   slots: the k experts first in the order (logit desc, id asc), slot 0 = largest;
+ *   topk_w[t,j] = p[t,idx_j] / s with s = ((p_idx0 + p_idx1) + ...) left to right;
+ *   prob_mass[e] = sum_t q_t p[t,e] (q_t = token_mult[t], or 1 when token_mult is NULL),
+ *     summed in a fixed order.
+ * x [T,d] (dtype), w_router [E,d] (dtype), logit_bias [E] f32 or NULL,
+ * topk_idx [T,k] i32 and topk_w [T,k] f32 (outputs, required),
+ * logits [T,E] f32 output or NULL (then held in the workspace),
+ * prob_mass [E] f32 output or NULL, token_mult [T] i32 or NULL.
+ * Non-finite logits set MOE_DERR_NONFINITE. */
+moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router,
+                     const float *logit_bias, int32_t *topk_idx, float *topk_w,
+                     float *logits, float *prob_mass, const int32_t *token_mult,
+                     int32_t *d_err, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Routing replay [TRR][RP]: the caller's expert ids (int32) and normalised FP32 weights,
+ * one per token per slot, are validated and passed through unchanged: no
+ * renormalisation, no reordering. idx_in/w_in [T,k] -> topk_idx/topk_w [T,k]; the output
+ * may alias the input. Ids outside [0,E) set MOE_DERR_IDX_RANGE, an id repeated within a
+ * row sets MOE_DERR_IDX_DUP, a non-finite weight sets MOE_DERR_NONFINITE. */
+moe_status moe_route_replay(const moe_dims *dims, const int32_t *idx_in, const float *w_in,
+                            int32_t *topk_idx, float *topk_w, int32_t *d_err, void *stream);
+
+/* Dispatch and load statistics [RP][HA]. Flat assignments a = t*k + j are
+ * counting-sorted by expert, stably (increasing a inside each expert's segment):
+ *   counts[e] = #{a : topk_idx[a] == e};  offsets[0] = 0, offsets[e+1] = offsets[e] +
+ *   counts[e];  perm[p] = a and inv[a] = p for the sorted position p;
+ *   x_perm[p,:] = x[perm[p] / k, :] (exact copy; NULL skips the gather);
+ *   seq_counts[s,e] = assignments to e from tokens [cu_seqlens[s], cu_seqlens[s+1])
+ *     (cu_seqlens [S+1] i32 and seq_counts [S,E] i32, both NULL or both given);
+ *   weighted_counts[e] = sum_t q_t [e in topk_idx[t]] (int64; q_t = 1 if token_mult is
+ *     NULL).
+ * topk_idx [T,k] i32, x [T,d] dtype, x_perm [T*k,d] dtype, perm/inv [T*k] i32,
+ * counts [E] i32, offsets [E+1] i32 (all outputs except topk_idx/x/token_mult/cu).
+ * Ids outside [0,E) set MOE_DERR_IDX_RANGE and are left out (their inv is -1). */
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
+                       void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
+                       int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
+                       int32_t *seq_counts, const int32_t *token_mult,
+                       int64_t *weighted_counts, int32_t *d_err, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Grouped SwiGLU experts [MM][SW][EX]. For every expert e and row p in
+ * [offsets[e], offsets[e+1]):
+ *   g_i = sum_c x_perm[p,c] w13[e,i,c],  u_i = sum_c x_perm[p,c] w13[e,I+i,c]   (FP32)
+ *   h[p,i] = round_dtype( silu(g_i) * u_i ),  silu(g) = g / (1 + exp(-g)), in FP32,
+ *            rounded once (bf16 round-to-nearest-even; identity for f32);
+ *   y[p,o] = sum_i h[p,i] w2[e,o,i]   (FP32, stored FP32).
+ * Each sum runs over its K in one fixed order (bf16: 16x16x32 MFMA steps in increasing
+ * K; f32: 16x16x4 steps) whatever the segment lengths or tile_m.
+ * x_perm [T*k,d], w13 [E,2I,d], w2 [E,d,I], h [T*k,I] (all dtype), y [T*k,d] f32,
+ * offsets [E+1] i32 (device; read on the device only). Rows past offsets[E] are
+ * untouched. */
+moe_status moe_grouped_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                           const void *w13, const void *w2, void *h, float *y,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Weighted combine [EX][RT]:
+ *   out[t,o] = round_dtype( ((0 + w_0 y_0) + w_1 y_1) + ... )  over slots j = 0..k-1,
+ * where w_j = topk_w[t,j] and y_j = y[inv[t*k+j], o]; each product and sum in FP32, in
+ * slot order, one final rounding. y [T*k,d] f32, inv [T*k] i32, topk_w [T,k] f32,
+ * out [T,d] dtype. */
+moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
+                       const float *topk_w, void *out, void *stream);
+
+/* Everything moe_forward needs. Replay mode iff idx_in != NULL (then w_in is required
+ * and w_router/logit_bias/logits/prob_mass are ignored); router mode otherwise.
+ * Required: x, w13, w2, out, topk_idx, topk_w, counts, offsets, perm, inv, x_perm, h, y,
+ * workspace. Optional (NULL = not produced / not used): logit_bias, logits, prob_mass,
+ * token_mult, cu_seqlens + seq_counts, weighted_counts, d_err, prof_events.
+ * prof_events: NULL, or three hipEvent_t handles recorded on `stream` before the
+ * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing). */
+typedef struct moe_forward_args {
+    const void *x;
+    const void *w_router;
+    const float *logit_bias;
+    const int32_t *idx_in;
+    const float *w_in;
+    const void *w13;
+    const void *w2;
+    const int32_t *token_mult;
+    const int32_t *cu_seqlens;
+    int32_t num_seqs;
+    void *out;
+    int32_t *topk_idx;
+    float *topk_w;
+    float *logits;
+    float *prob_mass;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv;
+    int32_t *seq_counts;
+    int64_t *weighted_counts;
+    void *x_perm;
+    void *h;
+    float *y;
+    int32_t *d_err;
+    void *workspace;
+    size_t workspace_bytes;
+    void *const *prof_events;
+} moe_forward_args;
+
+/* The whole layer: route (or replay) -> permute -> grouped FFN -> combine, each step as
+ * the entry point above defines it, enqueued on `stream` with no host synchronisation
+ * (graph-capturable). */
+moe_status moe_forward(const moe_dims *dims, const moe_forward_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_ROUTING_AMD_MOE_H */

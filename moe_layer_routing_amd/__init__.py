@@ -1,0 +1,221 @@
+"""Python binding of the MI355X MoE-layer hot-path library (``libmoe_hip.so``).
+
+Argument marshalling only: every function passes torch tensors' device pointers and the
+current HIP stream to the C ABI declared in ``include/moe.h`` and raises ``MoeError`` on a
+non-OK status. All computation runs in the library's HIP kernels; there is no fallback.
+If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+DERR_IDX_RANGE, DERR_IDX_DUP, DERR_NONFINITE, DERR_SEQLENS = 1, 2, 4, 8
+STATUS = {0: "MOE_OK", 1: "MOE_E_NULLPTR", 2: "MOE_E_SHAPE", 3: "MOE_E_DTYPE",
+          4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("inter", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"Dims(T={self.T}, d={self.d}, E={self.E}, k={self.k}, inter={self.inter}, "
+                f"dtype={self.dtype}, tile_m={self.tile_m})")
+
+
+_P = ctypes.c_void_p
+
+
+class ForwardArgs(ctypes.Structure):
+    _fields_ = [("x", _P), ("w_router", _P), ("logit_bias", _P), ("idx_in", _P), ("w_in", _P),
+                ("w13", _P), ("w2", _P), ("token_mult", _P), ("cu_seqlens", _P),
+                ("num_seqs", ctypes.c_int32), ("out", _P), ("topk_idx", _P), ("topk_w", _P),
+                ("logits", _P), ("prob_mass", _P), ("counts", _P), ("offsets", _P),
+                ("perm", _P), ("inv", _P), ("seq_counts", _P), ("weighted_counts", _P),
+                ("x_perm", _P), ("h", _P), ("y", _P), ("d_err", _P), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t), ("prof_events", _P)]
+
+
+# exported symbols and their signatures (argument types after the dims pointer)
+_SIGS = {
+    "moe_workspace_size": ([ctypes.POINTER(Dims)], ctypes.c_size_t),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_version": ([], ctypes.c_int),
+    "moe_route": ([ctypes.POINTER(Dims)] + [_P] * 9 + [_P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_route_replay": ([ctypes.POINTER(Dims)] + [_P] * 5 + [_P], ctypes.c_int),
+    "moe_permute": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_grouped_ffn": ([ctypes.POINTER(Dims)] + [_P] * 6 + [_P, ctypes.c_size_t, _P],
+                        ctypes.c_int),
+    "moe_combine": ([ctypes.POINTER(Dims)] + [_P] * 4 + [_P], ctypes.c_int),
+    "moe_forward": ([ctypes.POINTER(Dims), ctypes.POINTER(ForwardArgs), _P], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+# ------------------------------------------------------------------------ marshalling
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def storage_dtype(dtype: int) -> torch.dtype:
+    return torch.bfloat16 if dtype == MOE_BF16 else torch.float32
+
+
+def make_dims(T: int, d: int, E: int, k: int, inter: int, dtype: int, tile_m: int = 0) -> Dims:
+    return Dims(int(T), int(d), int(E), int(k), int(inter), int(dtype), int(tile_m))
+
+
+def workspace_size(dims: Dims) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(dims)))
+
+
+def alloc_workspace(dims: Dims, device="cuda") -> torch.Tensor:
+    n = workspace_size(dims)
+    if n == 0:
+        raise MoeError(2, "moe_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- entry points
+
+def route(dims, x, w_router, logit_bias, topk_idx, topk_w, logits=None, prob_mass=None,
+          token_mult=None, d_err=None, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(dims, x.device)
+    _check(lib().moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                           _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(prob_mass),
+                           _ptr(token_mult), _ptr(d_err), _ptr(ws), ws.numel(),
+                           _stream(stream)), "moe_route")
+
+
+def route_replay(dims, idx_in, w_in, topk_idx, topk_w, d_err=None, stream=None):
+    _check(lib().moe_route_replay(ctypes.byref(dims), _ptr(idx_in), _ptr(w_in), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(d_err), _stream(stream)),
+           "moe_route_replay")
+
+
+def permute(dims, topk_idx, x, x_perm, perm, inv, counts, offsets, cu_seqlens=None,
+            seq_counts=None, token_mult=None, weighted_counts=None, d_err=None,
+            workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(dims, counts.device)
+    S = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(lib().moe_permute(ctypes.byref(dims), _ptr(topk_idx), _ptr(x), _ptr(x_perm),
+                             _ptr(perm), _ptr(inv), _ptr(counts), _ptr(offsets),
+                             _ptr(cu_seqlens), S, _ptr(seq_counts), _ptr(token_mult),
+                             _ptr(weighted_counts), _ptr(d_err), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_permute")
+
+
+def grouped_ffn(dims, x_perm, offsets, w13, w2, h, y, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(dims, offsets.device)
+    _check(lib().moe_grouped_ffn(ctypes.byref(dims), _ptr(x_perm), _ptr(offsets), _ptr(w13),
+                                 _ptr(w2), _ptr(h), _ptr(y), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "moe_grouped_ffn")
+
+
+def combine(dims, y, inv, topk_w, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(dims), _ptr(y), _ptr(inv), _ptr(topk_w), _ptr(out),
+                             _stream(stream)), "moe_combine")
+
+
+def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=None):
+    """Run moe_forward. ``bufs`` maps ForwardArgs field names to tensors (or None);
+    ``prof_events`` is None or a sequence of three raw hipEvent_t handles."""
+    a = ForwardArgs()
+    for name, _ in ForwardArgs._fields_:
+        if name in ("num_seqs", "workspace", "workspace_bytes", "prof_events"):
+            continue
+        setattr(a, name, _ptr(bufs.get(name)))
+    cu = bufs.get("cu_seqlens")
+    a.num_seqs = 0 if cu is None else cu.numel() - 1
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    ev_arr = None
+    if prof_events is not None:
+        ev_arr = (ctypes.c_void_p * 3)(*prof_events)
+        a.prof_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(a), _stream(stream)),
+           "moe_forward")
+
+
+def alloc_forward_buffers(dims: Dims, device="cuda", router: bool = True,
+                          num_seqs: int = 0, weighted: bool = False) -> dict:
+    """Allocate every output and intermediate of moe_forward for ``dims``."""
+    T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.inter
+    A = T * k
+    sd = storage_dtype(dims.dtype)
+    i32 = dict(dtype=torch.int32, device=device)
+    b = dict(
+        out=torch.empty((T, d), dtype=sd, device=device),
+        topk_idx=torch.empty((T, k), **i32),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+        counts=torch.empty(E, **i32),
+        offsets=torch.empty(E + 1, **i32),
+        perm=torch.empty(A, **i32),
+        inv=torch.empty(A, **i32),
+        x_perm=torch.empty((A, d), dtype=sd, device=device),
+        h=torch.empty((A, I), dtype=sd, device=device),
+        y=torch.empty((A, d), dtype=torch.float32, device=device),
+        d_err=torch.zeros(1, **i32),
+    )
+    if router:
+        b["logits"] = torch.empty((T, E), dtype=torch.float32, device=device)
+        b["prob_mass"] = torch.empty(E, dtype=torch.float32, device=device)
+    if num_seqs:
+        b["seq_counts"] = torch.empty((num_seqs, E), **i32)
+    if weighted:
+        b["weighted_counts"] = torch.empty(E, dtype=torch.int64, device=device)
+    return b

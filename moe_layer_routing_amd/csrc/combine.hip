@@ -1,0 +1,77 @@
+// combine.hip -- weighted combine of the k expert outputs of every token.
+//
+// "0 train-infer mismatch for Open-weight MoE RL in Open-source code", "Sharding the
+// experts" and "The experts: keeping the route weight inside the accumulator": each
+// token's routing slots are accumulated in FP32 in slot order, the route weight applied
+// inside that FP32 accumulator, and the sum rounded once to the output type. Here
+// acc = ((0 + w_0*y_0) + w_1*y_1) + ... with every product and sum a separate FP32
+// operation (the library is built without floating-point contraction).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// One wave per token; lane l handles the 4 consecutive features 4*l + 256*i.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+                                                      const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ topk_w,
+                                                      int64_t T, int k, int d, int64_t A,
+                                                      void *__restrict__ out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    int64_t src[kMaxK];
+    float w[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        int32_t p = (j < k) ? inv[t * k + j] : 0;
+        p = (p < 0 || p >= A) ? 0 : p;   // invalid ids were reported by the permute step
+        src[j] = (int64_t)p * d;
+        w[j] = (j < k) ? topk_w[t * k + j] : 0.f;
+    }
+    for (int c = lane * 4; c < d; c += 256) {
+        float4 v[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) v[j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                a0 = a0 + w[j] * v[j].x;
+                a1 = a1 + w[j] * v[j].y;
+                a2 = a2 + w[j] * v[j].z;
+                a3 = a3 + w[j] * v[j].w;
+            }
+        }
+        if constexpr (kBF16) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+            pk.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + t * d + c) = pk;
+        } else {
+            *reinterpret_cast<float4 *>(static_cast<float *>(out) + t * d + c) =
+                make_float4(a0, a1, a2, a3);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
+                          const float *topk_w, void *out, hipStream_t s) {
+    if (dm.T > 0) {
+        const dim3 grid((unsigned)((dm.T + 3) / 4));
+        const int64_t A = dm.T * dm.k;
+        if (dm.dtype == MOE_BF16)
+            combine_kernel<true><<<grid, dim3(256), 0, s>>>(y, inv, topk_w, dm.T, dm.k, dm.d,
+                                                            A, out);
+        else
+            combine_kernel<false><<<grid, dim3(256), 0, s>>>(y, inv, topk_w, dm.T, dm.k, dm.d,
+                                                             A, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+// moe_api.hip -- the C ABI: argument checks, workspace carving, launches.
+// Nothing here allocates, synchronises the host or throws.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+int64_t perm_chunks(int64_t A) { return (A + kPermChunk - 1) / kPermChunk; }
+
+static bool dims_ok(const moe_dims *d) {
+    if (!d) return false;
+    if (d->T < 0 || d->E < 1 || d->E > kMaxE || d->k < 1 || d->k > kMaxK || d->k > d->E)
+        return false;
+    if (d->T * (int64_t)d->k >= (int64_t(1) << 31)) return false;
+    if (d->d < 64 || d->d > 16384 || d->d % 64) return false;
+    if (d->inter < 64 || d->inter > 16384 || d->inter % 64) return false;
+    if (d->tile_m != 0 && d->tile_m != 16 && d->tile_m != 32 && d->tile_m != 64 &&
+        d->tile_m != 128)
+        return false;
+    return true;
+}
+
+static bool dtype_ok(const moe_dims *d) { return d->dtype == MOE_F32 || d->dtype == MOE_BF16; }
+
+Workspace carve_workspace(const moe_dims &d, void *base) {
+    Workspace w{};
+    const int64_t T = d.T, E = d.E, A = d.T * d.k;
+    const int64_t nchunks = perm_chunks(A);
+    const int64_t tblk = (T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
+    // the tile list must hold the smallest tile height any launch may use
+    const int64_t tiles = max_m_tiles(A, d.E, 16);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return base ? static_cast<char *>(base) + o : nullptr;
+    };
+    w.logits = reinterpret_cast<float *>(take(sizeof(float) * T * E));
+    w.mass_part = reinterpret_cast<float *>(take(sizeof(float) * std::max<int64_t>(tblk, 1) * E));
+    w.blk_hist = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * std::max<int64_t>(nchunks, 1) * E));
+    w.blk_whist = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * std::max<int64_t>(nchunks, 1) * E));
+    w.tiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (1 + 3 * tiles)));
+    w.total = off;
+    return w;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+#define MOE_REQUIRE(cond, code) \
+    do {                        \
+        if (!(cond)) return (code); \
+    } while (0)
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULLPTR: return "required pointer is NULL";
+    case MOE_E_SHAPE: return "size outside the supported range";
+    case MOE_E_DTYPE: return "unsupported dtype";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_LAUNCH: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t moe_workspace_size(const moe_dims *dims) {
+    if (!dims_ok(dims) || !dtype_ok(dims)) return 0;
+    return carve_workspace(*dims, nullptr).total;
+}
+
+static moe_status check_common(const moe_dims *dims) {
+    if (!dims) return MOE_E_NULLPTR;
+    if (!dtype_ok(dims)) return MOE_E_DTYPE;
+    if (!dims_ok(dims)) return MOE_E_SHAPE;
+    return MOE_OK;
+}
+
+static moe_status check_ws(const moe_dims *dims, void *ws, size_t bytes) {
+    if (!ws) return MOE_E_WORKSPACE;
+    if (bytes < carve_workspace(*dims, nullptr).total) return MOE_E_WORKSPACE;
+    return MOE_OK;
+}
+
+static moe_status to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_LAUNCH; }
+
+moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router,
+                     const float *logit_bias, int32_t *topk_idx, float *topk_w, float *logits,
+                     float *prob_mass, const int32_t *token_mult, int32_t *d_err,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(x && w_router && topk_idx && topk_w, MOE_E_NULLPTR);
+    st = check_ws(dims, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, workspace);
+    return to_status(launch_route(*dims, x, w_router, logit_bias, logits ? logits : ws.logits,
+                                  topk_idx, topk_w, ws.mass_part, prob_mass, token_mult, d_err,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_replay(const moe_dims *dims, const int32_t *idx_in, const float *w_in,
+                            int32_t *topk_idx, float *topk_w, int32_t *d_err, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(idx_in && w_in && topk_idx && topk_w, MOE_E_NULLPTR);
+    return to_status(launch_replay(*dims, idx_in, w_in, topk_idx, topk_w, d_err,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
+                       void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
+                       int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
+                       int32_t *seq_counts, const int32_t *token_mult,
+                       int64_t *weighted_counts, int32_t *d_err, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(counts && offsets, MOE_E_NULLPTR);
+    if (dims->T > 0) MOE_REQUIRE(topk_idx && perm && inv, MOE_E_NULLPTR);
+    if (dims->T > 0 && x_perm) MOE_REQUIRE(x, MOE_E_NULLPTR);
+    MOE_REQUIRE((cu_seqlens == nullptr) == (seq_counts == nullptr), MOE_E_NULLPTR);
+    if (seq_counts) MOE_REQUIRE(num_seqs >= 1 && num_seqs <= dims->T + 1, MOE_E_SHAPE);
+    st = check_ws(dims, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, workspace);
+    return to_status(launch_permute(*dims, topk_idx, x, x_perm, perm, inv, counts, offsets,
+                                    cu_seqlens, seq_counts ? num_seqs : 0, seq_counts,
+                                    token_mult, weighted_counts, d_err, ws,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                           const void *w13, const void *w2, void *h, float *y, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(x_perm && offsets && w13 && w2 && h && y, MOE_E_NULLPTR);
+    st = check_ws(dims, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, workspace);
+    return to_status(launch_grouped_ffn(*dims, x_perm, offsets, w13, w2, h, y, ws, nullptr,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
+                       const float *topk_w, void *out, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(y && inv && topk_w && out, MOE_E_NULLPTR);
+    return to_status(launch_combine(*dims, y, inv, topk_w, out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(a, MOE_E_NULLPTR);
+    MOE_REQUIRE(a->counts && a->offsets, MOE_E_NULLPTR);
+    const bool replay = a->idx_in != nullptr;
+    if (dims->T > 0) {
+        MOE_REQUIRE(a->x && a->w13 && a->w2 && a->out && a->topk_idx && a->topk_w && a->perm &&
+                        a->inv && a->x_perm && a->h && a->y,
+                    MOE_E_NULLPTR);
+        MOE_REQUIRE(replay ? (a->w_in != nullptr) : (a->w_router != nullptr), MOE_E_NULLPTR);
+    }
+    MOE_REQUIRE((a->cu_seqlens == nullptr) == (a->seq_counts == nullptr), MOE_E_NULLPTR);
+    if (a->seq_counts) MOE_REQUIRE(a->num_seqs >= 1 && a->num_seqs <= dims->T + 1, MOE_E_SHAPE);
+    st = check_ws(dims, a->workspace, a->workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, a->workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (replay)
+        e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
+    else
+        e = launch_route(*dims, a->x, a->w_router, a->logit_bias,
+                         a->logits ? a->logits : ws.logits, a->topk_idx, a->topk_w,
+                         ws.mass_part, a->prob_mass, a->token_mult, a->d_err, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_permute(*dims, a->topk_idx, a->x, a->x_perm, a->perm, a->inv, a->counts,
+                       a->offsets, a->cu_seqlens, a->seq_counts ? a->num_seqs : 0,
+                       a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
+                           a->prof_events, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s);
+    return to_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// moe_internal.h -- device helpers and the host-side launchers each kernel file
+// exports to the C-ABI layer (moe_api.hip). Internal to the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxE = 256;         // experts per layer supported by the LDS-resident paths
+constexpr int kMaxK = 8;           // experts per token
+constexpr int kPermChunk = 2048;   // flat assignments per permute block (fixed, T-free)
+constexpr int kTopkTokPerBlock = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bfloat16 widening (exact) and narrowing (round to nearest, ties to even; NaN kept quiet).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Error word update: one atomic OR, taken only when a check failed.
+__device__ __forceinline__ void raise_err(int32_t *d_err, int32_t bits) {
+    if (d_err && bits) atomicOr(d_err, bits);
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- workspace carving
+// Every entry point uses the same layout so that moe_forward can run all steps in one
+// workspace. Offsets are 256-byte aligned.
+struct Workspace {
+    float *logits;            // [T,E]   router logits when the caller passes none
+    float *mass_part;         // [ceil(T/64), E] per-block probability mass
+    int32_t *blk_hist;        // [nchunks, E] per-chunk expert histogram -> chunk offsets
+    uint64_t *blk_whist;      // [nchunks, E] per-chunk multiplicity-weighted histogram
+    int32_t *tiles;           // [1 + 3*max_tiles] grouped-GEMM tile list
+    size_t total;
+};
+
+int64_t perm_chunks(int64_t A);
+int64_t max_m_tiles(int64_t A, int E, int tile_m);
+Workspace carve_workspace(const moe_dims &d, void *base);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error. Sizes are already validated.
+hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
+                        const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
+                        float *mass_part, float *prob_mass, const int32_t *token_mult,
+                        int32_t *d_err, hipStream_t s);
+hipError_t launch_replay(const moe_dims &dm, const int32_t *idx_in, const float *w_in,
+                         int32_t *topk_idx, float *topk_w, int32_t *d_err, hipStream_t s);
+hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const void *x,
+                          void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
+                          int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
+                          int32_t *seq_counts, const int32_t *token_mult,
+                          int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
+                          hipStream_t s);
+hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
+                              const void *w13, const void *w2, void *h, float *y,
+                              const Workspace &ws, void *const *prof_events, hipStream_t s);
+hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
+                          const float *topk_w, void *out, hipStream_t s);
+
+int select_tile_m(const moe_dims &dm);
+
+}  // namespace moe

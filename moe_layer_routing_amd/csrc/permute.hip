@@ -1,0 +1,274 @@
+// permute.hip -- expert histogram, exclusive offsets, stable scatter into
+// expert-contiguous order, row gather, and load statistics.
+//
+// The counts are the planners' routing-replay demand ("RoutePack ...", Sec. 2.1 eq. (1),
+// Sec. 3.3: per-sample and aggregate assignment counts per expert) and the
+// multiplicity-weighted assignment counts of "HARTS ..." (eq. (20), "MoE execution and
+// objectives"). No assignment is dropped: every (token, slot) lands in exactly one row
+// of its expert's segment, in increasing flat order a = t*k + j.
+//
+// Determinism without order-defined atomics: the flat assignments are cut into fixed
+// chunks of kPermChunk; each chunk's histogram is an integer count (any order gives the
+// same value); one block scans those counts in chunk order; each chunk then ranks its own
+// assignments stably with wave ballots. Positions therefore depend only on the ids.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSubChunk = kPermChunk / 4;  // per wave
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ idx, int64_t A,
+                                                   int k, int E,
+                                                   const int32_t *__restrict__ q,
+                                                   int32_t *__restrict__ blk_hist,
+                                                   uint64_t *__restrict__ blk_whist,
+                                                   int32_t *__restrict__ d_err) {
+    __shared__ int32_t hist[kMaxE];
+    __shared__ unsigned long long whist[kMaxE];
+    for (int e = threadIdx.x; e < E; e += 256) {
+        hist[e] = 0;
+        whist[e] = 0;
+    }
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kPermChunk;
+    int err = 0;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        const int64_t a = base + i;
+        if (a >= A) break;
+        const int e = idx[a];
+        if (e < 0 || e >= E) {
+            err |= MOE_DERR_IDX_RANGE;
+            continue;
+        }
+        atomicAdd(&hist[e], 1);
+        if (blk_whist && q) atomicAdd(&whist[e], (unsigned long long)(uint32_t)q[a / k]);
+    }
+    raise_err(d_err, err);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        blk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
+        if (blk_whist) blk_whist[(int64_t)blockIdx.x * E + e] = whist[e];
+    }
+}
+
+// One block: counts, offsets, and each chunk's starting position per expert.
+__global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ blk_hist,
+                                                   const uint64_t *__restrict__ blk_whist,
+                                                   int64_t nchunks, int E, bool have_q,
+                                                   int32_t *__restrict__ counts,
+                                                   int32_t *__restrict__ offsets,
+                                                   int64_t *__restrict__ weighted_counts) {
+    __shared__ int32_t cnt[kMaxE + 1];
+    const int e = threadIdx.x;
+    int32_t run = 0;
+    if (e < E) {
+        uint64_t wsum = 0;
+        for (int64_t b = 0; b < nchunks; ++b) {
+            const int32_t c = blk_hist[b * E + e];
+            blk_hist[b * E + e] = run;
+            run += c;
+            if (have_q && weighted_counts) wsum += blk_whist[b * E + e];
+        }
+        counts[e] = run;
+        cnt[e] = run;
+        if (weighted_counts) weighted_counts[e] = have_q ? (int64_t)wsum : (int64_t)run;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int i = 0; i < E; ++i) {
+            const int32_t c = cnt[i];
+            cnt[i] = acc;
+            acc += c;
+        }
+        cnt[E] = acc;
+    }
+    __syncthreads();
+    if (e < E) {
+        const int32_t off = cnt[e];
+        offsets[e] = off;
+        for (int64_t b = 0; b < nchunks; ++b) blk_hist[b * E + e] += off;
+    }
+    if (e == 0) offsets[E] = cnt[E];
+}
+
+// Stable ranks inside a chunk. Wave w owns the sub-chunk [w*512, (w+1)*512) of the chunk;
+// a first pass counts each wave's experts, a second pass walks 64 assignments at a time
+// and places each one after the earlier lanes that hold the same expert (found with
+// ballots over the bits of the id).
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
+                                                      int64_t A, int E,
+                                                      const int32_t *__restrict__ blk_off,
+                                                      int32_t *__restrict__ perm,
+                                                      int32_t *__restrict__ inv) {
+    __shared__ int32_t cur[4][kMaxE];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < 4 * kMaxE; i += 256) (&cur[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kPermChunk + wave * kSubChunk;
+    for (int it = 0; it < kSubChunk / kWave; ++it) {
+        const int64_t a = base + it * kWave + lane;
+        const int e = a < A ? idx[a] : -1;
+        if (e >= 0 && e < E) atomicAdd(&cur[wave][e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        int32_t run = blk_off[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int32_t c = cur[w][e];
+            cur[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int it = 0; it < kSubChunk / kWave; ++it) {
+        const int64_t a = base + it * kWave + lane;
+        const int e0 = a < A ? idx[a] : -1;
+        const bool valid = e0 >= 0 && e0 < E;
+        const uint32_t key = valid ? (uint32_t)e0 : 0x1ffu;  // 9 bits; invalid never matches
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int bit = 0; bit < 9; ++bit) {
+            const bool b = (key >> bit) & 1u;
+            const uint64_t m = __ballot(b);
+            peers &= b ? m : ~m;
+        }
+        if (valid) {
+            const int32_t before = __popcll(peers & lt_mask);
+            const int32_t pos = cur[wave][e0] + before;
+            perm[pos] = (int32_t)a;
+            inv[a] = pos;
+        } else if (a < A) {
+            inv[a] = -1;
+        }
+        // the highest lane of each group advances that expert's cursor; the next
+        // iteration's reads come after this write in the wave's LDS order
+        const bool leader = valid && ((peers >> lane) == 1ull);
+        __builtin_amdgcn_wave_barrier();
+        if (leader) cur[wave][e0] += __popcll(peers);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Token-major gather: each wave reads one token's row once and writes it to its k rows.
+template <int kElemBytes>
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__ x, int64_t T,
+                                                     int k, int64_t row_bytes,
+                                                     const int32_t *__restrict__ inv,
+                                                     int64_t A,
+                                                     uint8_t *__restrict__ x_perm) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    int32_t dst[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) dst[j] = (j < k) ? inv[t * k + j] : -1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + t * row_bytes);
+    const int64_t nvec = row_bytes >> 4;
+    for (int64_t v = lane; v < nvec; v += kWave) {
+        const uint4 val = src[v];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            const int32_t p = dst[j];
+            if (j < k && p >= 0 && p < A)
+                reinterpret_cast<uint4 *>(x_perm + (int64_t)p * row_bytes)[v] = val;
+        }
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * 256)
+        p[i] = v;
+}
+
+constexpr int kSeqTok = 256;  // tokens per block in the per-sequence histogram
+
+// Per-sequence counts over packed microbatches. Block b owns tokens [b*256, b*256+256);
+// for each sequence overlapping that range it histograms in LDS and adds the non-zero
+// bins to seq_counts with integer atomics (any order, same sums).
+__global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict__ idx,
+                                                       int64_t T, int k, int E,
+                                                       const int32_t *__restrict__ cu,
+                                                       int S,
+                                                       int32_t *__restrict__ seq_counts,
+                                                       int32_t *__restrict__ d_err) {
+    __shared__ int32_t hist[kMaxE];
+    // validate cu_seqlens: 0 = c_0 <= c_1 <= ... <= c_S = T
+    int bad = 0;
+    for (int s = threadIdx.x; s < S; s += 256)
+        if (cu[s + 1] < cu[s]) bad = 1;
+    if (threadIdx.x == 0 && (cu[0] != 0 || (int64_t)cu[S] != T)) bad = 1;
+    if (__syncthreads_or(bad)) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) raise_err(d_err, MOE_DERR_SEQLENS);
+        return;
+    }
+    const int64_t t0 = (int64_t)blockIdx.x * kSeqTok;
+    const int64_t t1 = min<int64_t>(t0 + kSeqTok, T);
+    // first sequence whose end is past t0 (empty sequences are skipped naturally)
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)cu[mid + 1] <= t0) lo = mid + 1;
+        else hi = mid;
+    }
+    for (int s = lo; s < S && (int64_t)cu[s] < t1; ++s) {
+        const int64_t a0 = max<int64_t>(t0, cu[s]) * k;
+        const int64_t a1 = min<int64_t>(t1, cu[s + 1]) * k;
+        if (a1 <= a0) continue;
+        for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+        __syncthreads();
+        for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
+            const int e = idx[a];
+            if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += 256)
+            if (hist[e]) atomicAdd(&seq_counts[(int64_t)s * E + e], hist[e]);
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const void *x,
+                          void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
+                          int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
+                          int32_t *seq_counts, const int32_t *token_mult,
+                          int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
+                          hipStream_t s) {
+    const int64_t T = dm.T, A = dm.T * dm.k;
+    const int E = dm.E, k = dm.k;
+    const int64_t nchunks = perm_chunks(A);
+    const bool have_q = token_mult != nullptr;
+    if (nchunks > 0)
+        hist_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
+            topk_idx, A, k, E, token_mult, ws.blk_hist,
+            (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err);
+    scan_kernel<<<dim3(1), dim3(256), 0, s>>>(ws.blk_hist, ws.blk_whist, nchunks, E, have_q,
+                                              counts, offsets, weighted_counts);
+    if (nchunks > 0)
+        scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
+                                                                     ws.blk_hist, perm, inv);
+    if (x_perm && T > 0) {
+        const int64_t row_bytes = (int64_t)dm.d * (dm.dtype == MOE_BF16 ? 2 : 4);
+        gather_kernel<16><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(
+            static_cast<const uint8_t *>(x), T, k, row_bytes, inv, A,
+            static_cast<uint8_t *>(x_perm));
+    }
+    if (seq_counts && num_seqs > 0) {
+        const int64_t n = (int64_t)num_seqs * E;
+        fill_i32_kernel<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256),
+                          0, s>>>(seq_counts, n, 0);
+        if (T > 0)
+            seq_hist_kernel<<<dim3((unsigned)((T + kSeqTok - 1) / kSeqTok)), dim3(256), 0, s>>>(
+                topk_idx, T, k, E, cu_seqlens, num_seqs, seq_counts, d_err);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol the header
+declares, and its host-side checks reject bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def M():
+    import moe_layer_routing_amd as M
+    if not os.path.exists(M.LIB_PATH):
+        from moe_layer_routing_amd import _build
+        _build.build()
+    M.lib()
+    return M
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("moe_route", "moe_route_replay", "moe_permute", "moe_grouped_ffn", "moe_combine",
+              "moe_forward", "moe_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(M):
+    L = M.lib()
+    for n in header_functions():
+        assert hasattr(L, n), n
+    assert sorted(M.exported_symbols()) == header_functions()
+    # the exported names are plain C symbols
+    assert ctypes.CDLL(M.LIB_PATH).moe_version() == 100
+
+
+def test_struct_layouts_match_header(M, tmp_path):
+    """Field offsets of the ctypes mirrors equal what a C compiler makes of the header."""
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', 'int main(void){']
+    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs)):
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs)):
+        assert int(got[cname]) == ctypes.sizeof(py)
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, f
+
+
+def test_workspace_size(M):
+    d = M.make_dims(4096, 2048, 64, 8, 1408, M.MOE_BF16)
+    n = M.workspace_size(d)
+    assert n > 4096 * 64 * 4          # holds the router logits
+    assert n < 64 << 20                # never a full activation
+    for bad in (dict(E=0), dict(E=257), dict(k=9), dict(k=0), dict(d=100), dict(inter=96 + 1),
+                dict(dtype=7), dict(tile_m=48), dict(T=-1)):
+        kw = dict(T=10, d=128, E=8, k=2, inter=128, dtype=M.MOE_F32)
+        kw.update(bad)
+        assert M.workspace_size(M.make_dims(**kw)) == 0, bad
+    assert M.workspace_size(M.make_dims(0, 128, 8, 2, 128, M.MOE_F32)) > 0
+
+
+def test_status_strings(M):
+    L = M.lib()
+    for s in range(6):
+        assert L.moe_status_string(s)
+
+
+def test_host_checks_reject_before_any_launch(M):
+    """These calls fail validation, so they return without touching the HIP runtime."""
+    L = M.lib()
+    good = M.make_dims(16, 128, 8, 2, 128, M.MOE_BF16)
+    ws = ctypes.c_void_p(0x1000)
+    fake = ctypes.c_void_p(0x2000)
+    # NULL dims
+    assert L.moe_route(None, *([fake] * 9), ws, 1 << 30, None) == 1
+    # bad dtype / shape
+    bad = M.make_dims(16, 128, 8, 2, 128, 5)
+    assert L.moe_combine(ctypes.byref(bad), fake, fake, fake, fake, None) == 3
+    bad = M.make_dims(16, 128, 8, 9, 128, M.MOE_BF16)
+    assert L.moe_route_replay(ctypes.byref(bad), fake, fake, fake, fake, None, None) == 2
+    # required pointer missing
+    assert L.moe_route(ctypes.byref(good), None, fake, None, fake, fake, None, None, None, None,
+                       ws, 1 << 30, None) == 1
+    assert L.moe_combine(ctypes.byref(good), fake, None, fake, fake, None) == 1
+    # workspace too small / missing
+    assert L.moe_route(ctypes.byref(good), fake, fake, None, fake, fake, None, None, None, None,
+                       ws, 16, None) == 4
+    assert L.moe_grouped_ffn(ctypes.byref(good), fake, fake, fake, fake, fake, fake, None,
+                             1 << 30, None) == 4
+    # cu_seqlens without seq_counts
+    assert L.moe_permute(ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake, fake, 2,
+                         None, None, None, None, ws, 1 << 30, None) == 1

@@ -1,0 +1,325 @@
+"""GPU parity of every entry point against the CPU oracle, on sizes the oracle finishes
+in seconds that still span several tiles and ragged tails, plus edge cases.
+
+Integer and index outputs (top-k ids, counts, offsets, perm, inv, per-sequence and
+weighted counts) must be bit-exact; the router's discrete decisions are compared on the
+GPU's own exported logits (the oracle recomputes everything after the logits from them).
+Floats must satisfy |gpu - ref| <= tol * max(1, |ref|) with tol = 1e-5 (fp32) or 2e-2
+(bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_routing_amd as M
+import oracle
+import workloads as W
+from gpu_util import TOL, U, as_f32, assert_close, dev, dims_of, host, run_forward, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    M.lib()
+    oracle.lib()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------- router
+
+ROUTE_CASES = [
+    dict(T=256, d=128, E=8, k=2, I=64, dtype="f32", seed=1),
+    dict(T=517, d=256, E=64, k=8, I=64, dtype="bf16", seed=2, bias="zipf", mult=True),
+    dict(T=130, d=512, E=256, k=8, I=64, dtype="bf16", seed=3, mult=True),
+    dict(T=33, d=64, E=3, k=3, I=64, dtype="f32", seed=4),
+    dict(T=1, d=128, E=128, k=1, I=64, dtype="bf16", seed=5),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"T{c['T']}_E{c['E']}_k{c['k']}_{c['dtype']}")
+def test_route(case):
+    L = W.make_layer(mode="router", weights=False, **case)
+    _print("route", case)
+    dims = dims_of(L)
+    T, E, k = L.T, L.E, L.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    mass = torch.empty(E, dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.route(dims, dev(L.x), dev(L.w_router), dev(L.logit_bias), idx, w, lg, mass,
+            dev(L.token_mult), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    g_lg = host(lg)
+    ref_lg = oracle.router_logits(L.x, L.w_router, L.logit_bias, L.dtype)
+    assert_close(g_lg, ref_lg, L.dtype, "logits")
+    # any fixed summation order lies within 2*gamma_d * sum|x w| of the exact value
+    x = as_f32(L.x, L.dtype).astype(np.float64)
+    wr = as_f32(L.w_router, L.dtype).astype(np.float64)
+    exact = x @ wr.T + (0 if L.logit_bias is None else L.logit_bias.astype(np.float64))
+    bound = 2 * L.d * U * (np.abs(x) @ np.abs(wr).T) + 2 * U * np.abs(exact)
+    assert np.all(np.abs(g_lg - exact) <= bound + 1e-30)
+    # discrete decisions and weights from the GPU's own logits
+    r_idx, r_w, r_mass, r_err = oracle.route_from_logits(g_lg, k, L.token_mult)
+    assert r_err == 0
+    np.testing.assert_array_equal(host(idx), r_idx)
+    assert_close(host(w), r_w, L.dtype, "topk_w")
+    assert np.all(np.abs(host(w) - r_w) <= 256 * U * r_w)
+    assert_close(host(mass), r_mass, L.dtype, "prob_mass")
+
+
+def test_route_nonfinite_flag():
+    L = W.make_layer(T=70, d=128, E=16, k=4, I=64, dtype="bf16", mode="router", seed=7,
+                     weights=False)
+    L.x[33, 5] = W.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    dims = dims_of(L)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx = torch.empty((L.T, L.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L.T, L.k), dtype=torch.float32, device="cuda")
+    M.route(dims, dev(L.x), dev(L.w_router), None, idx, w, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & M.DERR_NONFINITE
+
+
+# ----------------------------------------------------------------------------- replay
+
+def test_replay_passthrough_and_errors():
+    L = W.make_layer(T=1000, d=64, E=32, k=6, I=64, dtype="bf16", mode="replay", seed=8,
+                     weights=False, replay="uniform")
+    dims = dims_of(L)
+    idx = torch.empty((L.T, L.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L.T, L.k), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.route_replay(dims, dev(L.idx_in), dev(L.w_in), idx, w, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == oracle.replay_check(L.idx_in, L.w_in, L.E) == 0
+    np.testing.assert_array_equal(host(idx), L.idx_in)
+    assert host(w).tobytes() == L.w_in.tobytes()
+    for mutate, bit in ((lambda i, ww: i.__setitem__((5, 2), 32), M.DERR_IDX_RANGE),
+                        (lambda i, ww: i.__setitem__((9, 0), -3), M.DERR_IDX_RANGE),
+                        (lambda i, ww: i.__setitem__((7, 3), i[7, 1]), M.DERR_IDX_DUP),
+                        (lambda i, ww: ww.__setitem__((999, 5), np.inf), M.DERR_NONFINITE),
+                        (lambda i, ww: ww.__setitem__((0, 0), np.nan), M.DERR_NONFINITE)):
+        bi, bw = L.idx_in.copy(), L.w_in.copy()
+        mutate(bi, bw)
+        err.zero_()
+        M.route_replay(dims, dev(bi), dev(bw), idx, w, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == bit == oracle.replay_check(bi, bw, L.E)
+
+
+# ---------------------------------------------------------------------------- permute
+
+PERM_CASES = [
+    dict(T=300, d=128, E=8, k=2, I=64, dtype="f32", seed=11, replay="uniform"),
+    dict(T=1000, d=256, E=64, k=8, I=64, dtype="bf16", seed=12, replay="dirichlet", mult=True),
+    dict(T=2049, d=64, E=13, k=5, I=64, dtype="bf16", seed=13, replay="uniform", mult=True),
+    dict(T=1, d=64, E=4, k=4, I=64, dtype="f32", seed=14, replay="uniform"),
+]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"T{c['T']}_E{c['E']}_k{c['k']}")
+def test_permute(case):
+    L = W.make_layer(mode="replay", weights=False, **case)
+    _check_permute(L)
+
+
+def test_permute_c4_ids():
+    """The heavily imbalanced replay ids (hot expert in every row, 16 empty experts)."""
+    L = W.make_config("c4", weights=False)
+    L.d = 64
+    L.x = L.x[:, :64].copy()
+    L.token_mult = W.token_multiplicities(L.T, 4)
+    _check_permute(L)
+
+
+def test_permute_all_tokens_one_expert_set():
+    L = W.make_layer(T=5000, d=64, E=40, k=3, I=64, dtype="bf16", mode="replay", seed=15,
+                     weights=False, replay="uniform")
+    L.idx_in[:] = np.array([7, 39, 0], np.int32)
+    _check_permute(L)
+
+
+def _check_permute(L):
+    _print("permute", L.T, L.E, L.k)
+    dims = dims_of(L)
+    T, E, k, A = L.T, L.E, L.k, L.A
+    i32 = dict(dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((A, L.d), dtype=torch.bfloat16 if L.dtype == "bf16" else torch.float32,
+                         device="cuda")
+    perm, inv = torch.empty(A, **i32), torch.empty(A, **i32)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    S = 0 if L.cu_seqlens is None else len(L.cu_seqlens) - 1
+    seqc = torch.empty((S, E), **i32) if S else None
+    wc = torch.empty(E, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, **i32)
+    M.permute(dims, dev(L.idx_in), dev(L.x), x_perm, perm, inv, counts, offsets,
+              dev(L.cu_seqlens) if S else None, seqc, dev(L.token_mult), wc, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    r_counts, r_off, r_perm, r_inv, r_err = oracle.permute(L.idx_in, E)
+    np.testing.assert_array_equal(host(counts), r_counts)
+    np.testing.assert_array_equal(host(offsets), r_off)
+    np.testing.assert_array_equal(host(perm), r_perm)
+    np.testing.assert_array_equal(host(inv), r_inv)
+    r_wc, _ = oracle.weighted_counts(L.idx_in, E, L.token_mult)
+    np.testing.assert_array_equal(host(wc), r_wc)
+    if S:
+        r_sc, _ = oracle.seq_counts(L.idx_in, E, L.cu_seqlens)
+        np.testing.assert_array_equal(host(seqc), r_sc)
+    np.testing.assert_array_equal(host(x_perm), oracle.gather(L.x, r_perm, k))
+
+
+def test_permute_bad_ids_and_seqlens():
+    L = W.make_layer(T=100, d=64, E=8, k=2, I=64, dtype="f32", mode="replay", seed=16,
+                     weights=False, replay="uniform")
+    L.idx_in[10, 1] = 8
+    dims = dims_of(L)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    perm, inv = torch.empty(L.A, **i32), torch.empty(L.A, **i32)
+    counts, offsets = torch.empty(L.E, **i32), torch.empty(L.E + 1, **i32)
+    err = torch.zeros(1, **i32)
+    cu = torch.tensor([0, 60, 50, 100], **i32)
+    seqc = torch.empty((3, L.E), **i32)
+    M.permute(dims, dev(L.idx_in), None, None, perm, inv, counts, offsets, cu, seqc,
+              d_err=err)
+    torch.cuda.synchronize()
+    e = int(err.item())
+    assert e & M.DERR_IDX_RANGE and e & M.DERR_SEQLENS
+    r_counts, r_off, r_perm, r_inv, _ = oracle.permute(L.idx_in, L.E)
+    np.testing.assert_array_equal(host(counts), r_counts)
+    np.testing.assert_array_equal(host(inv), r_inv)     # -1 for the dropped id
+    n = int(r_off[-1])
+    np.testing.assert_array_equal(host(perm)[:n], r_perm[:n])
+
+
+# ------------------------------------------------------------------------ whole layer
+
+FWD_CASES = [
+    dict(name="c1", cfg="c1"),
+    dict(name="bf16_ragged", T=300, d=256, E=8, k=2, I=192, dtype="bf16", mode="router", seed=21,
+         bias="zipf", mult=True),
+    dict(name="f32_ragged", T=301, d=192, E=6, k=3, I=128, dtype="f32", mode="router", seed=22),
+    dict(name="bf16_replay_seqs", T=777, d=128, E=32, k=8, I=320, dtype="bf16", mode="replay",
+         seed=23, replay="dirichlet", mult=True),
+    dict(name="bf16_E1_k1", T=150, d=128, E=1, k=1, I=128, dtype="bf16", mode="router", seed=24),
+    dict(name="bf16_kE", T=90, d=64, E=8, k=8, I=64, dtype="bf16", mode="router", seed=25),
+    dict(name="bf16_T1", T=1, d=256, E=16, k=4, I=128, dtype="bf16", mode="router", seed=26),
+    dict(name="bf16_skew", T=400, d=128, E=40, k=2, I=192, dtype="bf16", mode="replay", seed=27,
+         replay="uniform", skew=True),
+]
+
+
+def _make(case):
+    c = dict(case)
+    name = c.pop("name")
+    if "cfg" in c:
+        return W.make_config(c["cfg"])
+    skew = c.pop("skew", False)
+    L = W.make_layer(name=name, **c)
+    if skew:  # every token on experts {3, 17}: 38 empty segments, two long ones
+        L.idx_in[:, 0] = 3
+        L.idx_in[:, 1] = 17
+    return L
+
+
+def _check_layer(L, b, tokens=None):
+    """Compare a moe_forward result with the oracle (on the GPU's logits)."""
+    dtype = L.dtype
+    assert int(b["d_err"].item()) == 0
+    logits = host(b["logits"]) if L.mode == "router" else None
+    if L.mode == "router":
+        ref_lg = oracle.router_logits(L.x, L.w_router, L.logit_bias, dtype)
+        assert_close(logits, ref_lg, dtype, "logits")
+    ref = oracle.forward(L, logits=logits)
+    assert ref["err"] == 0
+    np.testing.assert_array_equal(host(b["topk_idx"]), ref["idx"])
+    assert_close(host(b["topk_w"]), ref["w"], dtype, "topk_w")
+    for n in ("counts", "offsets", "perm", "inv", "weighted_counts"):
+        np.testing.assert_array_equal(host(b[n]), ref[n], err_msg=n)
+    if "seq_counts" in b:
+        np.testing.assert_array_equal(host(b["seq_counts"]), ref["seq_counts"])
+    if L.mode == "router":
+        assert_close(host(b["prob_mass"]), ref["prob_mass"], dtype, "prob_mass")
+    np.testing.assert_array_equal(host(b["x_perm"]), ref["x_perm"])
+    eh = assert_close(as_f32(host(b["h"]), dtype), as_f32(ref["h"], dtype), dtype, "h")
+    ey = assert_close(host(b["y"]), ref["y"], dtype, "y")
+    eo = assert_close(as_f32(host(b["out"]), dtype), as_f32(ref["out"], dtype), dtype, "out")
+    _print(f"  max scaled err h={eh:.2e} y={ey:.2e} out={eo:.2e}")
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: c["name"])
+def test_forward(case):
+    L = _make(case)
+    _print("forward", case["name"], L.T, L.d, L.E, L.k, L.I, L.dtype, L.mode)
+    b, _ = run_forward(L)
+    _check_layer(L, b)
+
+
+@pytest.mark.parametrize("case", [FWD_CASES[1], FWD_CASES[2], FWD_CASES[3], FWD_CASES[7]],
+                         ids=lambda c: c["name"])
+def test_tile_m_invariance(case):
+    """Every token-tile height gives bitwise identical rows (launch shape only)."""
+    L = _make(case)
+    inp = upload(L)
+    base, _ = run_forward(L, inp, tile_m=16)
+    for tm in (32, 64, 128, 0):
+        b, _ = run_forward(L, inp, tile_m=tm)
+        for n in ("topk_idx", "topk_w", "perm", "x_perm", "h", "y", "out"):
+            assert host(b[n]).tobytes() == host(base[n]).tobytes(), (tm, n)
+
+
+def test_run_twice_identical():
+    L = _make(FWD_CASES[3])
+    inp = upload(L)
+    a, _ = run_forward(L, inp)
+    b, _ = run_forward(L, inp)
+    for n in a:
+        if torch.is_tensor(a[n]) and n not in ("x", "w13", "w2", "idx_in", "w_in",
+                                                 "token_mult", "cu_seqlens"):
+            assert host(a[n]).tobytes() == host(b[n]).tobytes(), n
+
+
+def test_zero_tokens():
+    L = W.make_layer(T=0, d=64, E=8, k=2, I=64, dtype="bf16", mode="router", seed=30)
+    dims = dims_of(L)
+    b = M.alloc_forward_buffers(dims, "cuda", router=True, weighted=True)
+    b.update(x=torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+             w_router=dev(L.w_router), w13=dev(L.w13), w2=dev(L.w2))
+    b["counts"].fill_(-1)
+    b["offsets"].fill_(-1)
+    M.forward(dims, b, M.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    assert host(b["counts"]).tolist() == [0] * 8
+    assert host(b["offsets"]).tolist() == [0] * 9
+    assert host(b["prob_mass"]).tolist() == [0.0] * 8
+    assert host(b["weighted_counts"]).tolist() == [0] * 8
+
+
+def test_batch_invariance_small():
+    """A token's routing and output row do not depend on which other tokens share the
+    batch or where it sits (bf16, router mode)."""
+    L = W.make_layer(T=200, d=256, E=16, k=4, I=128, dtype="bf16", mode="router", seed=31,
+                     bias="zipf")
+    inp = upload(L)
+    full, _ = run_forward(L, inp)
+    for T2, perm_seed in ((1, 0), (7, 1), (64, 2), (200, 3)):
+        rng = np.random.default_rng(perm_seed)
+        rows = rng.permutation(L.T)[:T2]
+        L2 = W.make_layer(T=T2, d=256, E=16, k=4, I=128, dtype="bf16", mode="router", seed=31,
+                          bias="zipf", weights=False)
+        L2.w13, L2.w2 = L.w13, L.w2
+        L2.w_router, L2.logit_bias = L.w_router, L.logit_bias
+        L2.x = np.ascontiguousarray(L.x[rows])
+        inp2 = dict(inp)
+        inp2["x"] = dev(L2.x)
+        sub, _ = run_forward(L2, inp2, stats=False)
+        assert host(sub["out"]).tobytes() == host(full["out"])[rows].tobytes()
+        assert host(sub["topk_idx"]).tobytes() == host(full["topk_idx"])[rows].tobytes()
+        assert host(sub["topk_w"]).tobytes() == host(full["topk_w"])[rows].tobytes()
+        assert host(sub["logits"]).tobytes() == host(full["logits"])[rows].tobytes()
