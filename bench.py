@@ -1,0 +1,236 @@
+"""Benchmark of one MoE layer's hot path on one MI355X.
+
+One step = route -> permute (+ load statistics) -> grouped SwiGLU GEMMs -> combine for one
+batch of synthetic tokens (moe_forward), with inputs already resident in HBM. Default
+workload: the training-shaped bf16 layer (T=4096, d=2048, E=64, top-8, I=1408, router
+logits with a per-expert Zipf(1.1) log bias).
+
+Prints ONE JSON line with the throughput (tokens/s), a roofline entry for the dominant
+kernel (the fused gate/up + SwiGLU grouped GEMM, timed live with HIP events recorded by
+the library around it on the launch stream) and the CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 MI355X; grouped-GEMM TFLOP/s as % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "c2": "training-shaped bf16 MoE layer: T=4096 tokens, d=2048, E=64 experts, top-8, SwiGLU "
+          "inter=1408, router logits + per-expert Zipf(1.1) log bias",
+    "c3": "packed RL microbatch: T=16384 tokens in lognormal-length sequences, d=4096, E=128, "
+          "top-8, inter=1536, bf16, routing replay with per-sequence Dirichlet demand",
+    "c4": "heavily imbalanced replay: T=32768, d=2048, E=256, top-8, inter=768, bf16",
+}
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the launch stream)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.rt.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a),
+                                           ctypes.c_void_p(b)) == 0
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(L, sample_tokens: int):
+    """The oracle, untuned, on the first ``sample_tokens`` tokens of the workload: every
+    stage (router or replay check, permutation + statistics, gather, expert FFN,
+    combine). Returns (tokens/s, seconds, threads)."""
+    import oracle
+    oracle.lib()
+    toks = np.arange(min(sample_tokens, L.T))
+    t0 = time.perf_counter()
+    x = np.ascontiguousarray(L.x[toks])
+    if L.mode == "router":
+        lg = oracle.router_logits(x, L.w_router, L.logit_bias, L.dtype)
+        idx, w, _, _ = oracle.route_from_logits(lg, L.k)
+    else:
+        idx, w = L.idx_in[toks], L.w_in[toks]
+        oracle.replay_check(idx, w, L.E)
+    counts, offsets, perm, inv, _ = oracle.permute(idx, L.E)
+    oracle.weighted_counts(idx, L.E, None)
+    xp = oracle.gather(x, perm, L.k)
+    rowexp = np.repeat(np.arange(L.E, dtype=np.int32), counts)
+    h, y = oracle.expert_ffn(xp, rowexp, L.w13, L.w2, L.dtype)
+    oracle.combine(y, inv, w, L.dtype)
+    dt = time.perf_counter() - t0
+    return len(toks) / dt, dt, oracle.num_threads()
+
+
+def upload(L, dev):
+    """Host (numpy) inputs of layer L -> device tensors (bf16 bit patterns as bfloat16)."""
+    import torch
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    return {n: up(getattr(L, n)) for n in ("x", "w_router", "logit_bias", "idx_in", "w_in",
+                                           "w13", "w2", "token_mult", "cu_seqlens")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-sample", type=int, default=4096,
+                    help="tokens of the workload the CPU oracle runs (0 = skip)")
+    ap.add_argument("--tile-m", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(expert-parallel sharding is a design note only); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_layer_routing_amd as M
+    import workloads as W
+    L = W.make_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dims = M.make_dims(L.T, L.d, L.E, L.k, L.I, M.MOE_BF16 if L.dtype == "bf16" else M.MOE_F32,
+                       args.tile_m)
+    inp = upload(L, dev)
+    S = 0 if L.cu_seqlens is None else len(L.cu_seqlens) - 1
+    b = M.alloc_forward_buffers(dims, dev, router=(L.mode == "router"), num_seqs=S,
+                                weighted=True)
+    for n in ("x", "w13", "w2"):
+        b[n] = inp[n]
+    if L.mode == "router":
+        b["w_router"], b["logit_bias"] = inp["w_router"], inp["logit_bias"]
+    else:
+        b["idx_in"], b["w_in"] = inp["idx_in"], inp["w_in"]
+    if S:
+        b["cu_seqlens"] = inp["cu_seqlens"]
+    ws = M.alloc_workspace(dims, dev)
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+
+    for _ in range(args.warmup):
+        M.forward(dims, b, ws)
+    torch.cuda.synchronize()
+    assert int(b["d_err"].item()) == 0, "device error word set"
+
+    K = args.steps
+    evs = hip.create(3 * K + 2)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    hip.record(evs[-2], stream.cuda_stream)
+    for i in range(K):
+        M.forward(dims, b, ws, prof_events=evs[3 * i:3 * i + 3])
+    hip.record(evs[-1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = hip.ms(evs[-2], evs[-1])
+    t13 = np.array([hip.ms(evs[3 * i], evs[3 * i + 1]) for i in range(K)])
+    t2 = np.array([hip.ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)])
+    hip.destroy(evs)
+
+    A = L.T * L.k
+    ms_step = total_ms / K
+    tokens_per_s = L.T / (ms_step * 1e-3)
+    flops13 = 4.0 * A * L.d * L.I
+    flops2 = 2.0 * A * L.I * L.d
+    t13_avg = float(t13.mean())
+    t2_avg = float(t2.mean())
+    ach13 = flops13 / (t13_avg * 1e-3) / 1e12
+    ach_ffn = (flops13 + flops2) / ((t13_avg + t2_avg) * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if L.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "T": L.T, "d": L.d,
+                   "E": L.E, "k": L.k, "inter": L.I, "mode": L.mode,
+                   "tile_m": args.tile_m or "auto"},
+        "roofline": {
+            "kernel": "grouped_gemm_kernel<gate/up + SwiGLU>",
+            "bound": "mfma",
+            "achieved": round(ach13, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach13 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic": f"4*T*k*d*I = {flops13:.4g} FLOP per launch",
+            "avg_launch_ms": round(t13_avg, 5),
+        },
+        "grouped_gemm": {
+            "tflops": round(ach_ffn, 2),
+            "frac_bf16_peak": round(ach_ffn / PEAK_BF16_TFLOPS, 4),
+            "gate_up_ms": round(t13_avg, 5),
+            "down_ms": round(t2_avg, 5),
+            "down_tflops": round(flops2 / (t2_avg * 1e-3) / 1e12, 2),
+        },
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if args.cpu_sample > 0:
+        tps, secs, threads = cpu_baseline(L, args.cpu_sample)
+        rec["cpu_baseline"] = {
+            "value": round(tps, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {min(args.cpu_sample, L.T)} of the {L.T} tokens, every stage "
+                      f"({secs:.1f} s)",
+        }
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
