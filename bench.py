@@ -201,7 +201,7 @@ def main():
                    "E": L.E, "k": L.k, "inter": L.I, "mode": L.mode,
                    "tile_m": args.tile_m or "auto"},
         "roofline": {
-            "kernel": "grouped_gemm_kernel<gate/up + SwiGLU>",
+            "kernel": "grouped_gemm_dma_kernel<gate/up + SwiGLU> (bf16 prefill tiles)",
             "bound": "mfma",
             "achieved": round(ach13, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -70,8 +70,8 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * 64 <= d <= 16384 and 64 <= inter <= 16384, both multiples of 64.
  * dtype is the storage type of x, w_router, w13, w2, x_perm, h and out; logits,
  * probabilities, routing weights, y and all accumulators are FP32.
- * tile_m: 0 selects the grouped-GEMM token-tile height automatically; 16, 32, 64 or 128
- * forces it. Results are bitwise identical for every value (launch shape only). */
+ * tile_m: 0 selects the grouped-GEMM token-tile height automatically; 16, 32, 64, 128 or
+ * 256 forces it. Results are bitwise identical for every value (launch shape only). */
 typedef struct moe_dims {
     int64_t T;
     int32_t d;

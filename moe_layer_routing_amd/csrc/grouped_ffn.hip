@@ -20,14 +20,13 @@
 // (output features), the B operand a 16-token slice of activations. With the result
 // layout of v_mfma_f32_16x16x{32bf16,4f32} (lane l holds token l%16 and features
 // 4*(l/16)+0..3) every lane stores 4 consecutive features of one token row.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;                // one K-stage of a row: 64 bf16 or 32 f32
-constexpr int kLdsStride = kRowBytes + 16;    // padded LDS row (bank spread)
-constexpr int kVecPerRow = kRowBytes / 16;    // 16-byte vectors per staged row
 
 // tiles[0] = number of token tiles; tiles[1 + 3*i ..] = (expert, first row, rows).
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets,
@@ -69,42 +68,35 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
     }
 }
 
-template <bool kBF16>
-struct Elem;
-template <>
-struct Elem<true> {
-    static constexpr int kPerVec = 8;       // bf16 per 16 bytes
-    static constexpr int kSub = 2;          // MFMA K-steps (32 each) per 128-byte stage
-    static constexpr int kSubBytes = 64;
-};
-template <>
-struct Elem<false> {
-    static constexpr int kPerVec = 4;
-    static constexpr int kSub = 8;          // K-steps of 4 floats
-    static constexpr int kSubBytes = 16;
-};
-
 // kGateUp: out = h[A, I] = round(silu(x w_gate^T) * (x w_up^T)), K = d, N = I,
 //          the weight tile stacks BW/2 gate rows over the matching BW/2 up rows.
 // else:    out = y[A, d] (FP32) = h w2^T, K = I, N = d.
-template <bool kBF16, bool kGateUp, int BW, int BT, int WF, int WT>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(const uint8_t *__restrict__ act,
-                                                           const uint8_t *__restrict__ wgt,
-                                                           void *__restrict__ out,
-                                                           const int32_t *__restrict__ tiles,
-                                                           int K, int N, int nft) {
-    using EL = Elem<kBF16>;
+// Block tile: BW weight rows x BT tokens; WF x WT waves, each owning (BW/WF) x (BT/WT).
+// K advances in stages of SRB bytes per row (64 or 128), double-buffered in LDS with a
+// 16-byte pad per row; PF = 1 or 2 stages are in flight in registers ahead of the stage
+// being computed. Every configuration walks K in the same MFMA steps, in the same order.
+template <bool kBF16, bool kGateUp, int BW, int BT, int WF, int WT, int PF, int SRB, int WPE>
+__global__ __launch_bounds__(64 * WF * WT)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
+    const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
+    const int32_t *__restrict__ tiles, int K, int N, int nft) {
+    constexpr int NTHR = 64 * WF * WT;
+    constexpr int kRowBytes = SRB;                     // K bytes of one row per stage
+    constexpr int kLdsStride = kRowBytes + 16;         // padded LDS row (bank spread)
+    constexpr int kVecPerRow = kRowBytes / 16;         // 16-byte vectors per staged row
     constexpr int kEB = kBF16 ? 2 : 4;                 // element bytes
+    constexpr int kSubBytes = kBF16 ? 64 : 16;         // bytes of K per MFMA step
+    constexpr int kSub = kRowBytes / kSubBytes;        // MFMA K-steps per stage
     constexpr int kFeat = kGateUp ? BW / 2 : BW;       // output features per block
     constexpr int kWaveRows = (kGateUp ? BW / 2 : BW) / WF;
     constexpr int NFh = kWaveRows / 16;                // fragments per half (gate/up)
     constexpr int NF = kGateUp ? 2 * NFh : NFh;
     constexpr int NT = BT / WT / 16;
-    constexpr int kVW = BW * kVecPerRow;               // 16-byte vectors per stage
-    constexpr int kVT = BT * kVecPerRow;
-    constexpr int kLW = (kVW + 255) / 256;
-    constexpr int kLT = (kVT + 255) / 256;
-    static_assert(NFh >= 1 && NT >= 1 && WF * WT == 4, "bad tile shape");
+    constexpr int RPI = NTHR / kVecPerRow;             // rows one load round covers
+    constexpr int LW = (BW + RPI - 1) / RPI;
+    constexpr int LT = (BT + RPI - 1) / RPI;
+    static_assert(NFh >= 1 && NT >= 1 && (PF == 1 || PF == 2), "bad tile shape");
+    static_assert((kGateUp ? BW / 2 : BW) % (16 * WF) == 0 && BT % (16 * WT) == 0, "tile");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BW + BT) * kLdsStride];
 
@@ -122,66 +114,60 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const uint8_t *__rest
     const int wf = wv % WF, wt = wv / WF;
     const int n0 = ft * kFeat;
     const int64_t rows_per_expert = kGateUp ? 2 * (int64_t)N : (int64_t)N;
-    const int64_t krow_bytes = (int64_t)K * kEB;
+    const uint32_t krow = (uint32_t)K * kEB;
+    const uint8_t *wbase = wgt + (int64_t)e * rows_per_expert * krow;
+    const uint8_t *abase = act + (int64_t)p0 * krow;
 
-    // global row base pointers for this thread's staged vectors
-    const uint8_t *gw[kLW];
-    const uint8_t *gt[kLT];
+    // byte offsets of this thread's staged 16-byte vectors (chunk c of rows r0 + i*RPI)
+    const int c = tid % kVecPerRow, r0 = tid / kVecPerRow;
+    uint32_t wo[LW], to[LT];
 #pragma unroll
-    for (int i = 0; i < kLW; ++i) {
-        const int v = tid + i * 256;
-        const int r = v / kVecPerRow, c = v % kVecPerRow;
+    for (int i = 0; i < LW; ++i) {
+        const int r = min(r0 + i * RPI, BW - 1);
         int grow;
         if (kGateUp) {
             const int half = r >= BW / 2;
-            const int rr = half ? r - BW / 2 : r;
-            grow = min(n0 + rr, N - 1) + (half ? N : 0);
+            grow = min(n0 + (half ? r - BW / 2 : r), N - 1) + (half ? N : 0);
         } else {
             grow = min(n0 + r, N - 1);
         }
-        gw[i] = wgt + ((int64_t)e * rows_per_expert + grow) * krow_bytes + c * 16;
+        wo[i] = (uint32_t)grow * krow + c * 16;
     }
 #pragma unroll
-    for (int i = 0; i < kLT; ++i) {
-        const int v = tid + i * 256;
-        const int r = v / kVecPerRow, c = v % kVecPerRow;
-        const int rr = min(r, nrows - 1);
-        gt[i] = act + ((int64_t)p0 + rr) * krow_bytes + c * 16;
-    }
-    u32x4_t rw[kLW], rt[kLT];
+    for (int i = 0; i < LT; ++i)
+        to[i] = (uint32_t)min(r0 + i * RPI, nrows - 1) * krow + c * 16;
 
-    auto load_global = [&](int kt) {
-        const int64_t ko = (int64_t)kt * kRowBytes;
+    u32x4_t rw[PF][LW], rt[PF][LT];
+    auto load_global = [&](int kt, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        const uint32_t ko = (uint32_t)kt * kRowBytes;
 #pragma unroll
-        for (int i = 0; i < kLW; ++i)
-            if (kVW % 256 == 0 || tid + i * 256 < kVW)
-                rw[i] = *reinterpret_cast<const u32x4_t *>(gw[i] + ko);
+        for (int i = 0; i < LW; ++i)
+            if (BW % RPI == 0 || r0 + i * RPI < BW)
+                rw[S][i] = *reinterpret_cast<const u32x4_t *>(wbase + wo[i] + ko);
 #pragma unroll
-        for (int i = 0; i < kLT; ++i)
-            if (kVT % 256 == 0 || tid + i * 256 < kVT)
-                rt[i] = *reinterpret_cast<const u32x4_t *>(gt[i] + ko);
+        for (int i = 0; i < LT; ++i)
+            if (BT % RPI == 0 || r0 + i * RPI < BT)
+                rt[S][i] = *reinterpret_cast<const u32x4_t *>(abase + to[i] + ko);
     };
-    auto store_lds = [&](int b) {
+    auto store_lds = [&](int b, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        uint8_t *sb = smem[b] + r0 * kLdsStride + c * 16;
 #pragma unroll
-        for (int i = 0; i < kLW; ++i) {
-            const int v = tid + i * 256;
-            if (kVW % 256 == 0 || v < kVW)
-                *reinterpret_cast<u32x4_t *>(&smem[b][(v / kVecPerRow) * kLdsStride +
-                                                    (v % kVecPerRow) * 16]) = rw[i];
-        }
+        for (int i = 0; i < LW; ++i)
+            if (BW % RPI == 0 || r0 + i * RPI < BW)
+                *reinterpret_cast<u32x4_t *>(sb + i * RPI * kLdsStride) = rw[S][i];
 #pragma unroll
-        for (int i = 0; i < kLT; ++i) {
-            const int v = tid + i * 256;
-            if (kVT % 256 == 0 || v < kVT)
-                *reinterpret_cast<u32x4_t *>(&smem[b][(BW + v / kVecPerRow) * kLdsStride +
-                                                    (v % kVecPerRow) * 16]) = rt[i];
-        }
+        for (int i = 0; i < LT; ++i)
+            if (BT % RPI == 0 || r0 + i * RPI < BT)
+                *reinterpret_cast<u32x4_t *>(sb + (BW + i * RPI) * kLdsStride) = rt[S][i];
     };
 
-    // LDS row of weight fragment f (16 rows) and token fragment t for this wave
+    // LDS byte offsets of this lane's fragment rows
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int frag_lane = r16 * kLdsStride + g4 * (kBF16 ? 16 : 4);
     auto wrow = [&](int f) {
-        if (kGateUp)
-            return (f < NFh ? 0 : BW / 2) + wf * kWaveRows + (f % NFh) * 16;
+        if (kGateUp) return (f < NFh ? 0 : BW / 2) + wf * kWaveRows + (f % NFh) * 16;
         return wf * kWaveRows + f * 16;
     };
     auto trow = [&](int t) { return BW + wt * (BT / WT) + t * 16; };
@@ -192,54 +178,82 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const uint8_t *__rest
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const int nk = K / (kRowBytes / kEB);
-
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cb = kt & 1;
-        if (kt + 1 < nk) load_global(kt + 1);
-        const uint8_t *sb = smem[cb];
+    // One stage: kSub MFMA K-steps. Fragments are double-buffered across K-steps: all LDS
+    // reads of step kk+1 are issued before the MFMAs of step kk, and scheduling barriers
+    // keep the compiler from folding the two phases back into one serial chain.
+    using FragT = typename std::conditional<kBF16, bf16x8_t, float>::type;
+    auto read_frags = [&](const uint8_t *sb, int kk, FragT (&a)[NF], FragT (&bv)[NT]) {
 #pragma unroll
-        for (int kk = 0; kk < EL::kSub; ++kk) {
-            if constexpr (kBF16) {
-                bf16x8_t a[NF], b[NT];
+        for (int f = 0; f < NF; ++f)
+            a[f] = *reinterpret_cast<const FragT *>(sb + wrow(f) * kLdsStride + kk * kSubBytes);
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    a[f] = *reinterpret_cast<const bf16x8_t *>(
-                        sb + (wrow(f) + r16) * kLdsStride + kk * EL::kSubBytes + g4 * 16);
+        for (int t = 0; t < NT; ++t)
+            bv[t] = *reinterpret_cast<const FragT *>(sb + trow(t) * kLdsStride + kk * kSubBytes);
+    };
+    auto mfmas = [&](const FragT (&a)[NF], const FragT (&bv)[NT]) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    b[t] = *reinterpret_cast<const bf16x8_t *>(
-                        sb + (trow(t) + r16) * kLdsStride + kk * EL::kSubBytes + g4 * 16);
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (kBF16)
+                    acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], bv[t], acc[f][t],
+                                                                        0, 0, 0);
+                else
+                    acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[f], bv[t], acc[f][t], 0,
+                                                                     0, 0);
+            }
+    };
+    auto compute = [&](int b) {
+        const uint8_t *sb = smem[b] + frag_lane;
+        FragT a0[NF], b0[NT], a1[NF], b1[NT];
+        read_frags(sb, 0, a0, b0);
 #pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b[t],
-                                                                            acc[f][t], 0, 0, 0);
-            } else {
-                float a[NF], b[NT];
-#pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    a[f] = *reinterpret_cast<const float *>(
-                        sb + (wrow(f) + r16) * kLdsStride + kk * EL::kSubBytes + g4 * 4);
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    b[t] = *reinterpret_cast<const float *>(
-                        sb + (trow(t) + r16) * kLdsStride + kk * EL::kSubBytes + g4 * 4);
-#pragma unroll
-                for (int f = 0; f < NF; ++f)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[f], b[t], acc[f][t],
-                                                                         0, 0, 0);
+        for (int kk = 0; kk < kSub; kk += 2) {
+            if (kk + 1 < kSub) read_frags(sb, kk + 1, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < kSub) {
+                if (kk + 2 < kSub) read_frags(sb, kk + 2, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (kt + 1 < nk) store_lds(cb ^ 1);
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    const int nk = K / (kRowBytes / kEB);
+    if constexpr (PF == 1) {
+        load_global(0, S0{});
+        store_lds(0, S0{});
         __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + 1 < nk) load_global(kt + 1, S0{});
+            compute(kt & 1);
+            if (kt + 1 < nk) store_lds((kt + 1) & 1, S0{});
+            __syncthreads();
+        }
+    } else {
+        // two register stages: stage kt+2 is fetched while stage kt is computed, so each
+        // global load has two compute phases to arrive. Unrolled by two so every register
+        // stage index is a compile-time constant.
+        load_global(0, S0{});
+        if (nk > 1) load_global(1, S1{});
+        store_lds(0, S0{});
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            if (kt + 2 < nk) load_global(kt + 2, S0{});
+            compute(0);
+            if (kt + 1 < nk) store_lds(1, S1{});
+            __syncthreads();
+            if (kt + 1 >= nk) break;
+            if (kt + 3 < nk) load_global(kt + 3, S1{});
+            compute(1);
+            if (kt + 2 < nk) store_lds(0, S0{});
+            __syncthreads();
+        }
     }
 
     // epilogue
@@ -283,43 +297,323 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const uint8_t *__rest
     }
 }
 
-template <bool kBF16, int BW, int BT, int WF, int WT>
-hipError_t run_ffn(const moe_dims &dm, const void *x_perm, const void *w13, const void *w2,
-                   void *h, float *y, const int32_t *tiles, int64_t mtiles,
-                   void *const *ev, hipStream_t s) {
-    const int d = dm.d, I = dm.inter;
-    const int nft13 = (I + BW / 2 - 1) / (BW / 2);
-    const int nft2 = (d + BW - 1) / BW;
-    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess)
-        return hipErrorInvalidValue;
-    grouped_gemm_kernel<kBF16, true, BW, BT, WF, WT>
-        <<<dim3((unsigned)(mtiles * nft13)), dim3(256), 0, s>>>(
-            static_cast<const uint8_t *>(x_perm), static_cast<const uint8_t *>(w13), h, tiles,
-            d, I, nft13);
-    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess)
-        return hipErrorInvalidValue;
-    grouped_gemm_kernel<kBF16, false, BW, BT, WF, WT>
-        <<<dim3((unsigned)(mtiles * nft2)), dim3(256), 0, s>>>(
-            static_cast<const uint8_t *>(h), static_cast<const uint8_t *>(w2), y, tiles, I, d,
-            nft2);
-    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[2]), s) != hipSuccess)
-        return hipErrorInvalidValue;
+// ------------------------------------------------------------------------------------
+// bf16 grouped GEMM fed by direct global->LDS loads (gfx950 global_load_lds_dwordx4).
+//
+// The block stages K in steps of 32 bf16 (64 bytes per row) through an NS-slot LDS ring.
+// Each wave-wide DMA instruction fills one 16-row x 64-byte LDS block (lane l's 16 bytes
+// land at block + 16*l); lanes fetch their row's 16-byte K-chunks in an XOR-swizzled order
+// so that the MFMA fragment reads (16 rows, one chunk each) spread over all LDS banks.
+// Loads run NS-2 stages ahead of the stage whose fragments are being read, and the
+// fragments of stage kt+1 are read while the MFMAs of stage kt run; no register staging.
+// Synchronisation per stage: wait for this wave's DMA of the next stage, one s_barrier.
+// Every output element is the same 16x16x32 MFMA sequence over K in increasing order as in
+// grouped_gemm_kernel, so both kernels produce identical bits.
+__device__ __forceinline__ int chunk_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// One K-stage of DMA for this wave: its NBW 16-row blocks of slot kt % NS.
+template <int NBW, int NW, int NS, int kStageBytes>
+__device__ __forceinline__ void dma_stage(uint8_t *ring, const uint8_t *(&src)[NBW], int kt,
+                                          int wv) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this; it cannot parse the builtin
+    uint8_t *dst = ring + (kt % NS) * kStageBytes;
+    const int64_t ko = (int64_t)kt * 64;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            src[i] + ko, (__attribute__((address_space(3))) void *)(dst + (wv + i * NW) * 1024), 16,
+            0, 0);
+#endif
+}
+
+// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 immediate encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+template <bool kGateUp, int BW, int BT, int WF, int WT, int NS, int WPE, bool DB>
+__global__ __launch_bounds__(64 * WF * WT)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
+    const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
+    const int32_t *__restrict__ tiles, int K, int N, int nft) {
+    constexpr int NW = WF * WT;
+    constexpr int NBLK = (BW + BT) / 16;               // 16-row LDS blocks per stage
+    constexpr int NBW = NBLK / NW;                     // DMA instructions per wave per stage
+    constexpr int kStageBytes = NBLK * 1024;
+    constexpr int kFeat = kGateUp ? BW / 2 : BW;
+    constexpr int kWaveRows = (kGateUp ? BW / 2 : BW) / WF;
+    constexpr int NFh = kWaveRows / 16;
+    constexpr int NF = kGateUp ? 2 * NFh : NFh;
+    constexpr int NT = BT / WT / 16;
+    static_assert(NBLK % NW == 0 && NS >= 3 && NFh >= 1 && NT >= 1, "bad tile shape");
+    static_assert(BW % 16 == 0 && (BW / 2) % 16 == 0, "16-row blocks");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStageBytes];
+
+    const uint32_t nwg = gridDim.x, bid = blockIdx.x;
+    const uint32_t xcd = bid & 7u, loc = bid >> 3, per = nwg >> 3, rem = nwg & 7u;
+    const uint32_t L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+    const int mt = (int)(L / (uint32_t)nft), ft = (int)(L % (uint32_t)nft);
+    if (mt >= tiles[0]) return;
+    const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wf = wv % WF, wt = wv / WF;
+    const int n0 = ft * kFeat;
+    const int64_t rows_per_expert = kGateUp ? 2 * (int64_t)N : (int64_t)N;
+    const int64_t krow = (int64_t)K * 2;
+    const uint8_t *wbase = wgt + (int64_t)e * rows_per_expert * krow;
+    const uint8_t *abase = act + (int64_t)p0 * krow;
+
+    // DMA sources: this lane's row in each of the wave's blocks, at its swizzled chunk
+    const int r4 = lane >> 2;
+    const int chunk = (lane & 3) ^ chunk_swizzle(r4);
+    const uint8_t *src[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        const int row = (wv + i * NW) * 16 + r4;
+        if (row < BW) {
+            int grow;
+            if (kGateUp) {
+                const int half = row >= BW / 2;
+                grow = min(n0 + (half ? row - BW / 2 : row), N - 1) + (half ? N : 0);
+            } else {
+                grow = min(n0 + row, N - 1);
+            }
+            src[i] = wbase + (int64_t)grow * krow + chunk * 16;
+        } else {
+            src[i] = abase + (int64_t)min(row - BW, nrows - 1) * krow + chunk * 16;
+        }
+    }
+#define MOE_ISSUE(kt_) dma_stage<NBW, NW, NS, kStageBytes>(ring, src, (kt_), wv)
+
+    // fragment read offsets inside a stage
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int lane_off = r16 * 64 + ((g4 ^ chunk_swizzle(r16)) << 4);
+    auto wrow = [&](int f) {
+        if (kGateUp) return (f < NFh ? 0 : BW / 2) + wf * kWaveRows + (f % NFh) * 16;
+        return wf * kWaveRows + f * 16;
+    };
+    auto trow = [&](int t) { return BW + wt * (BT / WT) + t * 16; };
+
+    f32x4_t acc[NF][NT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto read_frags = [&](int kt, bf16x8_t (&a)[NF], bf16x8_t (&b)[NT]) {
+        const uint8_t *sb = ring + (kt % NS) * kStageBytes + lane_off;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 4) * 1024);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 4) * 1024);
+    };
+    auto mfmas = [&](const bf16x8_t (&a)[NF], const bf16x8_t (&b)[NT]) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b[t], acc[f][t], 0, 0, 0);
+    };
+
+    const int nk = K >> 5;
+    // prologue: stages 0..NS-2 in flight, stage 0 resident
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) MOE_ISSUE(s);
+    if (nk > 1) wait_vm_lgkm0<NBW * (NS - 2)>();
+    else wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    bf16x8_t ca[NF], cb[NT];
+    bf16x8_t na[DB ? NF : 1], nb[DB ? NT : 1];
+    read_frags(0, ca, cb);
+
+    // Stage kt+1 becomes readable: own DMA of it done (later stages may still fly), every
+    // LDS read this wave issued has returned, then one barrier for all waves. After it the
+    // slot of stage kt-1 is free and receives stage kt+NS-1.
+    auto advance = [&](int kt) {
+        if (kt + NS - 2 < nk) wait_vm_lgkm0<NBW * (NS - 3)>();
+        else wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
+    };
+    if constexpr (DB) {
+        // steady state, unrolled by two so the fragment sets swap roles without copies
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {
+            advance(kt);
+            read_frags(kt + 1, na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ca, cb);
+            __builtin_amdgcn_sched_barrier(0);
+            advance(kt + 1);
+            read_frags(kt + 2, ca, cb);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < nk) {          // two stages left
+            advance(kt);
+            read_frags(kt + 1, na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ca, cb);
+            mfmas(na, nb);
+        } else {                    // one stage left
+            mfmas(ca, cb);
+        }
+    } else {
+        // one fragment set: read stage kt, then its MFMAs (another wave on the SIMD covers
+        // the LDS latency)
+        mfmas(ca, cb);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            advance(kt);
+            read_frags(kt + 1, ca, cb);
+            mfmas(ca, cb);
+        }
+    }
+
+    // epilogue (same arithmetic and layout as grouped_gemm_kernel)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int m = wt * (BT / WT) + t * 16 + r16;
+        if (m >= nrows) continue;
+        const int64_t row = (int64_t)p0 + m;
+        if constexpr (kGateUp) {
+#pragma unroll
+            for (int f = 0; f < NFh; ++f) {
+                const int feat = n0 + wf * kWaveRows + f * 16 + g4 * 4;
+                if (feat >= N) continue;
+                float hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float gv = acc[f][t][i];
+                    const float uv = acc[f + NFh][t][i];
+                    const float silu = gv / (1.0f + expf(-gv));
+                    hv[i] = silu * uv;
+                }
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(hv[2]) | ((uint32_t)f32_to_bf16(hv[3]) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + row * N + feat) = pk;
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int feat = n0 + wf * kWaveRows + f * 16 + g4 * 4;
+                if (feat >= N) continue;
+                *reinterpret_cast<float4 *>(static_cast<float *>(out) + row * N + feat) =
+                    make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]);
+            }
+        }
+    }
+}
+
+template <int BW_, int BT_, int WF_, int WT_, int NS_, bool DB_ = true,
+          int WPE_ = WF_ * WT_ / 4>
+struct DmaCfg {
+    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, NS = NS_, WPE = WPE_;
+    static constexpr bool DB = DB_;
+    static constexpr int kThreads = 64 * WF_ * WT_;
+    static constexpr bool kDma = true;
+};
+
+// Launch shape of one GEMM: block tile and waves. Any shape gives the same bits.
+// WPE: waves per SIMD the kernel is compiled for (the register budget follows from it).
+template <int BW_, int BT_, int WF_, int WT_, int PF_, int SRB_ = 128, int WPE_ = 1>
+struct Cfg {
+    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, PF = PF_, SRB = SRB_,
+                         WPE = WPE_;
+    static constexpr int kThreads = 64 * WF_ * WT_;
+};
+
+template <class C, class = void>
+struct IsDma : std::false_type {};
+template <class C>
+struct IsDma<C, std::void_t<decltype(C::kDma)>> : std::true_type {};
+
+template <bool kBF16, bool kGateUp, class C>
+hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_t *tiles,
+                       int64_t mtiles, int K, int N, hipStream_t s) {
+    constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
+    const int nft = (N + feat - 1) / feat;
+    if constexpr (IsDma<C>::value && kBF16) {
+        grouped_gemm_dma_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::NS, C::WPE, C::DB>
+            <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
+                static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
+                K, N, nft);
+    } else if constexpr (!IsDma<C>::value) {
+        grouped_gemm_kernel<kBF16, kGateUp, C::BW, C::BT, C::WF, C::WT, C::PF, C::SRB, C::WPE>
+            <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
+                static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
+                K, N, nft);
+    } else {
+        // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
+        // same token tiles
+        using F = Cfg<256, C::BT, 2, 2, 1, 64, 1>;
+        return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s);
+    }
     return hipGetLastError();
 }
+
+template <bool kBF16, class C13, class C2>
+hipError_t run_ffn(const moe_dims &dm, const void *x_perm, const void *w13, const void *w2,
+                   void *h, float *y, const int32_t *tiles, int64_t mtiles, void *const *ev,
+                   hipStream_t s) {
+    static_assert(C13::BT == C2::BT, "both GEMMs walk the same token tiles");
+    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipError_t e = launch_gemm<kBF16, true, C13>(x_perm, w13, h, tiles, mtiles, dm.d, dm.inter, s);
+    if (e != hipSuccess) return e;
+    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess)
+        return hipErrorInvalidValue;
+    e = launch_gemm<kBF16, false, C2>(h, w2, y, tiles, mtiles, dm.inter, dm.d, s);
+    if (e != hipSuccess) return e;
+    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[2]), s) != hipSuccess)
+        return hipErrorInvalidValue;
+    return hipSuccess;
+}
+
+// Prefill-shaped launches: 8 waves (2 per SIMD), 128x64 per wave, 4-slot DMA ring.
+// 128-token tiles stage 512 weight rows (256 output features of gate/up), 256-token tiles
+// stage 256 weight rows; both keep the ring within the 160 KB of LDS.
+#ifndef MOE_FFN_LARGE_CFG13
+#define MOE_FFN_LARGE_CFG13 DmaCfg<512, 128, 4, 2, 4, false>
+#define MOE_FFN_LARGE_CFG2 DmaCfg<512, 128, 4, 2, 4, false>
+#endif
+#ifndef MOE_FFN_HUGE_CFG13
+#define MOE_FFN_HUGE_CFG13 DmaCfg<256, 256, 2, 4, 4, false>
+#define MOE_FFN_HUGE_CFG2 DmaCfg<256, 256, 2, 4, 4, false>
+#endif
 
 template <bool kBF16>
 hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const void *w13,
                         const void *w2, void *h, float *y, const int32_t *tiles,
                         int64_t mtiles, void *const *ev, hipStream_t s) {
     switch (bt) {
-    case 16:
-        return run_ffn<kBF16, 128, 16, 4, 1>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
-    case 32:
-        return run_ffn<kBF16, 128, 32, 4, 1>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
-    case 64:
-        return run_ffn<kBF16, 128, 64, 2, 2>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+    case 16: {
+        using C = Cfg<128, 16, 4, 1, 1, 128, 3>;
+        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+    }
+    case 32: {
+        using C = Cfg<128, 32, 4, 1, 1, 128, 3>;
+        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+    }
+    case 64: {
+        using C = Cfg<128, 64, 2, 2, 1, 128, 2>;
+        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+    }
+    case 128:
+        return run_ffn<kBF16, MOE_FFN_LARGE_CFG13, MOE_FFN_LARGE_CFG2>(dm, x_perm, w13, w2, h, y,
+                                                                       tiles, mtiles, ev, s);
     default:
-        return run_ffn<kBF16, 256, 128, 2, 2>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, MOE_FFN_HUGE_CFG13, MOE_FFN_HUGE_CFG2>(dm, x_perm, w13, w2, h, y,
+                                                                     tiles, mtiles, ev, s);
     }
 }
 
@@ -332,7 +626,8 @@ int select_tile_m(const moe_dims &dm) {
     if (dm.T <= 16 || avg <= 16) return 16;
     if (dm.T <= 32 || avg <= 32) return 32;
     if (dm.T <= 64 || avg <= 96) return 64;
-    return 128;
+    if (avg < 1024) return 128;
+    return 256;
 }
 
 int64_t max_m_tiles(int64_t A, int E, int tile_m) { return (A + tile_m - 1) / tile_m + E; }

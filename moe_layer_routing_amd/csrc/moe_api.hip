@@ -16,7 +16,7 @@ static bool dims_ok(const moe_dims *d) {
     if (d->d < 64 || d->d > 16384 || d->d % 64) return false;
     if (d->inter < 64 || d->inter > 16384 || d->inter % 64) return false;
     if (d->tile_m != 0 && d->tile_m != 16 && d->tile_m != 32 && d->tile_m != 64 &&
-        d->tile_m != 128)
+        d->tile_m != 128 && d->tile_m != 256)
         return false;
     return true;
 }

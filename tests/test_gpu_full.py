@@ -114,7 +114,7 @@ def test_c5_batch_invariance():
         assert w.tobytes() == ref_w[:T].tobytes(), T
     out, idx, _, _ = run(pool[::-1])
     assert out.tobytes() == ref_out[::-1].tobytes()
-    for tm in (16, 32, 64, 128):
+    for tm in (16, 32, 64, 128, 256):
         out, _, _, _ = run(pool, tile_m=tm)
         assert out.tobytes() == ref_out.tobytes(), tm
     # prefill-shaped: the 64 pool rows scattered through 4096 other tokens

@@ -268,7 +268,7 @@ def test_tile_m_invariance(case):
     L = _make(case)
     inp = upload(L)
     base, _ = run_forward(L, inp, tile_m=16)
-    for tm in (32, 64, 128, 0):
+    for tm in (32, 64, 128, 256, 0):
         b, _ = run_forward(L, inp, tile_m=tm)
         for n in ("topk_idx", "topk_w", "perm", "x_perm", "h", "y", "out"):
             assert host(b[n]).tobytes() == host(base[n]).tobytes(), (tm, n)

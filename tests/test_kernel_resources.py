@@ -1,0 +1,70 @@
+"""Compile-time properties of the gfx950 kernels that correctness depends on.
+
+The DMA-fed grouped GEMM waits for its own global->LDS loads with hand-placed vmcnt
+counts. Scratch (register spill) traffic would share that counter, so every such kernel
+must compile without scratch. Checked on the device assembly hipcc produces here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "moe_layer_routing_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "grouped_ffn.s"
+    from moe_layer_routing_amd import _build
+    cmd = [_build.HIPCC, *[f for f in _build.FLAGS if f not in ("-shared", "-fPIC")],
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-S", "--cuda-device-only",
+           os.path.join(CSRC, "grouped_ffn.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(asm):
+    """(name, metadata block) for every kernel in the code object metadata."""
+    blocks = asm.split("- .agpr_count:")[1:]
+    for b in blocks:
+        m = re.search(r"\.name:\s+(\S+)", b)
+        yield m.group(1), b
+
+
+def test_dma_gemm_kernels_have_no_scratch(gemm_asm):
+    found = 0
+    for name, b in _kernels(gemm_asm):
+        if "grouped_gemm_dma_kernel" not in name:
+            continue
+        found += 1
+        priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", b).group(1))
+        spill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", b).group(1))
+        assert priv == 0 and spill == 0, f"{name}: scratch {priv} B, {spill} VGPR spills"
+    assert found >= 2
+
+
+def test_gemm_kernels_fit_lds(gemm_asm):
+    for name, b in _kernels(gemm_asm):
+        lds = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", b).group(1))
+        assert lds <= 160 * 1024, name
+
+
+def test_one_mfma_shape_per_dtype(gemm_asm):
+    """Batch invariance rests on every bf16 GEMM using the same MFMA instruction (and every
+    f32 GEMM the same f32 one)."""
+    ops = set(re.findall(r"\b(v_mfma_\w+)", gemm_asm))
+    assert ops == {"v_mfma_f32_16x16x32_bf16", "v_mfma_f32_16x16x4_f32"}, ops
+
+
+def test_no_packed_fp32_arithmetic():
+    """Packed FP32 add/mul/fma are kept out of every kernel."""
+    from moe_layer_routing_amd import _build
+    for f in sorted(os.listdir(CSRC)):
+        if not f.endswith(".hip"):
+            continue
+        r = subprocess.run([_build.HIPCC, *[x for x in _build.FLAGS if x not in ("-shared", "-fPIC")],
+                            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-S",
+                            "--cuda-device-only", os.path.join(CSRC, f), "-o", "-"],
+                           check=True, capture_output=True, text=True)
+        assert not re.search(r"v_pk_(add|mul|fma)_f32", r.stdout), f
