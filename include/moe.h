@@ -163,9 +163,12 @@ moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
 
 /* Everything moe_forward needs. Replay mode iff idx_in != NULL (then w_in is required
  * and w_router/logit_bias/logits/prob_mass are ignored); router mode otherwise.
- * Required: x, w13, w2, out, topk_idx, topk_w, counts, offsets, perm, inv, x_perm, h, y,
+ * Required: x, w13, w2, out, topk_idx, topk_w, counts, offsets, perm, inv, h, y,
  * workspace. Optional (NULL = not produced / not used): logit_bias, logits, prob_mass,
- * token_mult, cu_seqlens + seq_counts, weighted_counts, d_err, prof_events.
+ * token_mult, cu_seqlens + seq_counts, weighted_counts, d_err, prof_events, x_perm.
+ * x_perm NULL: the dispatch gather is fused into the gate/up GEMM, which reads token rows
+ * of x through perm (identical results; x must then be smaller than 4 GiB, else
+ * MOE_E_SHAPE).
  * prof_events: NULL, or three hipEvent_t handles recorded on `stream` before the
  * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing). */
 typedef struct moe_forward_args {

@@ -30,29 +30,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         src[j] = (int64_t)p * d;
         w[j] = (j < k) ? topk_w[t * k + j] : 0.f;
     }
-    for (int c = lane * 4; c < d; c += 256) {
-        float4 v[kMaxK];
+    // two 256-feature chunks per iteration: 2k 16-byte loads in flight per lane
+    for (int c0 = lane * 4; c0 < d; c0 += 512) {
+        float4 v[2][kMaxK];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) v[j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        for (int u = 0; u < 2; ++u) {
+            const int c = min(c0 + 256 * u, d - 4);
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k) {
-                a0 = a0 + w[j] * v[j].x;
-                a1 = a1 + w[j] * v[j].y;
-                a2 = a2 + w[j] * v[j].z;
-                a3 = a3 + w[j] * v[j].w;
-            }
+            for (int j = 0; j < kMaxK; ++j)
+                if (j < k) v[u][j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
         }
-        if constexpr (kBF16) {
-            uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
-            pk.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + t * d + c) = pk;
-        } else {
-            *reinterpret_cast<float4 *>(static_cast<float *>(out) + t * d + c) =
-                make_float4(a0, a1, a2, a3);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = c0 + 256 * u;
+            if (c >= d) break;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k) {
+                    a0 = a0 + w[j] * v[u][j].x;
+                    a1 = a1 + w[j] * v[u][j].y;
+                    a2 = a2 + w[j] * v[u][j].z;
+                    a3 = a3 + w[j] * v[u][j].w;
+                }
+            }
+            if constexpr (kBF16) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+                pk.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + t * d + c) = pk;
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(out) + t * d + c) =
+                    make_float4(a0, a1, a2, a3);
+            }
         }
     }
 }

@@ -68,6 +68,16 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
     }
 }
 
+// Row of the activation matrix that tile row rr reads: rr itself (segment-relative rows of
+// x_perm / h), or, when the dispatch gather is fused, the token perm[p0+rr] / k of x
+// (clamped into [0, gT) so that a corrupted permutation cannot read outside x).
+__device__ __forceinline__ int64_t act_row(const int32_t *gperm, int gk, int64_t gT, int p0,
+                                           int rr) {
+    if (!gperm) return rr;
+    const int64_t t = (int64_t)max(gperm[p0 + rr], 0) / gk;
+    return t < gT ? t : gT - 1;
+}
+
 // kGateUp: out = h[A, I] = round(silu(x w_gate^T) * (x w_up^T)), K = d, N = I,
 //          the weight tile stacks BW/2 gate rows over the matching BW/2 up rows.
 // else:    out = y[A, d] (FP32) = h w2^T, K = I, N = d.
@@ -79,7 +89,8 @@ template <bool kBF16, bool kGateUp, int BW, int BT, int WF, int WT, int PF, int 
 __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
-    const int32_t *__restrict__ tiles, int K, int N, int nft) {
+    const int32_t *__restrict__ tiles, int K, int N, int nft,
+    const int32_t *__restrict__ gperm, int gk, int64_t gT) {
     constexpr int NTHR = 64 * WF * WT;
     constexpr int kRowBytes = SRB;                     // K bytes of one row per stage
     constexpr int kLdsStride = kRowBytes + 16;         // padded LDS row (bank spread)
@@ -116,7 +127,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     const int64_t rows_per_expert = kGateUp ? 2 * (int64_t)N : (int64_t)N;
     const uint32_t krow = (uint32_t)K * kEB;
     const uint8_t *wbase = wgt + (int64_t)e * rows_per_expert * krow;
-    const uint8_t *abase = act + (int64_t)p0 * krow;
+    // activation rows: the tile's segment rows, or (gathered) the token rows perm[p] / k
+    const uint8_t *abase = gperm ? act : act + (int64_t)p0 * krow;
 
     // byte offsets of this thread's staged 16-byte vectors (chunk c of rows r0 + i*RPI)
     const int c = tid % kVecPerRow, r0 = tid / kVecPerRow;
@@ -135,7 +147,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < LT; ++i)
-        to[i] = (uint32_t)min(r0 + i * RPI, nrows - 1) * krow + c * 16;
+        to[i] = (uint32_t)act_row(gperm, gk, gT, p0, min(r0 + i * RPI, nrows - 1)) * krow + c * 16;
 
     u32x4_t rw[PF][LW], rt[PF][LT];
     auto load_global = [&](int kt, auto slot) {
@@ -297,35 +309,6 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     }
 }
 
-// ------------------------------------------------------------------------------------
-// bf16 grouped GEMM fed by direct global->LDS loads (gfx950 global_load_lds_dwordx4).
-//
-// The block stages K in steps of 32 bf16 (64 bytes per row) through an NS-slot LDS ring.
-// Each wave-wide DMA instruction fills one 16-row x 64-byte LDS block (lane l's 16 bytes
-// land at block + 16*l); lanes fetch their row's 16-byte K-chunks in an XOR-swizzled order
-// so that the MFMA fragment reads (16 rows, one chunk each) spread over all LDS banks.
-// Loads run NS-2 stages ahead of the stage whose fragments are being read, and the
-// fragments of stage kt+1 are read while the MFMAs of stage kt run; no register staging.
-// Synchronisation per stage: wait for this wave's DMA of the next stage, one s_barrier.
-// Every output element is the same 16x16x32 MFMA sequence over K in increasing order as in
-// grouped_gemm_kernel, so both kernels produce identical bits.
-__device__ __forceinline__ int chunk_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// One K-stage of DMA for this wave: its NBW 16-row blocks of slot kt % NS.
-template <int NBW, int NW, int NS, int kStageBytes>
-__device__ __forceinline__ void dma_stage(uint8_t *ring, const uint8_t *(&src)[NBW], int kt,
-                                          int wv) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this; it cannot parse the builtin
-    uint8_t *dst = ring + (kt % NS) * kStageBytes;
-    const int64_t ko = (int64_t)kt * 64;
-#pragma unroll
-    for (int i = 0; i < NBW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            src[i] + ko, (__attribute__((address_space(3))) void *)(dst + (wv + i * NW) * 1024), 16,
-            0, 0);
-#endif
-}
-
 // s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 immediate encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -333,13 +316,39 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
-template <bool kGateUp, int BW, int BT, int WF, int WT, int NS, int WPE, bool DB>
+// ------------------------------------------------------------------------------------
+// Same GEMM with 128-byte K stages (64 bf16 per row): every DMA lane group of 8 covers one
+// full 128-byte line of a row, which the global->LDS path moves at about 1.7x the rate of
+// 64-byte halves. A stage is 8-row x 128-byte LDS blocks; lane l of a DMA instruction
+// fetches chunk (l%8) ^ swz(row) of row l/8, so that the 16 rows of an MFMA fragment read
+// their chunk from 16 different bank groups. Two slots: stage kt+1 is in flight while the
+// two 32-deep MFMA K-steps of stage kt run; one wait + one s_barrier per stage.
+__device__ __forceinline__ int chunk_swizzle8(int r) { return (r & 7) ^ (((r >> 3) & 1) << 2); }
+
+template <int NBW, int NW>
+__device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase,
+                                             const uint8_t *abase, const uint32_t (&off)[NBW],
+                                             uint32_t is_act_mask, int kt, int wv) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this; it cannot parse the builtin
+    const uint32_t ko = (uint32_t)kt * 128u;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+        const uint8_t *base = ((is_act_mask >> i) & 1u) ? abase : wbase;
+        __builtin_amdgcn_global_load_lds(
+            base + off[i] + ko,
+            (__attribute__((address_space(3))) void *)(slot + (wv + i * NW) * 1024), 16, 0, 0);
+    }
+#endif
+}
+
+template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE>
 __global__ __launch_bounds__(64 * WF * WT)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
-    const int32_t *__restrict__ tiles, int K, int N, int nft) {
+    const int32_t *__restrict__ tiles, int K, int N, int nft,
+    const int32_t *__restrict__ gperm, int gk, int64_t gT) {
     constexpr int NW = WF * WT;
-    constexpr int NBLK = (BW + BT) / 16;               // 16-row LDS blocks per stage
+    constexpr int NBLK = (BW + BT) / 8;                // 8-row LDS blocks per stage
     constexpr int NBW = NBLK / NW;                     // DMA instructions per wave per stage
     constexpr int kStageBytes = NBLK * 1024;
     constexpr int kFeat = kGateUp ? BW / 2 : BW;
@@ -347,10 +356,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
     constexpr int NFh = kWaveRows / 16;
     constexpr int NF = kGateUp ? 2 * NFh : NFh;
     constexpr int NT = BT / WT / 16;
-    static_assert(NBLK % NW == 0 && NS >= 3 && NFh >= 1 && NT >= 1, "bad tile shape");
-    static_assert(BW % 16 == 0 && (BW / 2) % 16 == 0, "16-row blocks");
+    static_assert(NBLK % NW == 0 && NBW <= 32 && NFh >= 1 && NT >= 1, "bad tile shape");
+    static_assert(BW % 16 == 0 && (BW / 2) % 16 == 0, "16-row fragments");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
 
     const uint32_t nwg = gridDim.x, bid = blockIdx.x;
     const uint32_t xcd = bid & 7u, loc = bid >> 3, per = nwg >> 3, rem = nwg & 7u;
@@ -363,17 +372,18 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
     const int wf = wv % WF, wt = wv / WF;
     const int n0 = ft * kFeat;
     const int64_t rows_per_expert = kGateUp ? 2 * (int64_t)N : (int64_t)N;
-    const int64_t krow = (int64_t)K * 2;
+    const uint32_t krow = (uint32_t)K * 2u;
     const uint8_t *wbase = wgt + (int64_t)e * rows_per_expert * krow;
-    const uint8_t *abase = act + (int64_t)p0 * krow;
+    const uint8_t *abase = gperm ? act : act + (int64_t)p0 * krow;
 
-    // DMA sources: this lane's row in each of the wave's blocks, at its swizzled chunk
-    const int r4 = lane >> 2;
-    const int chunk = (lane & 3) ^ chunk_swizzle(r4);
-    const uint8_t *src[NBW];
+    // DMA sources (byte offsets from wbase / abase) of this lane's row in each block
+    const int rb = lane >> 3;
+    uint32_t off[NBW];
+    uint32_t is_act = 0;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        const int row = (wv + i * NW) * 16 + r4;
+        const int row = (wv + i * NW) * 8 + rb;
+        const int chunk = (lane & 7) ^ chunk_swizzle8(row);
         if (row < BW) {
             int grow;
             if (kGateUp) {
@@ -382,16 +392,19 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
             } else {
                 grow = min(n0 + row, N - 1);
             }
-            src[i] = wbase + (int64_t)grow * krow + chunk * 16;
+            off[i] = (uint32_t)grow * krow + chunk * 16;
         } else {
-            src[i] = abase + (int64_t)min(row - BW, nrows - 1) * krow + chunk * 16;
+            off[i] = (uint32_t)act_row(gperm, gk, gT, p0, min(row - BW, nrows - 1)) * krow +
+                     chunk * 16;
+            is_act |= 1u << i;
         }
     }
-#define MOE_ISSUE(kt_) dma_stage<NBW, NW, NS, kStageBytes>(ring, src, (kt_), wv)
 
-    // fragment read offsets inside a stage
+    // fragment read offsets: row r16 of a 16-row fragment, K-chunk kk*4 + g4 of the stage
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int lane_off = r16 * 64 + ((g4 ^ chunk_swizzle(r16)) << 4);
+    const int lane_off0 = (r16 >> 3) * 1024 + (r16 & 7) * 128 + ((g4 ^ chunk_swizzle8(r16)) << 4);
+    const int lane_off1 = (r16 >> 3) * 1024 + (r16 & 7) * 128 +
+                          (((4 + g4) ^ chunk_swizzle8(r16)) << 4);
     auto wrow = [&](int f) {
         if (kGateUp) return (f < NFh ? 0 : BW / 2) + wf * kWaveRows + (f % NFh) * 16;
         return wf * kWaveRows + f * 16;
@@ -404,16 +417,14 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto read_frags = [&](int kt, bf16x8_t (&a)[NF], bf16x8_t (&b)[NT]) {
-        const uint8_t *sb = ring + (kt % NS) * kStageBytes + lane_off;
+    auto kstep = [&](const uint8_t *sb) {
+        bf16x8_t a[NF], b[NT];
 #pragma unroll
         for (int f = 0; f < NF; ++f)
-            a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 4) * 1024);
+            a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 3) * 1024);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 4) * 1024);
-    };
-    auto mfmas = [&](const bf16x8_t (&a)[NF], const bf16x8_t (&b)[NT]) {
+            b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -421,60 +432,21 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
                 acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b[t], acc[f][t], 0, 0, 0);
     };
 
-    const int nk = K >> 5;
-    // prologue: stages 0..NS-2 in flight, stage 0 resident
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) MOE_ISSUE(s);
-    if (nk > 1) wait_vm_lgkm0<NBW * (NS - 2)>();
-    else wait_vm_lgkm0<0>();
+    const int nk = K >> 6;
+    dma_stage128<NBW, NW>(ring, wbase, abase, off, is_act, 0, wv);
+    wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
-    bf16x8_t ca[NF], cb[NT];
-    bf16x8_t na[DB ? NF : 1], nb[DB ? NT : 1];
-    read_frags(0, ca, cb);
-
-    // Stage kt+1 becomes readable: own DMA of it done (later stages may still fly), every
-    // LDS read this wave issued has returned, then one barrier for all waves. After it the
-    // slot of stage kt-1 is free and receives stage kt+NS-1.
-    auto advance = [&](int kt) {
-        if (kt + NS - 2 < nk) wait_vm_lgkm0<NBW * (NS - 3)>();
-        else wait_vm_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + NS - 1 < nk) MOE_ISSUE(kt + NS - 1);
-    };
-    if constexpr (DB) {
-        // steady state, unrolled by two so the fragment sets swap roles without copies
-        int kt = 0;
-        for (; kt + 2 < nk; kt += 2) {
-            advance(kt);
-            read_frags(kt + 1, na, nb);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(ca, cb);
-            __builtin_amdgcn_sched_barrier(0);
-            advance(kt + 1);
-            read_frags(kt + 2, ca, cb);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(na, nb);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kt + 1 < nk) {          // two stages left
-            advance(kt);
-            read_frags(kt + 1, na, nb);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(ca, cb);
-            mfmas(na, nb);
-        } else {                    // one stage left
-            mfmas(ca, cb);
-        }
-    } else {
-        // one fragment set: read stage kt, then its MFMAs (another wave on the SIMD covers
-        // the LDS latency)
-        mfmas(ca, cb);
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            advance(kt);
-            read_frags(kt + 1, ca, cb);
-            mfmas(ca, cb);
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t *cur = ring + (kt & 1) * kStageBytes;
+        if (kt + 1 < nk)
+            dma_stage128<NBW, NW>(ring + ((kt + 1) & 1) * kStageBytes, wbase, abase, off, is_act,
+                                  kt + 1, wv);
+        kstep(cur + lane_off0);
+        kstep(cur + lane_off1);
+        if (kt + 1 < nk) {
+            // own DMA of stage kt+1 and own LDS reads of stage kt done; then all waves'
+            wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
         }
     }
 
@@ -514,13 +486,11 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma_kernel(
     }
 }
 
-template <int BW_, int BT_, int WF_, int WT_, int NS_, bool DB_ = true,
-          int WPE_ = WF_ * WT_ / 4>
-struct DmaCfg {
-    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, NS = NS_, WPE = WPE_;
-    static constexpr bool DB = DB_;
+template <int BW_, int BT_, int WF_, int WT_, int WPE_ = WF_ * WT_ / 4>
+struct Dma128Cfg {
+    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, WPE = WPE_;
     static constexpr int kThreads = 64 * WF_ * WT_;
-    static constexpr bool kDma = true;
+    static constexpr bool kDma128 = true;
 };
 
 // Launch shape of one GEMM: block tile and waves. Any shape gives the same bits.
@@ -533,42 +503,48 @@ struct Cfg {
 };
 
 template <class C, class = void>
-struct IsDma : std::false_type {};
+struct IsDma128 : std::false_type {};
 template <class C>
-struct IsDma<C, std::void_t<decltype(C::kDma)>> : std::true_type {};
+struct IsDma128<C, std::void_t<decltype(C::kDma128)>> : std::true_type {};
 
+
+// gperm != nullptr: activation rows are gathered (token perm[p] / gk of act, gT rows).
 template <bool kBF16, bool kGateUp, class C>
 hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_t *tiles,
-                       int64_t mtiles, int K, int N, hipStream_t s) {
+                       int64_t mtiles, int K, int N, hipStream_t s,
+                       const int32_t *gperm = nullptr, int gk = 1, int64_t gT = 0) {
     constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
     const int nft = (N + feat - 1) / feat;
-    if constexpr (IsDma<C>::value && kBF16) {
-        grouped_gemm_dma_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::NS, C::WPE, C::DB>
+    if constexpr (IsDma128<C>::value && kBF16) {
+        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
-                K, N, nft);
-    } else if constexpr (!IsDma<C>::value) {
-        grouped_gemm_kernel<kBF16, kGateUp, C::BW, C::BT, C::WF, C::WT, C::PF, C::SRB, C::WPE>
-            <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
-                static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
-                K, N, nft);
-    } else {
+                K, N, nft, gperm, gk, gT);
+    } else if constexpr (IsDma128<C>::value) {
         // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
         // same token tiles
         using F = Cfg<256, C::BT, 2, 2, 1, 64, 1>;
-        return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s);
+        return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s, gperm, gk,
+                                              gT);
+    } else {
+        grouped_gemm_kernel<kBF16, kGateUp, C::BW, C::BT, C::WF, C::WT, C::PF, C::SRB, C::WPE>
+            <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
+                static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
+                K, N, nft, gperm, gk, gT);
     }
     return hipGetLastError();
 }
 
+// act13: x_perm (segment rows), or x with gperm = perm (gather fused into the gate/up GEMM)
 template <bool kBF16, class C13, class C2>
-hipError_t run_ffn(const moe_dims &dm, const void *x_perm, const void *w13, const void *w2,
-                   void *h, float *y, const int32_t *tiles, int64_t mtiles, void *const *ev,
-                   hipStream_t s) {
+hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, const void *w13,
+                   const void *w2, void *h, float *y, const int32_t *tiles, int64_t mtiles,
+                   void *const *ev, hipStream_t s) {
     static_assert(C13::BT == C2::BT, "both GEMMs walk the same token tiles");
     if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess)
         return hipErrorInvalidValue;
-    hipError_t e = launch_gemm<kBF16, true, C13>(x_perm, w13, h, tiles, mtiles, dm.d, dm.inter, s);
+    hipError_t e = launch_gemm<kBF16, true, C13>(act13, w13, h, tiles, mtiles, dm.d, dm.inter, s,
+                                                 gperm, dm.k, dm.T);
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess)
         return hipErrorInvalidValue;
@@ -579,40 +555,40 @@ hipError_t run_ffn(const moe_dims &dm, const void *x_perm, const void *w13, cons
     return hipSuccess;
 }
 
-// Prefill-shaped launches: 8 waves (2 per SIMD), 128x64 per wave, 4-slot DMA ring.
-// 128-token tiles stage 512 weight rows (256 output features of gate/up), 256-token tiles
-// stage 256 weight rows; both keep the ring within the 160 KB of LDS.
+// Prefill-shaped launches: 8 waves (2 per SIMD), 128x64 per wave, two 128-byte K stages
+// in LDS. 128-token tiles stage 512 weight rows (256 output features of gate/up), 256-token
+// tiles 256 weight rows; both rings fit the 160 KB of LDS.
 #ifndef MOE_FFN_LARGE_CFG13
-#define MOE_FFN_LARGE_CFG13 DmaCfg<512, 128, 4, 2, 4, false>
-#define MOE_FFN_LARGE_CFG2 DmaCfg<512, 128, 4, 2, 4, false>
+#define MOE_FFN_LARGE_CFG13 Dma128Cfg<512, 128, 4, 2>
+#define MOE_FFN_LARGE_CFG2 Dma128Cfg<512, 128, 4, 2>
 #endif
 #ifndef MOE_FFN_HUGE_CFG13
-#define MOE_FFN_HUGE_CFG13 DmaCfg<256, 256, 2, 4, 4, false>
-#define MOE_FFN_HUGE_CFG2 DmaCfg<256, 256, 2, 4, 4, false>
+#define MOE_FFN_HUGE_CFG13 Dma128Cfg<256, 256, 2, 4>
+#define MOE_FFN_HUGE_CFG2 Dma128Cfg<256, 256, 2, 4>
 #endif
 
 template <bool kBF16>
-hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const void *w13,
-                        const void *w2, void *h, float *y, const int32_t *tiles,
-                        int64_t mtiles, void *const *ev, hipStream_t s) {
+hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const int32_t *gperm,
+                        const void *w13, const void *w2, void *h, float *y,
+                        const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s) {
     switch (bt) {
     case 16: {
         using C = Cfg<128, 16, 4, 1, 1, 128, 3>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 32: {
         using C = Cfg<128, 32, 4, 1, 1, 128, 3>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 64: {
         using C = Cfg<128, 64, 2, 2, 1, 128, 2>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 128:
-        return run_ffn<kBF16, MOE_FFN_LARGE_CFG13, MOE_FFN_LARGE_CFG2>(dm, x_perm, w13, w2, h, y,
+        return run_ffn<kBF16, MOE_FFN_LARGE_CFG13, MOE_FFN_LARGE_CFG2>(dm, x_perm, gperm, w13, w2, h, y,
                                                                        tiles, mtiles, ev, s);
     default:
-        return run_ffn<kBF16, MOE_FFN_HUGE_CFG13, MOE_FFN_HUGE_CFG2>(dm, x_perm, w13, w2, h, y,
+        return run_ffn<kBF16, MOE_FFN_HUGE_CFG13, MOE_FFN_HUGE_CFG2>(dm, x_perm, gperm, w13, w2, h, y,
                                                                      tiles, mtiles, ev, s);
     }
 }
@@ -634,7 +610,8 @@ int64_t max_m_tiles(int64_t A, int E, int tile_m) { return (A + tile_m - 1) / ti
 
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
-                              const Workspace &ws, void *const *prof_events, hipStream_t s) {
+                              const Workspace &ws, void *const *prof_events, hipStream_t s,
+                              const void *x, const int32_t *perm) {
     const int64_t A = dm.T * dm.k;
     const int bt = select_tile_m(dm);
     const int64_t cap = max_m_tiles(A, dm.E, bt);
@@ -646,9 +623,14 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
         return hipGetLastError();
     }
     build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
+    // x_perm == nullptr: the gate/up GEMM gathers token rows of x through perm itself
+    const void *act13 = x_perm ? x_perm : x;
+    const int32_t *gperm = x_perm ? nullptr : perm;
     if (dm.dtype == MOE_BF16)
-        return dispatch_ffn<true>(dm, bt, x_perm, w13, w2, h, y, ws.tiles, cap, prof_events, s);
-    return dispatch_ffn<false>(dm, bt, x_perm, w13, w2, h, y, ws.tiles, cap, prof_events, s);
+        return dispatch_ffn<true>(dm, bt, act13, gperm, w13, w2, h, y, ws.tiles, cap, prof_events,
+                                  s);
+    return dispatch_ffn<false>(dm, bt, act13, gperm, w13, w2, h, y, ws.tiles, cap, prof_events,
+                               s);
 }
 
 }  // namespace moe

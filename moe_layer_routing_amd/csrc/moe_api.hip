@@ -165,8 +165,11 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     const bool replay = a->idx_in != nullptr;
     if (dims->T > 0) {
         MOE_REQUIRE(a->x && a->w13 && a->w2 && a->out && a->topk_idx && a->topk_w && a->perm &&
-                        a->inv && a->x_perm && a->h && a->y,
+                        a->inv && a->h && a->y,
                     MOE_E_NULLPTR);
+        // the fused gather addresses token rows of x with 32-bit byte offsets
+        const int64_t x_bytes = dims->T * (int64_t)dims->d * (dims->dtype == MOE_BF16 ? 2 : 4);
+        if (!a->x_perm) MOE_REQUIRE(x_bytes < (int64_t(1) << 32), MOE_E_SHAPE);
         MOE_REQUIRE(replay ? (a->w_in != nullptr) : (a->w_router != nullptr), MOE_E_NULLPTR);
     }
     MOE_REQUIRE((a->cu_seqlens == nullptr) == (a->seq_counts == nullptr), MOE_E_NULLPTR);
@@ -188,7 +191,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
                        a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
-                           a->prof_events, s);
+                           a->prof_events, s, a->x, a->perm);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s);
     return to_status(e);

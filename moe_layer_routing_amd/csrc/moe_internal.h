@@ -14,7 +14,7 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kMaxE = 256;         // experts per layer supported by the LDS-resident paths
 constexpr int kMaxK = 8;           // experts per token
 constexpr int kPermChunk = 2048;   // flat assignments per permute block (fixed, T-free)
-constexpr int kTopkTokPerBlock = 64;
+constexpr int kTopkTokPerBlock = 16;  // 4 waves x 4 tokens
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -68,9 +68,11 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
                           hipStream_t s);
+// x_perm == nullptr: gather token rows of x through perm inside the gate/up GEMM.
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
-                              const Workspace &ws, void *const *prof_events, hipStream_t s);
+                              const Workspace &ws, void *const *prof_events, hipStream_t s,
+                              const void *x = nullptr, const int32_t *perm = nullptr);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s);
 

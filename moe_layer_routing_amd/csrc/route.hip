@@ -36,23 +36,43 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void *__restric
     const int e_row = min(eb + r, E - 1);
     const int64_t t_row = min<int64_t>(tb + r, T - 1);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // K-steps w, w+4, w+8, ... of this wave, accumulated in that order; the operands of
+    // up to 8 steps are loaded before their MFMAs so that the loads overlap.
+    constexpr int kGroup = 8;
     if constexpr (kBF16) {
         const uint16_t *wp = static_cast<const uint16_t *>(wr_) + (int64_t)e_row * d + g * 8;
         const uint16_t *xp = static_cast<const uint16_t *>(x_) + t_row * d + g * 8;
         const int nsteps = d >> 5;
-#pragma unroll 4
-        for (int s = wave; s < nsteps; s += 4) {
-            bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(wp + s * 32);
-            bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(xp + s * 32);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        for (int s0 = wave; s0 < nsteps; s0 += 4 * kGroup) {
+            bf16x8_t a[kGroup], b[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                const int s = min(s0 + 4 * i, nsteps - 1);
+                a[i] = *reinterpret_cast<const bf16x8_t *>(wp + s * 32);
+                b[i] = *reinterpret_cast<const bf16x8_t *>(xp + s * 32);
+            }
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i)
+                if (s0 + 4 * i < nsteps)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[i], acc, 0, 0, 0);
         }
     } else {
         const float *wp = static_cast<const float *>(wr_) + (int64_t)e_row * d + g;
         const float *xp = static_cast<const float *>(x_) + t_row * d + g;
         const int nsteps = d >> 2;
-#pragma unroll 8
-        for (int s = wave; s < nsteps; s += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wp[s * 4], xp[s * 4], acc, 0, 0, 0);
+        for (int s0 = wave; s0 < nsteps; s0 += 4 * kGroup) {
+            float a[kGroup], b[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                const int s = min(s0 + 4 * i, nsteps - 1);
+                a[i] = wp[s * 4];
+                b[i] = xp[s * 4];
+            }
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i)
+                if (s0 + 4 * i < nsteps)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+        }
     }
     __shared__ float part[4][4][64];
     for (int i = 0; i < 4; ++i) part[wave][i][lane] = acc[i];
@@ -92,6 +112,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+// Wave-wide maximum through DPP lane moves (no LDS round trip): within quads (xor 1, 2),
+// half-rows and rows (mirrors), then across rows (broadcast of lane 15 / lane 31); lane 63
+// ends with the maximum of all 64 lanes, which readlane makes uniform.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t o) { return o > v ? o : v; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Butterfly sum: every lane ends with the same bits (each level adds the same two
 // operands, only commuted), and the tree shape is fixed by the wave width alone.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -101,8 +135,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------- softmax + top-k
-// One wave per token (16 tokens per wave, 4 waves per block). Lane l holds experts
+// One wave per token; a block of 4 waves handles kTopkTokPerBlock tokens, each wave
+// kTopkTokPerBlock/4 of them with all their logits loaded up front. Lane l holds experts
 // l, l+64, l+128, l+192. Every per-token result depends only on that token's E logits.
+constexpr int kTokPerWave = kTopkTokPerBlock / 4;
+
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ q,
                                                          int64_t T, int E, int k,
@@ -111,47 +148,62 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                                                          float *__restrict__ mass_part,
                                                          int32_t *__restrict__ d_err) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * 16;
-    float macc[4] = {0.f, 0.f, 0.f, 0.f};
-    int err = 0;
-    for (int tt = 0; tt < 16; ++tt) {
-        const int64_t t = t0 + tt;
-        if (t >= T) break;
-        const float *lr = logits + t * E;
-        float l[4];
-        uint64_t key[4];
+    const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * kTokPerWave;
+    const int nlv = (E + 63) >> 6;    // logits per lane actually used
+    float lv[kTokPerWave][4];
+#pragma unroll
+    for (int tt = 0; tt < kTokPerWave; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
-            const bool valid = e < E;
-            l[i] = valid ? lr[e] : 0.f;
-            if (valid && !__builtin_isfinite(l[i])) err |= MOE_DERR_NONFINITE;
-            key[i] = valid ? ((static_cast<uint64_t>(ordered_bits(l[i])) << 32) |
-                              static_cast<uint32_t>(~e))
-                           : 0ull;
+            const int64_t t = t0 + tt;
+            lv[tt][i] = (t < T && e < E) ? logits[t * E + e] : 0.f;
         }
+    float macc[4] = {0.f, 0.f, 0.f, 0.f};
+    int err = 0;
+#pragma unroll
+    for (int tt = 0; tt < kTokPerWave; ++tt) {
+        const int64_t t = t0 + tt;
+        if (t >= T) break;
+        uint32_t hi[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            valid[i] = e < E;
+            if (valid[i] && !__builtin_isfinite(lv[tt][i])) err |= MOE_DERR_NONFINITE;
+            hi[i] = valid[i] ? ordered_bits(lv[tt][i]) : 0u;
+        }
+        // k rounds: the largest remaining logit (wave max of its ordered bits), ties to
+        // the lowest expert id (lowest lane of the lowest 64-expert group holding it)
         uint32_t taken = 0;
         int sel[kMaxK];
-        uint64_t top_key = 0;
+        uint32_t top_hi = 0;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             sel[j] = 0;
             if (j < k) {
-                uint64_t best = 0;
+                uint32_t best = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (!((taken >> i) & 1u) && key[i] > best) best = key[i];
-                best = wave_max_u64(best);
-                const int we = static_cast<int>(~static_cast<uint32_t>(best));
+                    if (i < nlv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
+                const uint32_t m = wave_max_u32(best);
+                int we = -1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t mask =
+                        __ballot(i < nlv && valid[i] && !((taken >> i) & 1u) && hi[i] == m);
+                    if (we < 0 && mask) we = 64 * i + (int)__builtin_ctzll(mask);
+                }
                 sel[j] = we;
-                if (j == 0) top_key = best;
+                if (j == 0) top_hi = m;
                 if ((we & 63) == lane) taken |= 1u << (we >> 6);
             }
         }
-        const float m = from_ordered_bits(static_cast<uint32_t>(top_key >> 32));
+        const float mx = from_ordered_bits(top_hi);
         float z[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = (lane + 64 * i < E) ? expf(l[i] - m) : 0.f;
+        for (int i = 0; i < 4; ++i) z[i] = valid[i] ? expf(lv[tt][i] - mx) : 0.f;
         float zl = z[0] + z[1];
         zl = zl + z[2];
         zl = zl + z[3];
@@ -173,20 +225,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                 ps[j] = __shfl(mine, sel[j] & 63);
             }
         }
-        float s = ps[0];
+        float sum = ps[0];
 #pragma unroll
         for (int j = 1; j < kMaxK; ++j)
-            if (j < k) s = s + ps[j];
+            if (j < k) sum = sum + ps[j];
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             if (j < k && lane == j) {
                 topk_idx[t * k + j] = sel[j];
-                topk_w[t * k + j] = ps[j] / s;
+                topk_w[t * k + j] = ps[j] / sum;
             }
         }
     }
     if (__ballot(err != 0)) {
-        // one lane reports the OR of the wave's bits
         int e_all = err;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) e_all |= __shfl_xor(e_all, off);
@@ -210,15 +261,24 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
     }
 }
 
-// prob_mass[e] = per-block partials added in block order (fixed for a given T).
+// prob_mass[e]: one block per expert; thread i adds the partials of blocks i, i+256, ...
+// in order, then a fixed binary tree over the 256 threads. The order depends only on the
+// number of partials (i.e. on T).
 __global__ __launch_bounds__(256) void mass_reduce_kernel(const float *__restrict__ part,
                                                           int64_t nblk, int E,
                                                           float *__restrict__ mass) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
+    __shared__ float red[256];
+    const int e = blockIdx.x;
     float acc = 0.f;
-    for (int64_t b = 0; b < nblk; ++b) acc = acc + part[b * E + e];
-    mass[e] = acc;
+    for (int64_t b = threadIdx.x; b < nblk; b += 256) acc = acc + part[b * E + e];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int s = 128; s >= 1; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) mass[e] = red[0];
 }
 
 // ------------------------------------------------------------------------ replay
@@ -272,11 +332,9 @@ hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
             logits, token_mult, T, E, dm.k, topk_idx, topk_w, prob_mass ? mass_part : nullptr,
             d_err);
         if (prob_mass)
-            mass_reduce_kernel<<<dim3((E + 255) / 256), dim3(256), 0, s>>>(mass_part, tblk, E,
-                                                                          prob_mass);
+            mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
     } else if (prob_mass) {
-        mass_reduce_kernel<<<dim3((E + 255) / 256), dim3(256), 0, s>>>(mass_part, 0, E,
-                                                                      prob_mass);
+        mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, 0, E, prob_mass);
     }
     return hipGetLastError();
 }

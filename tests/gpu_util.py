@@ -53,8 +53,9 @@ def upload(L, device="cuda"):
                 token_mult=dev(L.token_mult, device), cu_seqlens=dev(L.cu_seqlens, device))
 
 
-def run_forward(L, inputs=None, tile_m=0, device="cuda", stats=True):
-    """moe_forward on layer L; returns (buffers dict, dims)."""
+def run_forward(L, inputs=None, tile_m=0, device="cuda", stats=True, fused_gather=False):
+    """moe_forward on layer L; returns (buffers dict, dims). fused_gather: pass no x_perm,
+    so that the gate/up GEMM gathers token rows itself."""
     dims = dims_of(L, tile_m)
     inp = inputs if inputs is not None else upload(L, device)
     S = 0 if (L.cu_seqlens is None or not stats) else len(L.cu_seqlens) - 1
@@ -72,6 +73,8 @@ def run_forward(L, inputs=None, tile_m=0, device="cuda", stats=True):
         b["token_mult"] = inp["token_mult"]
         if S:
             b["cu_seqlens"] = inp["cu_seqlens"]
+    if fused_gather:
+        del b["x_perm"]
     ws = M.alloc_workspace(dims, device)
     M.forward(dims, b, ws)
     torch.cuda.synchronize()

@@ -75,8 +75,13 @@ def test_full_config(cfg):
     L = W.make_config(cfg)
     L.token_mult = W.token_multiplicities(L.T, L.seed)
     _print("running", cfg, L.T, L.d, L.E, L.k, L.I)
-    b, dims = run_forward(L)
+    inp = upload(L)
+    b, dims = run_forward(L, inp)
     _check_full(L, b)
+    # the launch the benchmark times (gather fused into the gate/up GEMM): same bytes
+    f, _ = run_forward(L, inp, fused_gather=True)
+    for n in ("topk_idx", "topk_w", "perm", "inv", "h", "y", "out", "counts", "offsets"):
+        assert host(f[n]).tobytes() == host(b[n]).tobytes(), n
 
 
 def test_c1_full_exact_oracle():

@@ -274,6 +274,20 @@ def test_tile_m_invariance(case):
             assert host(b[n]).tobytes() == host(base[n]).tobytes(), (tm, n)
 
 
+@pytest.mark.parametrize("case", [FWD_CASES[0], FWD_CASES[1], FWD_CASES[2], FWD_CASES[3],
+                                  FWD_CASES[7]], ids=lambda c: c["name"])
+def test_fused_gather_identical(case):
+    """moe_forward without x_perm (gather fused into the gate/up GEMM) gives the same bytes
+    as with the materialised x_perm, for every tile height."""
+    L = _make(case)
+    inp = upload(L)
+    ref, _ = run_forward(L, inp)
+    for tm in (0, 16, 64, 128, 256):
+        b, _ = run_forward(L, inp, tile_m=tm, fused_gather=True)
+        for n in ("topk_idx", "topk_w", "perm", "inv", "h", "y", "out"):
+            assert host(b[n]).tobytes() == host(ref[n]).tobytes(), (tm, n)
+
+
 def test_run_twice_identical():
     L = _make(FWD_CASES[3])
     inp = upload(L)

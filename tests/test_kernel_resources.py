@@ -35,7 +35,7 @@ def _kernels(asm):
 def test_dma_gemm_kernels_have_no_scratch(gemm_asm):
     found = 0
     for name, b in _kernels(gemm_asm):
-        if "grouped_gemm_dma_kernel" not in name:
+        if "grouped_gemm_dma" not in name:
             continue
         found += 1
         priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", b).group(1))

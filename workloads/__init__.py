@@ -217,6 +217,8 @@ def make_layer(T: int, d: int, E: int, k: int, I: int, dtype: str = "bf16",
     """Build one layer's inputs. ``mode='router'`` makes a router weight (and optional
     Zipf bias); ``mode='replay'`` makes replay ids/weights (``replay`` in
     {'dirichlet', 'hot', 'uniform'})."""
+    if not (1 <= k <= E):
+        raise ValueError(f"need 1 <= k <= E (k={k}, E={E})")
     std = 1.0 / math.sqrt(d)
     x = _normal(seed, TID_X, (T, d), 1.0, dtype, chunks=max(1, min(64, T // 256)))
     if weights:
