@@ -35,6 +35,8 @@ WORKLOADS = {
     "c3": "packed RL microbatch: T=16384 tokens in lognormal-length sequences, d=4096, E=128, "
           "top-8, inter=1536, bf16, routing replay with per-sequence Dirichlet demand",
     "c4": "heavily imbalanced replay: T=32768, d=2048, E=256, top-8, inter=768, bf16",
+    "c5": "decode-shaped bf16 MoE layer: T = 1..64 tokens, d=4096, E=128, top-8, SwiGLU "
+          "inter=1536, router logits (memory-bound)",
 }
 
 
@@ -112,6 +114,70 @@ def upload(L, dev):
                                            "w13", "w2", "token_mult", "cu_seqlens")}
 
 
+def decode_sweep(args):
+    """Decode-shaped layer: one timed moe_forward per batch size T, each after a 512 MB
+    scrub write so that the expert weights come from HBM, reported in tokens/s and in
+    effective HBM GB/s = algorithmic bytes / time, where the algorithmic bytes are the
+    active experts' w13 and w2 (read once), the router weights, x and out, and the
+    routing outputs."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = W.make_config("c5")
+    inp = upload(L, dev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+    Ts = [1, 2, 4, 8, 16, 32, 64]
+    rows = []
+    for T in Ts:
+        dims = M.make_dims(T, L.d, L.E, L.k, L.I, M.MOE_BF16, args.tile_m)
+        b = M.alloc_forward_buffers(dims, dev, router=True)
+        del b["x_perm"]
+        b.update(x=inp["x"][:T].contiguous(), w_router=inp["w_router"], w13=inp["w13"],
+                 w2=inp["w2"])
+        ws = M.alloc_workspace(dims, dev)
+        for _ in range(args.warmup):
+            M.forward(dims, b, ws)
+        times = []
+        for _ in range(args.steps):
+            scrub.fill_(1)
+            ev = hip.create(2)
+            hip.record(ev[0], stream.cuda_stream)
+            M.forward(dims, b, ws)
+            hip.record(ev[1], stream.cuda_stream)
+            torch.cuda.synchronize()
+            times.append(hip.ms(ev[0], ev[1]))
+            hip.destroy(ev)
+        assert int(b["d_err"].item()) == 0
+        t_ms = float(np.median(times))
+        active = int((b["counts"] > 0).sum().item())
+        nbytes = (active * 3 * L.d * L.I * 2 + L.E * L.d * 2 + 2 * T * L.d * 2 + 8 * T * L.k)
+        rows.append({"T": T, "ms": round(t_ms, 4), "tokens_per_s": round(T / (t_ms * 1e-3), 1),
+                     "active_experts": active, "hbm_gbs": round(nbytes / (t_ms * 1e-3) / 1e9, 1)})
+    best = max(rows, key=lambda r: r["hbm_gbs"])
+    rec = {
+        "metric": METRIC + " (decode-shaped layer, HBM GB/s)",
+        "value": rows[-1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rows[-1]["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS["c5"], "name": "c5", "d": L.d, "E": L.E, "k": L.k,
+                   "inter": L.I, "mode": "router", "scrub_mb": 512},
+        "roofline": {"kernel": "whole layer (weights stream)", "bound": "hbm",
+                     "achieved": best["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(best["hbm_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "at_T": best["T"]},
+        "sweep": rows,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +194,10 @@ def main():
               "(expert-parallel sharding is a design note only); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.config == "c5":
+        decode_sweep(args)
+        return
 
     import torch
 

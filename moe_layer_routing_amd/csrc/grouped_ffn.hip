@@ -78,6 +78,23 @@ __device__ __forceinline__ int64_t act_row(const int32_t *gperm, int gk, int64_t
     return t < gT ? t : gT - 1;
 }
 
+// Block -> (token tile, feature tile). The grid is sized for the most tiles any routing
+// can produce, but only ntiles*nft blocks have work; the hardware deals consecutive block
+// ids round-robin over the 8 XCDs, so the live blocks are ids 0..live-1 and the rest leave
+// at once. Among the live ids, each XCD gets one contiguous range of logical tiles in
+// (token tile, feature tile) order, so blocks that share a token slice or an expert's
+// weights share that XCD's L2. Renumbering over the live count (not the grid) keeps all 8
+// XCDs busy when few tiles are live (decode) and when padding leaves the grid's tail empty.
+__device__ __forceinline__ bool block_tile(int ntiles, int nft, int &mt, int &ft) {
+    const uint32_t live = (uint32_t)ntiles * (uint32_t)nft, bid = blockIdx.x;
+    if (bid >= live) return false;
+    const uint32_t xcd = bid & 7u, loc = bid >> 3, per = live >> 3, rem = live & 7u;
+    const uint32_t L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+    mt = (int)(L / (uint32_t)nft);
+    ft = (int)(L % (uint32_t)nft);
+    return true;
+}
+
 // kGateUp: out = h[A, I] = round(silu(x w_gate^T) * (x w_up^T)), K = d, N = I,
 //          the weight tile stacks BW/2 gate rows over the matching BW/2 up rows.
 // else:    out = y[A, d] (FP32) = h w2^T, K = I, N = d.
@@ -111,14 +128,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BW + BT) * kLdsStride];
 
-    // XCD-aware order: the hardware deals consecutive block ids round-robin over the 8
-    // XCDs; renumber so each XCD gets one contiguous range of logical tiles (tiles that
-    // share a token slice or an expert's weights then share that XCD's L2).
-    const uint32_t nwg = gridDim.x, bid = blockIdx.x;
-    const uint32_t xcd = bid & 7u, loc = bid >> 3, per = nwg >> 3, rem = nwg & 7u;
-    const uint32_t L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
-    const int mt = (int)(L / (uint32_t)nft), ft = (int)(L % (uint32_t)nft);
-    if (mt >= tiles[0]) return;
+    int mt, ft;
+    if (!block_tile(tiles[0], nft, mt, ft)) return;
     const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -341,7 +352,7 @@ __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase
 #endif
 }
 
-template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE>
+template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS>
 __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
@@ -358,14 +369,12 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     constexpr int NT = BT / WT / 16;
     static_assert(NBLK % NW == 0 && NBW <= 32 && NFh >= 1 && NT >= 1, "bad tile shape");
     static_assert(BW % 16 == 0 && (BW / 2) % 16 == 0, "16-row fragments");
+    static_assert(NS >= 2 && NBW * (NS - 2) < 64, "ring depth");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStageBytes];
 
-    const uint32_t nwg = gridDim.x, bid = blockIdx.x;
-    const uint32_t xcd = bid & 7u, loc = bid >> 3, per = nwg >> 3, rem = nwg & 7u;
-    const uint32_t L = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
-    const int mt = (int)(L / (uint32_t)nft), ft = (int)(L % (uint32_t)nft);
-    if (mt >= tiles[0]) return;
+    int mt, ft;
+    if (!block_tile(tiles[0], nft, mt, ft)) return;
     const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -432,20 +441,28 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
                 acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b[t], acc[f][t], 0, 0, 0);
     };
 
+    // NS-slot ring: stages kt+1 .. kt+NS-1 are in flight while stage kt is computed. At
+    // iteration kt (after the barrier that made stage kt resident) stage kt+NS-1 goes into
+    // the slot stage kt-1 has left; before the next barrier each wave waits for its own DMA
+    // of stage kt+1 (the NS-2 newer stages may stay in flight) and its own LDS reads.
     const int nk = K >> 6;
-    dma_stage128<NBW, NW>(ring, wbase, abase, off, is_act, 0, wv);
-    wait_vm_lgkm0<0>();
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nk)
+            dma_stage128<NBW, NW>(ring + st * kStageBytes, wbase, abase, off, is_act, st, wv);
+    if (NS - 2 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
+    else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     for (int kt = 0; kt < nk; ++kt) {
-        uint8_t *cur = ring + (kt & 1) * kStageBytes;
-        if (kt + 1 < nk)
-            dma_stage128<NBW, NW>(ring + ((kt + 1) & 1) * kStageBytes, wbase, abase, off, is_act,
-                                  kt + 1, wv);
+        uint8_t *cur = ring + (kt % NS) * kStageBytes;
+        if (kt + NS - 1 < nk)
+            dma_stage128<NBW, NW>(ring + ((kt + NS - 1) % NS) * kStageBytes, wbase, abase, off,
+                                  is_act, kt + NS - 1, wv);
         kstep(cur + lane_off0);
         kstep(cur + lane_off1);
         if (kt + 1 < nk) {
-            // own DMA of stage kt+1 and own LDS reads of stage kt done; then all waves'
-            wait_vm_lgkm0<0>();
+            if (kt + NS - 1 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
+            else wait_vm_lgkm0<0>();
             __builtin_amdgcn_s_barrier();
         }
     }
@@ -486,9 +503,9 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     }
 }
 
-template <int BW_, int BT_, int WF_, int WT_, int WPE_ = WF_ * WT_ / 4>
+template <int BW_, int BT_, int WF_, int WT_, int NS_ = 2, int WPE_ = (WF_ * WT_ + 3) / 4>
 struct Dma128Cfg {
-    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, WPE = WPE_;
+    static constexpr int BW = BW_, BT = BT_, WF = WF_, WT = WT_, WPE = WPE_, NS = NS_;
     static constexpr int kThreads = 64 * WF_ * WT_;
     static constexpr bool kDma128 = true;
 };
@@ -516,14 +533,17 @@ hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_
     constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
     const int nft = (N + feat - 1) / feat;
     if constexpr (IsDma128<C>::value && kBF16) {
-        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE>
+        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE, C::NS>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
                 K, N, nft, gperm, gk, gT);
     } else if constexpr (IsDma128<C>::value) {
         // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
         // same token tiles
-        using F = Cfg<256, C::BT, 2, 2, 1, 64, 1>;
+        using F = typename std::conditional<
+            (C::BT <= 32), Cfg<128, C::BT, 4, 1, 1, 128, 3>,
+            typename std::conditional<(C::BT == 64), Cfg<128, 64, 2, 2, 1, 128, 2>,
+                                      Cfg<256, C::BT, 2, 2, 1, 64, 1>>::type>::type;
         return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s, gperm, gk,
                                               gT);
     } else {
@@ -571,17 +591,19 @@ template <bool kBF16>
 hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const int32_t *gperm,
                         const void *w13, const void *w2, void *h, float *y,
                         const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s) {
+    // Decode-shaped launches stream the weights: narrow 64-row weight slices (many blocks per
+    // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block.
     switch (bt) {
     case 16: {
-        using C = Cfg<128, 16, 4, 1, 1, 128, 3>;
+        using C = Dma128Cfg<64, 16, 2, 1, 6>;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 32: {
-        using C = Cfg<128, 32, 4, 1, 1, 128, 3>;
+        using C = Dma128Cfg<64, 32, 2, 1, 6>;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 64: {
-        using C = Cfg<128, 64, 2, 2, 1, 128, 2>;
+        using C = Dma128Cfg<128, 64, 2, 2, 4>;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
     }
     case 128:
