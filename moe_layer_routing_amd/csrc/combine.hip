@@ -11,7 +11,12 @@
 namespace moe {
 namespace {
 
-// One wave per token; lane l handles the 4 consecutive features 4*l + 256*i.
+// One wave per (token, 512-feature slice); lane l handles features s*512 + 4*l and
+// s*512 + 256 + 4*l. Slicing only spreads the rows over more waves (every output feature
+// is the same slot-order sum whichever wave computes it), so decode-sized batches still
+// fill the chip.
+constexpr int kSlice = 512;
+
 template <bool kBF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const int32_t *__restrict__ inv,
@@ -19,8 +24,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       int64_t T, int k, int d, int64_t A,
                                                       void *__restrict__ out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    const int nslice = (d + kSlice - 1) / kSlice;
+    const int64_t W = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t t = W / nslice;
     if (t >= T) return;
+    const int c0 = (int)(W % nslice) * kSlice + lane * 4;
     int64_t src[kMaxK];
     float w[kMaxK];
 #pragma unroll
@@ -30,8 +38,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         src[j] = (int64_t)p * d;
         w[j] = (j < k) ? topk_w[t * k + j] : 0.f;
     }
-    // two 256-feature chunks per iteration: 2k 16-byte loads in flight per lane
-    for (int c0 = lane * 4; c0 < d; c0 += 512) {
+    // two 256-feature chunks: 2k 16-byte loads in flight per lane
+    {
         float4 v[2][kMaxK];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -72,7 +80,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s) {
     if (dm.T > 0) {
-        const dim3 grid((unsigned)((dm.T + 3) / 4));
+        const int64_t waves = dm.T * ((dm.d + kSlice - 1) / kSlice);
+        const dim3 grid((unsigned)((waves + 3) / 4));
         const int64_t A = dm.T * dm.k;
         if (dm.dtype == MOE_BF16)
             combine_kernel<true><<<grid, dim3(256), 0, s>>>(y, inv, topk_w, dm.T, dm.k, dm.d,

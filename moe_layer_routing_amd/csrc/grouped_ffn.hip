@@ -633,7 +633,7 @@ int64_t max_m_tiles(int64_t A, int E, int tile_m) { return (A + tile_m - 1) / ti
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
                               const Workspace &ws, void *const *prof_events, hipStream_t s,
-                              const void *x, const int32_t *perm) {
+                              const void *x, const int32_t *perm, bool tiles_ready) {
     const int64_t A = dm.T * dm.k;
     const int bt = select_tile_m(dm);
     const int64_t cap = max_m_tiles(A, dm.E, bt);
@@ -644,7 +644,8 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                     return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
+    if (!tiles_ready)
+        build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
     // x_perm == nullptr: the gate/up GEMM gathers token rows of x through perm itself
     const void *act13 = x_perm ? x_perm : x;
     const int32_t *gperm = x_perm ? nullptr : perm;

@@ -179,6 +179,26 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     const Workspace ws = carve_workspace(*dims, a->workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (dims->T >= 1 && dims->T <= kSmallT && !a->seq_counts) {
+        // small batch: logits, then the whole routing tail (and the tile list) in one block
+        float *logits = a->logits ? a->logits : ws.logits;
+        if (!replay) {
+            e = launch_router_logits(*dims, a->x, a->w_router, a->logit_bias, logits, s);
+            if (e != hipSuccess) return MOE_E_LAUNCH;
+        }
+        e = launch_small_tail(*dims, logits, a->token_mult, a->idx_in, a->w_in, a->topk_idx,
+                              a->topk_w, a->prob_mass, a->counts, a->offsets, a->perm, a->inv,
+                              a->weighted_counts, ws.tiles, a->d_err, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        if (a->x_perm) {
+            e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);
+            if (e != hipSuccess) return MOE_E_LAUNCH;
+        }
+        e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
+                               a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        return to_status(launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s));
+    }
     if (replay)
         e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
     else

@@ -15,6 +15,7 @@ constexpr int kMaxE = 256;         // experts per layer supported by the LDS-res
 constexpr int kMaxK = 8;           // experts per token
 constexpr int kPermChunk = 2048;   // flat assignments per permute block (fixed, T-free)
 constexpr int kTopkTokPerBlock = 16;  // 4 waves x 4 tokens
+constexpr int kSmallT = 64;           // largest batch the single-block routing tail takes
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -34,6 +35,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // Error word update: one atomic OR, taken only when a check failed.
 __device__ __forceinline__ void raise_err(int32_t *d_err, int32_t bits) {
     if (d_err && bits) atomicOr(d_err, bits);
+}
+
+// Lanes of the wave whose 9-bit key equals this lane's, found with one ballot per key bit.
+__device__ __forceinline__ uint64_t wave_match9(uint32_t key) {
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+        const bool b = (key >> bit) & 1u;
+        const uint64_t m = __ballot(b);
+        peers &= b ? m : ~m;
+    }
+    return peers;
+}
+
+// Inclusive prefix sum over the 64 lanes (integers: exact in any order).
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -72,10 +96,28 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
                               const Workspace &ws, void *const *prof_events, hipStream_t s,
-                              const void *x = nullptr, const int32_t *perm = nullptr);
+                              const void *x = nullptr, const int32_t *perm = nullptr,
+                              bool tiles_ready = false);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s);
 
 int select_tile_m(const moe_dims &dm);
+
+// Router logits only (the first step of launch_route).
+hipError_t launch_router_logits(const moe_dims &dm, const void *x, const void *w_router,
+                                const float *bias, float *logits, hipStream_t s);
+// Token-major row gather x -> x_perm through inv (part of launch_permute).
+hipError_t launch_gather(const moe_dims &dm, const void *x, const int32_t *inv, void *x_perm,
+                         hipStream_t s);
+// Routing tail of a small batch (1 <= T <= kSmallT) in one block: top-k from logits (or,
+// with idx_in, replay validation), probability mass, counts, offsets, weighted counts,
+// perm / inv, and the token-tile list for tile height select_tile_m(dm). Every output is
+// bitwise the one the multi-kernel steps produce for the same T.
+hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
+                             const int32_t *idx_in, const float *w_in, int32_t *topk_idx,
+                             float *topk_w, float *prob_mass, int32_t *counts,
+                             int32_t *offsets, int32_t *perm, int32_t *inv,
+                             int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
+                             hipStream_t s);
 
 }  // namespace moe

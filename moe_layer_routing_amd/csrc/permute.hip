@@ -129,13 +129,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
         const int e0 = a < A ? idx[a] : -1;
         const bool valid = e0 >= 0 && e0 < E;
         const uint32_t key = valid ? (uint32_t)e0 : 0x1ffu;  // 9 bits; invalid never matches
-        uint64_t peers = ~0ull;
-#pragma unroll
-        for (int bit = 0; bit < 9; ++bit) {
-            const bool b = (key >> bit) & 1u;
-            const uint64_t m = __ballot(b);
-            peers &= b ? m : ~m;
-        }
+        const uint64_t peers = wave_match9(key);
         if (valid) {
             const int32_t before = __popcll(peers & lt_mask);
             const int32_t pos = cur[wave][e0] + before;
@@ -235,6 +229,17 @@ __global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict
 
 }  // namespace
 
+hipError_t launch_gather(const moe_dims &dm, const void *x, const int32_t *inv, void *x_perm,
+                         hipStream_t s) {
+    if (dm.T > 0) {
+        const int64_t row_bytes = (int64_t)dm.d * (dm.dtype == MOE_BF16 ? 2 : 4);
+        gather_kernel<16><<<dim3((unsigned)((dm.T + 3) / 4)), dim3(256), 0, s>>>(
+            static_cast<const uint8_t *>(x), dm.T, dm.k, row_bytes, inv, dm.T * dm.k,
+            static_cast<uint8_t *>(x_perm));
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const void *x,
                           void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
@@ -254,12 +259,7 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
     if (nchunks > 0)
         scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
                                                                      ws.blk_hist, perm, inv);
-    if (x_perm && T > 0) {
-        const int64_t row_bytes = (int64_t)dm.d * (dm.dtype == MOE_BF16 ? 2 : 4);
-        gather_kernel<16><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(
-            static_cast<const uint8_t *>(x), T, k, row_bytes, inv, A,
-            static_cast<uint8_t *>(x_perm));
-    }
+    if (x_perm) launch_gather(dm, x, inv, x_perm, s);
     if (seq_counts && num_seqs > 0) {
         const int64_t n = (int64_t)num_seqs * E;
         fill_i32_kernel<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256),

@@ -1,0 +1,213 @@
+// route_tail.hip -- the routing tail of a small batch (1 <= T <= kSmallT) in one block.
+//
+// Decode-sized batches spend most of their routing time in kernel boundaries: every step
+// of the multi-kernel path (top-k, probability-mass reduction, histogram, scan, stable
+// scatter, tile list) is a launch plus a memory round trip for a few hundred bytes. This
+// kernel runs those steps back to back in one 1024-thread block, with the ids, counts and
+// offsets kept in LDS. It computes the same functions as the multi-kernel path, in the
+// same floating-point order, so each output is bitwise the one that path gives for the
+// same T:
+//   * top-k: wave w routes tokens 4w .. 4w+3 with the routine the multi-block kernel uses
+//     ("0 train-infer mismatch for Open-weight MoE RL in Open-source code", "The router:
+//     matching expert ids and weights"); replay ("Total Router Recall") is validated and
+//     passed through;
+//   * probability mass ("HARTS ...", eq. (20)): waves 4b .. 4b+3 form the 16-token group
+//     b of the multi-block kernel; group partials are ((m0 + m1) + m2) + m3 and the groups
+//     (at most four) are added as the 256-thread reduction tree adds them,
+//     (P0 + P2) + (P1 + P3), absent groups being exact zeros;
+//   * permutation ("RoutePack ...", Sec. 2.1): the stable counting sort by expert, which
+//     has one result; wave w ranks the flat assignments [64w, 64w + 64);
+//   * token tiles: ceil(count_e / bt) tiles per expert in expert order.
+#include "route_dev.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTailWaves = 16;
+constexpr int kTailTokPerWave = kTopkTokPerBlock / 4;
+constexpr int kTailMaxA = kSmallT * kMaxK;
+static_assert(kTailWaves * kTailTokPerWave == kSmallT, "one wave per 4 tokens");
+static_assert(kTailMaxA / kWave <= kTailWaves, "one wave per 64 assignments");
+
+template <bool kReplay>
+__global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ q,
+    const int32_t *__restrict__ idx_in, const float *__restrict__ w_in, int T, int E, int k,
+    int bt, int cap, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    float *__restrict__ prob_mass, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int64_t *__restrict__ weighted_counts, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ d_err) {
+    __shared__ int32_t ids[kTailMaxA];
+    __shared__ int32_t wstart[kTailMaxA / kWave][kMaxE];  // per-wave counts -> run starts
+    __shared__ int32_t eoff[kMaxE + 1];                    // counts -> exclusive offsets
+    __shared__ int32_t toff[kMaxE + 1];                    // tile starts
+    __shared__ unsigned long long wsum[kMaxE];
+    __shared__ float mp[kTailWaves][kMaxE];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int A = T * k;
+    for (int i = tid; i < (kTailMaxA / kWave) * kMaxE; i += 64 * kTailWaves)
+        (&wstart[0][0])[i] = 0;
+    for (int i = tid; i < kMaxE; i += 64 * kTailWaves) wsum[i] = 0;
+
+    // ---- top-k (or replay validation); ids also go to LDS
+    int err = 0;
+    if constexpr (kReplay) {
+        if (tid < T) {
+            int seen[kMaxK];
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                seen[j] = -1;
+                if (j < k) {
+                    const int e = idx_in[tid * k + j];
+                    const float wv = w_in[tid * k + j];
+                    seen[j] = e;
+                    if (e < 0 || e >= E) err |= MOE_DERR_IDX_RANGE;
+                    if (!__builtin_isfinite(wv)) err |= MOE_DERR_NONFINITE;
+#pragma unroll
+                    for (int i = 0; i < kMaxK; ++i)
+                        if (i < j && seen[i] == e) err |= MOE_DERR_IDX_DUP;
+                    topk_idx[tid * k + j] = e;
+                    topk_w[tid * k + j] = wv;
+                    ids[tid * k + j] = e;
+                }
+            }
+        }
+    } else {
+        float macc[4] = {0.f, 0.f, 0.f, 0.f};
+        route_wave<kTailTokPerWave>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k,
+                                    topk_idx, topk_w, ids, macc, err);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E) mp[wave][e] = macc[i];
+        }
+    }
+    wave_raise(err, d_err);
+    __syncthreads();
+
+    // ---- per-wave expert counts and in-wave stable ranks
+    const int nwv = (A + kWave - 1) / kWave;
+    const int a = wave * kWave + lane;
+    int e0 = -1, before = 0;
+    bool valid = false;
+    err = 0;
+    if (wave < nwv) {  // uniform per wave
+        e0 = a < A ? ids[a] : -1;
+        valid = e0 >= 0 && e0 < E;
+        if (a < A && !valid) err |= MOE_DERR_IDX_RANGE;
+        const uint64_t peers = wave_match9(valid ? (uint32_t)e0 : 0x1ffu);
+        const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        before = __popcll(peers & lt_mask);
+        if (valid && (peers >> lane) == 1ull) wstart[wave][e0] = __popcll(peers);
+        if (valid && weighted_counts && q)
+            atomicAdd(&wsum[e0], (unsigned long long)(uint32_t)q[a / k]);
+    }
+    wave_raise(err, d_err);
+    __syncthreads();
+
+    // ---- per expert: run starts of each wave, totals, weighted counts, probability mass
+    if (tid < E) {
+        int32_t run = 0;
+        for (int w = 0; w < nwv; ++w) {
+            const int32_t c = wstart[w][tid];
+            wstart[w][tid] = run;
+            run += c;
+        }
+        counts[tid] = run;
+        eoff[tid] = run;
+        if (weighted_counts) weighted_counts[tid] = q ? (int64_t)wsum[tid] : (int64_t)run;
+        if (!kReplay && prob_mass) {
+            float P[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                float v = mp[4 * b][tid];
+                v = v + mp[4 * b + 1][tid];
+                v = v + mp[4 * b + 2][tid];
+                v = v + mp[4 * b + 3][tid];
+                P[b] = v;
+            }
+            prob_mass[tid] = (P[0] + P[2]) + (P[1] + P[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- exclusive scans over experts (wave 0; lane l holds experts 4l .. 4l+3)
+    if (wave == 0) {
+        int32_t c[4], nt[4], cs = 0, ts = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            c[i] = e < E ? eoff[e] : 0;
+            nt[i] = (c[i] + bt - 1) / bt;
+            cs += c[i];
+            ts += nt[i];
+        }
+        int32_t cx = wave_incl_scan(cs) - cs, tx = wave_incl_scan(ts) - ts;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) {
+                eoff[e] = cx;
+                toff[e] = tx;
+            }
+            cx += c[i];
+            tx += nt[i];
+        }
+        if (lane == 63) {
+            eoff[E] = cx;
+            toff[E] = tx;
+        }
+    }
+    __syncthreads();
+
+    // ---- outputs: offsets, perm / inv, tile list
+    if (tid <= E) offsets[tid] = eoff[tid];
+    if (tid == 0) tiles[0] = min(toff[E], cap);
+    if (wave < nwv) {
+        if (valid) {
+            const int32_t pos = eoff[e0] + wstart[wave][e0] + before;
+            perm[pos] = a;
+            inv[a] = pos;
+        } else if (a < A) {
+            inv[a] = -1;
+        }
+    }
+    if (tid < E) {
+        const int32_t cnt = eoff[tid + 1] - eoff[tid], p0 = eoff[tid];
+        const int32_t nt = (cnt + bt - 1) / bt;
+        for (int i = 0; i < nt; ++i) {
+            const int32_t slot = toff[tid] + i;
+            if (slot >= cap) break;
+            int32_t *d = tiles + 1 + 3 * slot;
+            d[0] = tid;
+            d[1] = p0 + i * bt;
+            d[2] = min(bt, cnt - i * bt);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
+                             const int32_t *idx_in, const float *w_in, int32_t *topk_idx,
+                             float *topk_w, float *prob_mass, int32_t *counts,
+                             int32_t *offsets, int32_t *perm, int32_t *inv,
+                             int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
+                             hipStream_t s) {
+    if (dm.T < 1 || dm.T > kSmallT || dm.E > kMaxE || dm.k > kMaxK)
+        return hipErrorInvalidValue;
+    const int bt = select_tile_m(dm);
+    const int cap = (int)max_m_tiles(dm.T * dm.k, dm.E, bt);
+    if (idx_in)
+        route_tail_kernel<true><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
+            logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
+            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err);
+    else
+        route_tail_kernel<false><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
+            logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
+            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err);
+    return hipGetLastError();
+}
+
+}  // namespace moe

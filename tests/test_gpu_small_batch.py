@@ -1,0 +1,143 @@
+"""Small batches (T <= 64): moe_forward runs the routing tail (top-k or replay check,
+probability mass, counts, offsets, stable permutation, weighted counts, tile list) in one
+block. Every output must be bitwise what the separate entry points (multi-kernel routing
+and permutation) give on the same inputs, and the oracle must agree with both."""
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_routing_amd as M
+import oracle
+import workloads as W
+from gpu_util import as_f32, assert_close, dev, dims_of, host, run_forward, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    M.lib()
+    oracle.lib()
+
+
+def _steps(L, inp, mult=True):
+    """The layer through moe_route / moe_route_replay, moe_permute, moe_grouped_ffn and
+    moe_combine (multi-kernel routing and permutation at every T)."""
+    dims = dims_of(L)
+    b = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
+    ws = M.alloc_workspace(dims)
+    q = inp["token_mult"] if mult else None
+    if L.mode == "router":
+        M.route(dims, inp["x"], inp["w_router"], inp["logit_bias"], b["topk_idx"], b["topk_w"],
+                logits=b["logits"], prob_mass=b["prob_mass"], token_mult=q, d_err=b["d_err"],
+                workspace=ws)
+    else:
+        M.route_replay(dims, inp["idx_in"], inp["w_in"], b["topk_idx"], b["topk_w"],
+                       d_err=b["d_err"])
+    M.permute(dims, b["topk_idx"], inp["x"], b["x_perm"], b["perm"], b["inv"], b["counts"],
+              b["offsets"], token_mult=q, weighted_counts=b["weighted_counts"],
+              d_err=b["d_err"], workspace=ws)
+    M.grouped_ffn(dims, b["x_perm"], b["offsets"], inp["w13"], inp["w2"], b["h"], b["y"],
+                  workspace=ws)
+    M.combine(dims, b["y"], b["inv"], b["topk_w"], b["out"])
+    torch.cuda.synchronize()
+    return b
+
+
+def _fused(L, inp, mult=True):
+    dims = dims_of(L)
+    b = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
+    for n in ("x", "w13", "w2"):
+        b[n] = inp[n]
+    if L.mode == "router":
+        b["w_router"], b["logit_bias"] = inp["w_router"], inp["logit_bias"]
+    else:
+        b["idx_in"], b["w_in"] = inp["idx_in"], inp["w_in"]
+    if mult:
+        b["token_mult"] = inp["token_mult"]
+    M.forward(dims, b, M.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    return b
+
+
+OUTS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "weighted_counts", "x_perm",
+        "h", "y", "out", "d_err")
+
+CASES = [
+    dict(T=1, E=16, k=4, mode="router"),
+    dict(T=3, E=8, k=8, mode="router"),
+    dict(T=16, E=64, k=8, mode="router"),
+    dict(T=17, E=64, k=8, mode="router"),     # two 16-token groups in the mass sum
+    dict(T=33, E=128, k=6, mode="router"),    # three
+    dict(T=48, E=40, k=2, mode="router"),
+    dict(T=64, E=256, k=8, mode="router"),    # 512 assignments, 8 ranking waves
+    dict(T=64, E=128, k=1, mode="router"),
+    dict(T=1, E=1, k=1, mode="router"),
+    dict(T=5, E=32, k=8, mode="replay"),
+    dict(T=64, E=256, k=8, mode="replay"),
+    dict(T=40, E=200, k=3, mode="replay"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"T{c['T']}_E{c['E']}_k{c['k']}_{c['mode']}")
+@pytest.mark.parametrize("mult", [True, False], ids=["q", "noq"])
+def test_small_tail_matches_steps(case, mult):
+    L = W.make_layer(T=case["T"], d=128, E=case["E"], k=case["k"], I=128, dtype="bf16",
+                     mode=case["mode"], seed=60 + case["T"] + case["E"], bias="zipf",
+                     replay="dirichlet")
+    L.token_mult = W.token_multiplicities(L.T, 3)
+    inp = upload(L)
+    ref = _steps(L, inp, mult)
+    got = _fused(L, inp, mult)
+    assert int(got["d_err"].item()) == 0
+    names = OUTS + (("logits", "prob_mass") if L.mode == "router" else ())
+    for n in names:
+        assert host(got[n]).tobytes() == host(ref[n]).tobytes(), n
+    # and the oracle agrees (on the GPU's logits)
+    logits = host(got["logits"]) if L.mode == "router" else None
+    r = oracle.forward(L, logits=logits) if mult else None
+    if r is not None:
+        np.testing.assert_array_equal(host(got["topk_idx"]), r["idx"])
+        for n in ("counts", "offsets", "perm", "inv", "weighted_counts"):
+            np.testing.assert_array_equal(host(got[n]), r[n], err_msg=n)
+        if L.mode == "router":
+            assert_close(host(got["prob_mass"]), r["prob_mass"], "bf16", "prob_mass")
+        assert_close(as_f32(host(got["out"]), "bf16"), as_f32(r["out"], "bf16"), "bf16", "out")
+
+
+def test_small_tail_bad_replay_ids():
+    """Out-of-range replay ids: the same error bits, counts and inv (-1) as the steps."""
+    L = W.make_layer(T=20, d=64, E=16, k=4, I=64, dtype="bf16", mode="replay", seed=77,
+                     replay="uniform")
+    L.idx_in = L.idx_in.copy()
+    L.idx_in[3, 1] = 16
+    L.idx_in[11, 0] = -2
+    inp = upload(L)
+    ref = _steps(L, inp)
+    got = _fused(L, inp)
+    assert int(got["d_err"].item()) == int(ref["d_err"].item())
+    assert int(got["d_err"].item()) & M.DERR_IDX_RANGE
+    for n in ("counts", "offsets", "inv", "weighted_counts"):
+        assert host(got[n]).tobytes() == host(ref[n]).tobytes(), n
+    nvalid = int(host(ref["offsets"])[-1])
+    assert nvalid == L.T * L.k - 2
+    assert host(got["perm"])[:nvalid].tobytes() == host(ref["perm"])[:nvalid].tobytes()
+
+
+def test_small_and_large_paths_agree_per_row():
+    """T = 64 (single-block tail) and T = 65 (multi-kernel path): the first 64 rows'
+    routing and output bytes are the same."""
+    L = W.make_layer(T=65, d=256, E=32, k=4, I=128, dtype="bf16", mode="router", seed=90,
+                     bias="zipf")
+    inp = upload(L)
+    big, _ = run_forward(L, inp, stats=False)
+    L64 = W.make_layer(T=64, d=256, E=32, k=4, I=128, dtype="bf16", mode="router", seed=90,
+                       bias="zipf", weights=False)
+    L64.w13, L64.w2, L64.w_router, L64.logit_bias = L.w13, L.w2, L.w_router, L.logit_bias
+    L64.x = np.ascontiguousarray(L.x[:64])
+    inp64 = dict(inp)
+    inp64["x"] = dev(L64.x)
+    small, _ = run_forward(L64, inp64, stats=False)
+    for n in ("logits", "topk_idx", "topk_w", "out"):
+        assert host(small[n]).tobytes() == host(big[n])[:64].tobytes(), n
