@@ -180,6 +180,43 @@ def decode_sweep(args):
     print(json.dumps(rec), flush=True)
 
 
+def copy_calibration(mib: int):
+    """A plain copy of known size (read mib MiB, write mib MiB), five times: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the counters' scale."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_calibration_bytes": n, "read_kib": n // 1024, "write_kib": n // 1024,
+                      "approx_ms": round(dt * 1e3, 4)}), flush=True)
+
+
+def gemm_traffic(config: str):
+    """HBM bytes per launch of the gate/up grouped GEMM as measured by the rocprofv3
+    FETCH_SIZE + WRITE_SIZE passes recorded in profiles/, or None when that record is
+    missing or was taken on a different grouped-GEMM source (its sha1 is stored with it)."""
+    import hashlib
+    rec = os.path.join(ROOT, "profiles", f"gemm_traffic_{config}.md")
+    src = os.path.join(ROOT, "moe_layer_routing_amd", "csrc", "grouped_ffn.hip")
+    if not os.path.exists(rec):
+        return None
+    fields = {}
+    for line in open(rec):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    if fields.get("grouped_ffn.hip sha1") != sha or "gate/up bytes per launch" not in fields:
+        return None
+    return int(fields["gate/up bytes per launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +226,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs (0 = skip)")
     ap.add_argument("--tile-m", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -197,6 +237,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.config == "c5":
         decode_sweep(args)
         return
@@ -274,13 +317,13 @@ def main():
                    "E": L.E, "k": L.k, "inter": L.I, "mode": L.mode,
                    "tile_m": args.tile_m or "auto"},
         "roofline": {
-            "kernel": "grouped_gemm_dma_kernel<gate/up + SwiGLU> (bf16 prefill tiles)",
+            "kernel": "grouped_gemm_dma128_kernel<gate/up + SwiGLU, fused gather>",
             "bound": "mfma",
             "achieved": round(ach13, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach13 / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": gemm_traffic(args.config) if not args.tile_m else None,
             "algorithmic": f"4*T*k*d*I = {flops13:.4g} FLOP per launch",
             "avg_launch_ms": round(t13_avg, 5),
         },
