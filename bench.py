@@ -98,6 +98,85 @@ def cpu_baseline(L, sample_tokens: int):
     return len(toks) / dt, dt, oracle.num_threads()
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stage_rates(L, dims, inp, K, hip, stream):
+    """The memory-bound stages through their own entry points (router or replay check,
+    permutation with the materialised gather, combine), each timed over K calls with HIP
+    events, as effective HBM GB/s = algorithmic bytes / median time. Algorithmic bytes:
+    route = x + w_router + logits + top-k ids/weights; replay = ids/weights in and out;
+    permute = ids + x + x_perm + perm/inv + counts; combine = Y + inv/weights + out."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    dev = inp["x"].device
+    eb = 2 if L.dtype == "bf16" else 4
+    T, d, E, k, A = L.T, L.d, L.E, L.k, L.T * L.k
+    b = M.alloc_forward_buffers(dims, dev, router=(L.mode == "router"), weighted=False)
+    ws = M.alloc_workspace(dims, dev)
+    b["y"].normal_()
+
+    def timed(fn):
+        fn()
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+        hip.destroy(ev)
+        return ms
+
+    out = {}
+    if L.mode == "router":
+        nb = T * d * eb + E * d * eb + T * E * 4 + T * k * 8
+        ms = timed(lambda: M.route(dims, inp["x"], inp["w_router"], inp["logit_bias"],
+                                   b["topk_idx"], b["topk_w"], logits=b["logits"],
+                                   d_err=b["d_err"], workspace=ws))
+        out["route"] = {"ms": round(ms, 5), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+    else:
+        nb = 2 * T * k * 8
+        ms = timed(lambda: M.route_replay(dims, inp["idx_in"], inp["w_in"], b["topk_idx"],
+                                          b["topk_w"], d_err=b["d_err"]))
+        out["replay"] = {"ms": round(ms, 5), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+    nb = T * k * 4 + T * d * eb + A * d * eb + A * 8 + (2 * E + 1) * 4
+    ms = timed(lambda: M.permute(dims, b["topk_idx"], inp["x"], b["x_perm"], b["perm"],
+                                 b["inv"], b["counts"], b["offsets"], d_err=b["d_err"],
+                                 workspace=ws))
+    out["permute"] = {"ms": round(ms, 5), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+    nb = A * d * 4 + A * 4 + T * k * 4 + T * d * eb
+    ms = timed(lambda: M.combine(dims, b["y"], b["inv"], b["topk_w"], b["out"]))
+    out["combine"] = {"ms": round(ms, 5), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+    out["peak_gbs"] = PEAK_HBM_GBS
+    return out
+
+
+def copy_gbs(dev, mib=512, reps=10):
+    """Measured device-to-device copy rate, (read + write bytes) / median time."""
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        c.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(c))
+    return round(2 * (mib << 20) / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+
+
 def upload(L, dev):
     """Host (numpy) inputs of layer L -> device tensors (bf16 bit patterns as bfloat16)."""
     import torch
@@ -145,35 +224,46 @@ def decode_sweep(args):
         ws = M.alloc_workspace(dims, dev)
         for _ in range(args.warmup):
             M.forward(dims, b, ws)
-        times = []
+        times, t13 = [], []
         for _ in range(args.steps):
             scrub.sum()
-            ev = hip.create(2)
+            ev = hip.create(5)
             hip.record(ev[0], stream.cuda_stream)
-            M.forward(dims, b, ws)
-            hip.record(ev[1], stream.cuda_stream)
+            M.forward(dims, b, ws, prof_events=ev[1:4])
+            hip.record(ev[4], stream.cuda_stream)
             torch.cuda.synchronize()
-            times.append(hip.ms(ev[0], ev[1]))
+            times.append(hip.ms(ev[0], ev[4]))
+            t13.append(hip.ms(ev[1], ev[2]))
             hip.destroy(ev)
         assert int(b["d_err"].item()) == 0
         t_ms = float(np.median(times))
+        g_ms = float(np.median(t13))
         active = int((b["counts"] > 0).sum().item())
+        A = T * L.k
         nbytes = (active * 3 * L.d * L.I * 2 + L.E * L.d * 2 + 2 * T * L.d * 2 + 8 * T * L.k)
-        rows.append({"T": T, "ms": round(t_ms, 4), "tokens_per_s": round(T / (t_ms * 1e-3), 1),
-                     "active_experts": active, "hbm_gbs": round(nbytes / (t_ms * 1e-3) / 1e9, 1)})
-    best = max(rows, key=lambda r: r["hbm_gbs"])
+        g_bytes = active * 2 * L.I * L.d * 2 + A * L.d * 2 + A * L.I * 2
+        rows.append({"T": T, "ms": round(t_ms, 4), "p10_ms": round(float(np.percentile(times, 10)), 4),
+                     "p90_ms": round(float(np.percentile(times, 90)), 4),
+                     "tokens_per_s": round(T / (t_ms * 1e-3), 1),
+                     "active_experts": active, "hbm_gbs": round(nbytes / (t_ms * 1e-3) / 1e9, 1),
+                     "gate_up_ms": round(g_ms, 4), "gate_up_bytes": g_bytes,
+                     "gate_up_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1)})
+    top = rows[-1]
     rec = {
         "metric": METRIC + " (decode-shaped layer, HBM GB/s)",
-        "value": rows[-1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rows[-1]["ms"],
+        "value": top["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": top["ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS["c5"], "name": "c5", "d": L.d, "E": L.E, "k": L.k,
-                   "inter": L.I, "mode": "router", "evict_read_mb": 512},
-        "roofline": {"kernel": "whole layer (weights stream)", "bound": "hbm",
-                     "achieved": best["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(best["hbm_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
-                     "at_T": best["T"]},
+        "config": {"workload": WORKLOADS["c5"], "name": "c5", "T": top["T"], "d": L.d,
+                   "E": L.E, "k": L.k, "inter": L.I, "mode": "router", "evict_read_mb": 512},
+        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (decode tiles), T=64",
+                     "bound": "hbm", "achieved": top["gate_up_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(top["gate_up_gbs"] / PEAK_HBM_GBS, 4),
+                     "traffic": None,
+                     "algorithmic": "active experts' w13 + gathered x rows + h, per launch",
+                     "avg_launch_ms": top["gate_up_ms"]},
+        "copy_gbs_read_plus_write": copy_gbs(dev),
         "sweep": rows,
         "cpu_baseline": None,
     }
@@ -276,19 +366,23 @@ def main():
     assert int(b["d_err"].item()) == 0, "device error word set"
 
     K = args.steps
-    evs = hip.create(3 * K + 2)
+    evs = hip.create(3 * K)
+    bnd = hip.create(K + 1)                 # step boundaries
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    hip.record(evs[-2], stream.cuda_stream)
     for i in range(K):
+        hip.record(bnd[i], stream.cuda_stream)
         M.forward(dims, b, ws, prof_events=evs[3 * i:3 * i + 3])
-    hip.record(evs[-1], stream.cuda_stream)
+    hip.record(bnd[K], stream.cuda_stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = hip.ms(evs[-2], evs[-1])
+    total_ms = hip.ms(bnd[0], bnd[K])
+    step_ms = np.array([hip.ms(bnd[i], bnd[i + 1]) for i in range(K)])
     t13 = np.array([hip.ms(evs[3 * i], evs[3 * i + 1]) for i in range(K)])
     t2 = np.array([hip.ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)])
     hip.destroy(evs)
+    hip.destroy(bnd)
+    stages = stage_rates(L, dims, inp, K, hip, stream)
 
     A = L.T * L.k
     ms_step = total_ms / K
@@ -334,12 +428,17 @@ def main():
             "down_ms": round(t2_avg, 5),
             "down_tflops": round(flops2 / (t2_avg * 1e-3) / 1e12, 2),
         },
+        "step_ms": {"median": round(float(np.median(step_ms)), 5),
+                    "p10": round(float(np.percentile(step_ms, 10)), 5),
+                    "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "stages_hbm": stages,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:
         tps, secs, threads = cpu_baseline(L, args.cpu_sample)
         rec["cpu_baseline"] = {
             "value": round(tps, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"first {min(args.cpu_sample, L.T)} of the {L.T} tokens, every stage "
                       f"({secs:.1f} s)",
         }
