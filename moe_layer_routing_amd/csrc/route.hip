@@ -14,81 +14,107 @@ namespace moe {
 namespace {
 
 // ------------------------------------------------------------------ router logits
-// One 1024-thread block computes a 16-expert x 16-token tile of logits. The 16 waves split
-// K statically: wave w takes K-steps w, w+16, w+32, ... (one MFMA each, in that order) and
-// the 16 partial tiles are added in wave order. The split depends only on d, never on T,
-// so every logit is the same sequence of MFMA steps and additions at any batch size; with
-// 16 short chains each wave issues all of its loads at once for d up to 4096 (bf16).
+// Logits come in 16-expert x 16-token MFMA tiles. Each logit is split statically over K
+// into 16 partial chains: chain w takes K-steps w, w+16, w+32, ... (one MFMA each, in that
+// order), and the 16 partials are added in chain order. The split depends only on d,
+// never on T or on the launch shape, so every logit is the same sequence of MFMA steps and
+// additions at any batch size.
+//
+// A 1024-thread block holds the 16 chains of EPB expert tiles of one token tile (wave w
+// runs chain w of each): the token fragment of a K-step is loaded once and used for EPB
+// expert tiles. EPB only groups tiles into blocks; it is chosen per launch so that small
+// batches still spread over enough blocks.
 //
 // MFMA operand mapping (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4f32): the A operand
 // rows are experts, the B operand columns are tokens; lane l feeds row/column l%16 and
 // K-slice l/16; the result lane l holds column l%16 and rows 4*(l/16) + 0..3.
 constexpr int kLogitSplit = 16;
 
-template <bool kBF16>
+template <bool kBF16, int EPB>
 __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
     const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int E) {
-    const int n_eb = (E + 15) >> 4;
-    const int eb = (int)(blockIdx.x % n_eb) * 16;
-    const int64_t tb = (int64_t)(blockIdx.x / n_eb) * 16;
+    const int n_et = (E + 15) >> 4;
+    const int n_eg = (n_et + EPB - 1) / EPB;
+    const int et0 = (int)(blockIdx.x % n_eg) * EPB;
+    const int64_t tb = (int64_t)(blockIdx.x / n_eg) * 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int e_row = min(eb + r, E - 1);
     const int64_t t_row = min<int64_t>(tb + r, T - 1);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[EPB];
+#pragma unroll
+    for (int j = 0; j < EPB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // K-steps w, w+16, ... of this wave, accumulated in that order; the operands of up to
-    // 8 steps are loaded before their MFMAs so that the loads overlap.
-    constexpr int kGroup = 8;
+    // kGroup steps are loaded before their MFMAs so that the loads overlap.
+    constexpr int kGroup = EPB >= 4 ? 2 : (EPB == 2 ? 4 : 8);
     constexpr int kStride = kLogitSplit;
     if constexpr (kBF16) {
-        const uint16_t *wp = static_cast<const uint16_t *>(wr_) + (int64_t)e_row * d + g * 8;
+        const uint16_t *wp[EPB];
+#pragma unroll
+        for (int j = 0; j < EPB; ++j)
+            wp[j] = static_cast<const uint16_t *>(wr_) +
+                    (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g * 8;
         const uint16_t *xp = static_cast<const uint16_t *>(x_) + t_row * d + g * 8;
         const int nsteps = d >> 5;
         for (int s0 = wave; s0 < nsteps; s0 += kStride * kGroup) {
-            bf16x8_t a[kGroup], b[kGroup];
+            bf16x8_t a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                const int s = min(s0 + kStride * i, nsteps - 1);
-                a[i] = *reinterpret_cast<const bf16x8_t *>(wp + s * 32);
-                b[i] = *reinterpret_cast<const bf16x8_t *>(xp + s * 32);
+                const int st = min(s0 + kStride * i, nsteps - 1);
+                b[i] = *reinterpret_cast<const bf16x8_t *>(xp + st * 32);
+#pragma unroll
+                for (int j = 0; j < EPB; ++j)
+                    a[i][j] = *reinterpret_cast<const bf16x8_t *>(wp[j] + st * 32);
             }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i)
                 if (s0 + kStride * i < nsteps)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[i], acc, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < EPB; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][j], b[i], acc[j],
+                                                                         0, 0, 0);
         }
     } else {
-        const float *wp = static_cast<const float *>(wr_) + (int64_t)e_row * d + g;
+        const float *wp[EPB];
+#pragma unroll
+        for (int j = 0; j < EPB; ++j)
+            wp[j] = static_cast<const float *>(wr_) +
+                    (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g;
         const float *xp = static_cast<const float *>(x_) + t_row * d + g;
         const int nsteps = d >> 2;
         for (int s0 = wave; s0 < nsteps; s0 += kStride * kGroup) {
-            float a[kGroup], b[kGroup];
+            float a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                const int s = min(s0 + kStride * i, nsteps - 1);
-                a[i] = wp[s * 4];
-                b[i] = xp[s * 4];
+                const int st = min(s0 + kStride * i, nsteps - 1);
+                b[i] = xp[st * 4];
+#pragma unroll
+                for (int j = 0; j < EPB; ++j) a[i][j] = wp[j][st * 4];
             }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i)
                 if (s0 + kStride * i < nsteps)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < EPB; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][j], b[i], acc[j],
+                                                                      0, 0, 0);
         }
     }
-    __shared__ float part[kLogitSplit][4][64];
-    for (int i = 0; i < 4; ++i) part[wave][i][lane] = acc[i];
-    __syncthreads();
-    // wave 0 adds the partials in wave order for the 4 accumulator rows of each lane
-    if (wave == 0) {
-        const int64_t t = tb + r;
-        for (int i = 0; i < 4; ++i) {
-            float v = part[0][i][lane];
+    __shared__ float part[kLogitSplit][EPB][4][64];
 #pragma unroll
-            for (int w = 1; w < kLogitSplit; ++w) v = v + part[w][i][lane];
-            const int e = eb + 4 * g + i;
-            if (t < T && e < E) logits[t * E + e] = bias ? v + bias[e] : v;
-        }
+    for (int j = 0; j < EPB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][j][i][lane] = acc[j][i];
+    __syncthreads();
+    // one thread per logit adds the 16 partials in chain order
+    for (int o = threadIdx.x; o < EPB * 256; o += 64 * kLogitSplit) {
+        const int j = o >> 8, i = (o >> 6) & 3, l = o & 63;
+        float v = part[0][j][i][l];
+#pragma unroll
+        for (int w = 1; w < kLogitSplit; ++w) v = v + part[w][j][i][l];
+        const int64_t t = tb + (l & 15);
+        const int e = (et0 + j) * 16 + 4 * (l >> 4) + i;
+        if (t < T && e < E && et0 + j < n_et) logits[t * E + e] = bias ? v + bias[e] : v;
     }
 }
 
@@ -181,16 +207,36 @@ __global__ __launch_bounds__(256) void replay_kernel(const int32_t *__restrict__
 
 }  // namespace
 
+// Expert tiles per block: as many as keep at least 256 blocks (the x fragment of a K-step
+// then serves several expert tiles), at most 8.
+static int logits_epb(int64_t T, int E) {
+    const int64_t n_tt = (T + 15) / 16;
+    const int n_et = (E + 15) / 16;
+    int epb = 1;
+    while (epb * 2 <= 8 && epb * 2 <= n_et && n_tt * ((n_et + epb * 2 - 1) / (epb * 2)) >= 256)
+        epb *= 2;
+    return epb;
+}
+
+template <bool kBF16>
+static void launch_logits_t(const moe_dims &dm, const void *x, const void *w_router,
+                            const float *bias, float *logits, hipStream_t s) {
+    const int epb = logits_epb(dm.T, dm.E);
+    const int n_eg = ((dm.E + 15) / 16 + epb - 1) / epb;
+    const dim3 grid((unsigned)(((dm.T + 15) / 16) * n_eg)), block(64 * kLogitSplit);
+    switch (epb) {
+    case 1: route_logits_kernel<kBF16, 1><<<grid, block, 0, s>>>(x, w_router, bias, logits, dm.T, dm.d, dm.E); break;
+    case 2: route_logits_kernel<kBF16, 2><<<grid, block, 0, s>>>(x, w_router, bias, logits, dm.T, dm.d, dm.E); break;
+    case 4: route_logits_kernel<kBF16, 4><<<grid, block, 0, s>>>(x, w_router, bias, logits, dm.T, dm.d, dm.E); break;
+    default: route_logits_kernel<kBF16, 8><<<grid, block, 0, s>>>(x, w_router, bias, logits, dm.T, dm.d, dm.E); break;
+    }
+}
+
 hipError_t launch_router_logits(const moe_dims &dm, const void *x, const void *w_router,
                                 const float *bias, float *logits, hipStream_t s) {
     if (dm.T > 0) {
-        const int64_t nblk = ((dm.E + 15) / 16) * ((dm.T + 15) / 16);
-        if (dm.dtype == MOE_BF16)
-            route_logits_kernel<true><<<dim3((unsigned)nblk), dim3(64 * kLogitSplit), 0, s>>>(
-                x, w_router, bias, logits, dm.T, dm.d, dm.E);
-        else
-            route_logits_kernel<false><<<dim3((unsigned)nblk), dim3(64 * kLogitSplit), 0, s>>>(
-                x, w_router, bias, logits, dm.T, dm.d, dm.E);
+        if (dm.dtype == MOE_BF16) launch_logits_t<true>(dm, x, w_router, bias, logits, s);
+        else launch_logits_t<false>(dm, x, w_router, bias, logits, s);
     }
     return hipGetLastError();
 }
@@ -202,7 +248,8 @@ hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
     const int64_t T = dm.T;
     const int E = dm.E;
     if (T > 0) {
-        launch_router_logits(dm, x, w_router, bias, logits, s);
+        const hipError_t le = launch_router_logits(dm, x, w_router, bias, logits, s);
+        if (le != hipSuccess) return le;
         const int64_t tblk = (T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
         route_topk_kernel<<<dim3((unsigned)tblk), dim3(256), 0, s>>>(
             logits, token_mult, T, E, dm.k, topk_idx, topk_w, prob_mass ? mass_part : nullptr,

@@ -31,12 +31,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Butterfly sum: every lane ends with the same bits (each level adds the same two
-// operands, only commuted), and the tree shape is fixed by the wave width alone.
+// Wave-wide sum in a fixed DPP tree: quads (xor 1, xor 2), half-rows and rows
+// (mirrors), then rows 1 and 3 add rows 0 and 2, and rows 2 and 3 add the first
+// 32-lane sum; lane 63 ends with the total, which readlane makes uniform. Lanes a DPP
+// move leaves out add 0, which is exact for the non-negative sums taken here.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_out) {
+    return v + __int_as_float(ctrl_out);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off);
-    return v;
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Softmax + top-k + renormalisation ("0 train-infer mismatch ...", "The router: matching
@@ -45,10 +54,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 // the largest remaining logit (wave max of its ordered bits) with ties to the lowest
 // expert id; probabilities are exp(l - max) / Z with Z summed in a fixed tree; the k
 // selected probabilities are renormalised by their left-to-right sum. Writes topk_idx /
-// topk_w (and the ids to lds_ids when given), adds q[t] * p to macc (lane's experts) and
-// ORs MOE_DERR_NONFINITE into err for a non-finite logit.
+// topk_w (and the ids to lds_ids when given), adds q[t] * p to macc (lane's experts, in
+// token order) and ORs MOE_DERR_NONFINITE into err for a non-finite logit.
+//
+// The NTOK tokens go through each round together (their reductions are independent and
+// overlap); tokens past T are computed on zeros and their results dropped.
 template <int NTOK>
-__device__ __forceinline__ void route_wave(const float *__restrict__ logits,
+__device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
                                            const int32_t *__restrict__ q, int64_t t0,
                                            int64_t T, int E, int k,
                                            int32_t *__restrict__ topk_idx,
@@ -57,54 +69,70 @@ __device__ __forceinline__ void route_wave(const float *__restrict__ logits,
     const int lane = threadIdx.x & 63;
     const int nlv = (E + 63) >> 6;    // logits per lane actually used
     float lv[NTOK][4];
+    bool tv[NTOK];                    // token exists (uniform over the wave)
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) valid[i] = lane + 64 * i < E;
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+        tv[tt] = t0 + tt < T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lv[tt][i] = (tv[tt] && valid[i]) ? logits[(t0 + tt) * E + lane + 64 * i] : 0.f;
+    }
+    uint32_t hi[NTOK][4];
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            const int64_t t = t0 + tt;
-            lv[tt][i] = (t < T && e < E) ? logits[t * E + e] : 0.f;
+            if (tv[tt] && valid[i] && !__builtin_isfinite(lv[tt][i])) err |= MOE_DERR_NONFINITE;
+            hi[tt][i] = valid[i] ? ordered_bits(lv[tt][i]) : 0u;
         }
+    // k rounds: per token the largest remaining logit, ties to the lowest expert id
+    // (lowest lane of the lowest 64-expert group holding it)
+    uint32_t taken[NTOK], top_hi[NTOK];
+    int sel[NTOK][kMaxK];
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt) {
-        const int64_t t = t0 + tt;
-        if (t >= T) break;
-        uint32_t hi[4];
-        bool valid[4];
+        taken[tt] = 0;
+        top_hi[tt] = 0;
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            valid[i] = e < E;
-            if (valid[i] && !__builtin_isfinite(lv[tt][i])) err |= MOE_DERR_NONFINITE;
-            hi[i] = valid[i] ? ordered_bits(lv[tt][i]) : 0u;
-        }
-        // k rounds: the largest remaining logit (wave max of its ordered bits), ties to
-        // the lowest expert id (lowest lane of the lowest 64-expert group holding it)
-        uint32_t taken = 0;
-        int sel[kMaxK];
-        uint32_t top_hi = 0;
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            uint32_t m[NTOK];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            sel[j] = 0;
-            if (j < k) {
+            for (int tt = 0; tt < NTOK; ++tt) {
                 uint32_t best = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (i < nlv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
-                const uint32_t m = wave_max_u32(best);
+                    if (i < nlv && valid[i] && !((taken[tt] >> i) & 1u) && hi[tt][i] > best)
+                        best = hi[tt][i];
+                m[tt] = wave_max_u32(best);
+            }
+#pragma unroll
+            for (int tt = 0; tt < NTOK; ++tt) {
                 int we = -1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint64_t mask =
-                        __ballot(i < nlv && valid[i] && !((taken >> i) & 1u) && hi[i] == m);
+                    const uint64_t mask = __ballot(i < nlv && valid[i] &&
+                                                   !((taken[tt] >> i) & 1u) && hi[tt][i] == m[tt]);
                     if (we < 0 && mask) we = 64 * i + (int)__builtin_ctzll(mask);
                 }
-                sel[j] = we;
-                if (j == 0) top_hi = m;
-                if ((we & 63) == lane) taken |= 1u << (we >> 6);
+                sel[tt][j] = we;
+                if (j == 0) top_hi[tt] = m[tt];
+                if ((we & 63) == lane) taken[tt] |= 1u << (we >> 6);
             }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < NTOK; ++tt) sel[tt][j] = 0;
         }
-        const float mx = from_ordered_bits(top_hi);
+    }
+    // softmax over all E, renormalisation of the k selected probabilities
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+        const int64_t t = t0 + tt;
+        const float mx = from_ordered_bits(top_hi[tt]);
         float z[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = valid[i] ? expf(lv[tt][i] - mx) : 0.f;
@@ -113,34 +141,55 @@ __device__ __forceinline__ void route_wave(const float *__restrict__ logits,
         zl = zl + z[3];
         const float Z = wave_sum(zl);
         float p[4];
-        const float qt = q ? static_cast<float>(q[t]) : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = z[i] / Z;
-            macc[i] = macc[i] + qt * p[i];
+        for (int i = 0; i < 4; ++i) p[i] = z[i] / Z;
+        if (tv[tt]) {
+            const float qt = q ? static_cast<float>(q[t]) : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) macc[i] = macc[i] + qt * p[i];
         }
         float ps[kMaxK];
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             ps[j] = 0.f;
             if (j < k) {
-                const int ri = sel[j] >> 6;
+                const int e = sel[tt][j];          // uniform over the wave
+                const int ri = e >> 6;
                 const float mine = ri == 0 ? p[0] : ri == 1 ? p[1] : ri == 2 ? p[2] : p[3];
-                ps[j] = __shfl(mine, sel[j] & 63);
+                ps[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
             }
         }
         float sum = ps[0];
 #pragma unroll
         for (int j = 1; j < kMaxK; ++j)
             if (j < k) sum = sum + ps[j];
+        if (tv[tt]) {
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k && lane == j) {
-                topk_idx[t * k + j] = sel[j];
-                topk_w[t * k + j] = ps[j] / sum;
-                if (lds_ids) lds_ids[t * k + j] = sel[j];
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k && lane == j) {
+                    topk_idx[t * k + j] = sel[tt][j];
+                    topk_w[t * k + j] = ps[j] / sum;
+                    if (lds_ids) lds_ids[t * k + j] = sel[tt][j];
+                }
             }
         }
+    }
+}
+
+// The wave's tokens: all NTOK together when they all exist, else one at a time (the
+// per-token arithmetic is the same either way; macc is added in token order).
+template <int NTOK>
+__device__ __forceinline__ void route_wave(const float *__restrict__ logits,
+                                           const int32_t *__restrict__ q, int64_t t0,
+                                           int64_t T, int E, int k,
+                                           int32_t *__restrict__ topk_idx,
+                                           float *__restrict__ topk_w, int32_t *lds_ids,
+                                           float (&macc)[4], int &err) {
+    if (t0 + NTOK <= T) {
+        route_tokens<NTOK>(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, macc, err);
+    } else {
+        for (int64_t t = t0; t < T; ++t)
+            route_tokens<1>(logits, q, t, T, E, k, topk_idx, topk_w, lds_ids, macc, err);
     }
 }
 

@@ -128,9 +128,11 @@ def test_c5_batch_invariance():
                        seed=55, weights=False).x
     pos = np.sort(rng.choice(4096, 64, replace=False))
     big[pos] = pool
-    out, idx, _, _ = run(big)
+    out, idx, _, bb = run(big)
     assert out[pos].tobytes() == ref_out.tobytes()
     assert idx[pos].tobytes() == ref_idx.tobytes()
+    # the 4096-token launch groups several expert tiles per logits block; same bits
+    assert host(bb["logits"])[pos].tobytes() == host(b64["logits"]).tobytes()
     # and the decode rows agree with the oracle
     toks = np.array([0, 1, 31, 63])
     rh, ry, rout = oracle.forward_tokens(L, toks, ref_idx, ref_w)
