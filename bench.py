@@ -213,7 +213,7 @@ def decode_sweep(args):
     scrub = torch.ones(128 << 20, dtype=torch.int32, device=dev)      # 512 MB
     hip = HipEvents()
     stream = torch.cuda.current_stream()
-    Ts = [1, 2, 4, 8, 16, 32, 64]
+    Ts = [int(t) for t in args.decode_t.split(",")]
     rows = []
     for T in Ts:
         dims = M.make_dims(T, L.d, L.E, L.k, L.I, M.MOE_BF16, args.tile_m)
@@ -316,6 +316,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs (0 = skip)")
     ap.add_argument("--tile-m", type=int, default=0)
+    ap.add_argument("--decode-t", default="1,2,4,8,16,32,64",
+                    help="batch sizes of the decode-shaped sweep (--config c5)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")

@@ -259,7 +259,10 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
     if (nchunks > 0)
         scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
                                                                      ws.blk_hist, perm, inv);
-    if (x_perm) launch_gather(dm, x, inv, x_perm, s);
+    if (x_perm) {
+        const hipError_t ge = launch_gather(dm, x, inv, x_perm, s);
+        if (ge != hipSuccess) return ge;
+    }
     if (seq_counts && num_seqs > 0) {
         const int64_t n = (int64_t)num_seqs * E;
         fill_i32_kernel<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256),
