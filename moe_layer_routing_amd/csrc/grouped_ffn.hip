@@ -331,10 +331,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // Same GEMM with 128-byte K stages (64 bf16 per row): every DMA lane group of 8 covers one
 // full 128-byte line of a row, which the global->LDS path moves at about 1.7x the rate of
 // 64-byte halves. A stage is 8-row x 128-byte LDS blocks; lane l of a DMA instruction
-// fetches chunk (l%8) ^ swz(row) of row l/8, so that the 16 rows of an MFMA fragment read
-// their chunk from 16 different bank groups. Two slots: stage kt+1 is in flight while the
-// two 32-deep MFMA K-steps of stage kt run; one wait + one s_barrier per stage.
-__device__ __forceinline__ int chunk_swizzle8(int r) { return (r & 7) ^ (((r >> 3) & 1) << 2); }
+// fetches chunk (l%8) ^ swz(row) of row l/8. With swz(row) = row % 8, the fragment reads
+// (16 rows, one 16-byte chunk each) are free of LDS bank conflicts on gfx950 (measured
+// with SQ_LDS_BANK_CONFLICT; also folding bit 3 of the row into the swizzle conflicts).
+// Two slots: stage kt+1 is in flight while the two 32-deep MFMA K-steps of stage kt run;
+// one wait + one s_barrier per stage.
+__device__ __forceinline__ int chunk_swizzle8(int r) { return r & 7; }
 
 template <int NBW, int NW>
 __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase,
