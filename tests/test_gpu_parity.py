@@ -212,6 +212,11 @@ FWD_CASES = [
     dict(name="bf16_T1", T=1, d=256, E=16, k=4, I=128, dtype="bf16", mode="router", seed=26),
     dict(name="bf16_skew", T=400, d=128, E=40, k=2, I=192, dtype="bf16", mode="replay", seed=27,
          replay="uniform", skew=True),
+    # the largest d and inter the ABI accepts (32-bit byte offsets inside the DMA kernels)
+    dict(name="bf16_max_d", T=70, d=16384, E=4, k=2, I=64, dtype="bf16", mode="router", seed=28),
+    dict(name="bf16_max_inter", T=70, d=128, E=4, k=2, I=16384, dtype="bf16", mode="replay",
+         seed=29, replay="uniform"),
+    dict(name="f32_max_d", T=20, d=16384, E=2, k=1, I=64, dtype="f32", mode="router", seed=30),
 ]
 
 
@@ -275,7 +280,8 @@ def test_tile_m_invariance(case):
 
 
 @pytest.mark.parametrize("case", [FWD_CASES[0], FWD_CASES[1], FWD_CASES[2], FWD_CASES[3],
-                                  FWD_CASES[7]], ids=lambda c: c["name"])
+                                  FWD_CASES[7], FWD_CASES[8], FWD_CASES[9]],
+                         ids=lambda c: c["name"])
 def test_fused_gather_identical(case):
     """moe_forward without x_perm (gather fused into the gate/up GEMM) gives the same bytes
     as with the materialised x_perm, for every tile height."""
