@@ -119,10 +119,10 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
 }
 
 // ------------------------------------------------------------- softmax + top-k
-// One wave per kTokPerWave consecutive tokens; a block of 4 waves handles
-// kTopkTokPerBlock tokens and writes its per-expert probability-mass partial, the sum of
-// its waves' partials in wave order.
-constexpr int kTokPerWave = kTopkTokPerBlock / 4;
+// A block of 4 waves routes kTopkTokPerBlock = 16 tokens, 4 per wave (one per 16-lane
+// row), and writes its per-expert probability-mass partial: per wave the sum of its four
+// tokens' q·p in token order (starting from 0), then the four waves' sums in wave order.
+static_assert(kTopkTokPerBlock == 16, "4 waves x 4 tokens");
 
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ q,
@@ -132,24 +132,28 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                                                          float *__restrict__ mass_part,
                                                          int32_t *__restrict__ d_err) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * kTokPerWave;
-    float macc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * 4;
+    float qp[kRowVals];
     int err = 0;
-    route_wave<kTokPerWave>(logits, q, t0, T, E, k, topk_idx, topk_w, nullptr, macc, err);
+    route_rows4(logits, q, t0, T, E, k, topk_idx, topk_w, nullptr, qp, err);
     wave_raise(err, d_err);
     if (mass_part) {
-        __shared__ float mp[4][kMaxE];
+        __shared__ float mpt[kTopkTokPerBlock][kMaxE];
+        const int row = wave * 4 + (lane >> 4), c = lane & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E) mp[wave][e] = macc[i];
-        }
+        for (int i = 0; i < kRowVals; ++i)
+            if (c + 16 * i < E) mpt[row][c + 16 * i] = qp[i];
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += 256) {
-            float v = mp[0][e];
-            v = v + mp[1][e];
-            v = v + mp[2][e];
-            v = v + mp[3][e];
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float m = 0.f + mpt[4 * w][e];
+                m = m + mpt[4 * w + 1][e];
+                m = m + mpt[4 * w + 2][e];
+                m = m + mpt[4 * w + 3][e];
+                v = (w == 0) ? m : v + m;
+            }
             mass_part[(int64_t)blockIdx.x * E + e] = v;
         }
     }

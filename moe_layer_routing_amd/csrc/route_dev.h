@@ -8,7 +8,7 @@ namespace moe {
 
 // Total order used for expert selection: larger logit first, equal logits -> lower id.
 // The logit maps to an unsigned key that orders like the real number (-0 == +0); among
-// lanes holding the maximal key the lowest expert id is taken (see route_wave).
+// lanes holding the maximal key the lowest expert id is taken (see route_rows4).
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
     uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -48,148 +48,116 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Row-wide (16-lane) reductions through DPP lane moves (quad xor 1 and 2, half-row and
+// row mirrors): every lane of the row ends with the same result. For the sum, every level
+// adds the same two operands in every lane (only commuted), so all lanes hold equal bits.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return v;
+}
+__device__ __forceinline__ int row_min_i32(int v) {
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+    return v;
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // Softmax + top-k + renormalisation ("0 train-infer mismatch ...", "The router: matching
-// expert ids and weights") of the NTOK consecutive tokens t0 .. t0+NTOK-1 (those < T) of
-// the calling wave. Lane l holds experts l, l+64, l+128, l+192. The k rounds each take
-// the largest remaining logit (wave max of its ordered bits) with ties to the lowest
-// expert id; probabilities are exp(l - max) / Z with Z summed in a fixed tree; the k
-// selected probabilities are renormalised by their left-to-right sum. Writes topk_idx /
-// topk_w (and the ids to lds_ids when given), adds q[t] * p to macc (lane's experts, in
-// token order) and ORs MOE_DERR_NONFINITE into err for a non-finite logit.
-//
-// The NTOK tokens go through each round together (their reductions are independent and
-// overlap); tokens past T are computed on zeros and their results dropped.
-template <int NTOK>
-__device__ __forceinline__ void route_tokens(const float *__restrict__ logits,
-                                           const int32_t *__restrict__ q, int64_t t0,
-                                           int64_t T, int E, int k,
-                                           int32_t *__restrict__ topk_idx,
-                                           float *__restrict__ topk_w, int32_t *lds_ids,
-                                           float (&macc)[4], int &err) {
-    const int lane = threadIdx.x & 63;
-    const int nlv = (E + 63) >> 6;    // logits per lane actually used
-    float lv[NTOK][4];
-    bool tv[NTOK];                    // token exists (uniform over the wave)
-    bool valid[4];
+// expert ids and weights") of four consecutive tokens t0 .. t0+3, one per 16-lane row of
+// the calling wave: lane c of row r holds token t0+r's logits of experts c, c+16, c+32, ...
+// Each of the k rounds takes the row's largest remaining logit (row max of order-preserving
+// keys), ties to the lowest expert id (row min over the lanes holding that key); the
+// probabilities are exp(l - max) / Z with Z summed per lane in expert order and then in a
+// fixed row tree; the k selected probabilities (recomputed from the selected logit, the
+// same expression) are renormalised by their left-to-right sum. Writes topk_idx / topk_w
+// (and the ids to lds_ids when given) for rows with t < T, returns q[t]·p for the lane's
+// experts in qp (0 for rows past T) and ORs MOE_DERR_NONFINITE into err for a non-finite
+// logit of an existing token.
+constexpr int kRowVals = kMaxE / 16;   // logits per lane
+
+__device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
+                                            const int32_t *__restrict__ q, int64_t t0,
+                                            int64_t T, int E, int k,
+                                            int32_t *__restrict__ topk_idx,
+                                            float *__restrict__ topk_w, int32_t *lds_ids,
+                                            float (&qp)[kRowVals], int &err) {
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int64_t t = t0 + (lane >> 4);
+    const bool tv = t < T;
+    const int nv = (E + 15) >> 4;     // logits per lane actually used (uniform)
+    float lv[kRowVals];
+    uint32_t hi[kRowVals];
+    bool valid[kRowVals];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) valid[i] = lane + 64 * i < E;
-#pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt) {
-        tv[tt] = t0 + tt < T;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lv[tt][i] = (tv[tt] && valid[i]) ? logits[(t0 + tt) * E + lane + 64 * i] : 0.f;
+    for (int i = 0; i < kRowVals; ++i) {
+        valid[i] = i < nv && c + 16 * i < E;
+        lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
+        if (tv && valid[i] && !__builtin_isfinite(lv[i])) err |= MOE_DERR_NONFINITE;
+        hi[i] = valid[i] ? ordered_bits(lv[i]) : 0u;
     }
-    uint32_t hi[NTOK][4];
-#pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (tv[tt] && valid[i] && !__builtin_isfinite(lv[tt][i])) err |= MOE_DERR_NONFINITE;
-            hi[tt][i] = valid[i] ? ordered_bits(lv[tt][i]) : 0u;
-        }
-    // k rounds: per token the largest remaining logit, ties to the lowest expert id
-    // (lowest lane of the lowest 64-expert group holding it)
-    uint32_t taken[NTOK], top_hi[NTOK];
-    int sel[NTOK][kMaxK];
-#pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt) {
-        taken[tt] = 0;
-        top_hi[tt] = 0;
-    }
+    uint32_t taken = 0, mkey[kMaxK];
+    int sel[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
+        sel[j] = 0;
+        mkey[j] = 0;
         if (j < k) {
-            uint32_t m[NTOK];
+            uint32_t best = 0;
 #pragma unroll
-            for (int tt = 0; tt < NTOK; ++tt) {
-                uint32_t best = 0;
+            for (int i = 0; i < kRowVals; ++i)
+                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
+            const uint32_t m = row_max_u32(best);
+            int cand = 0x7fffffff;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i < nlv && valid[i] && !((taken[tt] >> i) & 1u) && hi[tt][i] > best)
-                        best = hi[tt][i];
-                m[tt] = wave_max_u32(best);
-            }
-#pragma unroll
-            for (int tt = 0; tt < NTOK; ++tt) {
-                int we = -1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint64_t mask = __ballot(i < nlv && valid[i] &&
-                                                   !((taken[tt] >> i) & 1u) && hi[tt][i] == m[tt]);
-                    if (we < 0 && mask) we = 64 * i + (int)__builtin_ctzll(mask);
-                }
-                sel[tt][j] = we;
-                if (j == 0) top_hi[tt] = m[tt];
-                if ((we & 63) == lane) taken[tt] |= 1u << (we >> 6);
-            }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < NTOK; ++tt) sel[tt][j] = 0;
+            for (int i = kRowVals - 1; i >= 0; --i)
+                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] == m) cand = c + 16 * i;
+            const int e = row_min_i32(cand);
+            sel[j] = e;
+            mkey[j] = m;
+            if ((e & 15) == c) taken |= 1u << (e >> 4);
         }
     }
     // softmax over all E, renormalisation of the k selected probabilities
+    const float mx = from_ordered_bits(mkey[0]);
+    float z[kRowVals];
+    float zl = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < NTOK; ++tt) {
-        const int64_t t = t0 + tt;
-        const float mx = from_ordered_bits(top_hi[tt]);
-        float z[4];
+    for (int i = 0; i < kRowVals; ++i) {
+        z[i] = valid[i] ? expf(lv[i] - mx) : 0.f;
+        if (i < nv) zl = (i == 0) ? z[0] : zl + z[i];
+    }
+    const float Z = row_sum(zl);
+    const float qt = (q && tv) ? static_cast<float>(q[t]) : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = valid[i] ? expf(lv[tt][i] - mx) : 0.f;
-        float zl = z[0] + z[1];
-        zl = zl + z[2];
-        zl = zl + z[3];
-        const float Z = wave_sum(zl);
-        float p[4];
+    for (int i = 0; i < kRowVals; ++i) qp[i] = (tv && valid[i]) ? qt * (z[i] / Z) : 0.f;
+    float ps[kMaxK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = z[i] / Z;
-        if (tv[tt]) {
-            const float qt = q ? static_cast<float>(q[t]) : 1.0f;
+    for (int j = 0; j < kMaxK; ++j)
+        ps[j] = (j < k) ? expf(from_ordered_bits(mkey[j]) - mx) / Z : 0.f;
+    float sum = ps[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) macc[i] = macc[i] + qt * p[i];
-        }
-        float ps[kMaxK];
+    for (int j = 1; j < kMaxK; ++j)
+        if (j < k) sum = sum + ps[j];
+    if (tv) {
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
-            ps[j] = 0.f;
-            if (j < k) {
-                const int e = sel[tt][j];          // uniform over the wave
-                const int ri = e >> 6;
-                const float mine = ri == 0 ? p[0] : ri == 1 ? p[1] : ri == 2 ? p[2] : p[3];
-                ps[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
+            if (j < k && c == j) {
+                topk_idx[t * k + j] = sel[j];
+                topk_w[t * k + j] = ps[j] / sum;
+                if (lds_ids) lds_ids[t * k + j] = sel[j];
             }
         }
-        float sum = ps[0];
-#pragma unroll
-        for (int j = 1; j < kMaxK; ++j)
-            if (j < k) sum = sum + ps[j];
-        if (tv[tt]) {
-#pragma unroll
-            for (int j = 0; j < kMaxK; ++j) {
-                if (j < k && lane == j) {
-                    topk_idx[t * k + j] = sel[tt][j];
-                    topk_w[t * k + j] = ps[j] / sum;
-                    if (lds_ids) lds_ids[t * k + j] = sel[tt][j];
-                }
-            }
-        }
-    }
-}
-
-// The wave's tokens: all NTOK together when they all exist, else one at a time (the
-// per-token arithmetic is the same either way; macc is added in token order).
-template <int NTOK>
-__device__ __forceinline__ void route_wave(const float *__restrict__ logits,
-                                           const int32_t *__restrict__ q, int64_t t0,
-                                           int64_t T, int E, int k,
-                                           int32_t *__restrict__ topk_idx,
-                                           float *__restrict__ topk_w, int32_t *lds_ids,
-                                           float (&macc)[4], int &err) {
-    if (t0 + NTOK <= T) {
-        route_tokens<NTOK>(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, macc, err);
-    } else {
-        for (int64_t t = t0; t < T; ++t)
-            route_tokens<1>(logits, q, t, T, E, k, topk_idx, topk_w, lds_ids, macc, err);
     }
 }
 

@@ -7,12 +7,14 @@
 // offsets kept in LDS. It computes the same functions as the multi-kernel path, in the
 // same floating-point order, so each output is bitwise the one that path gives for the
 // same T:
-//   * top-k: wave w routes tokens 4w .. 4w+3 with the routine the multi-block kernel uses
+//   * top-k: wave w routes tokens 4w .. 4w+3 (one per 16-lane row) with the routine the
+//     multi-block kernel uses
 //     ("0 train-infer mismatch for Open-weight MoE RL in Open-source code", "The router:
 //     matching expert ids and weights"); replay ("Total Router Recall") is validated and
 //     passed through;
-//   * probability mass ("HARTS ...", eq. (20)): waves 4b .. 4b+3 form the 16-token group
-//     b of the multi-block kernel; group partials are ((m0 + m1) + m2) + m3 and the groups
+//   * probability mass ("HARTS ...", eq. (20)): a wave's partial is its four tokens' q·p
+//     added in token order from 0; waves 4b .. 4b+3 form the 16-token group b of the
+//     multi-block kernel; group partials are ((m0 + m1) + m2) + m3 and the groups
 //     (at most four) are added as the 256-thread reduction tree adds them,
 //     (P0 + P2) + (P1 + P3), absent groups being exact zeros;
 //   * permutation ("RoutePack ...", Sec. 2.1): the stable counting sort by expert, which
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     __shared__ int32_t eoff[kMaxE + 1];                    // counts -> exclusive offsets
     __shared__ int32_t toff[kMaxE + 1];                    // tile starts
     __shared__ unsigned long long wsum[kMaxE];
-    __shared__ float mp[kTailWaves][kMaxE];
+    __shared__ float mpt[kSmallT][kMaxE];                  // q·p per token, router mode
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int A = T * k;
     for (int i = tid; i < (kTailMaxA / kWave) * kMaxE; i += 64 * kTailWaves)
@@ -74,13 +76,14 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
             }
         }
     } else {
-        float macc[4] = {0.f, 0.f, 0.f, 0.f};
-        route_wave<kTailTokPerWave>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k,
-                                    topk_idx, topk_w, ids, macc, err);
+        float qp[kRowVals];
+        route_rows4(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k, topk_idx, topk_w, ids,
+                    qp, err);
+        if (prob_mass) {
+            const int row = wave * 4 + (lane >> 4), c = lane & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E) mp[wave][e] = macc[i];
+            for (int i = 0; i < kRowVals; ++i)
+                if (c + 16 * i < E) mpt[row][c + 16 * i] = qp[i];
         }
     }
     wave_raise(err, d_err);
@@ -121,10 +124,15 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
             float P[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                float v = mp[4 * b][tid];
-                v = v + mp[4 * b + 1][tid];
-                v = v + mp[4 * b + 2][tid];
-                v = v + mp[4 * b + 3][tid];
+                float v = 0.f;
+#pragma unroll
+                for (int w = 4 * b; w < 4 * b + 4; ++w) {
+                    float m = 0.f + mpt[4 * w][tid];
+                    m = m + mpt[4 * w + 1][tid];
+                    m = m + mpt[4 * w + 2][tid];
+                    m = m + mpt[4 * w + 3][tid];
+                    v = (w == 4 * b) ? m : v + m;
+                }
                 P[b] = v;
             }
             prob_mass[tid] = (P[0] + P[2]) + (P[1] + P[3]);
