@@ -160,6 +160,78 @@ def stage_rates(L, dims, inp, K, hip, stream):
     return out
 
 
+def placement_report(L, dims, inp, counts, K, hip, stream, P=8):
+    """Logical -> physical expert placement over P expert-parallel ranks (layer-local LPT of
+    "RoutePack ...", Sec. 3) from this step's expert counts: rank-load coefficient of
+    variation for the identity and the LPT placement, the host planner's time, and the
+    step time with the LPT placement (weights stored in slot order) next to the identity
+    one, plus the placed and plain permutation alone."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    E, H = L.E, L.E // P
+    loads = counts.astype(np.int64)
+    ident = np.array([loads[p * H:(p + 1) * H].sum() for p in range(P)], dtype=np.float64)
+    cv_id = float(np.sqrt(((ident - ident.mean()) ** 2).mean()) / ident.mean())
+    t0 = time.perf_counter()
+    for _ in range(100):
+        slots, rank_load, cv = M.place_lpt(loads, P)
+    plan_us = (time.perf_counter() - t0) / 100 * 1e6
+    dev = inp["x"].device
+    slot_t = torch.from_numpy(slots).to(dev)
+    expert_of_slot = torch.empty_like(slot_t)
+    expert_of_slot[slot_t.long()] = torch.arange(E, dtype=slot_t.dtype, device=dev)
+    w13p = inp["w13"][expert_of_slot.long()].contiguous()
+    w2p = inp["w2"][expert_of_slot.long()].contiguous()
+
+    def step_ms(slot, w13, w2):
+        b = M.alloc_forward_buffers(dims, dev, router=(L.mode == "router"))
+        del b["x_perm"]
+        b.update(x=inp["x"], w13=w13, w2=w2, slot_of_expert=slot)
+        if L.mode == "router":
+            b["w_router"], b["logit_bias"] = inp["w_router"], inp["logit_bias"]
+        else:
+            b["idx_in"], b["w_in"] = inp["idx_in"], inp["w_in"]
+        ws = M.alloc_workspace(dims, dev)
+        M.forward(dims, b, ws)
+        ev = hip.create(2)
+        hip.record(ev[0], stream.cuda_stream)
+        for _ in range(K):
+            M.forward(dims, b, ws)
+        hip.record(ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(ev[0], ev[1]) / K
+        hip.destroy(ev)
+        assert int(b["d_err"].item()) == 0
+        return ms, b
+
+    ms_id, b_id = step_ms(None, inp["w13"], inp["w2"])
+    ms_lpt, b_lpt = step_ms(slot_t, w13p, w2p)
+    same = bool(torch.equal(b_id["out"].view(torch.int16), b_lpt["out"].view(torch.int16)))
+
+    def perm_ms(slot):
+        b = M.alloc_forward_buffers(dims, dev)
+        ws = M.alloc_workspace(dims, dev)
+        args = (dims, b_id["topk_idx"], inp["x"], None, b["perm"], b["inv"], b["counts"],
+                b["offsets"])
+        M.permute(*args, workspace=ws, slot_of_expert=slot)
+        ev = hip.create(2)
+        hip.record(ev[0], stream.cuda_stream)
+        for _ in range(K):
+            M.permute(*args, workspace=ws, slot_of_expert=slot)
+        hip.record(ev[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(ev[0], ev[1]) / K
+        hip.destroy(ev)
+        return ms
+
+    return {"ranks": P, "cv_identity": round(cv_id, 5), "cv_lpt": round(cv, 6),
+            "rank_load_lpt": rank_load.tolist(), "plan_us_host": round(plan_us, 2),
+            "step_ms_identity": round(ms_id, 5), "step_ms_lpt": round(ms_lpt, 5),
+            "out_bitwise_equal": same, "permute_ms": round(perm_ms(None), 5),
+            "permute_placed_ms": round(perm_ms(slot_t), 5)}
+
+
 def copy_gbs(dev, mib=512, reps=10):
     """Measured device-to-device copy rate, (read + write bytes) / median time."""
     import torch
@@ -366,6 +438,7 @@ def main():
         M.forward(dims, b, ws)
     torch.cuda.synchronize()
     assert int(b["d_err"].item()) == 0, "device error word set"
+    host_counts = b["counts"].cpu().numpy()
 
     K = args.steps
     evs = hip.create(3 * K)
@@ -385,6 +458,7 @@ def main():
     hip.destroy(evs)
     hip.destroy(bnd)
     stages = stage_rates(L, dims, inp, K, hip, stream)
+    placement = placement_report(L, dims, inp, host_counts, K, hip, stream) if L.E % 8 == 0 else None
 
     A = L.T * L.k
     ms_step = total_ms / K
@@ -434,6 +508,7 @@ def main():
                     "p10": round(float(np.percentile(step_ms, 10)), 5),
                     "p90": round(float(np.percentile(step_ms, 90)), 5)},
         "stages_hbm": stages,
+        "placement": placement,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:

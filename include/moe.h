@@ -61,7 +61,8 @@ enum {
     MOE_DERR_IDX_RANGE = 1, /* an expert id outside [0, E) */
     MOE_DERR_IDX_DUP = 2,   /* the same expert twice in one token's replayed row */
     MOE_DERR_NONFINITE = 4, /* a NaN/Inf router logit or replayed weight */
-    MOE_DERR_SEQLENS = 8    /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_S = T */
+    MOE_DERR_SEQLENS = 8,   /* cu_seqlens not 0 = c_0 <= c_1 <= ... <= c_S = T */
+    MOE_DERR_SLOTMAP = 16   /* slot_of_expert is not a permutation of 0..E-1 */
 };
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -138,6 +139,39 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
                        int64_t *weighted_counts, int32_t *d_err, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* Dispatch with a logical->physical expert placement [RP] (RoutePack, Sec. 3 "State-
+ * consistent materialization": routing stays in logical expert ids; the dispatcher sends
+ * logical expert e to physical slot slot_of_expert[e]). The same as moe_permute with
+ * every id e replaced by its slot: counts, offsets, seq_counts and weighted_counts are
+ * per physical slot, segments are in slot order, and x_perm rows of slot v are the rows
+ * routed to the expert placed there; the expert weights handed to moe_grouped_ffn must
+ * be stored in slot order (slot v holds the weights of the expert e with
+ * slot_of_expert[e] == v). slot_of_expert [E] i32, device. A map that is not a
+ * permutation of 0..E-1 sets MOE_DERR_SLOTMAP (an entry outside [0,E) also drops the
+ * expert's rows, like an invalid id). Every output row of the layer is then bitwise the
+ * one of the identity placement. */
+moe_status moe_permute_placed(const moe_dims *dims, const int32_t *topk_idx,
+                              const int32_t *slot_of_expert, const void *x, void *x_perm,
+                              int32_t *perm, int32_t *inv, int32_t *counts, int32_t *offsets,
+                              const int32_t *cu_seqlens, int32_t num_seqs, int32_t *seq_counts,
+                              const int32_t *token_mult, int64_t *weighted_counts,
+                              int32_t *d_err, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Layer-local LPT expert placement [RP] (RoutePack, Sec. 3, Algorithm 1): host function,
+ * host pointers, no GPU work. loads [E] int64 >= 0 (aggregate routed assignments per
+ * logical expert, e.g. counts summed over an optimizer step), P ranks of H = E / P slots
+ * each (slot v belongs to rank v / H). Experts are taken in order of (load descending, id
+ * ascending); each goes to the rank with the least assigned load among the ranks that
+ * still have a free slot (equal loads: the lower rank), into that rank's next free slot
+ * (rank p's slots fill in order p*H, p*H+1, ...). Writes slot_of_expert [E] (a
+ * permutation of 0..E-1); rank_load [P] (NULL: not written) = sum of the loads placed on
+ * each rank; cv (NULL: not written) = population standard deviation of rank_load over its
+ * mean (0 when the mean is 0). MOE_E_SHAPE: E < 1, P < 1, E % P != 0, E > 256 or a
+ * negative load; MOE_E_NULLPTR: loads or slot_of_expert NULL. */
+moe_status moe_place_lpt(const int64_t *loads, int32_t E, int32_t P, int32_t *slot_of_expert,
+                         int64_t *rank_load, double *cv);
+
 /* Grouped SwiGLU experts [MM][SW][EX]. For every expert e and row p in
  * [offsets[e], offsets[e+1]):
  *   g_i = sum_c x_perm[p,c] w13[e,i,c],  u_i = sum_c x_perm[p,c] w13[e,I+i,c]   (FP32)
@@ -170,7 +204,10 @@ moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
  * of x through perm (identical results; x must then be smaller than 4 GiB, else
  * MOE_E_SHAPE).
  * prof_events: NULL, or three hipEvent_t handles recorded on `stream` before the
- * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing). */
+ * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing).
+ * slot_of_expert: NULL, or a device placement map as in moe_permute_placed (w13 and w2
+ * then hold the experts in slot order; counts/offsets/statistics are per slot; topk_idx
+ * stays in logical ids). */
 typedef struct moe_forward_args {
     const void *x;
     const void *w_router;
@@ -200,6 +237,7 @@ typedef struct moe_forward_args {
     void *workspace;
     size_t workspace_bytes;
     void *const *prof_events;
+    const int32_t *slot_of_expert; /* NULL: identity placement; else as moe_permute_placed */
 } moe_forward_args;
 
 /* The whole layer: route (or replay) -> permute -> grouped FFN -> combine, each step as

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-DERR_IDX_RANGE, DERR_IDX_DUP, DERR_NONFINITE, DERR_SEQLENS = 1, 2, 4, 8
+DERR_IDX_RANGE, DERR_IDX_DUP, DERR_NONFINITE, DERR_SEQLENS, DERR_SLOTMAP = 1, 2, 4, 8, 16
 STATUS = {0: "MOE_OK", 1: "MOE_E_NULLPTR", 2: "MOE_E_SHAPE", 3: "MOE_E_DTYPE",
           4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH"}
 
@@ -48,7 +48,8 @@ class ForwardArgs(ctypes.Structure):
                 ("logits", _P), ("prob_mass", _P), ("counts", _P), ("offsets", _P),
                 ("perm", _P), ("inv", _P), ("seq_counts", _P), ("weighted_counts", _P),
                 ("x_perm", _P), ("h", _P), ("y", _P), ("d_err", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t), ("prof_events", _P)]
+                ("workspace_bytes", ctypes.c_size_t), ("prof_events", _P),
+                ("slot_of_expert", _P)]
 
 
 # exported symbols and their signatures (argument types after the dims pointer)
@@ -64,6 +65,10 @@ _SIGS = {
                         ctypes.c_int),
     "moe_combine": ([ctypes.POINTER(Dims)] + [_P] * 4 + [_P], ctypes.c_int),
     "moe_forward": ([ctypes.POINTER(Dims), ctypes.POINTER(ForwardArgs), _P], ctypes.c_int),
+    "moe_permute_placed": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                           ctypes.c_int),
+    "moe_place_lpt": ([_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -149,14 +154,37 @@ def route_replay(dims, idx_in, w_in, topk_idx, topk_w, d_err=None, stream=None):
 
 def permute(dims, topk_idx, x, x_perm, perm, inv, counts, offsets, cu_seqlens=None,
             seq_counts=None, token_mult=None, weighted_counts=None, d_err=None,
-            workspace=None, stream=None):
+            workspace=None, stream=None, slot_of_expert=None):
+    """moe_permute, or moe_permute_placed when a device slot map is given."""
     ws = workspace if workspace is not None else alloc_workspace(dims, counts.device)
     S = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    _check(lib().moe_permute(ctypes.byref(dims), _ptr(topk_idx), _ptr(x), _ptr(x_perm),
-                             _ptr(perm), _ptr(inv), _ptr(counts), _ptr(offsets),
-                             _ptr(cu_seqlens), S, _ptr(seq_counts), _ptr(token_mult),
-                             _ptr(weighted_counts), _ptr(d_err), _ptr(ws), ws.numel(),
-                             _stream(stream)), "moe_permute")
+    if slot_of_expert is None:
+        _check(lib().moe_permute(ctypes.byref(dims), _ptr(topk_idx), _ptr(x), _ptr(x_perm),
+                                 _ptr(perm), _ptr(inv), _ptr(counts), _ptr(offsets),
+                                 _ptr(cu_seqlens), S, _ptr(seq_counts), _ptr(token_mult),
+                                 _ptr(weighted_counts), _ptr(d_err), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "moe_permute")
+    else:
+        _check(lib().moe_permute_placed(ctypes.byref(dims), _ptr(topk_idx), _ptr(slot_of_expert),
+                                        _ptr(x), _ptr(x_perm), _ptr(perm), _ptr(inv),
+                                        _ptr(counts), _ptr(offsets), _ptr(cu_seqlens), S,
+                                        _ptr(seq_counts), _ptr(token_mult),
+                                        _ptr(weighted_counts), _ptr(d_err), _ptr(ws),
+                                        ws.numel(), _stream(stream)), "moe_permute_placed")
+
+
+def place_lpt(loads, P: int):
+    """moe_place_lpt on host arrays: loads [E] int64 -> (slot_of_expert [E] int32,
+    rank_load [P] int64, cv float)."""
+    import numpy as np
+    loads = np.ascontiguousarray(loads, dtype=np.int64)
+    E = loads.shape[0]
+    slots = np.empty(E, dtype=np.int32)
+    rank_load = np.empty(max(P, 1), dtype=np.int64)
+    cv = ctypes.c_double()
+    _check(lib().moe_place_lpt(loads.ctypes.data, E, P, slots.ctypes.data,
+                               rank_load.ctypes.data, ctypes.addressof(cv)), "moe_place_lpt")
+    return slots, rank_load[:P], cv.value
 
 
 def grouped_ffn(dims, x_perm, offsets, w13, w2, h, y, workspace=None, stream=None):

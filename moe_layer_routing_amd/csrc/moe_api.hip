@@ -114,12 +114,13 @@ moe_status moe_route_replay(const moe_dims *dims, const int32_t *idx_in, const f
                                    static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
-                       void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
-                       int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
-                       int32_t *seq_counts, const int32_t *token_mult,
-                       int64_t *weighted_counts, int32_t *d_err, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+static moe_status permute_impl(const moe_dims *dims, const int32_t *topk_idx,
+                               const int32_t *slot_map, const void *x, void *x_perm,
+                               int32_t *perm, int32_t *inv, int32_t *counts, int32_t *offsets,
+                               const int32_t *cu_seqlens, int32_t num_seqs,
+                               int32_t *seq_counts, const int32_t *token_mult,
+                               int64_t *weighted_counts, int32_t *d_err, void *workspace,
+                               size_t workspace_bytes, void *stream) {
     moe_status st = check_common(dims);
     if (st != MOE_OK) return st;
     MOE_REQUIRE(counts && offsets, MOE_E_NULLPTR);
@@ -133,7 +134,71 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void
     return to_status(launch_permute(*dims, topk_idx, x, x_perm, perm, inv, counts, offsets,
                                     cu_seqlens, seq_counts ? num_seqs : 0, seq_counts,
                                     token_mult, weighted_counts, d_err, ws,
-                                    static_cast<hipStream_t>(stream)));
+                                    static_cast<hipStream_t>(stream), slot_map));
+}
+
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, const void *x,
+                       void *x_perm, int32_t *perm, int32_t *inv, int32_t *counts,
+                       int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
+                       int32_t *seq_counts, const int32_t *token_mult,
+                       int64_t *weighted_counts, int32_t *d_err, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return permute_impl(dims, topk_idx, nullptr, x, x_perm, perm, inv, counts, offsets,
+                        cu_seqlens, num_seqs, seq_counts, token_mult, weighted_counts, d_err,
+                        workspace, workspace_bytes, stream);
+}
+
+moe_status moe_permute_placed(const moe_dims *dims, const int32_t *topk_idx,
+                              const int32_t *slot_of_expert, const void *x, void *x_perm,
+                              int32_t *perm, int32_t *inv, int32_t *counts, int32_t *offsets,
+                              const int32_t *cu_seqlens, int32_t num_seqs, int32_t *seq_counts,
+                              const int32_t *token_mult, int64_t *weighted_counts,
+                              int32_t *d_err, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    MOE_REQUIRE(slot_of_expert, MOE_E_NULLPTR);
+    return permute_impl(dims, topk_idx, slot_of_expert, x, x_perm, perm, inv, counts, offsets,
+                        cu_seqlens, num_seqs, seq_counts, token_mult, weighted_counts, d_err,
+                        workspace, workspace_bytes, stream);
+}
+
+// RoutePack, Sec. 3, Algorithm 1 ("Layer-local LPT expert placement"): experts in order of
+// (load desc, id asc), each onto the least-loaded rank that still has a free slot (ties to
+// the lower rank), into that rank's next free slot. Host code; E <= 256, so the
+// O(E log E + E P) cost is negligible.
+moe_status moe_place_lpt(const int64_t *loads, int32_t E, int32_t P, int32_t *slot_of_expert,
+                         int64_t *rank_load, double *cv) {
+    MOE_REQUIRE(loads && slot_of_expert, MOE_E_NULLPTR);
+    MOE_REQUIRE(E >= 1 && E <= kMaxE && P >= 1 && E % P == 0, MOE_E_SHAPE);
+    for (int32_t e = 0; e < E; ++e) MOE_REQUIRE(loads[e] >= 0, MOE_E_SHAPE);
+    const int32_t H = E / P;
+    int32_t order[kMaxE];
+    for (int32_t e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order, order + E, [&](int32_t a, int32_t b) {
+        return loads[a] > loads[b];  // stable: equal loads keep increasing id
+    });
+    int64_t G[kMaxE] = {0};
+    int32_t n[kMaxE] = {0};
+    for (int32_t i = 0; i < E; ++i) {
+        const int32_t e = order[i];
+        int32_t best = -1;
+        for (int32_t p = 0; p < P; ++p)
+            if (n[p] < H && (best < 0 || G[p] < G[best])) best = p;
+        slot_of_expert[e] = best * H + n[best];
+        G[best] += loads[e];
+        n[best] += 1;
+    }
+    if (rank_load)
+        for (int32_t p = 0; p < P; ++p) rank_load[p] = G[p];
+    if (cv) {
+        double mean = 0.0;
+        for (int32_t p = 0; p < P; ++p) mean += (double)G[p];
+        mean /= P;
+        double var = 0.0;
+        for (int32_t p = 0; p < P; ++p) var += ((double)G[p] - mean) * ((double)G[p] - mean);
+        var /= P;
+        *cv = mean > 0.0 ? std::sqrt(var) / mean : 0.0;
+    }
+    return MOE_OK;
 }
 
 moe_status moe_grouped_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
@@ -188,7 +253,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
         }
         e = launch_small_tail(*dims, logits, a->token_mult, a->idx_in, a->w_in, a->topk_idx,
                               a->topk_w, a->prob_mass, a->counts, a->offsets, a->perm, a->inv,
-                              a->weighted_counts, ws.tiles, a->d_err, s);
+                              a->weighted_counts, ws.tiles, a->d_err, s, a->slot_of_expert);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         if (a->x_perm) {
             e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);
@@ -208,7 +273,8 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_permute(*dims, a->topk_idx, a->x, a->x_perm, a->perm, a->inv, a->counts,
                        a->offsets, a->cu_seqlens, a->seq_counts ? a->num_seqs : 0,
-                       a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s);
+                       a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s,
+                       a->slot_of_expert);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                            a->prof_events, s, a->x, a->perm);

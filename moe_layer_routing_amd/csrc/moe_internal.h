@@ -37,6 +37,23 @@ __device__ __forceinline__ void raise_err(int32_t *d_err, int32_t bits) {
     if (d_err && bits) atomicOr(d_err, bits);
 }
 
+// Physical slot of routed expert id e under a placement map (identity when map is null):
+// -1 for an id outside [0, E) (*bits gets MOE_DERR_IDX_RANGE) or a map entry outside [0, E)
+// (*bits gets MOE_DERR_SLOTMAP).
+__device__ __forceinline__ int slot_of(const int32_t *map, int e, int E, int &bits) {
+    if (e < 0 || e >= E) {
+        bits |= MOE_DERR_IDX_RANGE;
+        return -1;
+    }
+    if (!map) return e;
+    const int v = map[e];
+    if (v < 0 || v >= E) {
+        bits |= MOE_DERR_SLOTMAP;
+        return -1;
+    }
+    return v;
+}
+
 // Lanes of the wave whose 9-bit key equals this lane's, found with one ballot per key bit.
 __device__ __forceinline__ uint64_t wave_match9(uint32_t key) {
     uint64_t peers = ~0ull;
@@ -91,7 +108,9 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
-                          hipStream_t s);
+                          hipStream_t s, const int32_t *slot_map = nullptr);
+// Raises MOE_DERR_SLOTMAP unless map[0..E-1] is a permutation of 0..E-1 (one block).
+hipError_t launch_check_slot_map(const int32_t *map, int E, int32_t *d_err, hipStream_t s);
 // x_perm == nullptr: gather token rows of x through perm inside the gate/up GEMM.
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
@@ -118,6 +137,6 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int3
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                             hipStream_t s);
+                             hipStream_t s, const int32_t *slot_map = nullptr);
 
 }  // namespace moe

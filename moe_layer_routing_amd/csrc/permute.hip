@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
                                                    const int32_t *__restrict__ q,
                                                    int32_t *__restrict__ blk_hist,
                                                    uint64_t *__restrict__ blk_whist,
-                                                   int32_t *__restrict__ d_err) {
+                                                   int32_t *__restrict__ d_err,
+                                                   const int32_t *__restrict__ slot) {
     __shared__ int32_t hist[kMaxE];
     __shared__ unsigned long long whist[kMaxE];
     for (int e = threadIdx.x; e < E; e += 256) {
@@ -36,11 +37,8 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
     for (int i = threadIdx.x; i < kPermChunk; i += 256) {
         const int64_t a = base + i;
         if (a >= A) break;
-        const int e = idx[a];
-        if (e < 0 || e >= E) {
-            err |= MOE_DERR_IDX_RANGE;
-            continue;
-        }
+        const int e = slot_of(slot, idx[a], E, err);
+        if (e < 0) continue;
         atomicAdd(&hist[e], 1);
         if (blk_whist && q) atomicAdd(&whist[e], (unsigned long long)(uint32_t)q[a / k]);
     }
@@ -101,7 +99,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
                                                       int64_t A, int E,
                                                       const int32_t *__restrict__ blk_off,
                                                       int32_t *__restrict__ perm,
-                                                      int32_t *__restrict__ inv) {
+                                                      int32_t *__restrict__ inv,
+                                                      const int32_t *__restrict__ slot) {
     __shared__ int32_t cur[4][kMaxE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int i = threadIdx.x; i < 4 * kMaxE; i += 256) (&cur[0][0])[i] = 0;
@@ -109,8 +108,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
     const int64_t base = (int64_t)blockIdx.x * kPermChunk + wave * kSubChunk;
     for (int it = 0; it < kSubChunk / kWave; ++it) {
         const int64_t a = base + it * kWave + lane;
-        const int e = a < A ? idx[a] : -1;
-        if (e >= 0 && e < E) atomicAdd(&cur[wave][e], 1);
+        int bits = 0;
+        const int e = a < A ? slot_of(slot, idx[a], E, bits) : -1;
+        if (e >= 0) atomicAdd(&cur[wave][e], 1);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) {
@@ -126,8 +126,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int it = 0; it < kSubChunk / kWave; ++it) {
         const int64_t a = base + it * kWave + lane;
-        const int e0 = a < A ? idx[a] : -1;
-        const bool valid = e0 >= 0 && e0 < E;
+        int bits = 0;
+        const int e0 = a < A ? slot_of(slot, idx[a], E, bits) : -1;
+        const bool valid = e0 >= 0;
         const uint32_t key = valid ? (uint32_t)e0 : 0x1ffu;  // 9 bits; invalid never matches
         const uint64_t peers = wave_match9(key);
         if (valid) {
@@ -190,7 +191,8 @@ __global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict
                                                        const int32_t *__restrict__ cu,
                                                        int S,
                                                        int32_t *__restrict__ seq_counts,
-                                                       int32_t *__restrict__ d_err) {
+                                                       int32_t *__restrict__ d_err,
+                                                       const int32_t *__restrict__ slot) {
     __shared__ int32_t hist[kMaxE];
     // validate cu_seqlens: 0 = c_0 <= c_1 <= ... <= c_S = T
     int bad = 0;
@@ -217,8 +219,9 @@ __global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict
         for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
         __syncthreads();
         for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
-            const int e = idx[a];
-            if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+            int bits = 0;
+            const int e = slot_of(slot, idx[a], E, bits);
+            if (e >= 0) atomicAdd(&hist[e], 1);
         }
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += 256)
@@ -227,7 +230,30 @@ __global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict
     }
 }
 
+// MOE_DERR_SLOTMAP unless map is a permutation of 0..E-1 (E <= kMaxE).
+__global__ __launch_bounds__(256) void check_slot_map_kernel(const int32_t *__restrict__ map,
+                                                             int E, int32_t *__restrict__ d_err) {
+    __shared__ int32_t seen[kMaxE];
+    for (int v = threadIdx.x; v < E; v += 256) seen[v] = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const int v = map[e];
+        if (v < 0 || v >= E) bad = 1;
+        else atomicAdd(&seen[v], 1);
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < E; v += 256)
+        if (seen[v] != 1) bad = 1;
+    if (bad) raise_err(d_err, MOE_DERR_SLOTMAP);
+}
+
 }  // namespace
+
+hipError_t launch_check_slot_map(const int32_t *map, int E, int32_t *d_err, hipStream_t s) {
+    check_slot_map_kernel<<<dim3(1), dim3(256), 0, s>>>(map, E, d_err);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather(const moe_dims &dm, const void *x, const int32_t *inv, void *x_perm,
                          hipStream_t s) {
@@ -245,20 +271,25 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
-                          hipStream_t s) {
+                          hipStream_t s, const int32_t *slot_map) {
     const int64_t T = dm.T, A = dm.T * dm.k;
     const int E = dm.E, k = dm.k;
     const int64_t nchunks = perm_chunks(A);
     const bool have_q = token_mult != nullptr;
+    if (slot_map) {
+        const hipError_t me = launch_check_slot_map(slot_map, E, d_err, s);
+        if (me != hipSuccess) return me;
+    }
     if (nchunks > 0)
         hist_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
             topk_idx, A, k, E, token_mult, ws.blk_hist,
-            (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err);
+            (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err, slot_map);
     scan_kernel<<<dim3(1), dim3(256), 0, s>>>(ws.blk_hist, ws.blk_whist, nchunks, E, have_q,
                                               counts, offsets, weighted_counts);
     if (nchunks > 0)
         scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
-                                                                     ws.blk_hist, perm, inv);
+                                                                     ws.blk_hist, perm, inv,
+                                                                     slot_map);
     if (x_perm) {
         const hipError_t ge = launch_gather(dm, x, inv, x_perm, s);
         if (ge != hipSuccess) return ge;
@@ -269,7 +300,7 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           0, s>>>(seq_counts, n, 0);
         if (T > 0)
             seq_hist_kernel<<<dim3((unsigned)((T + kSeqTok - 1) / kSeqTok)), dim3(256), 0, s>>>(
-                topk_idx, T, k, E, cu_seqlens, num_seqs, seq_counts, d_err);
+                topk_idx, T, k, E, cu_seqlens, num_seqs, seq_counts, d_err, slot_map);
     }
     return hipGetLastError();
 }

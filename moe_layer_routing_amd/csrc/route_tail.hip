@@ -17,8 +17,9 @@
 //     multi-block kernel; group partials are ((m0 + m1) + m2) + m3 and the groups
 //     (at most four) are added as the 256-thread reduction tree adds them,
 //     (P0 + P2) + (P1 + P3), absent groups being exact zeros;
-//   * permutation ("RoutePack ...", Sec. 2.1): the stable counting sort by expert, which
-//     has one result; wave w ranks the flat assignments [64w, 64w + 64);
+//   * permutation ("RoutePack ...", Sec. 2.1): the stable counting sort by expert (by the
+//     expert's physical slot under a placement map, Sec. 3), which has one result; wave w
+//     ranks the flat assignments [64w, 64w + 64);
 //   * token tiles: ceil(count_e / bt) tiles per expert in expert order.
 #include "route_dev.h"
 
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     float *__restrict__ prob_mass, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int64_t *__restrict__ weighted_counts, int32_t *__restrict__ tiles,
-    int32_t *__restrict__ d_err) {
+    int32_t *__restrict__ d_err, const int32_t *__restrict__ slot_map) {
     __shared__ int32_t ids[kTailMaxA];
     __shared__ int32_t wstart[kTailMaxA / kWave][kMaxE];  // per-wave counts -> run starts
     __shared__ int32_t eoff[kMaxE + 1];                    // counts -> exclusive offsets
@@ -96,9 +97,8 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     bool valid = false;
     err = 0;
     if (wave < nwv) {  // uniform per wave
-        e0 = a < A ? ids[a] : -1;
-        valid = e0 >= 0 && e0 < E;
-        if (a < A && !valid) err |= MOE_DERR_IDX_RANGE;
+        e0 = a < A ? slot_of(slot_map, ids[a], E, err) : -1;   // physical slot
+        valid = e0 >= 0;
         const uint64_t peers = wave_match9(valid ? (uint32_t)e0 : 0x1ffu);
         const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         before = __popcll(peers & lt_mask);
@@ -202,19 +202,23 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int3
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                             hipStream_t s) {
+                             hipStream_t s, const int32_t *slot_map) {
     if (dm.T < 1 || dm.T > kSmallT || dm.E > kMaxE || dm.k > kMaxK)
         return hipErrorInvalidValue;
+    if (slot_map) {
+        const hipError_t me = launch_check_slot_map(slot_map, dm.E, d_err, s);
+        if (me != hipSuccess) return me;
+    }
     const int bt = select_tile_m(dm);
     const int cap = (int)max_m_tiles(dm.T * dm.k, dm.E, bt);
     if (idx_in)
         route_tail_kernel<true><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
             logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
-            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err);
+            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map);
     else
         route_tail_kernel<false><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
             logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
-            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err);
+            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map);
     return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ def lib():
         L.orc_combine.restype = None
         L.orc_round_bf16.argtypes = [P, P, I64]
         L.orc_round_bf16.restype = None
+        L.orc_place_lpt.argtypes = [P, I32, I32, P, P]
+        L.orc_place_lpt.restype = I32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = I32
         _lib = L
@@ -145,6 +147,37 @@ def permute(idx, E: int):
     inv = np.empty(T * k, dtype=np.int32)
     err = lib().orc_permute(_p(idx), T, k, E, _p(counts), _p(offsets), _p(perm), _p(inv))
     return counts, offsets, perm, inv, err
+
+
+def place_lpt(loads, P: int):
+    """Layer-local LPT expert placement ("RoutePack ...", Sec. 3, Algorithm 1). Returns
+    (slot_of_expert [E] int32, rank_load [P] int64, cv) where cv is the population standard
+    deviation of the rank loads over their mean (the rank-load coefficient of variation of
+    the same page's Sec. 5; 0 for a zero mean), computed in float64."""
+    loads = _c(loads, np.int64)
+    E = loads.shape[0]
+    slots = np.empty(E, dtype=np.int32)
+    rank_load = np.empty(P, dtype=np.int64)
+    err = lib().orc_place_lpt(_p(loads), E, P, _p(slots), _p(rank_load))
+    if err:
+        raise ValueError("place_lpt: need E >= 1, P >= 1 and E % P == 0")
+    mean = float(rank_load.sum()) / P
+    var = sum((float(g) - mean) ** 2 for g in rank_load) / P
+    cv = (var ** 0.5) / mean if mean > 0 else 0.0
+    return slots, rank_load, cv
+
+
+def place(idx, slot_of_expert):
+    """The dispatcher's view of a placement ("RoutePack ...", Sec. 3, state-consistent
+    materialization): every logical id replaced by the physical slot that stores it. Ids
+    outside the map stay out of range (so they are still reported and dropped)."""
+    idx = np.asarray(idx)
+    m = np.asarray(slot_of_expert)
+    out = np.full(idx.shape, -1, dtype=np.int32)
+    ok = (idx >= 0) & (idx < len(m))
+    out[ok] = m[idx[ok]]
+    out[~ok] = idx[~ok]
+    return out
 
 
 def seq_counts(idx, E: int, cu_seqlens):

@@ -334,3 +334,37 @@ int orc_num_threads(void) {
     }
     return n;
 }
+
+/* Layer-local LPT placement ("RoutePack ...", Sec. 3, Algorithm 1). P ranks of H = E/P
+ * slots; slot v belongs to rank v / H. Experts are visited in order of decreasing load,
+ * equal loads by increasing id (picked by a plain selection scan over the unvisited
+ * experts); each goes to the rank with the smallest accumulated load among the ranks
+ * with a free slot, equal loads to the lower rank, and takes that rank's next slot.
+ * rank_load [P] receives the accumulated loads. Returns 0, or 1 for bad arguments. */
+int orc_place_lpt(const int64_t *loads, int E, int P, int32_t *slot_of_expert,
+                  int64_t *rank_load) {
+    if (E < 1 || P < 1 || E % P != 0) return 1;
+    const int H = E / P;
+    unsigned char *done = (unsigned char *)calloc((size_t)E, 1);
+    int32_t *filled = (int32_t *)calloc((size_t)P, sizeof(int32_t));
+    for (int p = 0; p < P; ++p) rank_load[p] = 0;
+    for (int step = 0; step < E; ++step) {
+        int pick = -1;
+        for (int e = 0; e < E; ++e) {
+            if (done[e]) continue;
+            if (pick < 0 || loads[e] > loads[pick]) pick = e;  /* first max = lowest id */
+        }
+        int rank = -1;
+        for (int p = 0; p < P; ++p) {
+            if (filled[p] >= H) continue;
+            if (rank < 0 || rank_load[p] < rank_load[rank]) rank = p; /* first min = lowest */
+        }
+        slot_of_expert[pick] = rank * H + filled[rank];
+        filled[rank] += 1;
+        rank_load[rank] += loads[pick];
+        done[pick] = 1;
+    }
+    free(done);
+    free(filled);
+    return 0;
+}
