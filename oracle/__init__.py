@@ -59,6 +59,12 @@ def lib():
         L.orc_expert_ffn.restype = None
         L.orc_combine.argtypes = [P, P, P, I64, I32, I32, I32, P]
         L.orc_combine.restype = None
+        L.orc_combine_scaled.argtypes = [P, P, P, I64, I32, I32, I32, ctypes.c_float, P]
+        L.orc_combine_scaled.restype = None
+        L.orc_route_scored.argtypes = [P, P, I64, I32, I32, I32, P, P, P, I32, P, P, P, P, P]
+        L.orc_route_scored.restype = I32
+        L.orc_objectives.argtypes = [P, P, I64, P, P, I32, I32, ctypes.c_float, P, P]
+        L.orc_objectives.restype = None
         L.orc_round_bf16.argtypes = [P, P, I64]
         L.orc_round_bf16.restype = None
         L.orc_place_lpt.argtypes = [P, I32, I32, P, P]
@@ -126,6 +132,57 @@ def route_from_logits(logits, k: int, token_mult=None, want_probs: bool = False)
     if want_probs:
         return idx, w, mass, err, probs
     return idx, w, mass, err
+
+
+SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
+
+
+def route_scored(logits, k: int, score: str = "sigmoid", corr_bias=None, hash_table=None,
+                 token_ids=None, token_mult=None):
+    """Router variants: softmax, or sigmoid / sqrt-softplus scores (FP64, rounded once to
+    FP32) with a selection-only FP32 correction bias ("0 train-infer mismatch ...",
+    "Choosing GLM's eight experts"), or hash routing from a frozen token-id table ("Hash and
+    learned expert routing"); weights = the selected pre-bias values normalised left to
+    right in FP32; q-weighted probability mass and per-token log-sum-exp (HARTS, eq. (20)).
+    Returns dict(idx, w, scores, prob_mass, lse, err)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    q = _c(token_mult, np.int32)
+    b = _c(corr_bias, np.float32)
+    tab = _c(hash_table, np.int32)
+    tok = _c(token_ids, np.int32)
+    V = 0 if tab is None else tab.shape[0]
+    if tab is not None and tab.shape[1] != k:
+        raise ValueError("hash table rows must hold k experts")
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    sc = np.empty((T, E), dtype=np.float32)
+    mass = np.empty(E, dtype=np.float32)
+    lse = np.empty(T, dtype=np.float32)
+    err = lib().orc_route_scored(_p(logits), _p(q), T, E, k, SCORES[score], _p(b), _p(tab),
+                                 _p(tok), V, _p(idx), _p(w), _p(sc), _p(mass), _p(lse))
+    if err < 0:
+        raise ValueError("bad router-variant arguments")
+    return dict(idx=idx, w=w, scores=sc, prob_mass=mass, lse=lse, err=err)
+
+
+def objectives(lse, token_mult, weighted_counts, prob_mass, k: int, rate: float = 0.0,
+               corr_bias=None):
+    """q-weighted router z-loss, load-balancing loss and expert-bias update (HARTS, eq. (20)
+    and "MoE execution and objectives"). Counts and mass in logical expert order. Returns
+    (z_loss, aux_loss, S, updated bias or None)."""
+    lse = _c(lse, np.float32)
+    q = _c(token_mult, np.int32)
+    C = _c(weighted_counts, np.int64)
+    M = _c(prob_mass, np.float32)
+    E = len(C) if C is not None else (len(M) if M is not None else 0)
+    T = 0 if lse is None else len(lse)
+    if lse is None and q is not None:
+        T = len(q)
+    b = None if corr_bias is None else np.array(corr_bias, dtype=np.float32, copy=True)
+    out = np.zeros(3, dtype=np.float64)
+    lib().orc_objectives(_p(lse), _p(q), T, _p(C), _p(M), E, k, rate, _p(b), _p(out))
+    return float(out[0]), float(out[1]), int(out[2]), b
 
 
 def replay_check(idx, w, E: int) -> int:
@@ -223,15 +280,19 @@ def expert_ffn(xrows, rowexp, w13, w2, dtype: str):
     return h, y
 
 
-def combine(y, inv, w, dtype: str):
-    """Slot-order FP32 weighted sum, rounded once to the output dtype."""
+def combine(y, inv, w, dtype: str, scale: float = 1.0):
+    """Slot-order FP32 weighted sum, times the routed scaling factor, rounded once to the
+    output dtype."""
     y = _c(y, np.float32)
     inv = _c(inv, np.int32)
     w = _c(w, np.float32)
     T, k = w.shape
     d = y.shape[1]
     out = np.empty((T, d), dtype=_store_dtype(dtype))
-    lib().orc_combine(_p(y), _p(inv), _p(w), T, k, d, _dt(dtype), _p(out))
+    if scale == 1.0:
+        lib().orc_combine(_p(y), _p(inv), _p(w), T, k, d, _dt(dtype), _p(out))
+    else:
+        lib().orc_combine_scaled(_p(y), _p(inv), _p(w), T, k, d, _dt(dtype), scale, _p(out))
     return out
 
 
@@ -245,7 +306,15 @@ def forward(L, logits: Optional[np.ndarray] = None, S_stats: bool = True) -> dic
         own = router_logits(L.x, L.w_router, L.logit_bias, L.dtype)
         res["logits"] = own
         use = own if logits is None else logits
-        idx, w, mass, e = route_from_logits(use, L.k, L.token_mult)
+        score = getattr(L, "score", "softmax")
+        if score == "softmax" and getattr(L, "hash_table", None) is None:
+            idx, w, mass, e = route_from_logits(use, L.k, L.token_mult)
+            res["lse"] = route_scored(use, L.k, "softmax", token_mult=L.token_mult)["lse"]
+        else:
+            r = route_scored(use, L.k, score, L.corr_bias, L.hash_table, L.token_ids,
+                             L.token_mult)
+            idx, w, mass, e = r["idx"], r["w"], r["prob_mass"], r["err"]
+            res["lse"] = r["lse"]
         res["prob_mass"] = mass
         err |= e
     else:
@@ -266,7 +335,7 @@ def forward(L, logits: Optional[np.ndarray] = None, S_stats: bool = True) -> dic
     rowexp = np.repeat(np.arange(L.E, dtype=np.int32), counts)
     h, y = expert_ffn(x_perm, rowexp, L.w13, L.w2, L.dtype)
     res["h"], res["y"] = h, y
-    res["out"] = combine(y, inv, w, L.dtype)
+    res["out"] = combine(y, inv, w, L.dtype, getattr(L, "routed_scale", 1.0))
     res["err"] = err
     return res
 
@@ -281,6 +350,6 @@ def forward_tokens(L, tokens, idx, w):
     xr = np.ascontiguousarray(np.repeat(L.x[tokens], k, axis=0))
     h, y = expert_ffn(xr, sel_idx.reshape(-1), L.w13, L.w2, L.dtype)
     inv = np.arange(len(tokens) * k, dtype=np.int32)
-    out = combine(y, inv, sel_w, L.dtype)
+    out = combine(y, inv, sel_w, L.dtype, getattr(L, "routed_scale", 1.0))
     n = len(tokens)
     return h.reshape(n, k, -1), y.reshape(n, k, -1), out

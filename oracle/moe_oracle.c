@@ -7,7 +7,9 @@
  * It shares no code, header, table or helper with the HIP library.
  *
  * Every floating-point step is FP32 (the precision the pages fix for router softmax,
- * routing weights and the expert accumulators), evaluated in one written-out sequential
+ * routing weights and the expert accumulators) except two: the sigmoid / sqrt-softplus
+ * router scores are evaluated in FP64 and rounded once to FP32, and the objective
+ * statistics accumulate in FP64. Each is evaluated in one written-out sequential
  * order, built with -ffp-contract=off and without fast-math so no step is fused or
  * reordered. OpenMP is used only across independent rows: each result is computed by
  * one thread in the same order whatever the thread count.
@@ -17,12 +19,15 @@
  *        "Matrix multiplication: the same reduction along K".
  *  [SW]  same page, "SwiGLU: rounding after the multiply".
  *  [RT]  same page, "Mixture-of-experts layers" / "The router: matching expert ids and
- *        weights".
+ *        weights" / "Choosing GLM's eight experts" (sigmoid scores, FP32 correction bias
+ *        for the choice only, FP32-normalised pre-bias weights, factor 2.5 applied by the
+ *        expert kernel).
  *  [EX]  same page, "The experts: keeping the route weight inside the accumulator" and
  *        "Sharding the experts" (slot-order FP32 accumulation, rounded once).
  *  [TRR] same page, "Total Router Recall" (replayed ids as ints + normalized FP32
- *        weights, used as given) and "Hash and learned expert routing" (weights, ids and
- *        slot order preserved through the expert forward).
+ *        weights, used as given) and "Hash and learned expert routing" (frozen token-id
+ *        table, sqrt-softplus scores; weights, ids and slot order preserved through the
+ *        expert forward).
  *  [SEL] same page, "Selecting sparse-attention positions" (lower position wins ties;
  *        adopted for expert ties).
  *  [RP]  "RoutePack: Expert Placement and Attention-Aware Data Packing for MoE
@@ -46,6 +51,10 @@
 #define ORC_ERR_IDX_DUP 2
 #define ORC_ERR_NONFINITE 4
 #define ORC_ERR_SEQLENS 8
+
+#define ORC_SCORE_SOFTMAX 0
+#define ORC_SCORE_SIGMOID 1
+#define ORC_SCORE_SQRT_SOFTPLUS 2
 
 /* bfloat16 <-> float32. Widening is exact; narrowing rounds to nearest, ties to even. */
 static float orc_bf16_to_f32(uint16_t b) {
@@ -305,8 +314,14 @@ void orc_expert_ffn(const void *xr, const int32_t *rowexp, int64_t n, int d, int
 /* [EX], [RT]: out[t,o] = round_out( ((0 + w_0 Y_0) + w_1 Y_1) + ... ) over the slots in
  * slot order, every product and sum in FP32, one final rounding (bf16 for dt=1). Y_j is
  * row inv[t*k+j] of y (the expert output of assignment (t,j)). */
-void orc_combine(const float *y, const int32_t *inv, const float *w, int64_t T, int k,
-                 int d, int dt, void *out) {
+/* [EX], [RT]: out[t,o] = round_out( scale * ( ((0 + w_0 Y_0) + w_1 Y_1) + ... ) ) over
+ * the slots in slot order, every product and sum in FP32, one final rounding (bf16 for
+ * dt=1). Y_j is row inv[t*k+j] of y (the expert output of assignment (t,j)). scale is the
+ * routed scaling factor the expert kernel applies to the weighted sum ("Choosing GLM's
+ * eight experts": the factor is applied inside the expert kernel to FP32 weights); 1 for
+ * routers without one (a multiplication by 1 is exact). */
+void orc_combine_scaled(const float *y, const int32_t *inv, const float *w, int64_t T,
+                        int k, int d, int dt, float scale, void *out) {
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int o = 0; o < d; ++o) {
@@ -315,9 +330,14 @@ void orc_combine(const float *y, const int32_t *inv, const float *w, int64_t T, 
                 float prod = w[t * k + j] * y[(int64_t)inv[t * k + j] * d + o];
                 acc = acc + prod;
             }
-            orc_store(out, t * (int64_t)d + o, acc, dt);
+            orc_store(out, t * (int64_t)d + o, scale * acc, dt);
         }
     }
+}
+
+void orc_combine(const float *y, const int32_t *inv, const float *w, int64_t T, int k,
+                 int d, int dt, void *out) {
+    orc_combine_scaled(y, inv, w, T, k, d, dt, 1.0f, out);
 }
 
 int orc_num_threads(void) {
@@ -367,4 +387,190 @@ int orc_place_lpt(const int64_t *loads, int E, int P, int32_t *slot_of_expert,
     free(done);
     free(filled);
     return 0;
+}
+
+/* Scores of the learned routers, each the real function evaluated in FP64 and rounded
+ * once to FP32 (so that two correct implementations agree on the FP32 score, and with it
+ * on the selection, except where the FP64 value falls within an FP64 rounding error of a
+ * point halfway between two FP32 numbers):
+ *   ORC_SCORE_SIGMOID        s = 1 / (1 + e^-l)   ("Choosing GLM's eight experts");
+ *   ORC_SCORE_SQRT_SOFTPLUS  s = sqrt(log(1 + e^l))   ("Hash and learned expert routing"),
+ *                            with log(1 + e^l) written as max(l, 0) + log1p(e^-|l|). */
+static float orc_score(float l, int fn) {
+    double x = (double)l;
+    if (fn == ORC_SCORE_SIGMOID) return (float)(1.0 / (1.0 + exp(-x)));
+    double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+    return (float)sqrt(sp);
+}
+
+/* Does expert a rank before expert b under selection key values ka, kb? */
+static int orc_key_before(float ka, int a, float kb, int b) {
+    if (ka > kb) return 1;
+    if (ka < kb) return 0;
+    return a < b;
+}
+
+/* Router variants, from the logits, token by token:
+ *  - per-expert value v[t,e]: fn ORC_SCORE_SOFTMAX: p = exp(l - m) / Z (m = the largest
+ *    logit, Z summed over e ascending) [RT]; fn SIGMOID / SQRT_SOFTPLUS: s = score(l);
+ *  - selection, when hash_table is NULL: fn SOFTMAX keys on the logit as
+ *    orc_route_from_logits does (corr_bias must then be NULL); the scored routers key on
+ *    s + corr_bias[e] (FP32 add; bias 0 when corr_bias is NULL): the k experts first in
+ *    the order (key desc, id asc), slot 0 = largest. The bias chooses the experts only
+ *    ("Choosing GLM's eight experts": FP32 correction bias added before choosing the top
+ *    eight);
+ *  - hash routing ("Hash and learned expert routing": a frozen table maps each token id to
+ *    its experts, the logits only set the weights): slot j holds
+ *    hash_table[token_ids[t] * k + j], in the table's order. A token id outside [0, V)
+ *    sets ORC_ERR_IDX_RANGE and the row gets ids -1 and weights 0; a table id outside
+ *    [0, E) or repeated within the row sets ORC_ERR_IDX_RANGE / ORC_ERR_IDX_DUP, the ids
+ *    pass through and the row's weights are 0;
+ *  - weights: w_j = v[sel_j] / ((v[sel_0] + v[sel_1]) + ...), the values before the bias
+ *    normalised in FP32, left to right in slot order;
+ *  - routing probabilities for the mass: fn SOFTMAX: p; the scored routers: s_e / sum_e s_e
+ *    (e ascending); prob_mass[e] = sum over t ascending of q_t * prob[t,e] [HA];
+ *  - lse[t] = m + log(Z), the log-sum-exp of the token's logits in FP32 (z-loss input).
+ * scores (optional [T,E]) receives v. Non-finite logits set ORC_ERR_NONFINITE.
+ * Returns the error bits, or -1 for bad dimensions or a bias with the softmax router. */
+int orc_route_scored(const float *logits, const int32_t *q, int64_t T, int E, int k, int fn,
+                     const float *corr_bias, const int32_t *hash_table,
+                     const int32_t *token_ids, int V, int32_t *idx, float *w, float *scores,
+                     float *prob_mass, float *lse) {
+    int err = 0;
+    if (E > 256 || k < 1 || k > E || fn < 0 || fn > 2) return -1;
+    if (fn == ORC_SCORE_SOFTMAX && corr_bias && !hash_table) return -1;
+    if (hash_table && (!token_ids || V < 1)) return -1;
+    float *pr = NULL;
+    if (prob_mass) pr = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * (size_t)E);
+#pragma omp parallel for schedule(static) reduction(| : err)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * (int64_t)E;
+        float v[256], key[256];
+        int32_t sel[8];
+        for (int e = 0; e < E; ++e)
+            if (!isfinite(l[e])) err |= ORC_ERR_NONFINITE;
+        float m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m) m = l[e];
+        float Z = 0.0f;
+        for (int e = 0; e < E; ++e) Z = Z + expf(l[e] - m);
+        if (lse) lse[t] = m + logf(Z);
+        if (fn == ORC_SCORE_SOFTMAX) {
+            for (int e = 0; e < E; ++e) v[e] = expf(l[e] - m) / Z;
+        } else {
+            for (int e = 0; e < E; ++e) v[e] = orc_score(l[e], fn);
+        }
+        int zero_w = 0;
+        if (hash_table) {
+            const int32_t tok = token_ids[t];
+            if (tok < 0 || tok >= V) {
+                err |= ORC_ERR_IDX_RANGE;
+                for (int j = 0; j < k; ++j) sel[j] = -1;
+                zero_w = 1;
+            } else {
+                for (int j = 0; j < k; ++j) {
+                    sel[j] = hash_table[(int64_t)tok * k + j];
+                    if (sel[j] < 0 || sel[j] >= E) {
+                        err |= ORC_ERR_IDX_RANGE;
+                        zero_w = 1;
+                    }
+                    for (int i = 0; i < j; ++i)
+                        if (sel[i] == sel[j]) {
+                            err |= ORC_ERR_IDX_DUP;
+                            zero_w = 1;
+                        }
+                }
+            }
+        } else {
+            for (int e = 0; e < E; ++e) {
+                if (fn == ORC_SCORE_SOFTMAX) key[e] = l[e];
+                else key[e] = v[e] + (corr_bias ? corr_bias[e] : 0.0f);
+            }
+            unsigned char taken[256];
+            memset(taken, 0, sizeof(taken));
+            for (int j = 0; j < k; ++j) {
+                int best = -1;
+                for (int e = 0; e < E; ++e) {
+                    if (taken[e]) continue;
+                    if (best < 0 || orc_key_before(key[e], e, key[best], best)) best = e;
+                }
+                sel[j] = best;
+                taken[best] = 1;
+            }
+        }
+        if (zero_w) {
+            for (int j = 0; j < k; ++j) w[t * k + j] = 0.0f;
+        } else {
+            float s = v[sel[0]];
+            for (int j = 1; j < k; ++j) s = s + v[sel[j]];
+            for (int j = 0; j < k; ++j) w[t * k + j] = v[sel[j]] / s;
+        }
+        for (int j = 0; j < k; ++j) idx[t * k + j] = sel[j];
+        if (scores)
+            for (int e = 0; e < E; ++e) scores[t * (int64_t)E + e] = v[e];
+        if (pr) {
+            if (fn == ORC_SCORE_SOFTMAX) {
+                for (int e = 0; e < E; ++e) pr[t * (int64_t)E + e] = v[e];
+            } else {
+                float ssum = 0.0f;
+                for (int e = 0; e < E; ++e) ssum = ssum + v[e];
+                for (int e = 0; e < E; ++e) pr[t * (int64_t)E + e] = v[e] / ssum;
+            }
+        }
+    }
+    if (prob_mass) {
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < E; ++e) {
+            float acc = 0.0f;
+            for (int64_t t = 0; t < T; ++t) {
+                float qt = q ? (float)q[t] : 1.0f;
+                acc = acc + qt * pr[t * (int64_t)E + e];
+            }
+            prob_mass[e] = acc;
+        }
+        free(pr);
+    }
+    return err;
+}
+
+/* [HA] eq. (20) and "MoE execution and objectives": the multiplicity q_t of a compact
+ * token weights its router z-loss term, and the probability mass and assignment counts of
+ * the load-balancing loss; the expert-bias update uses the same weighted counts.
+ *   S = sum_t q_t (q_t = 1 when q is NULL): the number of semantic token positions;
+ *   z_loss = (1/S) sum_t q_t lse_t^2, accumulated in FP64, t ascending (0 when lse is
+ *     NULL or S = 0);
+ *   aux_loss = E * sum_e (C_e / (k S)) * (M_e / S) = E / (k S^2) * sum_e C_e M_e, with
+ *     C = weighted assignment counts and M = probability mass, both in logical expert
+ *     order, FP64, e ascending (0 when M or C is NULL or S = 0);
+ *   bias update (bias not NULL): mean load Cbar = sum_e C_e / E; bias[e] + rate when
+ *     C_e < Cbar, bias[e] - rate when C_e > Cbar, unchanged when equal (one FP32 add).
+ * out[0] = z_loss, out[1] = aux_loss, out[2] = S. */
+void orc_objectives(const float *lse, const int32_t *q, int64_t T, const int64_t *C,
+                    const float *M, int E, int k, float rate, float *bias, double *out) {
+    int64_t S = 0;
+    double z = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t qt = q ? q[t] : 1;
+        S += qt;
+        if (lse) z += (double)qt * ((double)lse[t] * (double)lse[t]);
+    }
+    out[0] = (lse && S > 0) ? z / (double)S : 0.0;
+    double a = 0.0;
+    if (C && M && S > 0) {
+        for (int e = 0; e < E; ++e) a += (double)C[e] * (double)M[e];
+        out[1] = a * (double)E / ((double)k * (double)S * (double)S);
+    } else {
+        out[1] = 0.0;
+    }
+    out[2] = (double)S;
+    if (bias && C) {
+        int64_t tot = 0;
+        for (int e = 0; e < E; ++e) tot += C[e];
+        for (int e = 0; e < E; ++e) {
+            /* C_e < tot / E  <=>  E * C_e < tot, in exact integers */
+            const int64_t ec = (int64_t)E * C[e];
+            if (ec < tot) bias[e] = bias[e] + rate;
+            else if (ec > tot) bias[e] = bias[e] + (-rate);
+        }
+    }
 }

@@ -28,7 +28,7 @@ import numpy as np
 
 # tensor ids of the per-tensor random streams
 TID_X, TID_ROUTER, TID_W13, TID_W2, TID_BIAS, TID_LENS, TID_DIRICHLET, TID_REPLAY_IDS, \
-    TID_REPLAY_W, TID_MULT = range(10)
+    TID_REPLAY_W, TID_MULT, TID_CORR_BIAS, TID_HASH_TABLE, TID_TOKEN_IDS = range(13)
 
 _WORKERS = max(1, min(8, os.cpu_count() or 1))
 
@@ -108,6 +108,11 @@ class Layer:
     w_in: Optional[np.ndarray] = None           # float32 [T, k] (replay)
     cu_seqlens: Optional[np.ndarray] = None     # int32 [S+1]
     token_mult: Optional[np.ndarray] = None     # int32 [T]
+    score: str = "softmax"                      # "softmax", "sigmoid" or "sqrt_softplus"
+    corr_bias: Optional[np.ndarray] = None      # float32 [E], selection-only bias
+    hash_table: Optional[np.ndarray] = None     # int32 [V, k] frozen token id -> experts
+    token_ids: Optional[np.ndarray] = None      # int32 [T] (hash routing)
+    routed_scale: float = 1.0                   # routed scaling factor of the combine
     meta: dict = field(default_factory=dict)
 
     @property
@@ -208,6 +213,48 @@ def replay_hot(T: int, E: int, k: int, seed: int):
 def token_multiplicities(T: int, seed: int, qmax: int = 4) -> np.ndarray:
     """Per-token multiplicities q_t in 1..qmax (HARTS, MoE semantics, eq. (20))."""
     return _rng(seed, TID_MULT).integers(1, qmax + 1, size=T).astype(np.int32)
+
+
+SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
+
+
+def correction_bias(E: int, seed: int, std: float = 0.05) -> np.ndarray:
+    """Selection-only expert correction bias, N(0, std^2) in FP32 (the pages give no
+    values; std 0.05 is comparable to the gaps between neighbouring sigmoid scores of
+    unit-variance logits, so the bias changes some selections)."""
+    return (_rng(seed, TID_CORR_BIAS).standard_normal(E) * std).astype(np.float32)
+
+
+def hash_table(V: int, E: int, k: int, seed: int) -> np.ndarray:
+    """Frozen token-id -> expert table [V, k]: each row k distinct experts, uniformly at
+    random, in random order."""
+    rng = _rng(seed, TID_HASH_TABLE)
+    return np.argsort(rng.random((V, E)), axis=1)[:, :k].astype(np.int32)
+
+
+def token_ids(T: int, V: int, seed: int, s: float = 1.1) -> np.ndarray:
+    """Token ids drawn from a Zipf(s) law over a seeded ranking of the V ids (frequent
+    tokens repeat, so the table's experts are unevenly loaded)."""
+    rng = _rng(seed, TID_TOKEN_IDS)
+    p = 1.0 / np.arange(1, V + 1, dtype=np.float64) ** s
+    p /= p.sum()
+    rank = rng.choice(V, size=T, p=p)
+    return rng.permutation(V).astype(np.int32)[rank]
+
+
+def set_router(L: "Layer", score: str = "sigmoid", bias: bool = True,
+               hash_vocab: Optional[int] = None, routed_scale: float = 1.0) -> "Layer":
+    """Switch a router-mode layer to a router variant: score function, correction bias,
+    hash routing over a vocabulary of ``hash_vocab`` ids, routed scaling factor."""
+    if score not in SCORES:
+        raise ValueError(score)
+    L.score = score
+    L.corr_bias = correction_bias(L.E, L.seed) if bias else None
+    if hash_vocab:
+        L.hash_table = hash_table(hash_vocab, L.E, L.k, L.seed)
+        L.token_ids = token_ids(L.T, hash_vocab, L.seed)
+    L.routed_scale = float(routed_scale)
+    return L
 
 
 def make_layer(T: int, d: int, E: int, k: int, I: int, dtype: str = "bf16",
