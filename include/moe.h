@@ -32,6 +32,11 @@
  *        "Sharding the experts".
  *  [TRR] same page, "Total Router Recall"; "Hash and learned expert routing".
  *  [SEL] same page, "Selecting sparse-attention positions" (lower position wins ties).
+ *  [GLM] same page, "Choosing GLM's eight experts" (sigmoid scores, FP32 correction bias
+ *        for the choice only, weights from the pre-bias scores normalised in FP32, the
+ *        factor 2.5 applied inside the expert kernel).
+ *  [HL]  same page, "Hash and learned expert routing" (frozen token-id -> experts table;
+ *        sqrt-softplus scores with the correction bias in the learned layers).
  *  [RP]  "RoutePack: Expert Placement and Attention-Aware Data Packing for MoE
  *        Reinforcement Learning", Sec. 2.1 eq. (1), Sec. 3.3.
  *  [HA]  "HARTS: Efficient Agentic Reinforcement Learning for Hybrid-Attention Models
@@ -111,6 +116,57 @@ moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router,
                      const float *logit_bias, int32_t *topk_idx, float *topk_w,
                      float *logits, float *prob_mass, const int32_t *token_mult,
                      int32_t *d_err, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Score function of a router [RT][GLM][HL]. */
+typedef enum moe_score_fn {
+    MOE_SCORE_SOFTMAX = 0,      /* p = FP32 softmax over the E logits (as moe_route) */
+    MOE_SCORE_SIGMOID = 1,      /* s = 1 / (1 + exp(-l)) */
+    MOE_SCORE_SQRT_SOFTPLUS = 2 /* s = sqrt(log(1 + exp(l))) */
+} moe_score_fn;
+
+/* Router variant options (all device pointers; NULL = absent).
+ *  score_fn   moe_score_fn. The sigmoid and sqrt-softplus scores are the functions
+ *             evaluated in FP64 and rounded once to FP32, so that any two correct
+ *             implementations agree on the score (and on the choice) bit for bit except
+ *             where the FP64 value lies within an FP64 rounding error of a point halfway
+ *             between two FP32 numbers.
+ *  corr_bias  [E] f32: correction bias, added in FP32 to each score to choose the
+ *             experts and nowhere else [GLM]. Only with SIGMOID / SQRT_SOFTPLUS
+ *             (MOE_E_SHAPE with SOFTMAX, whose choice keys on the logits).
+ *  hash_table [vocab, k] i32: frozen token-id -> expert table [HL]; with it, slot j of
+ *             token t is hash_table[token_ids[t] * k + j] (the table's order; the bias
+ *             is not used) and the logits only set the weights. token_ids [T] i32 is then
+ *             required and vocab >= 1. A token id outside [0, vocab) sets
+ *             MOE_DERR_IDX_RANGE and gives the row ids -1 and weights 0; a table id
+ *             outside [0, E) or repeated within the row sets MOE_DERR_IDX_RANGE /
+ *             MOE_DERR_IDX_DUP and gives the row weights 0 (the ids pass through).
+ *  lse        [T] f32 output: log-sum-exp of each token's logits, max + log(sum exp(l -
+ *             max)), FP32 (the router z-loss input of moe_objectives). */
+typedef struct moe_router_opts {
+    int32_t score_fn;
+    const float *corr_bias;
+    const int32_t *hash_table;
+    const int32_t *token_ids;
+    int32_t vocab;
+    float *lse;
+} moe_router_opts;
+
+/* Router variants [RT][GLM][HL][HA]: logits as moe_route (same kernel, same bits), then
+ * per token, with v[e] = softmax probability (SOFTMAX) or score s[e] (otherwise):
+ *   choice: SOFTMAX without a table: as moe_route (logit desc, id asc); SIGMOID /
+ *     SQRT_SOFTPLUS without a table: the k experts first in the order (s[e] +
+ *     corr_bias[e] desc, id asc), slot 0 = largest; with a table: the table's row;
+ *   topk_w[t,j] = v[idx_j] / ((v[idx_0] + v[idx_1]) + ...), FP32, left to right: the
+ *     bias never enters a weight;
+ *   prob_mass[e] = sum_t q_t prob[t,e], prob = p (SOFTMAX) or s[e] / sum_e' s[e']
+ *     (the scores normalised over all E experts), summed in a fixed order.
+ * With score_fn SOFTMAX and neither bias nor table, every output is bitwise moe_route's.
+ * opts NULL = SOFTMAX with no options. Other arguments as moe_route. */
+moe_status moe_route_scored(const moe_dims *dims, const moe_router_opts *opts, const void *x,
+                            const void *w_router, const float *logit_bias, int32_t *topk_idx,
+                            float *topk_w, float *logits, float *prob_mass,
+                            const int32_t *token_mult, int32_t *d_err, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Routing replay [TRR][RP]: the caller's expert ids (int32) and normalised FP32 weights,
  * one per token per slot, are validated and passed through unchanged: no
@@ -195,6 +251,39 @@ moe_status moe_grouped_ffn(const moe_dims *dims, const void *x_perm, const int32
 moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
                        const float *topk_w, void *out, void *stream);
 
+/* Weighted combine with a routed scaling factor [GLM]: the factor multiplies the FP32
+ * slot-order sum before the one rounding,
+ *   out[t,o] = round_dtype( routed_scale * (((0 + w_0 y_0) + w_1 y_1) + ...) ).
+ * routed_scale 1 gives moe_combine's bits (a multiplication by 1 is exact); it must be
+ * finite (else MOE_E_SHAPE). */
+moe_status moe_combine_scaled(const moe_dims *dims, const float *y, const int32_t *inv,
+                              const float *topk_w, float routed_scale, void *out,
+                              void *stream);
+
+/* Objective statistics of one routed batch [HA] (HARTS, eq. (20) and "MoE execution and
+ * objectives": the multiplicity q_t of a compact token weights its router z-loss term, the
+ * probability mass and assignment counts of the load-balancing loss, and the counts of
+ * the expert-bias update). Device inputs, written by moe_route_scored / moe_permute:
+ *   lse [T] f32 or NULL, token_mult [T] i32 or NULL (q_t = 1), weighted_counts [E] i64 or
+ *   NULL, prob_mass [E] f32 or NULL; slot_of_expert [E] i32 or NULL: when the counts
+ *   came from moe_permute_placed, the map that placed them (the mass and the bias are in
+ *   logical expert order; the counts are read as C_e = weighted_counts[slot_of_expert[e]]).
+ * Writes out [3] f64 (device):
+ *   out[0] = z_loss = (1/S) sum_t q_t lse_t^2 (0 if lse is NULL or S = 0), where
+ *            S = sum_t q_t is the number of semantic token positions;
+ *   out[1] = aux_loss = E / (k S^2) sum_e C_e M_e, i.e. E sum_e (C_e / (k S)) (M_e / S)
+ *            (0 if weighted_counts or prob_mass is NULL, or S = 0);
+ *   out[2] = S.
+ * Every sum is FP64 in a fixed order. Unscaled: the caller multiplies by its coefficients.
+ * corr_bias [E] f32 (NULL: not touched) is updated in place with the sign rule: with the
+ * mean load Cbar = sum_e C_e / E, bias[e] += bias_rate if C_e < Cbar, -= bias_rate if
+ * C_e > Cbar, unchanged if equal (compared exactly in integers; requires
+ * weighted_counts). A slot_of_expert entry outside [0, E) sets MOE_DERR_SLOTMAP. */
+moe_status moe_objectives(const moe_dims *dims, const float *lse, const int32_t *token_mult,
+                          const int64_t *weighted_counts, const float *prob_mass,
+                          const int32_t *slot_of_expert, float bias_rate, float *corr_bias,
+                          double *out, int32_t *d_err, void *stream);
+
 /* Everything moe_forward needs. Replay mode iff idx_in != NULL (then w_in is required
  * and w_router/logit_bias/logits/prob_mass are ignored); router mode otherwise.
  * Required: x, w13, w2, out, topk_idx, topk_w, counts, offsets, perm, inv, h, y,
@@ -207,7 +296,10 @@ moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
  * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing).
  * slot_of_expert: NULL, or a device placement map as in moe_permute_placed (w13 and w2
  * then hold the experts in slot order; counts/offsets/statistics are per slot; topk_idx
- * stays in logical ids). */
+ * stays in logical ids).
+ * router: NULL, or the router variant of moe_route_scored (router mode only).
+ * routed_scale: the combine's routed scaling factor as in moe_combine_scaled; 0 means 1
+ * (no factor), so a zero-initialised struct keeps moe_combine's bits. */
 typedef struct moe_forward_args {
     const void *x;
     const void *w_router;
@@ -238,6 +330,8 @@ typedef struct moe_forward_args {
     size_t workspace_bytes;
     void *const *prof_events;
     const int32_t *slot_of_expert; /* NULL: identity placement; else as moe_permute_placed */
+    const moe_router_opts *router; /* host pointer; NULL: softmax router as moe_route */
+    float routed_scale;            /* 0 or 1: no factor */
 } moe_forward_args;
 
 /* The whole layer: route (or replay) -> permute -> grouped FFN -> combine, each step as

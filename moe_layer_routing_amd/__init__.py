@@ -49,7 +49,15 @@ class ForwardArgs(ctypes.Structure):
                 ("perm", _P), ("inv", _P), ("seq_counts", _P), ("weighted_counts", _P),
                 ("x_perm", _P), ("h", _P), ("y", _P), ("d_err", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t), ("prof_events", _P),
-                ("slot_of_expert", _P)]
+                ("slot_of_expert", _P), ("router", _P), ("routed_scale", ctypes.c_float)]
+
+
+class RouterOpts(ctypes.Structure):
+    _fields_ = [("score_fn", ctypes.c_int32), ("corr_bias", _P), ("hash_table", _P),
+                ("token_ids", _P), ("vocab", ctypes.c_int32), ("lse", _P)]
+
+
+SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 
 
 # exported symbols and their signatures (argument types after the dims pointer)
@@ -69,6 +77,12 @@ _SIGS = {
                             ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                            ctypes.c_int),
     "moe_place_lpt": ([_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P], ctypes.c_int),
+    "moe_route_scored": ([ctypes.POINTER(Dims), ctypes.POINTER(RouterOpts)] + [_P] * 9
+                         + [_P, ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_combine_scaled": ([ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_float, _P, _P],
+                           ctypes.c_int),
+    "moe_objectives": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                        _P], ctypes.c_int),
 }
 
 _lib = None
@@ -146,6 +160,39 @@ def route(dims, x, w_router, logit_bias, topk_idx, topk_w, logits=None, prob_mas
                            _stream(stream)), "moe_route")
 
 
+def router_opts(score="softmax", corr_bias=None, hash_table=None, token_ids=None,
+                lse=None) -> RouterOpts:
+    """moe_router_opts from tensors (hash_table [V, k] int32, token_ids [T] int32)."""
+    o = RouterOpts()
+    o.score_fn = SCORES[score]
+    o.corr_bias = _ptr(corr_bias)
+    o.hash_table = _ptr(hash_table)
+    o.token_ids = _ptr(token_ids)
+    o.vocab = 0 if hash_table is None else hash_table.shape[0]
+    o.lse = _ptr(lse)
+    return o
+
+
+def route_scored(dims, x, w_router, logit_bias, topk_idx, topk_w, score="sigmoid",
+                 corr_bias=None, hash_table=None, token_ids=None, lse=None, logits=None,
+                 prob_mass=None, token_mult=None, d_err=None, workspace=None, stream=None):
+    ws = workspace if workspace is not None else alloc_workspace(dims, x.device)
+    o = router_opts(score, corr_bias, hash_table, token_ids, lse)
+    _check(lib().moe_route_scored(ctypes.byref(dims), ctypes.byref(o), _ptr(x), _ptr(w_router),
+                                  _ptr(logit_bias), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                                  _ptr(prob_mass), _ptr(token_mult), _ptr(d_err), _ptr(ws),
+                                  ws.numel(), _stream(stream)), "moe_route_scored")
+
+
+def objectives(dims, out, lse=None, token_mult=None, weighted_counts=None, prob_mass=None,
+               slot_of_expert=None, bias_rate=0.0, corr_bias=None, d_err=None, stream=None):
+    """moe_objectives: out is a float64 device tensor of 3 (z_loss, aux_loss, S)."""
+    _check(lib().moe_objectives(ctypes.byref(dims), _ptr(lse), _ptr(token_mult),
+                                _ptr(weighted_counts), _ptr(prob_mass), _ptr(slot_of_expert),
+                                bias_rate, _ptr(corr_bias), _ptr(out), _ptr(d_err),
+                                _stream(stream)), "moe_objectives")
+
+
 def route_replay(dims, idx_in, w_in, topk_idx, topk_w, d_err=None, stream=None):
     _check(lib().moe_route_replay(ctypes.byref(dims), _ptr(idx_in), _ptr(w_in), _ptr(topk_idx),
                                   _ptr(topk_w), _ptr(d_err), _stream(stream)),
@@ -194,19 +241,33 @@ def grouped_ffn(dims, x_perm, offsets, w13, w2, h, y, workspace=None, stream=Non
                                  _stream(stream)), "moe_grouped_ffn")
 
 
-def combine(dims, y, inv, topk_w, out, stream=None):
-    _check(lib().moe_combine(ctypes.byref(dims), _ptr(y), _ptr(inv), _ptr(topk_w), _ptr(out),
-                             _stream(stream)), "moe_combine")
+def combine(dims, y, inv, topk_w, out, stream=None, routed_scale=None):
+    """moe_combine, or moe_combine_scaled when a routed scaling factor is given."""
+    if routed_scale is None:
+        _check(lib().moe_combine(ctypes.byref(dims), _ptr(y), _ptr(inv), _ptr(topk_w),
+                                 _ptr(out), _stream(stream)), "moe_combine")
+    else:
+        _check(lib().moe_combine_scaled(ctypes.byref(dims), _ptr(y), _ptr(inv), _ptr(topk_w),
+                                        routed_scale, _ptr(out), _stream(stream)),
+               "moe_combine_scaled")
 
 
-def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=None):
+def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=None,
+            router: Optional[dict] = None, routed_scale: float = 0.0):
     """Run moe_forward. ``bufs`` maps ForwardArgs field names to tensors (or None);
-    ``prof_events`` is None or a sequence of three raw hipEvent_t handles."""
+    ``prof_events`` is None or a sequence of three raw hipEvent_t handles; ``router`` is
+    None or the keyword arguments of router_opts; ``routed_scale`` 0 means no factor."""
     a = ForwardArgs()
     for name, _ in ForwardArgs._fields_:
-        if name in ("num_seqs", "workspace", "workspace_bytes", "prof_events"):
+        if name in ("num_seqs", "workspace", "workspace_bytes", "prof_events", "router",
+                    "routed_scale"):
             continue
         setattr(a, name, _ptr(bufs.get(name)))
+    ropts = None
+    if router is not None:
+        ropts = router_opts(**router)
+        a.router = ctypes.cast(ctypes.pointer(ropts), ctypes.c_void_p)
+    a.routed_scale = routed_scale
     cu = bufs.get("cu_seqlens")
     a.num_seqs = 0 if cu is None else cu.numel() - 1
     a.workspace = _ptr(workspace)

@@ -5,7 +5,10 @@
 // token's routing slots are accumulated in FP32 in slot order, the route weight applied
 // inside that FP32 accumulator, and the sum rounded once to the output type. Here
 // acc = ((0 + w_0*y_0) + w_1*y_1) + ... with every product and sum a separate FP32
-// operation (the library is built without floating-point contraction).
+// operation (the library is built without floating-point contraction). A routed scaling
+// factor ("Choosing GLM's eight experts": the expert kernel applies the factor to the
+// FP32-weighted result) multiplies acc once, in FP32, before the rounding; the factor 1
+// leaves every bit unchanged.
 #include "moe_internal.h"
 
 namespace moe {
@@ -22,7 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const int32_t *__restrict__ inv,
                                                       const float *__restrict__ topk_w,
                                                       int64_t T, int k, int d, int64_t A,
-                                                      void *__restrict__ out) {
+                                                      float scale, void *__restrict__ out) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nslice = (d + kSlice - 1) / kSlice;
     const int64_t W = (int64_t)blockIdx.x * 4 + wave;
@@ -62,6 +65,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                     a3 = a3 + w[j] * v[u][j].w;
                 }
             }
+            a0 = scale * a0;
+            a1 = scale * a1;
+            a2 = scale * a2;
+            a3 = scale * a3;
             if constexpr (kBF16) {
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
@@ -78,17 +85,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }  // namespace
 
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
-                          const float *topk_w, void *out, hipStream_t s) {
+                          const float *topk_w, void *out, hipStream_t s, float scale) {
     if (dm.T > 0) {
         const int64_t waves = dm.T * ((dm.d + kSlice - 1) / kSlice);
         const dim3 grid((unsigned)((waves + 3) / 4));
         const int64_t A = dm.T * dm.k;
         if (dm.dtype == MOE_BF16)
             combine_kernel<true><<<grid, dim3(256), 0, s>>>(y, inv, topk_w, dm.T, dm.k, dm.d,
-                                                            A, out);
+                                                            A, scale, out);
         else
             combine_kernel<false><<<grid, dim3(256), 0, s>>>(y, inv, topk_w, dm.T, dm.k, dm.d,
-                                                             A, out);
+                                                             A, scale, out);
     }
     return hipGetLastError();
 }

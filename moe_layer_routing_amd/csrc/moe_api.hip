@@ -1,6 +1,7 @@
 // moe_api.hip -- the C ABI: argument checks, workspace carving, launches.
 // Nothing here allocates, synchronises the host or throws.
 #include <algorithm>
+#include <cmath>
 
 #include "moe_internal.h"
 
@@ -103,6 +104,47 @@ moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router,
     return to_status(launch_route(*dims, x, w_router, logit_bias, logits ? logits : ws.logits,
                                   topk_idx, topk_w, ws.mass_part, prob_mass, token_mult, d_err,
                                   static_cast<hipStream_t>(stream)));
+}
+
+// Router options as the kernels take them; MOE_OK or the status of the first bad field.
+static moe_status router_opts(const moe_dims *dims, const moe_router_opts *o, RouteOpts *r) {
+    *r = RouteOpts();
+    if (!o) return MOE_OK;
+    if (o->score_fn < MOE_SCORE_SOFTMAX || o->score_fn > MOE_SCORE_SQRT_SOFTPLUS)
+        return MOE_E_SHAPE;
+    if (o->hash_table) {
+        if (!o->token_ids) return MOE_E_NULLPTR;
+        if (o->vocab < 1) return MOE_E_SHAPE;
+        if ((int64_t)o->vocab * dims->k >= (int64_t(1) << 31)) return MOE_E_SHAPE;
+    } else if (o->score_fn == MOE_SCORE_SOFTMAX && o->corr_bias) {
+        return MOE_E_SHAPE;   // the softmax router chooses on the logits
+    }
+    r->fn = o->score_fn;
+    r->corr_bias = o->hash_table ? nullptr : o->corr_bias;
+    r->hash_table = o->hash_table;
+    r->token_ids = o->hash_table ? o->token_ids : nullptr;
+    r->vocab = o->hash_table ? o->vocab : 0;
+    r->lse = o->lse;
+    return MOE_OK;
+}
+
+moe_status moe_route_scored(const moe_dims *dims, const moe_router_opts *opts, const void *x,
+                            const void *w_router, const float *logit_bias, int32_t *topk_idx,
+                            float *topk_w, float *logits, float *prob_mass,
+                            const int32_t *token_mult, int32_t *d_err, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(x && w_router && topk_idx && topk_w, MOE_E_NULLPTR);
+    RouteOpts ro;
+    st = router_opts(dims, opts, &ro);
+    if (st != MOE_OK) return st;
+    st = check_ws(dims, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, workspace);
+    return to_status(launch_route(*dims, x, w_router, logit_bias, logits ? logits : ws.logits,
+                                  topk_idx, topk_w, ws.mass_part, prob_mass, token_mult, d_err,
+                                  static_cast<hipStream_t>(stream), ro));
 }
 
 moe_status moe_route_replay(const moe_dims *dims, const int32_t *idx_in, const float *w_in,
@@ -222,6 +264,33 @@ moe_status moe_combine(const moe_dims *dims, const float *y, const int32_t *inv,
     return to_status(launch_combine(*dims, y, inv, topk_w, out, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_combine_scaled(const moe_dims *dims, const float *y, const int32_t *inv,
+                              const float *topk_w, float routed_scale, void *out,
+                              void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    if (dims->T > 0) MOE_REQUIRE(y && inv && topk_w && out, MOE_E_NULLPTR);
+    MOE_REQUIRE(std::isfinite(routed_scale), MOE_E_SHAPE);
+    return to_status(launch_combine(*dims, y, inv, topk_w, out,
+                                    static_cast<hipStream_t>(stream), routed_scale));
+}
+
+moe_status moe_objectives(const moe_dims *dims, const float *lse, const int32_t *token_mult,
+                          const int64_t *weighted_counts, const float *prob_mass,
+                          const int32_t *slot_of_expert, float bias_rate, float *corr_bias,
+                          double *out, int32_t *d_err, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(out, MOE_E_NULLPTR);
+    if (corr_bias) {
+        MOE_REQUIRE(weighted_counts, MOE_E_NULLPTR);
+        MOE_REQUIRE(std::isfinite(bias_rate), MOE_E_SHAPE);
+    }
+    return to_status(launch_objectives(*dims, lse, token_mult, weighted_counts, prob_mass,
+                                       slot_of_expert, bias_rate, corr_bias, out, d_err,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *stream) {
     moe_status st = check_common(dims);
     if (st != MOE_OK) return st;
@@ -239,6 +308,13 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     }
     MOE_REQUIRE((a->cu_seqlens == nullptr) == (a->seq_counts == nullptr), MOE_E_NULLPTR);
     if (a->seq_counts) MOE_REQUIRE(a->num_seqs >= 1 && a->num_seqs <= dims->T + 1, MOE_E_SHAPE);
+    RouteOpts ro;
+    if (!replay) {
+        st = router_opts(dims, a->router, &ro);
+        if (st != MOE_OK) return st;
+    }
+    MOE_REQUIRE(std::isfinite(a->routed_scale), MOE_E_SHAPE);
+    const float scale = a->routed_scale == 0.0f ? 1.0f : a->routed_scale;
     st = check_ws(dims, a->workspace, a->workspace_bytes);
     if (st != MOE_OK) return st;
     const Workspace ws = carve_workspace(*dims, a->workspace);
@@ -253,7 +329,8 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
         }
         e = launch_small_tail(*dims, logits, a->token_mult, a->idx_in, a->w_in, a->topk_idx,
                               a->topk_w, a->prob_mass, a->counts, a->offsets, a->perm, a->inv,
-                              a->weighted_counts, ws.tiles, a->d_err, s, a->slot_of_expert);
+                              a->weighted_counts, ws.tiles, a->d_err, s, a->slot_of_expert,
+                              ro);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         if (a->x_perm) {
             e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);
@@ -262,14 +339,14 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                                a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        return to_status(launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s));
+        return to_status(launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale));
     }
     if (replay)
         e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
     else
         e = launch_route(*dims, a->x, a->w_router, a->logit_bias,
                          a->logits ? a->logits : ws.logits, a->topk_idx, a->topk_w,
-                         ws.mass_part, a->prob_mass, a->token_mult, a->d_err, s);
+                         ws.mass_part, a->prob_mass, a->token_mult, a->d_err, s, ro);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_permute(*dims, a->topk_idx, a->x, a->x_perm, a->perm, a->inv, a->counts,
                        a->offsets, a->cu_seqlens, a->seq_counts ? a->num_seqs : 0,
@@ -279,7 +356,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                            a->prof_events, s, a->x, a->perm);
     if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s);
+    e = launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale);
     return to_status(e);
 }
 

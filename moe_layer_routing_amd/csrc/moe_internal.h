@@ -95,12 +95,27 @@ int64_t perm_chunks(int64_t A);
 int64_t max_m_tiles(int64_t A, int E, int tile_m);
 Workspace carve_workspace(const moe_dims &d, void *base);
 
+// ---------------------------------------------------------------- router variants
+enum { kScoreSoftmax = MOE_SCORE_SOFTMAX, kScoreSigmoid = MOE_SCORE_SIGMOID,
+       kScoreSqrtSoftplus = MOE_SCORE_SQRT_SOFTPLUS };
+
+// Router variant inputs as the kernels take them (validated by the API layer).
+struct RouteOpts {
+    int fn = kScoreSoftmax;
+    const float *corr_bias = nullptr;   // [E], scored routers only
+    const int32_t *hash_table = nullptr;  // [vocab, k]
+    const int32_t *token_ids = nullptr;   // [T]
+    int vocab = 0;
+    float *lse = nullptr;                 // [T] output
+    bool plain() const { return fn == kScoreSoftmax && !hash_table; }
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Sizes are already validated.
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                         const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
                         float *mass_part, float *prob_mass, const int32_t *token_mult,
-                        int32_t *d_err, hipStream_t s);
+                        int32_t *d_err, hipStream_t s, const RouteOpts &opts = RouteOpts());
 hipError_t launch_replay(const moe_dims &dm, const int32_t *idx_in, const float *w_in,
                          int32_t *topk_idx, float *topk_w, int32_t *d_err, hipStream_t s);
 hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const void *x,
@@ -118,7 +133,12 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                               const void *x = nullptr, const int32_t *perm = nullptr,
                               bool tiles_ready = false);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
-                          const float *topk_w, void *out, hipStream_t s);
+                          const float *topk_w, void *out, hipStream_t s, float scale = 1.0f);
+// Objective statistics (one block): out[3] = z_loss, aux_loss, S; optional bias update.
+hipError_t launch_objectives(const moe_dims &dm, const float *lse, const int32_t *q,
+                             const int64_t *wcounts, const float *mass,
+                             const int32_t *slot_map, float rate, float *bias, double *out,
+                             int32_t *d_err, hipStream_t s);
 
 int select_tile_m(const moe_dims &dm);
 
@@ -137,6 +157,7 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int3
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                             hipStream_t s, const int32_t *slot_map = nullptr);
+                             hipStream_t s, const int32_t *slot_map = nullptr,
+                             const RouteOpts &opts = RouteOpts());
 
 }  // namespace moe

@@ -8,6 +8,9 @@
 // sparse-attention scores, "Selecting sparse-attention positions"). Probability mass is
 // weighted by token multiplicity ("HARTS ...", eq. (20)). Replay ("Total Router Recall")
 // passes the sampler's ids and FP32 weights through untouched after validation.
+// Router variants share the logits and the block layout: sigmoid or sqrt-softplus scores
+// with a correction bias that only chooses ("Choosing GLM's eight experts"), and hash
+// routing from a frozen token-id table ("Hash and learned expert routing").
 #include "route_dev.h"
 
 namespace moe {
@@ -124,18 +127,20 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
 // tokens' q·p in token order (starting from 0), then the four waves' sums in wave order.
 static_assert(kTopkTokPerBlock == 16, "4 waves x 4 tokens");
 
+template <int kFn, bool kHash>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ q,
                                                          int64_t T, int E, int k,
                                                          int32_t *__restrict__ topk_idx,
                                                          float *__restrict__ topk_w,
                                                          float *__restrict__ mass_part,
-                                                         int32_t *__restrict__ d_err) {
+                                                         int32_t *__restrict__ d_err,
+                                                         RouteOpts opts) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * 4;
     float qp[kRowVals];
     int err = 0;
-    route_rows4(logits, q, t0, T, E, k, topk_idx, topk_w, nullptr, qp, err);
+    route_rows<kFn, kHash>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr, qp, err);
     wave_raise(err, d_err);
     if (mass_part) {
         __shared__ float mpt[kTopkTokPerBlock][kMaxE];
@@ -245,19 +250,34 @@ hipError_t launch_router_logits(const moe_dims &dm, const void *x, const void *w
     return hipGetLastError();
 }
 
+template <int kFn, bool kHash>
+static void launch_topk_t(const moe_dims &dm, int64_t tblk, const float *logits,
+                          const int32_t *q, int32_t *topk_idx, float *topk_w, float *mass_part,
+                          int32_t *d_err, const RouteOpts &o, hipStream_t s) {
+    route_topk_kernel<kFn, kHash><<<dim3((unsigned)tblk), dim3(256), 0, s>>>(
+        logits, q, dm.T, dm.E, dm.k, topk_idx, topk_w, mass_part, d_err, o);
+}
+
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                         const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
                         float *mass_part, float *prob_mass, const int32_t *token_mult,
-                        int32_t *d_err, hipStream_t s) {
+                        int32_t *d_err, hipStream_t s, const RouteOpts &o) {
     const int64_t T = dm.T;
     const int E = dm.E;
     if (T > 0) {
         const hipError_t le = launch_router_logits(dm, x, w_router, bias, logits, s);
         if (le != hipSuccess) return le;
         const int64_t tblk = (T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
-        route_topk_kernel<<<dim3((unsigned)tblk), dim3(256), 0, s>>>(
-            logits, token_mult, T, E, dm.k, topk_idx, topk_w, prob_mass ? mass_part : nullptr,
-            d_err);
+        float *mp = prob_mass ? mass_part : nullptr;
+        const bool h = o.hash_table != nullptr;
+        switch (o.fn * 2 + (h ? 1 : 0)) {
+        case 0: launch_topk_t<kScoreSoftmax, false>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        case 1: launch_topk_t<kScoreSoftmax, true>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        case 2: launch_topk_t<kScoreSigmoid, false>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        case 3: launch_topk_t<kScoreSigmoid, true>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        case 4: launch_topk_t<kScoreSqrtSoftplus, false>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        default: launch_topk_t<kScoreSqrtSoftplus, true>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
+        }
         if (prob_mass)
             mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
     } else if (prob_mass) {

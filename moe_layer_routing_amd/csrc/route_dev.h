@@ -83,7 +83,7 @@ __device__ __forceinline__ float row_sum(float v) {
 // same expression) are renormalised by their left-to-right sum. Writes topk_idx / topk_w
 // (and the ids to lds_ids when given) for rows with t < T, returns q[t]·p for the lane's
 // experts in qp (0 for rows past T) and ORs MOE_DERR_NONFINITE into err for a non-finite
-// logit of an existing token.
+// logit of an existing token. lse (optional) receives max + log(Z) per token.
 constexpr int kRowVals = kMaxE / 16;   // logits per lane
 
 __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
@@ -91,7 +91,8 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
                                             int64_t T, int E, int k,
                                             int32_t *__restrict__ topk_idx,
                                             float *__restrict__ topk_w, int32_t *lds_ids,
-                                            float (&qp)[kRowVals], int &err) {
+                                            float (&qp)[kRowVals], int &err,
+                                            float *__restrict__ lse = nullptr) {
     const int lane = threadIdx.x & 63, c = lane & 15;
     const int64_t t = t0 + (lane >> 4);
     const bool tv = t < T;
@@ -138,6 +139,7 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
         if (i < nv) zl = (i == 0) ? z[0] : zl + z[i];
     }
     const float Z = row_sum(zl);
+    if (lse && tv && c == 0) lse[t] = mx + logf(Z);
     const float qt = (q && tv) ? static_cast<float>(q[t]) : 1.0f;
 #pragma unroll
     for (int i = 0; i < kRowVals; ++i) qp[i] = (tv && valid[i]) ? qt * (z[i] / Z) : 0.f;
@@ -159,6 +161,183 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
             }
         }
     }
+}
+
+// Scores of the learned routers: the function evaluated in FP64 and rounded once to FP32.
+//   sigmoid:       1 / (1 + e^-x) for x >= 0 and e^x / (1 + e^x) for x < 0, i.e.
+//                  (x >= 0 ? 1 : e) / (1 + e) with e = e^-|x| (one exponential, no overflow);
+//   sqrt-softplus: sqrt(log(1 + e^x)) with log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
+template <int kFn>
+__device__ __forceinline__ float router_score(float l) {
+    const double x = static_cast<double>(l);
+    const double e = exp(-fabs(x));
+    if constexpr (kFn == kScoreSigmoid) {
+        return static_cast<float>((x >= 0.0 ? 1.0 : e) / (1.0 + e));
+    } else {
+        return static_cast<float>(sqrt(fmax(x, 0.0) + log1p(e)));
+    }
+}
+
+// Row-uniform value v[e] of the row's lane (e & 15), register e >> 4 (v >= 0 or NaN, so
+// its bits order like the value; non-owning lanes offer +0). 0 for e outside [0, 16 * nv).
+__device__ __forceinline__ float row_pick(const float (&v)[kRowVals], int e, int c, int nv) {
+    const bool own = e >= 0 && (e & 15) == c && (e >> 4) < nv;
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i)
+        if (own && i == (e >> 4)) b = __float_as_uint(v[i]);
+    return __uint_as_float(row_max_u32(b));
+}
+
+// Router variants of route_rows4 for the same row layout ("0 train-infer mismatch ...",
+// "Choosing GLM's eight experts" and "Hash and learned expert routing"; the mass per
+// "HARTS ...", eq. (20)). Per token, v[e] is the softmax probability (kFn = softmax) or the
+// score s[e] = router_score(l[e]).
+//  - kHash: slot j holds hash_table[token_ids[t] * k + j]; a token id outside [0, vocab)
+//    gives ids -1 and weights 0 (MOE_DERR_IDX_RANGE); a table id outside [0, E) or
+//    repeated in the row gives weights 0 (MOE_DERR_IDX_RANGE / MOE_DERR_IDX_DUP).
+//  - otherwise (scored routers only): k rounds of the row maximum of the FP32 key
+//    s[e] + corr_bias[e] (order-preserving bits), ties to the lowest id, as route_rows4.
+//  - weights: v at the chosen ids (row_pick), summed left to right, each divided by the
+//    sum: the bias never enters a weight.
+//  - qp: q[t] * prob[e], prob = p (softmax) or s[e] / (row sum of s) for the scored
+//    routers; lse: max logit + log(Z) with Z = row sum of exp(l - max).
+template <int kFn, bool kHash>
+__device__ __forceinline__ void route_rows4_scored(
+    const float *__restrict__ logits, const int32_t *__restrict__ q, int64_t t0, int64_t T,
+    int E, int k, const RouteOpts &o, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, int32_t *lds_ids, float (&qp)[kRowVals], int &err) {
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int64_t t = t0 + (lane >> 4);
+    const bool tv = t < T;
+    const int nv = (E + 15) >> 4;
+    float lv[kRowVals], v[kRowVals];
+    bool valid[kRowVals];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) {
+        valid[i] = i < nv && c + 16 * i < E;
+        lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
+        if (tv && valid[i] && !__builtin_isfinite(lv[i])) err |= MOE_DERR_NONFINITE;
+        if (valid[i]) lmax = max(lmax, ordered_bits(lv[i]));
+    }
+    const float mx = from_ordered_bits(row_max_u32(lmax));
+    float Z = 1.f;
+    if (kFn == kScoreSoftmax || o.lse) {
+        float zl = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRowVals; ++i) {
+            const float z = valid[i] ? expf(lv[i] - mx) : 0.f;
+            if (i < nv) zl = (i == 0) ? z : zl + z;
+            if constexpr (kFn == kScoreSoftmax) v[i] = z;
+        }
+        Z = row_sum(zl);
+        if (o.lse && tv && c == 0) o.lse[t] = mx + logf(Z);
+    }
+    float norm;
+    if constexpr (kFn == kScoreSoftmax) {
+#pragma unroll
+        for (int i = 0; i < kRowVals; ++i) v[i] = valid[i] ? v[i] / Z : 0.f;
+        norm = 1.f;
+    } else {
+        float sl = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRowVals; ++i) {
+            v[i] = valid[i] ? router_score<kFn>(lv[i]) : 0.f;
+            if (i < nv) sl = (i == 0) ? v[0] : sl + v[i];
+        }
+        norm = row_sum(sl);
+    }
+    const float qt = (q && tv) ? static_cast<float>(q[t]) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) {
+        if constexpr (kFn == kScoreSoftmax) qp[i] = (tv && valid[i]) ? qt * v[i] : 0.f;
+        else qp[i] = (tv && valid[i]) ? qt * (v[i] / norm) : 0.f;
+    }
+
+    int sel[kMaxK];
+    bool zero_w = false;
+    if constexpr (kHash) {
+        const int32_t tok = tv ? o.token_ids[t] : 0;
+        const bool bad_tok = tv && (tok < 0 || tok >= o.vocab);
+        if (bad_tok) err |= MOE_DERR_IDX_RANGE;
+        zero_w = bad_tok;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            sel[j] = -1;
+            if (j < k && tv && !bad_tok) {
+                sel[j] = o.hash_table[(int64_t)tok * k + j];
+                if (sel[j] < 0 || sel[j] >= E) {
+                    err |= MOE_DERR_IDX_RANGE;
+                    zero_w = true;
+                }
+#pragma unroll
+                for (int i = 0; i < kMaxK; ++i)
+                    if (i < j && sel[i] == sel[j]) {
+                        err |= MOE_DERR_IDX_DUP;
+                        zero_w = true;
+                    }
+            }
+        }
+    } else {
+        uint32_t hi[kRowVals];
+#pragma unroll
+        for (int i = 0; i < kRowVals; ++i) {
+            const float b = (o.corr_bias && valid[i]) ? o.corr_bias[c + 16 * i] : 0.f;
+            hi[i] = valid[i] ? ordered_bits(v[i] + b) : 0u;
+        }
+        uint32_t taken = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            sel[j] = 0;
+            if (j < k) {
+                uint32_t best = 0;
+#pragma unroll
+                for (int i = 0; i < kRowVals; ++i)
+                    if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
+                const uint32_t m = row_max_u32(best);
+                int cand = 0x7fffffff;
+#pragma unroll
+                for (int i = kRowVals - 1; i >= 0; --i)
+                    if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] == m) cand = c + 16 * i;
+                const int e = row_min_i32(cand);
+                sel[j] = e;
+                if ((e & 15) == c) taken |= 1u << (e >> 4);
+            }
+        }
+    }
+    float vs[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) vs[j] = (j < k) ? row_pick(v, sel[j], c, nv) : 0.f;
+    float sum = vs[0];
+#pragma unroll
+    for (int j = 1; j < kMaxK; ++j)
+        if (j < k) sum = sum + vs[j];
+    if (tv) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k && c == j) {
+                topk_idx[t * k + j] = sel[j];
+                topk_w[t * k + j] = zero_w ? 0.f : vs[j] / sum;
+                if (lds_ids) lds_ids[t * k + j] = sel[j];
+            }
+        }
+    }
+}
+
+// The row routine of a router variant (the plain softmax router is route_rows4).
+template <int kFn, bool kHash>
+__device__ __forceinline__ void route_rows(const float *__restrict__ logits,
+                                           const int32_t *__restrict__ q, int64_t t0,
+                                           int64_t T, int E, int k, const RouteOpts &o,
+                                           int32_t *__restrict__ topk_idx,
+                                           float *__restrict__ topk_w, int32_t *lds_ids,
+                                           float (&qp)[kRowVals], int &err) {
+    if constexpr (kFn == kScoreSoftmax && !kHash)
+        route_rows4(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, qp, err, o.lse);
+    else
+        route_rows4_scored<kFn, kHash>(logits, q, t0, T, E, k, o, topk_idx, topk_w, lds_ids,
+                                       qp, err);
 }
 
 // OR a per-lane error mask over the wave and raise it once.

@@ -8,7 +8,7 @@
 // same floating-point order, so each output is bitwise the one that path gives for the
 // same T:
 //   * top-k: wave w routes tokens 4w .. 4w+3 (one per 16-lane row) with the routine the
-//     multi-block kernel uses
+//     multi-block kernel uses (for every router variant)
 //     ("0 train-infer mismatch for Open-weight MoE RL in Open-source code", "The router:
 //     matching expert ids and weights"); replay ("Total Router Recall") is validated and
 //     passed through;
@@ -32,7 +32,7 @@ constexpr int kTailMaxA = kSmallT * kMaxK;
 static_assert(kTailWaves * kTailTokPerWave == kSmallT, "one wave per 4 tokens");
 static_assert(kTailMaxA / kWave <= kTailWaves, "one wave per 64 assignments");
 
-template <bool kReplay>
+template <bool kReplay, int kFn, bool kHash>
 __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ q,
     const int32_t *__restrict__ idx_in, const float *__restrict__ w_in, int T, int E, int k,
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     float *__restrict__ prob_mass, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int64_t *__restrict__ weighted_counts, int32_t *__restrict__ tiles,
-    int32_t *__restrict__ d_err, const int32_t *__restrict__ slot_map) {
+    int32_t *__restrict__ d_err, const int32_t *__restrict__ slot_map, RouteOpts opts) {
     __shared__ int32_t ids[kTailMaxA];
     __shared__ int32_t wstart[kTailMaxA / kWave][kMaxE];  // per-wave counts -> run starts
     __shared__ int32_t eoff[kMaxE + 1];                    // counts -> exclusive offsets
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
         }
     } else {
         float qp[kRowVals];
-        route_rows4(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k, topk_idx, topk_w, ids,
-                    qp, err);
+        route_rows<kFn, kHash>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k, opts,
+                               topk_idx, topk_w, ids, qp, err);
         if (prob_mass) {
             const int row = wave * 4 + (lane >> 4), c = lane & 15;
 #pragma unroll
@@ -197,12 +197,24 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
 
 }  // namespace
 
+template <bool kReplay, int kFn, bool kHash>
+static void launch_tail_t(const moe_dims &dm, int bt, int cap, const float *logits,
+                          const int32_t *q, const int32_t *idx_in, const float *w_in,
+                          int32_t *topk_idx, float *topk_w, float *prob_mass, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv,
+                          int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
+                          const int32_t *slot_map, const RouteOpts &o, hipStream_t s) {
+    route_tail_kernel<kReplay, kFn, kHash><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
+        logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w, prob_mass,
+        counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map, o);
+}
+
 hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
                              const int32_t *idx_in, const float *w_in, int32_t *topk_idx,
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                             hipStream_t s, const int32_t *slot_map) {
+                             hipStream_t s, const int32_t *slot_map, const RouteOpts &o) {
     if (dm.T < 1 || dm.T > kSmallT || dm.E > kMaxE || dm.k > kMaxK)
         return hipErrorInvalidValue;
     if (slot_map) {
@@ -211,14 +223,21 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int3
     }
     const int bt = select_tile_m(dm);
     const int cap = (int)max_m_tiles(dm.T * dm.k, dm.E, bt);
-    if (idx_in)
-        route_tail_kernel<true><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
-            logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
-            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map);
-    else
-        route_tail_kernel<false><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
-            logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
-            prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map);
+#define MOE_TAIL_ARGS dm, bt, cap, logits, q, idx_in, w_in, topk_idx, topk_w, prob_mass, \
+        counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map, o, s
+    if (idx_in) {
+        launch_tail_t<true, kScoreSoftmax, false>(MOE_TAIL_ARGS);
+    } else {
+        switch (o.fn * 2 + (o.hash_table ? 1 : 0)) {
+        case 0: launch_tail_t<false, kScoreSoftmax, false>(MOE_TAIL_ARGS); break;
+        case 1: launch_tail_t<false, kScoreSoftmax, true>(MOE_TAIL_ARGS); break;
+        case 2: launch_tail_t<false, kScoreSigmoid, false>(MOE_TAIL_ARGS); break;
+        case 3: launch_tail_t<false, kScoreSigmoid, true>(MOE_TAIL_ARGS); break;
+        case 4: launch_tail_t<false, kScoreSqrtSoftplus, false>(MOE_TAIL_ARGS); break;
+        default: launch_tail_t<false, kScoreSqrtSoftplus, true>(MOE_TAIL_ARGS); break;
+        }
+    }
+#undef MOE_TAIL_ARGS
     return hipGetLastError();
 }
 
