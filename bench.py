@@ -160,6 +160,88 @@ def stage_rates(L, dims, inp, K, hip, stream):
     return out
 
 
+def variant_report(L, dims, inp, K, hip, stream, vocab=131072):
+    """Router variants on the same layer ("0 train-infer mismatch ...", "Choosing GLM's
+    eight experts" and "Hash and learned expert routing"): the router alone (logits, choice,
+    weights, lse) for the softmax router, sigmoid and sqrt-softplus scores with a correction
+    bias, and hash routing over a vocabulary of ``vocab`` ids (a 128K-entry vocabulary is
+    assumed; the pages give none), as median ms and effective GB/s; the whole step with the
+    GLM-style router (sigmoid + bias, routed scaling factor 2.5) and the hash router next
+    to the softmax step; and the objective statistics (z-loss, load-balancing loss,
+    expert-bias update; HARTS eq. (20)). Algorithmic bytes: x + w_router + logits + ids and
+    weights (+ bias + lse, + token ids and table rows for hash)."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    import workloads as W
+    dev = inp["x"].device
+    eb = 2 if L.dtype == "bf16" else 4
+    T, d, E, k = L.T, L.d, L.E, L.k
+    bias = torch.from_numpy(W.correction_bias(E, L.seed)).to(dev)
+    table = torch.from_numpy(W.hash_table(vocab, E, k, L.seed)).to(dev)
+    tok = torch.from_numpy(W.token_ids(T, vocab, L.seed)).to(dev)
+    q = torch.from_numpy(W.token_multiplicities(T, L.seed)).to(dev)
+    ws = M.alloc_workspace(dims, dev)
+    b = M.alloc_forward_buffers(dims, dev, router=True, weighted=True)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+        hip.destroy(ev)
+        return ms
+
+    base = T * d * eb + E * d * eb + T * E * 4 + T * k * 8
+    routers = {
+        "softmax": (dict(score="softmax"), base),
+        "sigmoid_bias": (dict(score="sigmoid", corr_bias=bias), base + E * 4),
+        "sqrt_softplus_bias": (dict(score="sqrt_softplus", corr_bias=bias), base + E * 4),
+        "hash_sqrt_softplus": (dict(score="sqrt_softplus", hash_table=table, token_ids=tok),
+                               base + T * 4 + T * k * 4),
+    }
+    out = {"vocab": vocab}
+    for name, (kw, nb) in routers.items():
+        nb += T * 4                                     # lse
+        ms = timed(lambda: M.route_scored(dims, inp["x"], inp["w_router"], inp["logit_bias"],
+                                          b["topk_idx"], b["topk_w"], logits=b["logits"],
+                                          d_err=b["d_err"], workspace=ws, lse=lse, **kw))
+        out["route_" + name] = {"ms": round(ms, 5), "bytes": nb, "gbs": round(nb / ms / 1e6, 1)}
+
+    fb = M.alloc_forward_buffers(dims, dev, router=True, weighted=True)
+    del fb["x_perm"]
+    fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"], w_router=inp["w_router"],
+              logit_bias=inp["logit_bias"], token_mult=q)
+    steps = {"softmax": (None, 0.0),
+             "glm_sigmoid_bias_scale2.5": (dict(score="sigmoid", corr_bias=bias, lse=lse), 2.5),
+             "hash_sqrt_softplus": (dict(score="sqrt_softplus", hash_table=table, token_ids=tok,
+                                         lse=lse), 0.0)}
+    for name, (rkw, scale) in steps.items():
+        ms = timed(lambda: M.forward(dims, fb, ws, router=rkw, routed_scale=scale))
+        out["step_ms_" + name] = round(ms, 5)
+    assert int(fb["d_err"].item()) == 0
+    ob = torch.zeros(3, dtype=torch.float64, device=dev)
+    bias_w = bias.clone()
+    nb = T * 8 + E * (8 + 4 + 8) + 24
+    ms = timed(lambda: M.objectives(dims, ob, lse=lse, token_mult=q,
+                                    weighted_counts=fb["weighted_counts"],
+                                    prob_mass=fb["prob_mass"], bias_rate=1e-3,
+                                    corr_bias=bias_w))
+    z, aux, S = host_list(ob)
+    out["objectives"] = {"ms": round(ms, 5), "bytes": nb, "z_loss": round(z, 6),
+                         "aux_loss": round(aux, 6), "S": int(S)}
+    return out
+
+
+def host_list(t):
+    return [float(v) for v in t.cpu().tolist()]
+
+
 def placement_report(L, dims, inp, counts, K, hip, stream, P=8):
     """Logical -> physical expert placement over P expert-parallel ranks (layer-local LPT of
     "RoutePack ...", Sec. 3) from this step's expert counts: rank-load coefficient of
@@ -459,6 +541,7 @@ def main():
     hip.destroy(bnd)
     stages = stage_rates(L, dims, inp, K, hip, stream)
     placement = placement_report(L, dims, inp, host_counts, K, hip, stream) if L.E % 8 == 0 else None
+    variants = variant_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
 
     A = L.T * L.k
     ms_step = total_ms / K
@@ -509,6 +592,7 @@ def main():
                     "p90": round(float(np.percentile(step_ms, 90)), 5)},
         "stages_hbm": stages,
         "placement": placement,
+        "router_variants": variants,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:
