@@ -65,6 +65,11 @@ def lib():
         L.orc_route_scored.restype = I32
         L.orc_objectives.argtypes = [P, P, I64, P, P, I32, I32, ctypes.c_float, P, P]
         L.orc_objectives.restype = None
+        L.orc_round_f64_bf16.argtypes = [P, P, I64]
+        L.orc_round_f64_bf16.restype = None
+        L.orc_combine_ranks.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, P,
+                                        ctypes.c_float, I32, P, P]
+        L.orc_combine_ranks.restype = None
         L.orc_round_bf16.argtypes = [P, P, I64]
         L.orc_round_bf16.restype = None
         L.orc_place_lpt.argtypes = [P, I32, I32, P, P]
@@ -294,6 +299,51 @@ def combine(y, inv, w, dtype: str, scale: float = 1.0):
     else:
         lib().orc_combine_scaled(_p(y), _p(inv), _p(w), T, k, d, _dt(dtype), scale, _p(out))
     return out
+
+
+def round_f64_bf16(a) -> np.ndarray:
+    """float64 -> bfloat16 bits, round to nearest even in one step."""
+    a = _c(a, np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().orc_round_f64_bf16(_p(a), _p(out), a.size)
+    return out
+
+
+def shared_ffn(x, w13s, w2s, dtype: str):
+    """The shared expert sharded over R ranks along its inter dimension ("0 train-infer
+    mismatch ...", shared expert with the dense fixed-K projections and SwiGLU, one shard per
+    rank): w13s [R, 2 Is/R, d] (each rank's gate rows then up rows), w2s [R, d, Is/R].
+    Every rank's shard is the expert FFN of all T rows. Returns (h [R, T, Is/R],
+    y [R, T, d] FP32)."""
+    R = w13s.shape[0]
+    T = x.shape[0]
+    xr = np.ascontiguousarray(np.concatenate([x] * R, axis=0))
+    rowexp = np.repeat(np.arange(R, dtype=np.int32), T)
+    h, y = expert_ffn(xr, rowexp, w13s, w2s, dtype)
+    return h.reshape(R, T, -1), y.reshape(R, T, -1)
+
+
+def combine_ranks(y, inv, w, idx, E: int, R: int, dtype: str, slot_of_expert=None,
+                  y_shared=None, scale: float = 1.0):
+    """Rank partial outputs (slot-order FP32 sums with other ranks' slots as exact zeros,
+    routed scaling factor, shared-expert shard, one rounding) and their FP64 pairwise tree
+    in rank order, rounded once ("0 train-infer mismatch ...", "Sharding the experts").
+    Returns (partials [R, T, d], out [T, d]) in the storage type."""
+    y = _c(y, np.float32)
+    inv = _c(inv, np.int32)
+    w = _c(w, np.float32)
+    idx = _c(idx, np.int32)
+    sm = _c(slot_of_expert, np.int32)
+    ys = _c(y_shared, np.float32)
+    T, k = w.shape
+    d = y.shape[1]
+    if E % R or R > 64:
+        raise ValueError("R must divide E (and be at most 64)")
+    parts = np.empty((R, T, d), dtype=_store_dtype(dtype))
+    out = np.empty((T, d), dtype=_store_dtype(dtype))
+    lib().orc_combine_ranks(_p(y), _p(inv), _p(w), _p(idx), _p(sm), T, k, d, E, R, _p(ys),
+                            scale, _dt(dtype), _p(parts), _p(out))
+    return parts, out
 
 
 def forward(L, logits: Optional[np.ndarray] = None, S_stats: bool = True) -> dict:

@@ -574,3 +574,88 @@ void orc_objectives(const float *lse, const int32_t *q, int64_t T, const int64_t
         }
     }
 }
+
+/* Round a double to bfloat16, to nearest with ties to even, in one step (no intermediate
+ * FP32 rounding): |x| = m 2^e with m in [1/2, 1) has 8 significant bits in bf16, so its
+ * quantum is 2^(e-8), and never below the smallest subnormal 2^-133; scale by the quantum
+ * (exact), round to an integer with rint (ties to even in the default mode), scale back. */
+static uint16_t orc_f64_to_bf16(double x) {
+    if (isnan(x)) return 0x7fc0;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isinf(x)) return (uint16_t)(sign | 0x7f80);
+    if (x == 0.0) return sign;
+    int e;
+    frexp(fabs(x), &e);
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    const double r = ldexp(rint(ldexp(fabs(x), -qexp)), qexp);
+    if (r > 3.3895313892515355e38) return (uint16_t)(sign | 0x7f80); /* above bf16 max */
+    const float f = (float)r;                                         /* exact */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void orc_round_f64_bf16(const double *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(in[i]);
+}
+
+/* Expert-parallel output of one token, emulated on one device ("0 train-infer mismatch
+ * ...", "Sharding the experts", and the shared-expert passage of "The experts: keeping the
+ * route weight inside the accumulator"):
+ *  - R ranks; rank r owns physical slots [r E/R, (r+1) E/R); the slot of routed id e is
+ *    slot_map[e] (identity when NULL); an id outside [0, E) belongs to no rank;
+ *  - rank r's partial: acc = 0; for j = 0..k-1 in slot order acc = acc + (the slot's rank
+ *    is r ? w_j Y_j : 0) (other ranks' slots add exact zeros), all FP32; then
+ *    acc = scale * acc (the routed scaling factor, 1 for none), plus the rank's shard of
+ *    the shared expert ys[r, t, o] when ys is given; rounded once to the output type
+ *    (bf16 for dt = 1; FP32 stays);
+ *  - the R partials, in rank order, reduced by a pairwise tree: adjacent pairs added in
+ *    FP64, an odd last contributor carried to the next level unchanged, repeated until one
+ *    value remains, which is rounded once to the output type.
+ * partials (optional, [R, T, d], output type) receives the rank partials. */
+void orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const int32_t *idx,
+                       const int32_t *slot_map, int64_t T, int k, int d, int E, int R,
+                       const float *ys, float scale, int dt, void *partials, void *out) {
+    const int H = E / R;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        int owner[8];
+        for (int j = 0; j < k; ++j) {
+            int e = idx[t * k + j];
+            int v = (e >= 0 && e < E) ? (slot_map ? slot_map[e] : e) : -1;
+            owner[j] = (v >= 0 && v < E) ? v / H : -1;
+        }
+        for (int o = 0; o < d; ++o) {
+            double lvl[64];
+            for (int r = 0; r < R; ++r) {
+                float acc = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    float prod = (owner[j] == r) ? w[t * k + j] * y[(int64_t)inv[t * k + j] * d + o]
+                                                 : 0.0f;
+                    acc = acc + prod;
+                }
+                acc = scale * acc;
+                if (ys) acc = acc + ys[((int64_t)r * T + t) * d + o];
+                float part;
+                if (dt == 1) {
+                    uint16_t b = orc_f32_to_bf16(acc);
+                    part = orc_bf16_to_f32(b);
+                } else {
+                    part = acc;
+                }
+                if (partials) orc_store(partials, ((int64_t)r * T + t) * d + o, part, dt);
+                lvl[r] = (double)part;
+            }
+            int n = R;
+            while (n > 1) {
+                int m = 0;
+                for (int i = 0; i + 1 < n; i += 2) lvl[m++] = lvl[i] + lvl[i + 1];
+                if (n & 1) lvl[m++] = lvl[n - 1];
+                n = m;
+            }
+            if (dt == 1) ((uint16_t *)out)[t * (int64_t)d + o] = orc_f64_to_bf16(lvl[0]);
+            else ((float *)out)[t * (int64_t)d + o] = (float)lvl[0];
+        }
+    }
+}
