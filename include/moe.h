@@ -284,6 +284,44 @@ moe_status moe_objectives(const moe_dims *dims, const float *lse, const int32_t 
                           const int32_t *slot_of_expert, float bias_rate, float *corr_bias,
                           double *out, int32_t *d_err, void *stream);
 
+/* Expert-parallel output of the layer, emulated on one device [EX] ("Sharding the
+ * experts"; the shared-expert passage of "The experts: keeping the route weight inside the
+ * accumulator"). R = ranks (1 <= R <= 16, R divides E) each own E/R consecutive physical
+ * slots; the physical slot of routed id e is slot_of_expert[e] (identity when NULL).
+ *  partial_r[t,o] = round_dtype( routed_scale * acc_r + y_shared[r,t,o] ), where
+ *    acc_r = ((0 + c_0) + c_1) + ... over the slots j = 0..k-1 in slot order, FP32, with
+ *    c_j = w_j y[inv[t*k+j], o] when slot j's expert lives on rank r and an exact 0
+ *    otherwise (y_shared NULL: no shared expert; routed_scale 0 means 1);
+ *  out[t,o] = round_dtype( pairwise FP64 tree over partial_0 .. partial_{R-1} ): adjacent
+ *    pairs added in FP64, an odd last contributor carried to the next level unchanged,
+ *    until one value remains (8 ranks: three levels; 16: four), rounded once (bf16 round
+ *    to nearest even, directly from FP64).
+ * y [T*k,d] f32, inv [T*k] i32, topk_w [T,k] f32, topk_idx [T,k] i32 (logical ids; an id
+ * outside [0,E) belongs to no rank), slot_of_expert [E] i32 or NULL, y_shared [R,T,d] f32
+ * or NULL, partials [R,T,d] dtype output or NULL, out [T,d] dtype. With R = 1 and no shared
+ * expert, out is moe_combine_scaled's, bit for bit. MOE_E_SHAPE for a bad R or a
+ * non-finite routed_scale. */
+moe_status moe_combine_ranks(const moe_dims *dims, int32_t ranks, const float *y,
+                             const int32_t *inv, const float *topk_w, const int32_t *topk_idx,
+                             const int32_t *slot_of_expert, const float *y_shared,
+                             float routed_scale, void *partials, void *out, void *stream);
+
+/* The shared expert sharded over R ranks along its inter dimension [MM][SW][EX]: rank r
+ * holds gate/up rows w13_shared[r] = [2*Is/R, d] (its gate rows, then its up rows) and
+ * down columns w2_shared[r] = [d, Is/R] (Is = inter_shared), and computes for every token
+ *   h_shared[r,t,i] = round_dtype( silu(g_i) * u_i ),  g, u = fixed-K FP32 dot products of
+ *                     x[t] with its gate / up rows;
+ *   y_shared[r,t,o] = sum_i h_shared[r,t,i] w2_shared[r,o,i]   (FP32, fixed K order),
+ * the same fixed-K grouped GEMMs as the routed experts (every row is bitwise independent of
+ * T). x [T,d] dtype (< 4 GiB), h_shared [R,T,Is/R] dtype, y_shared [R,T,d] f32.
+ * Supported: 1 <= R <= 16, Is % R == 0, Is/R a multiple of 64 in [64, 16384], T*R < 2^31.
+ * Workspace: moe_shared_workspace_size() bytes (0 for invalid arguments). */
+size_t moe_shared_workspace_size(const moe_dims *dims, int32_t ranks, int32_t inter_shared);
+moe_status moe_shared_ffn(const moe_dims *dims, int32_t ranks, int32_t inter_shared,
+                          const void *x, const void *w13_shared, const void *w2_shared,
+                          void *h_shared, float *y_shared, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Everything moe_forward needs. Replay mode iff idx_in != NULL (then w_in is required
  * and w_router/logit_bias/logits/prob_mass are ignored); router mode otherwise.
  * Required: x, w13, w2, out, topk_idx, topk_w, counts, offsets, perm, inv, h, y,
@@ -299,7 +337,11 @@ moe_status moe_objectives(const moe_dims *dims, const float *lse, const int32_t 
  * stays in logical ids).
  * router: NULL, or the router variant of moe_route_scored (router mode only).
  * routed_scale: the combine's routed scaling factor as in moe_combine_scaled; 0 means 1
- * (no factor), so a zero-initialised struct keeps moe_combine's bits. */
+ * (no factor), so a zero-initialised struct keeps moe_combine's bits.
+ * ranks: 0 = the plain combine; R >= 1 = the output is moe_combine_ranks' (partials
+ * optional), with the shared expert of moe_shared_ffn when w13_shared is not NULL (then
+ * w2_shared, h_shared, y_shared and a shared_workspace of moe_shared_workspace_size()
+ * bytes are required). */
 typedef struct moe_forward_args {
     const void *x;
     const void *w_router;
@@ -332,6 +374,15 @@ typedef struct moe_forward_args {
     const int32_t *slot_of_expert; /* NULL: identity placement; else as moe_permute_placed */
     const moe_router_opts *router; /* host pointer; NULL: softmax router as moe_route */
     float routed_scale;            /* 0 or 1: no factor */
+    int32_t ranks;                 /* 0: plain combine; R: rank partials + FP64 tree */
+    void *partials;                /* [R,T,d] dtype or NULL */
+    const void *w13_shared;        /* [R, 2*inter_shared/R, d] or NULL: no shared expert */
+    const void *w2_shared;         /* [R, d, inter_shared/R] */
+    int32_t inter_shared;
+    void *h_shared;                /* [R, T, inter_shared/R] dtype */
+    float *y_shared;               /* [R, T, d] f32 */
+    void *shared_workspace;
+    size_t shared_workspace_bytes;
 } moe_forward_args;
 
 /* The whole layer: route (or replay) -> permute -> grouped FFN -> combine, each step as

@@ -49,7 +49,11 @@ class ForwardArgs(ctypes.Structure):
                 ("perm", _P), ("inv", _P), ("seq_counts", _P), ("weighted_counts", _P),
                 ("x_perm", _P), ("h", _P), ("y", _P), ("d_err", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t), ("prof_events", _P),
-                ("slot_of_expert", _P), ("router", _P), ("routed_scale", ctypes.c_float)]
+                ("slot_of_expert", _P), ("router", _P), ("routed_scale", ctypes.c_float),
+                ("ranks", ctypes.c_int32), ("partials", _P), ("w13_shared", _P),
+                ("w2_shared", _P), ("inter_shared", ctypes.c_int32), ("h_shared", _P),
+                ("y_shared", _P), ("shared_workspace", _P),
+                ("shared_workspace_bytes", ctypes.c_size_t)]
 
 
 class RouterOpts(ctypes.Structure):
@@ -83,6 +87,12 @@ _SIGS = {
                            ctypes.c_int),
     "moe_objectives": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                         _P], ctypes.c_int),
+    "moe_combine_ranks": ([ctypes.POINTER(Dims), ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                           ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "moe_shared_workspace_size": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32],
+                                  ctypes.c_size_t),
+    "moe_shared_ffn": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P,
+                        _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -193,6 +203,37 @@ def objectives(dims, out, lse=None, token_mult=None, weighted_counts=None, prob_
                                 _stream(stream)), "moe_objectives")
 
 
+def combine_ranks(dims, ranks: int, y, inv, topk_w, topk_idx, out, slot_of_expert=None,
+                  y_shared=None, routed_scale: float = 0.0, partials=None, stream=None):
+    """moe_combine_ranks: rank partial outputs and their FP64 pairwise tree."""
+    _check(lib().moe_combine_ranks(ctypes.byref(dims), ranks, _ptr(y), _ptr(inv), _ptr(topk_w),
+                                   _ptr(topk_idx), _ptr(slot_of_expert), _ptr(y_shared),
+                                   routed_scale, _ptr(partials), _ptr(out), _stream(stream)),
+           "moe_combine_ranks")
+
+
+def shared_workspace_size(dims, ranks: int, inter_shared: int) -> int:
+    return lib().moe_shared_workspace_size(ctypes.byref(dims), ranks, inter_shared)
+
+
+def alloc_shared_workspace(dims, ranks: int, inter_shared: int, device="cuda") -> torch.Tensor:
+    n = shared_workspace_size(dims, ranks, inter_shared)
+    if n == 0:
+        raise MoeError(2, "moe_shared_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def shared_ffn(dims, ranks: int, inter_shared: int, x, w13_shared, w2_shared, h_shared,
+               y_shared, workspace=None, stream=None):
+    """moe_shared_ffn: the shared expert sharded over ``ranks`` ranks."""
+    ws = workspace if workspace is not None else alloc_shared_workspace(dims, ranks,
+                                                                         inter_shared, x.device)
+    _check(lib().moe_shared_ffn(ctypes.byref(dims), ranks, inter_shared, _ptr(x),
+                                _ptr(w13_shared), _ptr(w2_shared), _ptr(h_shared),
+                                _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_shared_ffn")
+
+
 def route_replay(dims, idx_in, w_in, topk_idx, topk_w, d_err=None, stream=None):
     _check(lib().moe_route_replay(ctypes.byref(dims), _ptr(idx_in), _ptr(w_in), _ptr(topk_idx),
                                   _ptr(topk_w), _ptr(d_err), _stream(stream)),
@@ -253,14 +294,16 @@ def combine(dims, y, inv, topk_w, out, stream=None, routed_scale=None):
 
 
 def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=None,
-            router: Optional[dict] = None, routed_scale: float = 0.0):
+            router: Optional[dict] = None, routed_scale: float = 0.0, ranks: int = 0,
+            inter_shared: int = 0, shared_workspace: Optional[torch.Tensor] = None):
     """Run moe_forward. ``bufs`` maps ForwardArgs field names to tensors (or None);
     ``prof_events`` is None or a sequence of three raw hipEvent_t handles; ``router`` is
     None or the keyword arguments of router_opts; ``routed_scale`` 0 means no factor."""
     a = ForwardArgs()
     for name, _ in ForwardArgs._fields_:
         if name in ("num_seqs", "workspace", "workspace_bytes", "prof_events", "router",
-                    "routed_scale"):
+                    "routed_scale", "ranks", "inter_shared", "shared_workspace",
+                    "shared_workspace_bytes"):
             continue
         setattr(a, name, _ptr(bufs.get(name)))
     ropts = None
@@ -268,6 +311,11 @@ def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=
         ropts = router_opts(**router)
         a.router = ctypes.cast(ctypes.pointer(ropts), ctypes.c_void_p)
     a.routed_scale = routed_scale
+    a.ranks = ranks
+    a.inter_shared = inter_shared
+    if shared_workspace is not None:
+        a.shared_workspace = _ptr(shared_workspace)
+        a.shared_workspace_bytes = shared_workspace.numel()
     cu = bufs.get("cu_seqlens")
     a.num_seqs = 0 if cu is None else cu.numel() - 1
     a.workspace = _ptr(workspace)

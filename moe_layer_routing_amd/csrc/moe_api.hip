@@ -291,6 +291,73 @@ moe_status moe_objectives(const moe_dims *dims, const float *lse, const int32_t 
                                        static_cast<hipStream_t>(stream)));
 }
 
+static bool ranks_ok(const moe_dims *dims, int32_t R) {
+    return R >= 1 && R <= kMaxRanks && dims->E % R == 0;
+}
+
+// The shared expert alone needs no relation between R and E (the rank combine does).
+static bool shared_ok(const moe_dims *dims, int32_t R, int32_t Is) {
+    if (R < 1 || R > kMaxRanks || Is < 1 || Is % R) return false;
+    const int32_t s = Is / R;
+    if (s < 64 || s > 16384 || s % 64) return false;
+    if (dims->T * (int64_t)R >= (int64_t(1) << 31)) return false;
+    const int64_t x_bytes = dims->T * (int64_t)dims->d * (dims->dtype == MOE_BF16 ? 2 : 4);
+    return x_bytes < (int64_t(1) << 32);   // rows are gathered with 32-bit byte offsets
+}
+
+moe_status moe_combine_ranks(const moe_dims *dims, int32_t ranks, const float *y,
+                             const int32_t *inv, const float *topk_w, const int32_t *topk_idx,
+                             const int32_t *slot_of_expert, const float *y_shared,
+                             float routed_scale, void *partials, void *out, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(ranks_ok(dims, ranks), MOE_E_SHAPE);
+    MOE_REQUIRE(std::isfinite(routed_scale), MOE_E_SHAPE);
+    if (dims->T > 0) MOE_REQUIRE(y && inv && topk_w && topk_idx && out, MOE_E_NULLPTR);
+    const float scale = routed_scale == 0.0f ? 1.0f : routed_scale;
+    return to_status(launch_combine_ranks(*dims, ranks, y, inv, topk_w, topk_idx,
+                                          slot_of_expert, scale, y_shared, partials, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_shared_workspace_size(const moe_dims *dims, int32_t ranks, int32_t inter_shared) {
+    if (!dims_ok(dims) || !dtype_ok(dims) || !shared_ok(dims, ranks, inter_shared)) return 0;
+    return shared_workspace_bytes(*dims, ranks, inter_shared);
+}
+
+moe_status moe_shared_ffn(const moe_dims *dims, int32_t ranks, int32_t inter_shared,
+                          const void *x, const void *w13_shared, const void *w2_shared,
+                          void *h_shared, float *y_shared, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(shared_ok(dims, ranks, inter_shared), MOE_E_SHAPE);
+    if (dims->T > 0)
+        MOE_REQUIRE(x && w13_shared && w2_shared && h_shared && y_shared, MOE_E_NULLPTR);
+    MOE_REQUIRE(workspace, MOE_E_WORKSPACE);
+    MOE_REQUIRE(workspace_bytes >= shared_workspace_bytes(*dims, ranks, inter_shared),
+                MOE_E_WORKSPACE);
+    return to_status(launch_shared_ffn(*dims, ranks, inter_shared, x, w13_shared, w2_shared,
+                                       h_shared, y_shared, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+// The layer's output step: the plain combine, or (ranks >= 1) the shared expert's shards
+// and the rank partials with their FP64 tree.
+static hipError_t finish_layer(const moe_dims *dims, const moe_forward_args *a, float scale,
+                               hipStream_t s) {
+    if (!a->ranks) return launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale);
+    if (a->w13_shared) {
+        const hipError_t e = launch_shared_ffn(*dims, a->ranks, a->inter_shared, a->x,
+                                               a->w13_shared, a->w2_shared, a->h_shared,
+                                               a->y_shared, a->shared_workspace, s);
+        if (e != hipSuccess) return e;
+    }
+    return launch_combine_ranks(*dims, a->ranks, a->y, a->inv, a->topk_w, a->topk_idx,
+                                a->slot_of_expert, scale, a->w13_shared ? a->y_shared : nullptr,
+                                a->partials, a->out, s);
+}
+
 moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *stream) {
     moe_status st = check_common(dims);
     if (st != MOE_OK) return st;
@@ -315,6 +382,15 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     }
     MOE_REQUIRE(std::isfinite(a->routed_scale), MOE_E_SHAPE);
     const float scale = a->routed_scale == 0.0f ? 1.0f : a->routed_scale;
+    if (a->ranks) MOE_REQUIRE(ranks_ok(dims, a->ranks), MOE_E_SHAPE);
+    if (a->w13_shared) {
+        MOE_REQUIRE(a->ranks >= 1 && shared_ok(dims, a->ranks, a->inter_shared), MOE_E_SHAPE);
+        MOE_REQUIRE(a->w2_shared && a->h_shared && a->y_shared, MOE_E_NULLPTR);
+        MOE_REQUIRE(a->shared_workspace && a->shared_workspace_bytes >=
+                                               shared_workspace_bytes(*dims, a->ranks,
+                                                                      a->inter_shared),
+                    MOE_E_WORKSPACE);
+    }
     st = check_ws(dims, a->workspace, a->workspace_bytes);
     if (st != MOE_OK) return st;
     const Workspace ws = carve_workspace(*dims, a->workspace);
@@ -339,7 +415,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                                a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        return to_status(launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale));
+        return to_status(finish_layer(dims, a, scale, s));
     }
     if (replay)
         e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
@@ -356,8 +432,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                            a->prof_events, s, a->x, a->perm);
     if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale);
-    return to_status(e);
+    return to_status(finish_layer(dims, a, scale, s));
 }
 
 }  // extern "C"

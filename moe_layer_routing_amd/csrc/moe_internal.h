@@ -16,6 +16,7 @@ constexpr int kMaxK = 8;           // experts per token
 constexpr int kPermChunk = 2048;   // flat assignments per permute block (fixed, T-free)
 constexpr int kTopkTokPerBlock = 16;  // 4 waves x 4 tokens
 constexpr int kSmallT = 64;           // largest batch the single-block routing tail takes
+constexpr int kMaxRanks = 16;         // ranks of the emulated expert-parallel output
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -134,6 +135,18 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                               bool tiles_ready = false);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s, float scale = 1.0f);
+// Rank partial outputs and their FP64 pairwise tree (1 <= R <= kMaxRanks, R divides E).
+hipError_t launch_combine_ranks(const moe_dims &dm, int R, const float *y, const int32_t *inv,
+                                const float *topk_w, const int32_t *topk_idx,
+                                const int32_t *slot_map, float scale, const float *ys,
+                                void *partials, void *out, hipStream_t s);
+// The shared expert sharded over R ranks: the grouped problem it runs as, its workspace,
+// and the launch (rows gathered from x, so x must be under 4 GiB).
+moe_dims shared_dims(const moe_dims &dm, int R, int inter_shared);
+size_t shared_workspace_bytes(const moe_dims &dm, int R, int inter_shared);
+hipError_t launch_shared_ffn(const moe_dims &dm, int R, int inter_shared, const void *x,
+                             const void *w13s, const void *w2s, void *h_s, float *y_s,
+                             void *workspace, hipStream_t s);
 // Objective statistics (one block): out[3] = z_loss, aux_loss, S; optional bias update.
 hipError_t launch_objectives(const moe_dims &dm, const float *lse, const int32_t *q,
                              const int64_t *wcounts, const float *mass,
