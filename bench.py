@@ -238,6 +238,77 @@ def variant_report(L, dims, inp, K, hip, stream, vocab=131072):
     return out
 
 
+def ranks_report(L, dims, inp, K, hip, stream, inter_shared=2048):
+    """Expert-parallel output emulated on one GPU ("0 train-infer mismatch ...", "Sharding the
+    experts"): for R = 8 and 16 ranks, the shared expert sharded over the ranks
+    (inter_shared features in all; the pages give no size, 2048 is assumed) as TFLOP/s of
+    6*T*d*inter_shared, the rank combine (R partials + FP64 pairwise tree) as GB/s of its
+    algorithmic bytes (Y + inv + weights + ids + shared shards + out), and the whole step
+    with both, next to the plain step."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    dev = inp["x"].device
+    eb = 2 if L.dtype == "bf16" else 4
+    T, d, E, k = L.T, L.d, L.E, L.k
+    A = T * k
+    rng = np.random.default_rng(L.seed)
+
+    def timed(fn):
+        fn()
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+        hip.destroy(ev)
+        return ms
+
+    ws = M.alloc_workspace(dims, dev)
+    fb = M.alloc_forward_buffers(dims, dev, router=(L.mode == "router"))
+    del fb["x_perm"]
+    fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"])
+    if L.mode == "router":
+        fb["w_router"], fb["logit_bias"] = inp["w_router"], inp["logit_bias"]
+    else:
+        fb["idx_in"], fb["w_in"] = inp["idx_in"], inp["w_in"]
+    out = {"inter_shared": inter_shared,
+           "step_ms_plain": round(timed(lambda: M.forward(dims, fb, ws)), 5)}
+    sd = fb["out"].dtype
+    for R in (8, 16):
+        if E % R:
+            continue
+        S = inter_shared // R
+        std = 1.0 / np.sqrt(d)
+        w13s = torch.from_numpy((rng.standard_normal((R, 2 * S, d)) * std).astype(np.float32))
+        w2s = torch.from_numpy((rng.standard_normal((R, d, S)) * std).astype(np.float32))
+        w13s, w2s = w13s.to(dev).to(sd), w2s.to(dev).to(sd)
+        hs = torch.empty((R, T, S), dtype=sd, device=dev)
+        ys = torch.empty((R, T, d), dtype=torch.float32, device=dev)
+        sws = M.alloc_shared_workspace(dims, R, inter_shared, dev)
+        ms_sh = timed(lambda: M.shared_ffn(dims, R, inter_shared, inp["x"], w13s, w2s, hs, ys,
+                                           workspace=sws))
+        flops = 6.0 * T * d * inter_shared
+        nb = A * d * 4 + A * 4 + T * k * 8 + R * T * d * 4 + T * d * eb
+        ms_c = timed(lambda: M.combine_ranks(dims, R, fb["y"], fb["inv"], fb["topk_w"],
+                                             fb["topk_idx"], fb["out"], y_shared=ys,
+                                             routed_scale=2.5))
+        fb.update(w13_shared=w13s, w2_shared=w2s, h_shared=hs, y_shared=ys)
+        ms_step = timed(lambda: M.forward(dims, fb, ws, routed_scale=2.5, ranks=R,
+                                          inter_shared=inter_shared, shared_workspace=sws))
+        for n in ("w13_shared", "w2_shared", "h_shared", "y_shared"):
+            del fb[n]
+        out[f"R{R}"] = {"shared_ffn_ms": round(ms_sh, 5),
+                        "shared_ffn_tflops": round(flops / (ms_sh * 1e-3) / 1e12, 1),
+                        "combine_ranks_ms": round(ms_c, 5), "combine_ranks_bytes": nb,
+                        "combine_ranks_gbs": round(nb / ms_c / 1e6, 1),
+                        "step_ms": round(ms_step, 5)}
+    assert int(fb["d_err"].item()) == 0
+    return out
+
+
 def host_list(t):
     return [float(v) for v in t.cpu().tolist()]
 
@@ -542,6 +613,7 @@ def main():
     stages = stage_rates(L, dims, inp, K, hip, stream)
     placement = placement_report(L, dims, inp, host_counts, K, hip, stream) if L.E % 8 == 0 else None
     variants = variant_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
+    ranks = ranks_report(L, dims, inp, K, hip, stream)
 
     A = L.T * L.k
     ms_step = total_ms / K
@@ -593,6 +665,7 @@ def main():
         "stages_hbm": stages,
         "placement": placement,
         "router_variants": variants,
+        "expert_parallel": ranks,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:

@@ -22,8 +22,6 @@
 namespace moe {
 namespace {
 
-constexpr int kSlice = 512;   // features per wave, as the plain combine
-
 // Round a double to bf16, to nearest with ties to even, in one step: the double is first
 // rounded toward zero to FP32 with the lowest bit forced to 1 when inexact ("round to
 // odd"); FP32 keeps 16 more significand bits than bf16, so the RNE rounding of that odd
@@ -34,9 +32,49 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     return f32_to_bf16(t);
 }
 
-// One wave per (token, 512-feature slice); lane l takes features s*512 + 4l and
-// s*512 + 256 + 4l, as the plain combine. The R partials of each feature stay in
-// registers; the tree's shape is fixed by R alone.
+// Vector loads and stores of V consecutive floats / bf16 values (V = 1, 2, 4).
+template <int V>
+__device__ __forceinline__ void load_f(const float *p, float (&v)[V]) {
+    if constexpr (V == 4) {
+        const float4 q = *reinterpret_cast<const float4 *>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else if constexpr (V == 2) {
+        const float2 q = *reinterpret_cast<const float2 *>(p);
+        v[0] = q.x; v[1] = q.y;
+    } else {
+        v[0] = *p;
+    }
+}
+template <int V>
+__device__ __forceinline__ void store_f(float *p, const float (&v)[V]) {
+    if constexpr (V == 4) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (V == 2) *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+    else *p = v[0];
+}
+template <int V>
+__device__ __forceinline__ void store_b(uint16_t *p, const uint16_t (&b)[V]) {
+    if constexpr (V == 4) {
+        uint2 pk;
+        pk.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+        pk.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+        *reinterpret_cast<uint2 *>(p) = pk;
+    } else if constexpr (V == 2) {
+        *reinterpret_cast<uint32_t *>(p) = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+    } else {
+        *p = b[0];
+    }
+}
+
+// Features per lane: fewer as R grows, so that the R partials of every feature a lane
+// holds, and the FP64 tree over them, stay in registers at a useful occupancy.
+template <int R>
+constexpr int ranks_vec() { return R <= 4 ? 4 : 2; }
+
+// One wave per (token, slice of 128 V features); lane l takes features slice*128V + V*l
+// and slice*128V + 64V + V*l (two chunks). For each chunk: the k weighted expert rows
+// (FP32 products), then per rank the slot-order sum with foreign slots as exact zeros,
+// the factor, the shared shard and the rounding; then per feature the FP64 tree over the
+// R partials, whose shape is fixed by R alone.
 template <bool kBF16, int R>
 __global__ __launch_bounds__(256) void combine_ranks_kernel(
     const float *__restrict__ y, const int32_t *__restrict__ inv,
@@ -44,12 +82,14 @@ __global__ __launch_bounds__(256) void combine_ranks_kernel(
     const int32_t *__restrict__ slot_map, int64_t T, int k, int d, int E, int64_t A,
     float scale, const float *__restrict__ ys, void *__restrict__ partials,
     void *__restrict__ out) {
+    constexpr int V = ranks_vec<R>();
+    constexpr int kSl = 128 * V;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nslice = (d + kSlice - 1) / kSlice;
+    const int nslice = (d + kSl - 1) / kSl;
     const int64_t W = (int64_t)blockIdx.x * 4 + wave;
     const int64_t t = W / nslice;
     if (t >= T) return;
-    const int c0 = (int)(W % nslice) * kSlice + lane * 4;
+    const int c0 = (int)(W % nslice) * kSl + lane * V;
     const int H = E / R;
     int64_t src[kMaxK];
     float w[kMaxK];
@@ -69,86 +109,78 @@ __global__ __launch_bounds__(256) void combine_ranks_kernel(
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int c = c0 + 256 * u;
+        const int c = c0 + 64 * V * u;
         if (c >= d) break;
-        float4 v[kMaxK];
+        float prod[kMaxK][V];
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
-            if (j < k) v[j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
-        float4 prod[kMaxK];
+            if (j < k) load_f<V>(y + src[j] + c, prod[j]);
+        float part[R][V];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (ys) load_f<V>(ys + ((int64_t)r * T + t) * d + c, part[r]);
+            else
+#pragma unroll
+                for (int q = 0; q < V; ++q) part[r][q] = 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
             if (j < k)
-                prod[j] = make_float4(w[j] * v[j].x, w[j] * v[j].y, w[j] * v[j].z, w[j] * v[j].w);
-        double lv[4][R];
+#pragma unroll
+                for (int q = 0; q < V; ++q) prod[j][q] = w[j] * prod[j][q];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            float a[V];
+#pragma unroll
+            for (int q = 0; q < V; ++q) a[q] = 0.f;
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j) {
                 if (j < k) {
                     const bool own = owner[j] == r;
-                    a0 = a0 + (own ? prod[j].x : 0.f);
-                    a1 = a1 + (own ? prod[j].y : 0.f);
-                    a2 = a2 + (own ? prod[j].z : 0.f);
-                    a3 = a3 + (own ? prod[j].w : 0.f);
+#pragma unroll
+                    for (int q = 0; q < V; ++q) a[q] = a[q] + (own ? prod[j][q] : 0.f);
                 }
             }
-            a0 = scale * a0;
-            a1 = scale * a1;
-            a2 = scale * a2;
-            a3 = scale * a3;
-            if (ys) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(ys + ((int64_t)r * T + t) * d + c);
-                a0 = a0 + s4.x;
-                a1 = a1 + s4.y;
-                a2 = a2 + s4.z;
-                a3 = a3 + s4.w;
+#pragma unroll
+            for (int q = 0; q < V; ++q) {
+                a[q] = scale * a[q];
+                if (ys) a[q] = a[q] + part[r][q];
             }
             if constexpr (kBF16) {
-                const uint16_t b0 = f32_to_bf16(a0), b1 = f32_to_bf16(a1), b2 = f32_to_bf16(a2),
-                               b3 = f32_to_bf16(a3);
-                if (partials) {
-                    uint2 pk;
-                    pk.x = (uint32_t)b0 | ((uint32_t)b1 << 16);
-                    pk.y = (uint32_t)b2 | ((uint32_t)b3 << 16);
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(partials) +
-                                               ((int64_t)r * T + t) * d + c) = pk;
+                uint16_t b[V];
+#pragma unroll
+                for (int q = 0; q < V; ++q) {
+                    b[q] = f32_to_bf16(a[q]);
+                    part[r][q] = bf16_to_f32(b[q]);
                 }
-                lv[0][r] = bf16_to_f32(b0);
-                lv[1][r] = bf16_to_f32(b1);
-                lv[2][r] = bf16_to_f32(b2);
-                lv[3][r] = bf16_to_f32(b3);
-            } else {
                 if (partials)
-                    *reinterpret_cast<float4 *>(static_cast<float *>(partials) +
-                                                ((int64_t)r * T + t) * d + c) =
-                        make_float4(a0, a1, a2, a3);
-                lv[0][r] = a0;
-                lv[1][r] = a1;
-                lv[2][r] = a2;
-                lv[3][r] = a3;
+                    store_b<V>(static_cast<uint16_t *>(partials) + ((int64_t)r * T + t) * d + c, b);
+            } else {
+#pragma unroll
+                for (int q = 0; q < V; ++q) part[r][q] = a[q];
+                if (partials)
+                    store_f<V>(static_cast<float *>(partials) + ((int64_t)r * T + t) * d + c, a);
             }
         }
-        // adjacent pairs in FP64, the odd last value carried, level by level
+        // per feature: adjacent pairs in FP64, the odd last value carried, level by level
+        uint16_t ob[V];
+        float of[V];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < V; ++q) {
+            double lv[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) lv[r] = part[r][q];
 #pragma unroll
             for (int n = R; n > 1; n = (n + 1) / 2) {
 #pragma unroll
-                for (int i = 0; i < n / 2; ++i) lv[q][i] = lv[q][2 * i] + lv[q][2 * i + 1];
-                if (n & 1) lv[q][n / 2] = lv[q][n - 1];
+                for (int i = 0; i < n / 2; ++i) lv[i] = lv[2 * i] + lv[2 * i + 1];
+                if (n & 1) lv[n / 2] = lv[n - 1];
             }
+            if constexpr (kBF16) ob[q] = f64_to_bf16(lv[0]);
+            else of[q] = (float)lv[0];
         }
-        if constexpr (kBF16) {
-            uint2 pk;
-            pk.x = (uint32_t)f64_to_bf16(lv[0][0]) | ((uint32_t)f64_to_bf16(lv[1][0]) << 16);
-            pk.y = (uint32_t)f64_to_bf16(lv[2][0]) | ((uint32_t)f64_to_bf16(lv[3][0]) << 16);
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + t * d + c) = pk;
-        } else {
-            *reinterpret_cast<float4 *>(static_cast<float *>(out) + t * d + c) =
-                make_float4((float)lv[0][0], (float)lv[1][0], (float)lv[2][0], (float)lv[3][0]);
-        }
+        if constexpr (kBF16) store_b<V>(static_cast<uint16_t *>(out) + t * d + c, ob);
+        else store_f<V>(static_cast<float *>(out) + t * d + c, of);
     }
 }
 
@@ -169,7 +201,8 @@ template <bool kBF16, int R>
 void launch_ranks_t(const moe_dims &dm, const float *y, const int32_t *inv, const float *w,
                     const int32_t *idx, const int32_t *map, float scale, const float *ys,
                     void *partials, void *out, hipStream_t s) {
-    const int64_t waves = dm.T * ((dm.d + kSlice - 1) / kSlice);
+    constexpr int kSl = 128 * ranks_vec<R>();
+    const int64_t waves = dm.T * ((dm.d + kSl - 1) / kSl);
     combine_ranks_kernel<kBF16, R><<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
         y, inv, w, idx, map, dm.T, dm.k, dm.d, dm.E, dm.T * dm.k, scale, ys, partials, out);
 }
