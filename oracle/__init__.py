@@ -65,6 +65,11 @@ def lib():
         L.orc_route_scored.restype = I32
         L.orc_objectives.argtypes = [P, P, I64, P, P, I32, I32, ctypes.c_float, P, P]
         L.orc_objectives.restype = None
+        L.orc_backward_experts.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_float, I64,
+                                           I32, I32, I32, I32, I32] + [P] * 9
+        L.orc_backward_experts.restype = None
+        L.orc_backward_router.argtypes = [P, P, P, P, I64, I32, I32, I32, I32, P, P, P]
+        L.orc_backward_router.restype = None
         L.orc_round_f64_bf16.argtypes = [P, P, I64]
         L.orc_round_f64_bf16.restype = None
         L.orc_combine_ranks.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, P,
@@ -344,6 +349,45 @@ def combine_ranks(y, inv, w, idx, E: int, R: int, dtype: str, slot_of_expert=Non
     lib().orc_combine_ranks(_p(y), _p(inv), _p(w), _p(idx), _p(sm), T, k, d, E, R, _p(ys),
                             scale, _dt(dtype), _p(parts), _p(out))
     return parts, out
+
+
+def backward_experts(x, perm, inv, counts, w, w13, w2, h, y, dout, dtype: str,
+                     scale: float = 1.0) -> dict:
+    """Backward of the expert path (derivative of the forward definitions; FP32, sequential
+    sums): dw, dy, gu, dh, dgu, dxp, dx (experts' part), dw13, dw2."""
+    T, d = x.shape
+    k = w.shape[1]
+    E = len(counts)
+    I = w2.shape[2]
+    A = T * k
+    rowexp = np.repeat(np.arange(E, dtype=np.int32), counts)
+    f = lambda *sh: np.empty(sh, dtype=np.float32)
+    r = dict(dw=f(T, k), dy=f(A, d), gu=f(A, 2 * I), dh=f(A, I), dgu=f(A, 2 * I),
+             dxp=f(A, d), dx=f(T, d), dw13=f(E, 2 * I, d), dw2=f(E, d, I))
+    args = [np.ascontiguousarray(a) for a in (x, perm, inv, rowexp, w, w13, w2, h, y, dout)]
+    args[1], args[2], args[3] = (args[1].astype(np.int32), args[2].astype(np.int32),
+                                 args[3].astype(np.int32))
+    args[4], args[8] = args[4].astype(np.float32), args[8].astype(np.float32)
+    lib().orc_backward_experts(*[_p(a) for a in args], scale, T, k, d, I, E, _dt(dtype),
+                               *[_p(r[n]) for n in ("dw", "dy", "gu", "dh", "dgu", "dxp",
+                                                    "dx", "dw13", "dw2")])
+    return r
+
+
+def backward_router(logits, dw, x, w_router, dtype: str) -> dict:
+    """Backward of the softmax router from the weights' gradient by slot (its own choice
+    recomputed from the logits; also the replay stop-gradient's router gradient): dl,
+    dw_router, dx (router's part)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    k = dw.shape[1]
+    d = x.shape[1]
+    r = dict(dl=np.empty((T, E), np.float32), dw_router=np.empty((E, d), np.float32),
+             dx=np.empty((T, d), np.float32))
+    lib().orc_backward_router(_p(logits), _p(_c(dw, np.float32)), _p(np.ascontiguousarray(x)),
+                              _p(np.ascontiguousarray(w_router)), T, E, k, d, _dt(dtype),
+                              _p(r["dl"]), _p(r["dw_router"]), _p(r["dx"]))
+    return r
 
 
 def forward(L, logits: Optional[np.ndarray] = None, S_stats: bool = True) -> dict:

@@ -659,3 +659,173 @@ void orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const
         }
     }
 }
+
+/* Backward of the expert path of the layer (the derivative of the forward definitions
+ * above; "0 train-infer mismatch ...", "The experts: keeping the route weight inside the
+ * accumulator" and "SwiGLU: rounding after the multiply" fix the forward). Given the
+ * upstream gradient dout [T,d] of out, with the forward's saved h [A,I] (dt) and y [A,d]
+ * (FP32) and the routing (perm, inv, segments, weights w [T,k], routed scaling factor s):
+ *   dy[p,:]  = (s * w[t,j]) * dout[t,:]            for p = inv[t*k+j]   (FP32)
+ *   dw[t,j]  = s * (sum over o ascending of dout[t,o] * y[p,o])
+ *   gu[p,n]  = sum over c ascending of xr[p,c] * w13[e,n,c]   (xr = x[perm[p] / k]; the
+ *              forward's gate (n < I) and up (n >= I) pre-activations, recomputed)
+ *   dh[p,i]  = sum over o ascending of dy[p,o] * w2[e,o,i]
+ *   with g = gu[p,i], u = gu[p,I+i], sg = 1 / (1 + exp(-g)), silu = g / (1 + exp(-g)),
+ *        dsilu = sg * (1 + g * (1 - sg)):
+ *   dgu[p,i] = (dh * u) * dsilu,  dgu[p,I+i] = dh * silu
+ *   dxp[p,c] = sum over n ascending of dgu[p,n] * w13[e,n,c]
+ *   dx[t,c]  = ((0 + dxp[inv[t*k],c]) + dxp[inv[t*k+1],c]) + ...   (slot order)
+ *   dw2[e,o,i]  = sum over the segment's rows p ascending of dy[p,o] * h[p,i]
+ *   dw13[e,n,c] = sum over the segment's rows p ascending of dgu[p,n] * xr[p,c]
+ * All FP32, each sum sequential; rowexp [A] gives each row's expert. */
+void orc_backward_experts(const void *x, const int32_t *perm, const int32_t *inv,
+                          const int32_t *rowexp, const float *w, const void *w13,
+                          const void *w2, const void *h, const float *y, const void *dout,
+                          float s, int64_t T, int k, int d, int I, int E, int dt, float *dw,
+                          float *dy, float *gu, float *dh, float *dgu, float *dxp, float *dx,
+                          float *dw13, float *dw2) {
+    const int64_t A = T * k;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            const int64_t p = inv[t * k + j];
+            const float ws = s * w[t * k + j];
+            float acc = 0.0f;
+            for (int o = 0; o < d; ++o) {
+                const float g = orc_load(dout, t * (int64_t)d + o, dt);
+                dy[p * d + o] = ws * g;
+                acc = acc + g * y[p * d + o];
+            }
+            dw[t * k + j] = s * acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < A; ++p) {
+        const int e = rowexp[p];
+        const int64_t xt = perm[p] / k;
+        const int64_t wb13 = (int64_t)e * 2 * I * d, wb2 = (int64_t)e * d * I;
+        for (int n = 0; n < 2 * I; ++n) {
+            float acc = 0.0f;
+            for (int c = 0; c < d; ++c)
+                acc = acc + orc_load(x, xt * d + c, dt) * orc_load(w13, wb13 + (int64_t)n * d + c, dt);
+            gu[p * 2 * I + n] = acc;
+        }
+        for (int i = 0; i < I; ++i) {
+            float acc = 0.0f;
+            for (int o = 0; o < d; ++o)
+                acc = acc + dy[p * d + o] * orc_load(w2, wb2 + (int64_t)o * I + i, dt);
+            dh[p * I + i] = acc;
+            const float g = gu[p * 2 * I + i], u = gu[p * 2 * I + I + i];
+            const float sg = 1.0f / (1.0f + expf(-g));
+            const float silu = g / (1.0f + expf(-g));
+            const float dsilu = sg * (1.0f + g * (1.0f - sg));
+            dgu[p * 2 * I + i] = (acc * u) * dsilu;
+            dgu[p * 2 * I + I + i] = acc * silu;
+        }
+        for (int c = 0; c < d; ++c) {
+            float acc = 0.0f;
+            for (int n = 0; n < 2 * I; ++n)
+                acc = acc + dgu[p * 2 * I + n] * orc_load(w13, wb13 + (int64_t)n * d + c, dt);
+            dxp[p * d + c] = acc;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int c = 0; c < d; ++c) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) acc = acc + dxp[(int64_t)inv[t * k + j] * d + c];
+            dx[t * d + c] = acc;
+        }
+    /* segments: rows of expert e are contiguous; find each segment's bounds */
+#pragma omp parallel for schedule(dynamic)
+    for (int e = 0; e < E; ++e) {
+        int64_t p0 = 0;
+        while (p0 < A && rowexp[p0] != e) ++p0;
+        int64_t p1 = p0;
+        while (p1 < A && rowexp[p1] == e) ++p1;
+        for (int o = 0; o < d; ++o)
+            for (int i = 0; i < I; ++i) {
+                float acc = 0.0f;
+                for (int64_t p = p0; p < p1; ++p)
+                    acc = acc + dy[p * d + o] * orc_load(h, p * (int64_t)I + i, dt);
+                dw2[(int64_t)e * d * I + (int64_t)o * I + i] = acc;
+            }
+        for (int n = 0; n < 2 * I; ++n)
+            for (int c = 0; c < d; ++c) {
+                float acc = 0.0f;
+                for (int64_t p = p0; p < p1; ++p)
+                    acc = acc + dgu[p * 2 * I + n] * orc_load(x, (int64_t)(perm[p] / k) * d + c, dt);
+                dw13[(int64_t)e * 2 * I * d + (int64_t)n * d + c] = acc;
+            }
+    }
+}
+
+/* Backward of the softmax router ("The router: matching expert ids and weights"), given
+ * the gradient dw [T,k] of the routing weights by slot. The router's own choice is
+ * recomputed from the logits (the k experts first in (logit desc, id asc)); with
+ * p = softmax(l) (Z summed over e ascending), s = ((p_sel0 + p_sel1) + ...), w_j = p_selj / s:
+ *   a = sum_j dw_j w_j,  dp_j = (dw_j - a) / s,  c = sum_j dp_j p_selj   (j ascending)
+ *   dl[t,e] = p_e * (dp_e - c),  dp_e = dp_j for e = sel_j, 0 for an expert not chosen.
+ * Under routing replay the weights the layer used are the sampler's w*, passed forward
+ * as w - sg[w] + w* ("Total Router Recall"): the value is w*, the gradient reaches the
+ * router through w, the router's own weights at its own choice, slot by slot; this
+ * function is that gradient in both modes.
+ *   dw_router[e,c] = sum over t ascending of dl[t,e] * x[t,c];
+ *   dx_r[t,c]      = sum over e ascending of dl[t,e] * w_router[e,c]. */
+void orc_backward_router(const float *logits, const float *dw, const void *x,
+                         const void *w_router, int64_t T, int E, int k, int d, int dt,
+                         float *dl, float *dw_router, float *dx_r) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * (int64_t)E;
+        int sel[8];
+        unsigned char taken[256];
+        memset(taken, 0, sizeof(taken));
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || orc_ranks_before(l[e], e, l[best], best)) best = e;
+            }
+            sel[j] = best;
+            taken[best] = 1;
+        }
+        const float m = l[sel[0]];
+        float p[256], Z = 0.0f;
+        for (int e = 0; e < E; ++e) {
+            p[e] = expf(l[e] - m);
+            Z = Z + p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] = p[e] / Z;
+        float s = p[sel[0]];
+        for (int j = 1; j < k; ++j) s = s + p[sel[j]];
+        float a = 0.0f;
+        for (int j = 0; j < k; ++j) a = a + dw[t * k + j] * (p[sel[j]] / s);
+        float dp[8], c = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            dp[j] = (dw[t * k + j] - a) / s;
+            c = c + dp[j] * p[sel[j]];
+        }
+        for (int e = 0; e < E; ++e) {
+            float dpe = 0.0f;
+            for (int j = 0; j < k; ++j)
+                if (sel[j] == e) dpe = dp[j];
+            dl[t * E + e] = p[e] * (dpe - c);
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; ++e)
+        for (int c = 0; c < d; ++c) {
+            float acc = 0.0f;
+            for (int64_t t = 0; t < T; ++t) acc = acc + dl[t * E + e] * orc_load(x, t * (int64_t)d + c, dt);
+            dw_router[(int64_t)e * d + c] = acc;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int c = 0; c < d; ++c) {
+            float acc = 0.0f;
+            for (int e = 0; e < E; ++e)
+                acc = acc + dl[t * E + e] * orc_load(w_router, (int64_t)e * d + c, dt);
+            dx_r[t * d + c] = acc;
+        }
+}
