@@ -390,6 +390,71 @@ typedef struct moe_forward_args {
  * (graph-capturable). */
 moe_status moe_forward(const moe_dims *dims, const moe_forward_args *args, void *stream);
 
+/* Backward of the layer [EX][SW][RT][TRR]: the derivative of the forward definitions,
+ * every reduction in one fixed order (results bitwise identical run to run; every per-token
+ * row of d_x, d_y, d_h, d_gu, d_xp and d_topk_w is bitwise independent of T). With
+ * s = routed_scale (0 means 1), for assignment (t,j) at row p = inv[t*k+j] of expert e:
+ *   d_y[p,:]    = (s topk_w[t,j]) d_out[t,:]                                  (FP32)
+ *   d_topk_w[t,j] = s <d_out[t,:], y[p,:]>
+ *   gu[p,:]     = the forward's gate (n < I) and up (n >= I) pre-activations, recomputed by
+ *                 the forward's own GEMM (bit for bit the values the forward used)
+ *   d_h[p,i]    = sum_o d_y[p,o] w2[e,o,i]
+ *   d_gu[p,i]   = (d_h u) silu'(g),  d_gu[p,I+i] = d_h silu(g)   (g, u = gu[p,i], gu[p,I+i])
+ *   d_xp[p,c]   = sum_n d_gu[p,n] w13[e,n,c]
+ *   d_w2[e,o,i] = sum over the segment's rows p (ascending) of d_y[p,o] h[p,i]
+ *   d_w13[e,n,c]= sum over the segment's rows p (ascending) of d_gu[p,n] x[perm[p]/k,c]
+ *   router (w_router not NULL): its own top-k from the logits (saved, or recomputed from
+ *     x, w_router and logit_bias when logits is NULL), p = softmax, s' = sum of the chosen
+ *     p left to right; a = sum_j d_topk_w[t,j] p_j / s', dp_j = (d_topk_w[t,j] - a) / s',
+ *     c = sum_j dp_j p_j; d_logits[t,e] = p_e (dp_e - c) (dp_e = 0 for experts not chosen);
+ *     d_w_router = d_logits^T x; d_x_router = d_logits w_router.
+ *     Under routing replay this is the gradient of w - sg[w] + w* ("Total Router Recall"):
+ *     the forward value is the replayed w*, the router's gradient flows through its own
+ *     weights at its own choice, slot by slot.
+ *   d_x[t,:]    = ((0 + d_xp[inv[t*k]]) + d_xp[inv[t*k+1]] + ...) + d_x_router[t,:].
+ * The gradient GEMMs run FP32 MFMA on FP32 operands (bf16 storage widened exactly).
+ * Placement: with slot-ordered w13/w2 and the forward's per-slot offsets, d_w13/d_w2 come
+ * out in slot order; the router's gradients are in logical order.
+ * Buffers: inputs as moe_forward wrote them (offsets [E+1], perm/inv [T*k], topk_w [T,k],
+ * h [T*k,I] dtype, y [T*k,d] f32), d_out [T,d] dtype; outputs FP32: d_x [T,d],
+ * d_w13 [E,2I,d], d_w2 [E,d,I], d_topk_w [T,k], and with w_router: d_logits [T,E],
+ * d_w_router [E,d] (optional), d_x_router [T,d]; FP32 intermediates d_y [T*k,d],
+ * gu [T*k,2I], d_h [T*k,I], d_gu [T*k,2I], d_xp [T*k,d]; x_perm [T*k,d] or NULL (the
+ * recomputation gathers x through perm; x must then be under 4 GiB); workspace of
+ * moe_workspace_size() bytes. */
+typedef struct moe_backward_args {
+    const void *x;
+    const void *x_perm;
+    const void *w13;
+    const void *w2;
+    const void *w_router;
+    const float *logit_bias;
+    const float *logits;
+    const int32_t *offsets;
+    const int32_t *perm;
+    const int32_t *inv;
+    const float *topk_w;
+    const void *h;
+    const float *y;
+    const void *d_out;
+    float routed_scale;
+    float *d_x;
+    float *d_w13;
+    float *d_w2;
+    float *d_topk_w;
+    float *d_logits;
+    float *d_w_router;
+    float *d_x_router;
+    float *d_y;
+    float *gu;
+    float *d_h;
+    float *d_gu;
+    float *d_xp;
+    void *workspace;
+    size_t workspace_bytes;
+} moe_backward_args;
+moe_status moe_backward(const moe_dims *dims, const moe_backward_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,17 @@ class RouterOpts(ctypes.Structure):
 SCORES = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 
 
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "x_perm", "w13", "w2", "w_router", "logit_bias",
+                                  "logits", "offsets", "perm", "inv", "topk_w", "h", "y",
+                                  "d_out")] + \
+               [("routed_scale", ctypes.c_float)] + \
+               [(n, _P) for n in ("d_x", "d_w13", "d_w2", "d_topk_w", "d_logits", "d_w_router",
+                                  "d_x_router", "d_y", "gu", "d_h", "d_gu", "d_xp",
+                                  "workspace")] + \
+               [("workspace_bytes", ctypes.c_size_t)]
+
+
 # exported symbols and their signatures (argument types after the dims pointer)
 _SIGS = {
     "moe_workspace_size": ([ctypes.POINTER(Dims)], ctypes.c_size_t),
@@ -87,6 +98,7 @@ _SIGS = {
                            ctypes.c_int),
     "moe_objectives": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                         _P], ctypes.c_int),
+    "moe_backward": ([ctypes.POINTER(Dims), ctypes.POINTER(BackwardArgs), _P], ctypes.c_int),
     "moe_combine_ranks": ([ctypes.POINTER(Dims), ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                            ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "moe_shared_workspace_size": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32],
@@ -326,6 +338,33 @@ def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=
         a.prof_events = ctypes.cast(ev_arr, ctypes.c_void_p)
     _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(a), _stream(stream)),
            "moe_forward")
+
+
+def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.0,
+             stream=None):
+    """Run moe_backward. ``bufs`` maps BackwardArgs field names to tensors (or None)."""
+    a = BackwardArgs()
+    for name, _ in BackwardArgs._fields_:
+        if name in ("routed_scale", "workspace", "workspace_bytes"):
+            continue
+        setattr(a, name, _ptr(bufs.get(name)))
+    a.routed_scale = routed_scale
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    _check(lib().moe_backward(ctypes.byref(dims), ctypes.byref(a), _stream(stream)),
+           "moe_backward")
+
+
+def alloc_backward_buffers(dims: Dims, device="cuda", router: bool = True) -> dict:
+    """Allocate every output and FP32 intermediate of moe_backward for ``dims``."""
+    T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.inter
+    A = T * k
+    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=device)
+    b = dict(d_x=f(T, d), d_w13=f(E, 2 * I, d), d_w2=f(E, d, I), d_topk_w=f(T, k),
+             d_y=f(A, d), gu=f(A, 2 * I), d_h=f(A, I), d_gu=f(A, 2 * I), d_xp=f(A, d))
+    if router:
+        b.update(d_logits=f(T, E), d_w_router=f(E, d), d_x_router=f(T, d))
+    return b
 
 
 def alloc_forward_buffers(dims: Dims, device="cuda", router: bool = True,

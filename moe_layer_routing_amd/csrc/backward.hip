@@ -1,0 +1,593 @@
+// backward.hip -- backward of the MoE layer: combine, SwiGLU experts, softmax router.
+//
+// The derivative of the forward definitions ("0 train-infer mismatch for Open-weight MoE RL
+// in Open-source code": "The experts: keeping the route weight inside the accumulator",
+// "SwiGLU: rounding after the multiply", "The router: matching expert ids and weights"),
+// with every reduction in one fixed order:
+//   dy[p]      = (s w[t,j]) dout[t]             (p = inv[t*k+j], s = routed scaling factor)
+//   dw[t,j]    = s <dout[t], y[p]>              (per-lane partials, fixed DPP tree)
+//   g, u       = the forward's pre-activations, recomputed by the forward's own GEMM
+//   dh         = dy w2[e]                       (FP32 MFMA, K = d ascending)
+//   dg, du     = dh u silu'(g), dh silu(g)
+//   dxp        = [dg du] w13[e]                 (FP32 MFMA, K = 2I ascending)
+//   dx[t]      = sum over slots of dxp rows, slot order, + the router's part
+//   dw2[e]     = sum over the segment's rows of dy^T h      (rows ascending)
+//   dw13[e]    = sum over the segment's rows of [dg du]^T x  (rows ascending)
+//   router:    dl = the softmax / top-k / renormalisation Jacobian at the router's own
+//              choice applied to dw by slot; dw_router = dl^T x; dx += dl w_router.
+// Under routing replay ("Total Router Recall": the layer passes w - sg[w] + w*) the value
+// the experts saw is the sampler's w*, and the router's gradient flows through its own
+// renormalised weights at its own top-k, slot by slot: the same router step.
+//
+// The gradient GEMMs read token-major activations and row-major weights directly: the
+// FP32 MFMA (v_mfma_f32_16x16x4f32) takes one element per lane (lane l: row / column l%16,
+// K index l/16), so a K x N weight tile staged row-major in LDS and a rows x K activation
+// tile staged row-major both serve it without a transpose. Operands are FP32 (bf16
+// storage widened exactly); every output is one sum over K (or over the segment's rows)
+// in increasing order of 4-wide MFMA steps.
+#include "route_dev.h"
+
+namespace moe {
+namespace {
+
+constexpr int kKc = 16;   // K elements per LDS stage of the FP32 gradient GEMMs
+
+template <bool kBF16>
+__device__ __forceinline__ float ld_elem(const void *p, int64_t i) {
+    if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else return static_cast<const float *>(p)[i];
+}
+
+// ------------------------------------------------------------------ combine backward
+// One wave per token: lane l takes features 4l, 4l + 256, ... of every slot's y row;
+// dy = (s w_j) dout; the partial dot products <dout, y_j> are summed per lane in feature
+// order and then over the wave in the fixed DPP tree.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const void *__restrict__ dout, const float *__restrict__ y,
+    const int32_t *__restrict__ inv, const float *__restrict__ topk_w, int64_t T, int k,
+    int d, int64_t A, float scale, float *__restrict__ dy, float *__restrict__ dw) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    int64_t src[kMaxK];
+    float ws[kMaxK], acc[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        int32_t p = (j < k) ? inv[t * k + j] : 0;
+        p = (p < 0 || p >= A) ? 0 : p;
+        src[j] = (int64_t)p * d;
+        ws[j] = (j < k) ? scale * topk_w[t * k + j] : 0.f;
+        acc[j] = 0.f;
+    }
+    for (int c = lane * 4; c < d; c += 256) {
+        float g[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[q] = ld_elem<kBF16>(dout, t * d + c + q);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                const float4 yv = *reinterpret_cast<const float4 *>(y + src[j] + c);
+                *reinterpret_cast<float4 *>(dy + src[j] + c) =
+                    make_float4(ws[j] * g[0], ws[j] * g[1], ws[j] * g[2], ws[j] * g[3]);
+                acc[j] = acc[j] + g[0] * yv.x;
+                acc[j] = acc[j] + g[1] * yv.y;
+                acc[j] = acc[j] + g[2] * yv.z;
+                acc[j] = acc[j] + g[3] * yv.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            const float tot = wave_sum(acc[j]);
+            if (lane == 0) dw[t * k + j] = scale * tot;
+        }
+    }
+}
+
+// ----------------------------------------------------------------- SwiGLU backward
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict__ gu,
+                                                         const float *__restrict__ dh,
+                                                         int64_t A, int I,
+                                                         float *__restrict__ dgu) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= A * I) return;
+    const int64_t p = i / I;
+    const int n = (int)(i - p * I);
+    const float g = gu[p * 2 * I + n], u = gu[p * 2 * I + I + n], d = dh[i];
+    const float e = expf(-g);
+    const float sg = 1.0f / (1.0f + e);
+    const float silu = g / (1.0f + e);
+    const float dsilu = sg * (1.0f + g * (1.0f - sg));
+    dgu[p * 2 * I + n] = (d * u) * dsilu;
+    dgu[p * 2 * I + I + n] = d * silu;
+}
+
+// ------------------------------------------------------------ dx: slot-order sum
+__global__ __launch_bounds__(256) void dx_sum_kernel(const float *__restrict__ dxp,
+                                                     const int32_t *__restrict__ inv,
+                                                     const float *__restrict__ dxr,
+                                                     int64_t T, int k, int d, int64_t A,
+                                                     float *__restrict__ dx) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= T * d) return;
+    const int64_t t = i / d;
+    const int c = (int)(i - t * d);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+        int32_t p = inv[t * k + j];
+        p = (p < 0 || p >= A) ? 0 : p;
+        const float4 v = *reinterpret_cast<const float4 *>(dxp + (int64_t)p * d + c);
+        a0 = a0 + v.x;
+        a1 = a1 + v.y;
+        a2 = a2 + v.z;
+        a3 = a3 + v.w;
+    }
+    if (dxr) {
+        const float4 r = *reinterpret_cast<const float4 *>(dxr + i);
+        a0 = a0 + r.x;
+        a1 = a1 + r.y;
+        a2 = a2 + r.z;
+        a3 = a3 + r.w;
+    }
+    *reinterpret_cast<float4 *>(dx + i) = make_float4(a0, a1, a2, a3);
+}
+
+// ------------------------------------------------------------------ router backward
+// One 16-lane row per token (lane c holds experts c, c + 16, ...), as the forward router:
+// the router's own top-k by (logit desc, id asc), p = exp(l - max) / Z with Z in the
+// forward's order, then
+//   s = ((p_sel0 + p_sel1) + ...), a = sum_j dw_j (p_selj / s), dp_j = (dw_j - a) / s,
+//   c = sum_j dp_j p_selj, dl_e = p_e (dp_e - c)   (dp_e = 0 for an expert not chosen).
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict__ logits,
+                                                         const float *__restrict__ dw,
+                                                         int64_t T, int E, int k,
+                                                         float *__restrict__ dl) {
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool tv = t < T;
+    const int nv = (E + 15) >> 4;
+    float lv[kRowVals];
+    uint32_t hi[kRowVals];
+    bool valid[kRowVals];
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) {
+        valid[i] = i < nv && c + 16 * i < E;
+        lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
+        hi[i] = valid[i] ? ordered_bits(lv[i]) : 0u;
+    }
+    uint32_t taken = 0, mkey0 = 0;
+    int sel[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        sel[j] = -1;
+        if (j < k) {
+            uint32_t best = 0;
+#pragma unroll
+            for (int i = 0; i < kRowVals; ++i)
+                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
+            const uint32_t m = row_max_u32(best);
+            int cand = 0x7fffffff;
+#pragma unroll
+            for (int i = kRowVals - 1; i >= 0; --i)
+                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] == m) cand = c + 16 * i;
+            const int e = row_min_i32(cand);
+            sel[j] = e;
+            if (j == 0) mkey0 = m;
+            if ((e & 15) == c) taken |= 1u << (e >> 4);
+        }
+    }
+    const float mx = from_ordered_bits(mkey0);
+    float p[kRowVals];
+    float zl = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) {
+        p[i] = valid[i] ? expf(lv[i] - mx) : 0.f;
+        if (i < nv) zl = (i == 0) ? p[0] : zl + p[i];
+    }
+    const float Z = row_sum(zl);
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) p[i] = valid[i] ? p[i] / Z : 0.f;
+    float ps[kMaxK], dwj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        ps[j] = (j < k) ? row_pick(p, sel[j], c, nv) : 0.f;
+        dwj[j] = (j < k && tv) ? dw[t * k + j] : 0.f;
+    }
+    float s = ps[0];
+#pragma unroll
+    for (int j = 1; j < kMaxK; ++j)
+        if (j < k) s = s + ps[j];
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+        if (j < k) a = a + dwj[j] * (ps[j] / s);
+    float dp[kMaxK], cc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        dp[j] = 0.f;
+        if (j < k) {
+            dp[j] = (dwj[j] - a) / s;
+            cc = cc + dp[j] * ps[j];
+        }
+    }
+    if (!tv) return;
+#pragma unroll
+    for (int i = 0; i < kRowVals; ++i) {
+        if (!valid[i]) continue;
+        const int e = c + 16 * i;
+        float dpe = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k && sel[j] == e) dpe = dp[j];
+        dl[t * E + e] = p[i] * (dpe - cc);
+    }
+}
+
+// ---------------------------------------------------- FP32 gradient GEMMs (MFMA)
+// Data gradient: out[p, n] = sum_k act[p, k] wgt[e, k, n] for the rows p of each segment
+// (tile list (e, first row, rows)); act FP32 [rows, K], wgt [E, K, N] row-major (bf16 or
+// FP32), out FP32 [rows, N]. Block: BN features x BT rows, four waves of (BN/2) x (BT/2).
+// MFMA operand A = weight (rows = features n, K), B = activations (K, columns = rows p):
+// lane l holds wgt[k0 + l/16][n + l%16] and act[p + l%16][k0 + l/16]; the result lane l
+// holds row p + l%16, features n + 4(l/16) + 0..3.
+template <bool kWBF16, int BN, int BT>
+__global__ __launch_bounds__(256) void dgrad_kernel(const float *__restrict__ act,
+                                                    const void *__restrict__ wgt,
+                                                    float *__restrict__ out,
+                                                    const int32_t *__restrict__ tiles, int K,
+                                                    int N, int nft) {
+    constexpr int WN = BN / 2, WTk = BT / 2, NF = WN / 16, NT = WTk / 16;
+    constexpr int kAS = kKc + 1;                 // padded LDS row (floats), activations
+    constexpr int kWS = BN + 4;                  // padded LDS row (floats), weights
+    __shared__ float sa[2][BT * kAS];
+    __shared__ float sw[2][kKc * kWS];
+    const int mt = blockIdx.x / nft, ft = blockIdx.x % nft;
+    if (mt >= tiles[0]) return;
+    const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wn = wv & 1, wt = wv >> 1;
+    const int n0 = ft * BN;
+    const int64_t wbase = (int64_t)e * K * N;
+
+    // staging: activations BT rows x kKc (float4 per thread per 64 rows),
+    // weights kKc rows x BN (4 consecutive features per thread per 4*64 features)
+    constexpr int AR = BT * kKc / 4 / 256;       // float4 loads per thread (activations)
+    constexpr int WR = kKc * BN / 4 / 256;       // 4-element loads per thread (weights)
+    static_assert(AR >= 1 && WR >= 1, "tile too small for 256 threads");
+    float4 ra[AR], rw[WR];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < AR; ++i) {
+            const int q = tid + 256 * i, r = q / (kKc / 4), kc = (q % (kKc / 4)) * 4;
+            const int row = min(r, nrows - 1);
+            ra[i] = *reinterpret_cast<const float4 *>(act + (int64_t)(p0 + row) * K + k0 + kc);
+        }
+#pragma unroll
+        for (int i = 0; i < WR; ++i) {
+            const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
+            const int n = min(n0 + nc, N - 4);
+            const int64_t o = wbase + (int64_t)(k0 + r) * N + n;
+            if constexpr (kWBF16) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(wgt) + o);
+                rw[i] = make_float4(bf16_to_f32((uint16_t)(v.x & 0xffff)), bf16_to_f32((uint16_t)(v.x >> 16)),
+                                    bf16_to_f32((uint16_t)(v.y & 0xffff)), bf16_to_f32((uint16_t)(v.y >> 16)));
+            } else {
+                rw[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(wgt) + o);
+            }
+        }
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < AR; ++i) {
+            const int q = tid + 256 * i, r = q / (kKc / 4), kc = (q % (kKc / 4)) * 4;
+            float *d = sa[b] + r * kAS + kc;
+            d[0] = ra[i].x; d[1] = ra[i].y; d[2] = ra[i].z; d[3] = ra[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < WR; ++i) {
+            const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
+            *reinterpret_cast<float4 *>(sw[b] + r * kWS + nc) = rw[i];
+        }
+    };
+    f32x4_t acc[NF][NT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int nk = K / kKc;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int b = kt & 1;
+        if (kt + 1 < nk) load((kt + 1) * kKc);
+#pragma unroll
+        for (int kk = 0; kk < kKc; kk += 4) {
+            float av[NF], bv[NT];
+#pragma unroll
+            for (int f = 0; f < NF; ++f) av[f] = sw[b][(kk + g4) * kWS + wn * WN + f * 16 + r16];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) bv[t] = sa[b][(wt * WTk + t * 16 + r16) * kAS + kk + g4];
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[f], bv[t], acc[f][t], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store(b ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int m = wt * WTk + t * 16 + r16;
+        if (m >= nrows) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int n = n0 + wn * WN + f * 16 + g4 * 4;
+            if (n >= N) continue;
+            *reinterpret_cast<float4 *>(out + (int64_t)(p0 + m) * N + n) =
+                make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]);
+        }
+    }
+}
+
+// Weight gradient: out[e, n, c] = sum over the segment's rows p ascending of
+// a[p, n] b[p, c]; a FP32 [rows, N], b [rows, C] (bf16 or FP32; row of b = bperm[p] / bk
+// when bperm is given: the gathered token rows), out FP32 [E, N, C]. Segment e = rows
+// [off[e], off[e+1]) (off NULL: one segment of nrows rows). Block: BN x BC outputs of one
+// expert, four waves of (BN/2) x (BC/2); K = the segment's rows in stages of kKc, the tail
+// zero-filled. MFMA operand A = a (rows n, K = p), B = b (K = p, columns c): lane l holds
+// a[p0 + l/16][n + l%16] and b[p0 + l/16][c + l%16]; the result lane l holds column
+// c + l%16 of rows n + 4(l/16) + 0..3.
+template <bool kBBF16, int BN, int BC>
+__global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
+                                                    const void *__restrict__ b,
+                                                    const int32_t *__restrict__ bperm, int bk,
+                                                    int64_t bT, const int32_t *__restrict__ off,
+                                                    int64_t nrows, int N, int C, int nbn,
+                                                    int nbc, float *__restrict__ out) {
+    constexpr int WN = BN / 2, WC = BC / 2, NF = WN / 16, NC = WC / 16;
+    constexpr int kAS = BN + 4, kBS = BC + 4;
+    __shared__ float sa[2][kKc * kAS];
+    __shared__ float sb[2][kKc * kBS];
+    const int per_e = nbn * nbc;
+    const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
+    const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
+    int64_t r0 = 0, r1 = nrows;
+    if (off) {
+        r0 = min<int64_t>(max(off[e], 0), nrows);
+        r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wn = wv & 1, wc = wv >> 1;
+    constexpr int AR = kKc * BN / 4 / 256, BR = kKc * BC / 4 / 256;
+    static_assert(AR >= 1 && BR >= 1, "tile too small for 256 threads");
+    float4 ra[AR], rb[BR];
+    auto load = [&](int64_t p0) {
+#pragma unroll
+        for (int i = 0; i < AR; ++i) {
+            const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
+            const int64_t p = p0 + r;
+            ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p < r1)
+                ra[i] = *reinterpret_cast<const float4 *>(a + p * N + min(n0 + nc, N - 4));
+        }
+#pragma unroll
+        for (int i = 0; i < BR; ++i) {
+            const int q = tid + 256 * i, r = q / (BC / 4), cc = (q % (BC / 4)) * 4;
+            const int64_t p = p0 + r;
+            rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p < r1) {
+                int64_t row = p;
+                if (bperm) row = min<int64_t>((int64_t)max(bperm[p], 0) / bk, bT - 1);
+                const int64_t o = row * C + min(c0 + cc, C - 4);
+                if constexpr (kBBF16) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(b) + o);
+                    rb[i] = make_float4(bf16_to_f32((uint16_t)(v.x & 0xffff)), bf16_to_f32((uint16_t)(v.x >> 16)),
+                                        bf16_to_f32((uint16_t)(v.y & 0xffff)), bf16_to_f32((uint16_t)(v.y >> 16)));
+                } else {
+                    rb[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(b) + o);
+                }
+            }
+        }
+    };
+    auto store = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < AR; ++i) {
+            const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
+            *reinterpret_cast<float4 *>(sa[s] + r * kAS + nc) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < BR; ++i) {
+            const int q = tid + 256 * i, r = q / (BC / 4), cc = (q % (BC / 4)) * 4;
+            *reinterpret_cast<float4 *>(sb[s] + r * kBS + cc) = rb[i];
+        }
+    };
+    f32x4_t acc[NF][NC];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int64_t nk = (r1 - r0 + kKc - 1) / kKc;
+    if (nk > 0) {
+        load(r0);
+        store(0);
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int s = (int)(kt & 1);
+            if (kt + 1 < nk) load(r0 + (kt + 1) * kKc);
+#pragma unroll
+            for (int kk = 0; kk < kKc; kk += 4) {
+                float av[NF], bv[NC];
+#pragma unroll
+                for (int f = 0; f < NF; ++f) av[f] = sa[s][(kk + g4) * kAS + wn * WN + f * 16 + r16];
+#pragma unroll
+                for (int t = 0; t < NC; ++t) bv[t] = sb[s][(kk + g4) * kBS + wc * WC + t * 16 + r16];
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int t = 0; t < NC; ++t)
+                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[f], bv[t], acc[f][t], 0, 0, 0);
+            }
+            if (kt + 1 < nk) store(s ^ 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int cc = c0 + wc * WC + t * 16 + r16;
+        if (cc >= C) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + wn * WN + f * 16 + g4 * 4 + i;
+                if (n < N) out[((int64_t)e * N + n) * C + cc] = acc[f][t][i];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ launchers
+constexpr int kDgBN = 128, kDgBT = 64;     // data-gradient tile: features x rows
+constexpr int kWgBN = 64, kWgBC = 64;      // weight-gradient tile
+
+hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float *y,
+                              const int32_t *inv, const float *topk_w, float scale, float *dy,
+                              float *dw, hipStream_t s) {
+    if (dm.T == 0) return hipGetLastError();
+    const dim3 grid((unsigned)((dm.T + 3) / 4));
+    if (dm.dtype == MOE_BF16)
+        combine_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T, dm.k,
+                                                            dm.d, dm.T * dm.k, scale, dy, dw);
+    else
+        combine_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T, dm.k,
+                                                             dm.d, dm.T * dm.k, scale, dy, dw);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, float *dgu,
+                             hipStream_t s) {
+    const int64_t n = dm.T * dm.k * dm.inter;
+    if (n == 0) return hipGetLastError();
+    swiglu_bwd_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        gu, dh, dm.T * dm.k, dm.inter, dgu);
+    return hipGetLastError();
+}
+
+hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
+                         const float *dxr, float *dx, hipStream_t s) {
+    const int64_t n = dm.T * dm.d / 4;
+    if (n == 0) return hipGetLastError();
+    dx_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        dxp, inv, dxr, dm.T, dm.k, dm.d, dm.T * dm.k, dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const moe_dims &dm, const float *logits, const float *dw,
+                             float *dl, hipStream_t s) {
+    if (dm.T == 0) return hipGetLastError();
+    router_bwd_kernel<<<dim3((unsigned)((dm.T + 15) / 16)), dim3(256), 0, s>>>(
+        logits, dw, dm.T, dm.E, dm.k, dl);
+    return hipGetLastError();
+}
+
+// out[p, :] = act[p, :] wgt[e] over the segments of offsets (tiles built into ws.tiles).
+hipError_t launch_dgrad(const moe_dims &dm, const float *act, const void *wgt, bool wbf16,
+                        int K, int N, const int32_t *offsets, float *out, const Workspace &ws,
+                        hipStream_t s) {
+    const int64_t A = dm.T * dm.k;
+    if (A == 0) return hipGetLastError();
+    if (K % kKc || N % 4) return hipErrorInvalidValue;
+    const int64_t cap = max_m_tiles(A, dm.E, kDgBT);
+    const hipError_t e = launch_build_tiles(offsets, dm.E, A, kDgBT, cap, ws.tiles, s);
+    if (e != hipSuccess) return e;
+    const int nft = (N + kDgBN - 1) / kDgBN;
+    const dim3 grid((unsigned)(cap * nft));
+    if (wbf16)
+        dgrad_kernel<true, kDgBN, kDgBT><<<grid, dim3(256), 0, s>>>(act, wgt, out, ws.tiles, K, N, nft);
+    else
+        dgrad_kernel<false, kDgBN, kDgBT><<<grid, dim3(256), 0, s>>>(act, wgt, out, ws.tiles, K, N, nft);
+    return hipGetLastError();
+}
+
+// out[e] = a^T b over each segment's rows (off NULL: one segment of nrows rows).
+hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
+                        const int32_t *bperm, int bk, int64_t bT, const int32_t *off,
+                        int64_t nrows, int N, int C, float *out, hipStream_t s) {
+    if (N % 4 || C % 4 || nseg < 1) return hipErrorInvalidValue;
+    const int nbn = (N + kWgBN - 1) / kWgBN, nbc = (C + kWgBC - 1) / kWgBC;
+    const dim3 grid((unsigned)((int64_t)nseg * nbn * nbc));
+    if (bbf16)
+        wgrad_kernel<true, kWgBN, kWgBC><<<grid, dim3(256), 0, s>>>(a, b, bperm, bk, bT, off,
+                                                                   nrows, N, C, nbn, nbc, out);
+    else
+        wgrad_kernel<false, kWgBN, kWgBC><<<grid, dim3(256), 0, s>>>(a, b, bperm, bk, bT, off,
+                                                                    nrows, N, C, nbn, nbc, out);
+    return hipGetLastError();
+}
+
+// dx_r[t, c] = sum_e dl[t, e] w_router[e, c]: the data-gradient kernel with one segment of
+// T rows (K = E must be a multiple of kKc; other E take the plain loop below).
+__global__ __launch_bounds__(256) void router_dx_kernel(const float *__restrict__ dl,
+                                                        const void *__restrict__ wr, bool bf16,
+                                                        int64_t T, int E, int d,
+                                                        float *__restrict__ dx) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * d) return;
+    const int64_t t = i / d;
+    const int c = (int)(i - t * d);
+    float acc = 0.f;
+    for (int e = 0; e < E; ++e) {
+        const float w = bf16 ? bf16_to_f32(static_cast<const uint16_t *>(wr)[(int64_t)e * d + c])
+                             : static_cast<const float *>(wr)[(int64_t)e * d + c];
+        acc = acc + dl[t * E + e] * w;
+    }
+    dx[i] = acc;
+}
+
+// dw_router[e, c] = sum over t ascending of dl[t, e] x[t, c] when E is not a multiple of 4
+// (the MFMA weight-gradient kernel reads 4 experts at a time).
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restrict__ dl,
+                                                           const void *__restrict__ x, bool bf16,
+                                                           int64_t T, int E, int d,
+                                                           float *__restrict__ dwr) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)E * d) return;
+    const int e = (int)(i / d), c = (int)(i - (int64_t)e * d);
+    float acc = 0.f;
+    for (int64_t t = 0; t < T; ++t) {
+        const float xv = bf16 ? bf16_to_f32(static_cast<const uint16_t *>(x)[t * d + c])
+                              : static_cast<const float *>(x)[t * d + c];
+        acc = acc + dl[t * E + e] * xv;
+    }
+    dwr[i] = acc;
+}
+
+hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *x, float *dwr,
+                               hipStream_t s) {
+    if (dm.E % 4 == 0)
+        return launch_wgrad(1, dl, x, dm.dtype == MOE_BF16, nullptr, 1, dm.T, nullptr, dm.T,
+                            dm.E, dm.d, dwr, s);
+    const int64_t n = (int64_t)dm.E * dm.d;
+    router_wgrad_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        dl, x, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dwr);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
+                            float *dx, hipStream_t s) {
+    const int64_t n = dm.T * dm.d;
+    if (n == 0) return hipGetLastError();
+    router_dx_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        dl, w_router, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dx);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -435,4 +435,67 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     return to_status(finish_layer(dims, a, scale, s));
 }
 
+moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(a, MOE_E_NULLPTR);
+    MOE_REQUIRE(std::isfinite(a->routed_scale), MOE_E_SHAPE);
+    if (dims->T == 0) return MOE_OK;
+    MOE_REQUIRE(a->x && a->w13 && a->w2 && a->offsets && a->perm && a->inv && a->topk_w &&
+                    a->h && a->y && a->d_out && a->d_x && a->d_w13 && a->d_w2 &&
+                    a->d_topk_w && a->d_y && a->gu && a->d_h && a->d_gu && a->d_xp,
+                MOE_E_NULLPTR);
+    if (a->w_router) MOE_REQUIRE(a->d_logits && a->d_x_router, MOE_E_NULLPTR);
+    if (!a->x_perm) {
+        const int64_t x_bytes = dims->T * (int64_t)dims->d * (dims->dtype == MOE_BF16 ? 2 : 4);
+        MOE_REQUIRE(x_bytes < (int64_t(1) << 32), MOE_E_SHAPE);
+    }
+    st = check_ws(dims, a->workspace, a->workspace_bytes);
+    if (st != MOE_OK) return st;
+    const Workspace ws = carve_workspace(*dims, a->workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = a->routed_scale == 0.0f ? 1.0f : a->routed_scale;
+    const bool bf16 = dims->dtype == MOE_BF16;
+    const int64_t A = dims->T * dims->k;
+    const int I = dims->inter, d = dims->d;
+    hipError_t e = launch_combine_bwd(*dims, a->d_out, a->y, a->inv, a->topk_w, scale, a->d_y,
+                                      a->d_topk_w, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_plain_gemm(*dims, a->x_perm ? a->x_perm : a->x, a->x_perm ? nullptr : a->perm,
+                          a->w13, a->gu, 2 * I, a->offsets, ws, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_dgrad(*dims, a->d_y, a->w2, bf16, d, I, a->offsets, a->d_h, ws, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_dgrad(*dims, a->d_gu, a->w13, bf16, 2 * I, d, a->offsets, a->d_xp, ws, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_wgrad(dims->E, a->d_y, a->h, bf16, nullptr, 1, A, a->offsets, A, d, I, a->d_w2, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    e = launch_wgrad(dims->E, a->d_gu, a->x_perm ? a->x_perm : a->x, bf16,
+                     a->x_perm ? nullptr : a->perm, dims->k, a->x_perm ? A : dims->T,
+                     a->offsets, A, 2 * I, d, a->d_w13, s);
+    if (e != hipSuccess) return MOE_E_LAUNCH;
+    const float *dxr = nullptr;
+    if (a->w_router) {
+        const float *logits = a->logits;
+        if (!logits) {
+            e = launch_router_logits(*dims, a->x, a->w_router, a->logit_bias, ws.logits, s);
+            if (e != hipSuccess) return MOE_E_LAUNCH;
+            logits = ws.logits;
+        }
+        e = launch_router_bwd(*dims, logits, a->d_topk_w, a->d_logits, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        if (a->d_w_router) {
+            e = launch_router_wgrad(*dims, a->d_logits, a->x, a->d_w_router, s);
+            if (e != hipSuccess) return MOE_E_LAUNCH;
+        }
+        e = launch_router_dx(*dims, a->d_logits, a->w_router, a->d_x_router, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        dxr = a->d_x_router;
+    }
+    e = launch_dx_sum(*dims, a->d_xp, a->inv, dxr, a->d_x, s);
+    return to_status(e);
+}
+
 }  // extern "C"

@@ -147,6 +147,33 @@ size_t shared_workspace_bytes(const moe_dims &dm, int R, int inter_shared);
 hipError_t launch_shared_ffn(const moe_dims &dm, int R, int inter_shared, const void *x,
                              const void *w13s, const void *w2s, void *h_s, float *y_s,
                              void *workspace, hipStream_t s);
+// Grouped-GEMM helpers shared with the backward: the token-tile list for tile height bt,
+// and the plain FP32-output GEMM (the forward's down launch) with N features over K = d.
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, int64_t cap,
+                              int32_t *tiles, hipStream_t s);
+hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
+                             const void *wgt, float *out, int N, const int32_t *offsets,
+                             const Workspace &ws, hipStream_t s);
+// Backward steps (backward.hip).
+hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float *y,
+                              const int32_t *inv, const float *topk_w, float scale, float *dy,
+                              float *dw, hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, float *dgu,
+                             hipStream_t s);
+hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
+                         const float *dxr, float *dx, hipStream_t s);
+hipError_t launch_router_bwd(const moe_dims &dm, const float *logits, const float *dw,
+                             float *dl, hipStream_t s);
+hipError_t launch_dgrad(const moe_dims &dm, const float *act, const void *wgt, bool wbf16,
+                        int K, int N, const int32_t *offsets, float *out, const Workspace &ws,
+                        hipStream_t s);
+hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
+                        const int32_t *bperm, int bk, int64_t bT, const int32_t *off,
+                        int64_t nrows, int N, int C, float *out, hipStream_t s);
+hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *x, float *dwr,
+                               hipStream_t s);
+hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
+                            float *dx, hipStream_t s);
 // Objective statistics (one block): out[3] = z_loss, aux_loss, S; optional bias update.
 hipError_t launch_objectives(const moe_dims &dm, const float *lse, const int32_t *q,
                              const int64_t *wcounts, const float *mass,
