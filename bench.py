@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X; grouped-GEMM TFLOP/s as % bf16 MFMA peak"
+PEAK_FP32_TFLOPS = 157.3
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -307,6 +308,49 @@ def ranks_report(L, dims, inp, K, hip, stream, inter_shared=2048):
                         "step_ms": round(ms_step, 5)}
     assert int(fb["d_err"].item()) == 0
     return out
+
+
+def backward_report(L, dims, inp, K, hip, stream):
+    """Backward of the layer (moe_backward) after one forward, with the router's gradients:
+    the median time of K calls, and the gradient GEMMs' rate against the FP32 MFMA peak
+    (their operands are FP32): 16*T*k*d*I FLOP per call = the recomputed gate/up
+    pre-activations (4), the data gradients dh (2) and dx (4), the weight gradients dw2 (2)
+    and dw13 (4)."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    dev = inp["x"].device
+    ws = M.alloc_workspace(dims, dev)
+    fb = M.alloc_forward_buffers(dims, dev, router=True)
+    del fb["x_perm"]
+    fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"], w_router=inp["w_router"],
+              logit_bias=inp["logit_bias"])
+    M.forward(dims, fb, ws)
+    bb = M.alloc_backward_buffers(dims, dev, router=True)
+    g = torch.Generator(device=dev).manual_seed(L.seed)
+    dout = torch.randn((L.T, L.d), generator=g, device=dev).to(fb["out"].dtype)
+    bb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"], w_router=inp["w_router"],
+              logit_bias=inp["logit_bias"], logits=fb["logits"], offsets=fb["offsets"],
+              perm=fb["perm"], inv=fb["inv"], topk_w=fb["topk_w"], h=fb["h"], y=fb["y"],
+              d_out=dout)
+    M.backward(dims, bb, ws)
+    ev = hip.create(2 * K)
+    for i in range(K):
+        hip.record(ev[2 * i], stream.cuda_stream)
+        M.backward(dims, bb, ws)
+        hip.record(ev[2 * i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ts = [hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]
+    hip.destroy(ev)
+    ms = float(np.median(ts))
+    flops = 16.0 * L.T * L.k * L.d * L.I
+    assert int(fb["d_err"].item()) == 0
+    return {"ms": round(ms, 5), "p10": round(float(np.percentile(ts, 10)), 5),
+            "p90": round(float(np.percentile(ts, 90)), 5), "gemm_flop": flops,
+            "tflops_overall": round(flops / (ms * 1e-3) / 1e12, 2),
+            "peak_fp32_mfma_tflops": PEAK_FP32_TFLOPS,
+            "frac_overall": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "forward_ms_for_reference": None}
 
 
 def host_list(t):
@@ -614,6 +658,9 @@ def main():
     placement = placement_report(L, dims, inp, host_counts, K, hip, stream) if L.E % 8 == 0 else None
     variants = variant_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
     ranks = ranks_report(L, dims, inp, K, hip, stream)
+    bwd = backward_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
+    if bwd:
+        bwd["forward_ms_for_reference"] = round(ms_step_fwd := total_ms / K, 5)
 
     A = L.T * L.k
     ms_step = total_ms / K
@@ -666,6 +713,7 @@ def main():
         "placement": placement,
         "router_variants": variants,
         "expert_parallel": ranks,
+        "backward": bwd,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:

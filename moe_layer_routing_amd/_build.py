@@ -17,6 +17,8 @@ FLAGS = [
     # packed FP32 arithmetic stays off in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # a symbol missing from the library fails the build, not the first load
+    "-Wl,--no-undefined",
 ]
 
 

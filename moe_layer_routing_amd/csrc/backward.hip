@@ -533,23 +533,36 @@ hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
     return hipGetLastError();
 }
 
-// dx_r[t, c] = sum_e dl[t, e] w_router[e, c]: the data-gradient kernel with one segment of
-// T rows (K = E must be a multiple of kKc; other E take the plain loop below).
+// dx_r[t, c] = sum over e ascending of dl[t, e] w_router[e, c]; each thread takes four
+// consecutive features of one token (one dl value serves four products).
 __global__ __launch_bounds__(256) void router_dx_kernel(const float *__restrict__ dl,
                                                         const void *__restrict__ wr, bool bf16,
                                                         int64_t T, int E, int d,
                                                         float *__restrict__ dx) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= T * d) return;
     const int64_t t = i / d;
     const int c = (int)(i - t * d);
-    float acc = 0.f;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int e = 0; e < E; ++e) {
-        const float w = bf16 ? bf16_to_f32(static_cast<const uint16_t *>(wr)[(int64_t)e * d + c])
-                             : static_cast<const float *>(wr)[(int64_t)e * d + c];
-        acc = acc + dl[t * E + e] * w;
+        const float g = dl[t * E + e];
+        float w0, w1, w2, w3;
+        if (bf16) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(wr) + (int64_t)e * d + c);
+            w0 = bf16_to_f32((uint16_t)(v.x & 0xffff));
+            w1 = bf16_to_f32((uint16_t)(v.x >> 16));
+            w2 = bf16_to_f32((uint16_t)(v.y & 0xffff));
+            w3 = bf16_to_f32((uint16_t)(v.y >> 16));
+        } else {
+            const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(wr) + (int64_t)e * d + c);
+            w0 = v.x; w1 = v.y; w2 = v.z; w3 = v.w;
+        }
+        a0 = a0 + g * w0;
+        a1 = a1 + g * w1;
+        a2 = a2 + g * w2;
+        a3 = a3 + g * w3;
     }
-    dx[i] = acc;
+    *reinterpret_cast<float4 *>(dx + i) = make_float4(a0, a1, a2, a3);
 }
 
 // dw_router[e, c] = sum over t ascending of dl[t, e] x[t, c] when E is not a multiple of 4
@@ -583,7 +596,7 @@ hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *
 
 hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
                             float *dx, hipStream_t s) {
-    const int64_t n = dm.T * dm.d;
+    const int64_t n = dm.T * dm.d / 4;
     if (n == 0) return hipGetLastError();
     router_dx_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
         dl, w_router, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dx);
