@@ -447,6 +447,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     // iteration kt (after the barrier that made stage kt resident) stage kt+NS-1 goes into
     // the slot stage kt-1 has left; before the next barrier each wave waits for its own DMA
     // of stage kt+1 (the NS-2 newer stages may stay in flight) and its own LDS reads.
+    // a wave whose features or tokens are all padding issues no MFMAs (loop-invariant)
+    const bool active = (n0 + wf * kWaveRows < N) && (wt * (BT / WT) < nrows);
     const int nk = K >> 6;
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
@@ -460,8 +462,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
         if (kt + NS - 1 < nk)
             dma_stage128<NBW, NW>(ring + ((kt + NS - 1) % NS) * kStageBytes, wbase, abase, off,
                                   is_act, kt + NS - 1, wv);
-        kstep(cur + lane_off0);
-        kstep(cur + lane_off1);
+        if (active) {
+            kstep(cur + lane_off0);
+            kstep(cur + lane_off1);
+        }
         if (kt + 1 < nk) {
             if (kt + NS - 1 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
             else wait_vm_lgkm0<0>();
