@@ -587,6 +587,10 @@ def main():
     ap.add_argument("--tile-m", type=int, default=0)
     ap.add_argument("--decode-t", default="1,2,4,8,16,32,64",
                     help="batch sizes of the decode-shaped sweep (--config c5)")
+    ap.add_argument("--no-reports", action="store_true",
+                    help="time the layer steps only (no stage, placement, router-variant, "
+                         "expert-parallel or backward reports): for counter passes, whose "
+                         "per-dispatch averages must see the step's kernels alone")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -654,13 +658,17 @@ def main():
     t2 = np.array([hip.ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)])
     hip.destroy(evs)
     hip.destroy(bnd)
-    stages = stage_rates(L, dims, inp, K, hip, stream)
-    placement = placement_report(L, dims, inp, host_counts, K, hip, stream) if L.E % 8 == 0 else None
-    variants = variant_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
-    ranks = ranks_report(L, dims, inp, K, hip, stream)
-    bwd = backward_report(L, dims, inp, K, hip, stream) if L.mode == "router" else None
-    if bwd:
-        bwd["forward_ms_for_reference"] = round(ms_step_fwd := total_ms / K, 5)
+    stages = placement = variants = ranks = bwd = None
+    if not args.no_reports:
+        stages = stage_rates(L, dims, inp, K, hip, stream)
+        if L.E % 8 == 0:
+            placement = placement_report(L, dims, inp, host_counts, K, hip, stream)
+        if L.mode == "router":
+            variants = variant_report(L, dims, inp, K, hip, stream)
+        ranks = ranks_report(L, dims, inp, K, hip, stream)
+        if L.mode == "router":
+            bwd = backward_report(L, dims, inp, K, hip, stream)
+            bwd["forward_ms_for_reference"] = round(total_ms / K, 5)
 
     A = L.T * L.k
     ms_step = total_ms / K
