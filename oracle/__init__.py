@@ -68,6 +68,9 @@ def lib():
         L.orc_backward_experts.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_float, I64,
                                            I32, I32, I32, I32, I32] + [P] * 9
         L.orc_backward_experts.restype = None
+        L.orc_backward_experts_r.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_float,
+                                             I64, I32, I32, I32, I32, I32, I32] + [P] * 9
+        L.orc_backward_experts_r.restype = None
         L.orc_backward_router.argtypes = [P, P, P, P, I64, I32, I32, I32, I32, P, P, P]
         L.orc_backward_router.restype = None
         L.orc_round_f64_bf16.argtypes = [P, P, I64]
@@ -352,9 +355,10 @@ def combine_ranks(y, inv, w, idx, E: int, R: int, dtype: str, slot_of_expert=Non
 
 
 def backward_experts(x, perm, inv, counts, w, w13, w2, h, y, dout, dtype: str,
-                     scale: float = 1.0) -> dict:
+                     scale: float = 1.0, round_grads: bool = False) -> dict:
     """Backward of the expert path (derivative of the forward definitions; FP32, sequential
-    sums): dw, dy, gu, dh, dgu, dxp, dx (experts' part), dw13, dw2."""
+    sums; with round_grads, dy and dgu rounded once to bf16 where they are formed): dw, dy,
+    gu, dh, dgu, dxp, dx (experts' part), dw13, dw2."""
     T, d = x.shape
     k = w.shape[1]
     E = len(counts)
@@ -368,9 +372,10 @@ def backward_experts(x, perm, inv, counts, w, w13, w2, h, y, dout, dtype: str,
     args[1], args[2], args[3] = (args[1].astype(np.int32), args[2].astype(np.int32),
                                  args[3].astype(np.int32))
     args[4], args[8] = args[4].astype(np.float32), args[8].astype(np.float32)
-    lib().orc_backward_experts(*[_p(a) for a in args], scale, T, k, d, I, E, _dt(dtype),
-                               *[_p(r[n]) for n in ("dw", "dy", "gu", "dh", "dgu", "dxp",
-                                                    "dx", "dw13", "dw2")])
+    lib().orc_backward_experts_r(*[_p(a) for a in args], scale, T, k, d, I, E, _dt(dtype),
+                                 int(round_grads),
+                                 *[_p(r[n]) for n in ("dw", "dy", "gu", "dh", "dgu", "dxp",
+                                                      "dx", "dw13", "dw2")])
     return r
 
 

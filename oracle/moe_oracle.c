@@ -678,12 +678,35 @@ void orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const
  *   dw2[e,o,i]  = sum over the segment's rows p ascending of dy[p,o] * h[p,i]
  *   dw13[e,n,c] = sum over the segment's rows p ascending of dgu[p,n] * xr[p,c]
  * All FP32, each sum sequential; rowexp [A] gives each row's expert. */
+static float orc_round_to_bf16_value(float v) { return orc_bf16_to_f32(orc_f32_to_bf16(v)); }
+
+/* With round_grads = 1 the two upstream gradients that feed the gradient GEMMs, dy and
+ * dgu, are rounded once to bf16 (round to nearest even) where they are formed, as the
+ * forward rounds h once: every later use (dh, dw2, dxp, dw13) takes the rounded values.
+ * With 0 they stay FP32. */
+void orc_backward_experts_r(const void *x, const int32_t *perm, const int32_t *inv,
+                            const int32_t *rowexp, const float *w, const void *w13,
+                            const void *w2, const void *h, const float *y, const void *dout,
+                            float s, int64_t T, int k, int d, int I, int E, int dt,
+                            int round_grads, float *dw, float *dy, float *gu, float *dh,
+                            float *dgu, float *dxp, float *dx, float *dw13, float *dw2);
+
 void orc_backward_experts(const void *x, const int32_t *perm, const int32_t *inv,
                           const int32_t *rowexp, const float *w, const void *w13,
                           const void *w2, const void *h, const float *y, const void *dout,
                           float s, int64_t T, int k, int d, int I, int E, int dt, float *dw,
                           float *dy, float *gu, float *dh, float *dgu, float *dxp, float *dx,
                           float *dw13, float *dw2) {
+    orc_backward_experts_r(x, perm, inv, rowexp, w, w13, w2, h, y, dout, s, T, k, d, I, E, dt,
+                           0, dw, dy, gu, dh, dgu, dxp, dx, dw13, dw2);
+}
+
+void orc_backward_experts_r(const void *x, const int32_t *perm, const int32_t *inv,
+                            const int32_t *rowexp, const float *w, const void *w13,
+                            const void *w2, const void *h, const float *y, const void *dout,
+                            float s, int64_t T, int k, int d, int I, int E, int dt,
+                            int round_grads, float *dw, float *dy, float *gu, float *dh,
+                            float *dgu, float *dxp, float *dx, float *dw13, float *dw2) {
     const int64_t A = T * k;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
@@ -693,7 +716,7 @@ void orc_backward_experts(const void *x, const int32_t *perm, const int32_t *inv
             float acc = 0.0f;
             for (int o = 0; o < d; ++o) {
                 const float g = orc_load(dout, t * (int64_t)d + o, dt);
-                dy[p * d + o] = ws * g;
+                dy[p * d + o] = round_grads ? orc_round_to_bf16_value(ws * g) : ws * g;
                 acc = acc + g * y[p * d + o];
             }
             dw[t * k + j] = s * acc;
@@ -721,6 +744,10 @@ void orc_backward_experts(const void *x, const int32_t *perm, const int32_t *inv
             const float dsilu = sg * (1.0f + g * (1.0f - sg));
             dgu[p * 2 * I + i] = (acc * u) * dsilu;
             dgu[p * 2 * I + I + i] = acc * silu;
+            if (round_grads) {
+                dgu[p * 2 * I + i] = orc_round_to_bf16_value(dgu[p * 2 * I + i]);
+                dgu[p * 2 * I + I + i] = orc_round_to_bf16_value(dgu[p * 2 * I + I + i]);
+            }
         }
         for (int c = 0; c < d; ++c) {
             float acc = 0.0f;

@@ -129,3 +129,28 @@ def test_exact_properties(orc):
     d1 = np.ones((L1.T, L1.d), np.float32)
     _, b1 = _oracle_backward(orc, L1, r1, d1, 1.0, r1["idx"], r1["w"])
     assert (b1["dl"] == 0).all() and (b1["dw_router"] == 0).all()
+
+
+def test_rounded_gradient_mode(orc):
+    """With dy and dgu rounded once to bf16 where they are formed: dy is exactly the bf16 of
+    the FP32 mode's dy, dgu holds bf16 values, and every gradient stays within bf16
+    rounding of the float64 autograd gradient."""
+    L = W.make_layer(T=48, d=64, E=8, k=3, I=64, dtype="f32", mode="router", seed=13,
+                     bias="zipf")
+    r = orc.forward(L)
+    dout = np.random.default_rng(4).normal(0, 1, (L.T, L.d)).astype(np.float32)
+    args = (L.x, r["perm"], r["inv"], r["counts"], r["w"], L.w13, L.w2, r["h"], r["y"], dout,
+            "f32", 1.0)
+    be32 = orc.backward_experts(*args)
+    be16 = orc.backward_experts(*args, round_grads=True)
+    assert (orc.round_bf16(be32["dy"]) == W.f32_to_bf16_bits(be16["dy"])).all()
+    assert (be16["dy"].view(np.uint32) & 0xffff == 0).all()
+    assert (be16["dgu"].view(np.uint32) & 0xffff == 0).all()
+    logits = orc.router_logits(L.x, L.w_router, L.logit_bias, "f32")
+    br = orc.backward_router(logits, be16["dw"], L.x, L.w_router, "f32")
+    x, wr, w13, w2 = _torch_forward(L, r["idx"], lambda p, l: _renorm_at(p, r["idx"]), 1.0,
+                                    dout)
+    _close(be16["dx"] + br["dx"], x.grad, "dx", rel=2e-2)
+    _close(be16["dw13"], w13.grad, "dw13", rel=2e-2)
+    _close(be16["dw2"], w2.grad, "dw2", rel=2e-2)
+    _close(br["dw_router"], wr.grad, "dw_router", rel=2e-4)     # dw is not rounded
