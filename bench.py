@@ -333,24 +333,41 @@ def backward_report(L, dims, inp, K, hip, stream):
               logit_bias=inp["logit_bias"], logits=fb["logits"], offsets=fb["offsets"],
               perm=fb["perm"], inv=fb["inv"], topk_w=fb["topk_w"], h=fb["h"], y=fb["y"],
               d_out=dout)
-    M.backward(dims, bb, ws)
-    ev = hip.create(2 * K)
-    for i in range(K):
-        hip.record(ev[2 * i], stream.cuda_stream)
-        M.backward(dims, bb, ws)
-        hip.record(ev[2 * i + 1], stream.cuda_stream)
-    torch.cuda.synchronize()
-    ts = [hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]
-    hip.destroy(ev)
-    ms = float(np.median(ts))
+    def run(bufs, gd):
+        M.backward(dims, bufs, ws, grad_dtype=gd)
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            M.backward(dims, bufs, ws, grad_dtype=gd)
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ts = [hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]
+        hip.destroy(ev)
+        return float(np.median(ts)), ts
+
+    ms, ts = run(bb, M.MOE_F32)
     flops = 16.0 * L.T * L.k * L.d * L.I
+    out = {"ms": round(ms, 5), "p10": round(float(np.percentile(ts, 10)), 5),
+           "p90": round(float(np.percentile(ts, 90)), 5), "gemm_flop": flops,
+           "tflops_overall": round(flops / (ms * 1e-3) / 1e12, 2),
+           "peak_fp32_mfma_tflops": PEAK_FP32_TFLOPS,
+           "frac_overall": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+           "forward_ms_for_reference": None}
+    if L.dtype == "bf16":
+        b16 = M.alloc_backward_buffers(dims, dev, router=True, grad_dtype=M.MOE_BF16)
+        b16.update({n: bb[n] for n in ("x", "w13", "w2", "w_router", "logit_bias", "logits",
+                                       "offsets", "perm", "inv", "topk_w", "h", "y", "d_out")})
+        del bb
+        ms16, ts16 = run(b16, M.MOE_BF16)
+        out["bf16_operands"] = {
+            "ms": round(ms16, 5), "p10": round(float(np.percentile(ts16, 10)), 5),
+            "p90": round(float(np.percentile(ts16, 90)), 5),
+            "tflops_overall": round(flops / (ms16 * 1e-3) / 1e12, 2),
+            "frac_bf16_peak_overall": round(flops / (ms16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "dy and d_gu rounded once to bf16; bf16 MFMA for every gradient GEMM; "
+                    "includes the per-call transposes of w13 and w2"}
     assert int(fb["d_err"].item()) == 0
-    return {"ms": round(ms, 5), "p10": round(float(np.percentile(ts, 10)), 5),
-            "p90": round(float(np.percentile(ts, 90)), 5), "gemm_flop": flops,
-            "tflops_overall": round(flops / (ms * 1e-3) / 1e12, 2),
-            "peak_fp32_mfma_tflops": PEAK_FP32_TFLOPS,
-            "frac_overall": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
-            "forward_ms_for_reference": None}
+    return out
 
 
 def host_list(t):

@@ -42,11 +42,11 @@ __device__ __forceinline__ float ld_elem(const void *p, int64_t i) {
 // One wave per token: lane l takes features 4l, 4l + 256, ... of every slot's y row;
 // dy = (s w_j) dout; the partial dot products <dout, y_j> are summed per lane in feature
 // order and then over the wave in the fixed DPP tree.
-template <bool kBF16>
+template <bool kBF16, bool kDyBF16>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const void *__restrict__ dout, const float *__restrict__ y,
     const int32_t *__restrict__ inv, const float *__restrict__ topk_w, int64_t T, int k,
-    int d, int64_t A, float scale, float *__restrict__ dy, float *__restrict__ dw) {
+    int d, int64_t A, float scale, void *__restrict__ dyv, float *__restrict__ dw) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -68,8 +68,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         for (int j = 0; j < kMaxK; ++j) {
             if (j < k) {
                 const float4 yv = *reinterpret_cast<const float4 *>(y + src[j] + c);
-                *reinterpret_cast<float4 *>(dy + src[j] + c) =
-                    make_float4(ws[j] * g[0], ws[j] * g[1], ws[j] * g[2], ws[j] * g[3]);
+                if constexpr (kDyBF16) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16(ws[j] * g[0]) | ((uint32_t)f32_to_bf16(ws[j] * g[1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(ws[j] * g[2]) | ((uint32_t)f32_to_bf16(ws[j] * g[3]) << 16);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dyv) + src[j] + c) = pk;
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(dyv) + src[j] + c) =
+                        make_float4(ws[j] * g[0], ws[j] * g[1], ws[j] * g[2], ws[j] * g[3]);
+                }
                 acc[j] = acc[j] + g[0] * yv.x;
                 acc[j] = acc[j] + g[1] * yv.y;
                 acc[j] = acc[j] + g[2] * yv.z;
@@ -87,10 +94,11 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 }
 
 // ----------------------------------------------------------------- SwiGLU backward
+template <bool kOutBF16>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict__ gu,
                                                          const float *__restrict__ dh,
                                                          int64_t A, int I,
-                                                         float *__restrict__ dgu) {
+                                                         void *__restrict__ dguv) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= A * I) return;
     const int64_t p = i / I;
@@ -100,8 +108,14 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict
     const float sg = 1.0f / (1.0f + e);
     const float silu = g / (1.0f + e);
     const float dsilu = sg * (1.0f + g * (1.0f - sg));
-    dgu[p * 2 * I + n] = (d * u) * dsilu;
-    dgu[p * 2 * I + I + n] = d * silu;
+    const float dg = (d * u) * dsilu, du = d * silu;
+    if constexpr (kOutBF16) {
+        static_cast<uint16_t *>(dguv)[p * 2 * I + n] = f32_to_bf16(dg);
+        static_cast<uint16_t *>(dguv)[p * 2 * I + I + n] = f32_to_bf16(du);
+    } else {
+        static_cast<float *>(dguv)[p * 2 * I + n] = dg;
+        static_cast<float *>(dguv)[p * 2 * I + I + n] = du;
+    }
 }
 
 // ------------------------------------------------------------ dx: slot-order sum
@@ -452,6 +466,175 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
     }
 }
 
+// ------------------------------------------------- bf16 weight gradient (MFMA 16x16x32)
+// out[e, n, c] = sum over the segment's rows p ascending of a[p, n] b[p, c], a and b bf16
+// (b gathered through bperm / bk when given), FP32 accumulation and output. The MFMA takes
+// 8 consecutive K values (rows p) per lane, so each 32-row stage is staged transposed: a
+// thread loads 8 consecutive features of one row (16 bytes, as stored) and writes them to
+// the feature-major LDS tile [feature][row] (8 two-byte writes). A wave's 64 lanes cover
+// 32 rows x 2 groups of 8 features, so each write instruction fills two 64-byte row spans
+// that the 80-byte row pitch puts in different banks (a 64-row stage measured slower: its
+// registers and LDS allow fewer blocks per CU). Block: BN x BC outputs, four waves of
+// (BN/2) x (BC/2); MFMA operand A = a^T (rows n, K = p), B = b (K = p, columns c): lane l
+// reads 16 bytes of feature row n + l%16 (or c + l%16) at rows 8(l/16) .. 8(l/16)+7 of the
+// stage; the result lane l holds column c + l%16 of rows n + 4(l/16) + 0..3.
+constexpr int kWgRows = 32;                  // rows (K) per stage
+constexpr int kWgPitch = 80;                 // LDS bytes per feature row (64 + 16 pad)
+
+template <int BN, int BC>
+__global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restrict__ a,
+                                                         const uint16_t *__restrict__ b,
+                                                         const int32_t *__restrict__ bperm,
+                                                         int bk, int64_t bT,
+                                                         const int32_t *__restrict__ off,
+                                                         int64_t nrows, int N, int C, int nbn,
+                                                         int nbc, float *__restrict__ out) {
+    constexpr int WN = BN / 2, WC = BC / 2, NF = WN / 16, NC = WC / 16;
+    constexpr int AL = kWgRows * BN / 8 / 256, BL = kWgRows * BC / 8 / 256;  // loads / thread
+    static_assert(AL >= 1 && BL >= 1, "tile too small for 256 threads");
+    static_assert(BN == 128 && BC == 128 && kWgRows == 32, "load mapping: 16 groups x 32 rows");
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][BN * kWgPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][BC * kWgPitch];
+    const int per_e = nbn * nbc;
+    const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
+    const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
+    int64_t r0 = 0, r1 = nrows;
+    if (off) {
+        r0 = min<int64_t>(max(off[e], 0), nrows);
+        r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wn = wv & 1, wc = wv >> 1;
+    u32x4_t ra[AL], rb[BL];
+    auto load = [&](int64_t p0) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            const int64_t row = p0 + p;
+            ra[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (row < r1)
+                ra[i] = *reinterpret_cast<const u32x4_t *>(a + row * N + min(n0 + 8 * g, N - 8));
+        }
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            const int64_t row = p0 + p;
+            rb[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (row < r1) {
+                int64_t src = row;
+                if (bperm) src = min<int64_t>((int64_t)max(bperm[row], 0) / bk, bT - 1);
+                rb[i] = *reinterpret_cast<const u32x4_t *>(b + src * C + min(c0 + 8 * g, C - 8));
+            }
+        }
+    };
+    auto store = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            uint8_t *d = sa[s] + (8 * g) * kWgPitch + 2 * p;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t w = ra[i][j >> 1];
+                *reinterpret_cast<uint16_t *>(d + j * kWgPitch) = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffff));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            uint8_t *d = sb[s] + (8 * g) * kWgPitch + 2 * p;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t w = rb[i][j >> 1];
+                *reinterpret_cast<uint16_t *>(d + j * kWgPitch) = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffff));
+            }
+        }
+    };
+    f32x4_t acc[NF][NC];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int64_t nk = (r1 - r0 + kWgRows - 1) / kWgRows;
+    if (nk > 0) {
+        load(r0);
+        store(0);
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int s = (int)(kt & 1);
+            if (kt + 1 < nk) load(r0 + (kt + 1) * kWgRows);
+#pragma unroll
+            for (int kk = 0; kk < kWgRows / 32; ++kk) {
+                bf16x8_t av[NF], bv[NC];
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+                    av[f] = *reinterpret_cast<const bf16x8_t *>(
+                        sa[s] + (wn * WN + f * 16 + r16) * kWgPitch + 64 * kk + 16 * g4);
+#pragma unroll
+                for (int t = 0; t < NC; ++t)
+                    bv[t] = *reinterpret_cast<const bf16x8_t *>(
+                        sb[s] + (wc * WC + t * 16 + r16) * kWgPitch + 64 * kk + 16 * g4);
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int t = 0; t < NC; ++t)
+                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], bv[t], acc[f][t],
+                                                                            0, 0, 0);
+            }
+            if (kt + 1 < nk) store(s ^ 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int cc = c0 + wc * WC + t * 16 + r16;
+        if (cc >= C) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + wn * WN + f * 16 + g4 * 4 + i;
+                if (n < N) out[((int64_t)e * N + n) * C + cc] = acc[f][t][i];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- per-expert transpose
+// dst[e, c, r] = src[e, r, c] for 2-byte elements, through a 64 x 64 LDS tile: each thread
+// reads 8 consecutive elements of a source row (16 bytes) and writes 8 consecutive elements
+// of a destination row (16 bytes, gathered from 8 tile rows). R and C multiples of 64.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ src,
+                                                          uint16_t *__restrict__ dst, int R,
+                                                          int Cn, int nbr, int nbc) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int per_e = nbr * nbc;
+    const int64_t e = blockIdx.x / per_e;
+    const int rem = blockIdx.x % per_e;
+    const int r0 = (rem / nbc) * 64, c0 = (rem % nbc) * 64;
+    const uint16_t *sp = src + e * (int64_t)R * Cn;
+    uint16_t *dp = dst + e * (int64_t)R * Cn;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = tid + 256 * i, r = q >> 3, c8 = (q & 7) * 8;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sp + (int64_t)(r0 + r) * Cn + c0 + c8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            tile[r][c8 + j] = (uint16_t)((j & 1) ? (v[j >> 1] >> 16) : (v[j >> 1] & 0xffff));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = tid + 256 * i, c = q >> 3, r8 = (q & 7) * 8;
+        u32x4_t v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = (uint32_t)tile[r8 + 2 * j][c] | ((uint32_t)tile[r8 + 2 * j + 1][c] << 16);
+        *reinterpret_cast<u32x4_t *>(dp + (int64_t)(c0 + c) * R + r0 + r8) = v;
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ launchers
@@ -459,25 +642,54 @@ constexpr int kDgBN = 128, kDgBT = 64;     // data-gradient tile: features x row
 constexpr int kWgBN = 64, kWgBC = 64;      // weight-gradient tile
 
 hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float *y,
-                              const int32_t *inv, const float *topk_w, float scale, float *dy,
-                              float *dw, hipStream_t s) {
+                              const int32_t *inv, const float *topk_w, float scale, void *dy,
+                              float *dw, bool dy_bf16, hipStream_t s) {
     if (dm.T == 0) return hipGetLastError();
     const dim3 grid((unsigned)((dm.T + 3) / 4));
-    if (dm.dtype == MOE_BF16)
-        combine_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T, dm.k,
-                                                            dm.d, dm.T * dm.k, scale, dy, dw);
+    const int64_t A = dm.T * dm.k;
+    if (dm.dtype == MOE_BF16 && dy_bf16)
+        combine_bwd_kernel<true, true><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T,
+                                                                  dm.k, dm.d, A, scale, dy, dw);
+    else if (dm.dtype == MOE_BF16)
+        combine_bwd_kernel<true, false><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T,
+                                                                   dm.k, dm.d, A, scale, dy, dw);
     else
-        combine_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T, dm.k,
-                                                             dm.d, dm.T * dm.k, scale, dy, dw);
+        combine_bwd_kernel<false, false><<<grid, dim3(256), 0, s>>>(dout, y, inv, topk_w, dm.T,
+                                                                    dm.k, dm.d, A, scale, dy, dw);
     return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, float *dgu,
-                             hipStream_t s) {
+hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, void *dgu,
+                             bool out_bf16, hipStream_t s) {
     const int64_t n = dm.T * dm.k * dm.inter;
     if (n == 0) return hipGetLastError();
-    swiglu_bwd_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
-        gu, dh, dm.T * dm.k, dm.inter, dgu);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (out_bf16)
+        swiglu_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(gu, dh, dm.T * dm.k, dm.inter, dgu);
+    else
+        swiglu_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(gu, dh, dm.T * dm.k, dm.inter, dgu);
+    return hipGetLastError();
+}
+
+// bf16 weight gradient over segments (see wgrad_bf16_kernel); N and C multiples of 8.
+hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
+                             int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
+                             int C, float *out, hipStream_t s) {
+    constexpr int BN = 128, BC = 128;
+    if (N % 8 || C % 8 || nseg < 1) return hipErrorInvalidValue;
+    const int nbn = (N + BN - 1) / BN, nbc = (C + BC - 1) / BC;
+    wgrad_bf16_kernel<BN, BC><<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(256), 0, s>>>(
+        static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), bperm, bk, bT, off,
+        nrows, N, C, nbn, nbc, out);
+    return hipGetLastError();
+}
+
+// dst[e] = src[e]^T for E matrices of R x C 2-byte elements.
+hipError_t launch_transpose16(const void *src, void *dst, int E, int R, int C, hipStream_t s) {
+    if (R % 64 || C % 64) return hipErrorInvalidValue;
+    const int nbr = R / 64, nbc = C / 64;
+    transpose16_kernel<<<dim3((unsigned)((int64_t)E * nbr * nbc)), dim3(256), 0, s>>>(
+        static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), R, C, nbr, nbc);
     return hipGetLastError();
 }
 

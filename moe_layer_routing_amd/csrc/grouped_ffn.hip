@@ -644,35 +644,36 @@ hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, 
 }
 
 // out[p, n] = sum_k act[p, k] wgt[e, n, k] for the rows p of every segment e (FP32 output,
-// no activation): the down-GEMM launch with N output features and K = dm.d, gathered
+// no activation): the down-GEMM launch with N output features and K (0: dm.d), gathered
 // through gperm when given. Every output is the same sequence of MFMA steps over K as the
 // gate/up GEMM's pre-activations for the same weight row, so with wgt = w13 and N = 2I it
 // reproduces the forward's gate and up values bit for bit.
 hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
                              const void *wgt, float *out, int N, const int32_t *offsets,
-                             const Workspace &ws, hipStream_t s) {
+                             const Workspace &ws, hipStream_t s, int K) {
     const int64_t A = dm.T * dm.k;
     if (A == 0) return hipGetLastError();
+    if (K == 0) K = dm.d;
     const int bt = select_tile_m(dm);
     const int64_t cap = max_m_tiles(A, dm.E, bt);
     build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
     const bool b = dm.dtype == MOE_BF16;
     switch (bt) {
     case 16:
-        return b ? launch_gemm<true, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T);
+        return b ? launch_gemm<true, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
+                 : launch_gemm<false, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
     case 32:
-        return b ? launch_gemm<true, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T);
+        return b ? launch_gemm<true, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
+                 : launch_gemm<false, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
     case 64:
-        return b ? launch_gemm<true, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T);
+        return b ? launch_gemm<true, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
+                 : launch_gemm<false, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
     case 128:
-        return b ? launch_gemm<true, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T);
+        return b ? launch_gemm<true, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
+                 : launch_gemm<false, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
     default:
-        return b ? launch_gemm<true, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, dm.d, N, s, gperm, dm.k, dm.T);
+        return b ? launch_gemm<true, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
+                 : launch_gemm<false, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
     }
 }
 

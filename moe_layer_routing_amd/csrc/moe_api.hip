@@ -446,6 +446,12 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
                     a->d_topk_w && a->d_y && a->gu && a->d_h && a->d_gu && a->d_xp,
                 MOE_E_NULLPTR);
     if (a->w_router) MOE_REQUIRE(a->d_logits && a->d_x_router, MOE_E_NULLPTR);
+    MOE_REQUIRE(a->grad_dtype == MOE_F32 || a->grad_dtype == MOE_BF16, MOE_E_DTYPE);
+    const bool g16 = a->grad_dtype == MOE_BF16;
+    if (g16) {
+        MOE_REQUIRE(dims->dtype == MOE_BF16, MOE_E_DTYPE);
+        MOE_REQUIRE(a->w13_t && a->w2_t, MOE_E_NULLPTR);
+    }
     if (!a->x_perm) {
         const int64_t x_bytes = dims->T * (int64_t)dims->d * (dims->dtype == MOE_BF16 ? 2 : 4);
         MOE_REQUIRE(x_bytes < (int64_t(1) << 32), MOE_E_SHAPE);
@@ -459,23 +465,46 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     const int64_t A = dims->T * dims->k;
     const int I = dims->inter, d = dims->d;
     hipError_t e = launch_combine_bwd(*dims, a->d_out, a->y, a->inv, a->topk_w, scale, a->d_y,
-                                      a->d_topk_w, s);
+                                      a->d_topk_w, g16, s);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_plain_gemm(*dims, a->x_perm ? a->x_perm : a->x, a->x_perm ? nullptr : a->perm,
                           a->w13, a->gu, 2 * I, a->offsets, ws, s);
     if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_dgrad(*dims, a->d_y, a->w2, bf16, d, I, a->offsets, a->d_h, ws, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_dgrad(*dims, a->d_gu, a->w13, bf16, 2 * I, d, a->offsets, a->d_xp, ws, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_wgrad(dims->E, a->d_y, a->h, bf16, nullptr, 1, A, a->offsets, A, d, I, a->d_w2, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_wgrad(dims->E, a->d_gu, a->x_perm ? a->x_perm : a->x, bf16,
-                     a->x_perm ? nullptr : a->perm, dims->k, a->x_perm ? A : dims->T,
-                     a->offsets, A, 2 * I, d, a->d_w13, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
+    const void *xb = a->x_perm ? a->x_perm : a->x;
+    const int32_t *xperm = a->x_perm ? nullptr : a->perm;
+    const int64_t xrows = a->x_perm ? A : dims->T;
+    if (g16) {
+        e = launch_transpose16(a->w2, a->w2_t, dims->E, d, I, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_transpose16(a->w13, a->w13_t, dims->E, 2 * I, d, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_plain_gemm(*dims, a->d_y, nullptr, a->w2_t, a->d_h, I, a->offsets, ws, s, d);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, true, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_plain_gemm(*dims, a->d_gu, nullptr, a->w13_t, a->d_xp, d, a->offsets, ws, s,
+                              2 * I);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_wgrad_bf16(dims->E, a->d_y, a->h, nullptr, 1, A, a->offsets, A, d, I,
+                              a->d_w2, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_wgrad_bf16(dims->E, a->d_gu, xb, xperm, dims->k, xrows, a->offsets, A,
+                              2 * I, d, a->d_w13, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+    } else {
+        e = launch_dgrad(*dims, a->d_y, a->w2, bf16, d, I, a->offsets, a->d_h, ws, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, false, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_dgrad(*dims, a->d_gu, a->w13, bf16, 2 * I, d, a->offsets, a->d_xp, ws, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_wgrad(dims->E, a->d_y, a->h, bf16, nullptr, 1, A, a->offsets, A, d, I,
+                         a->d_w2, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+        e = launch_wgrad(dims->E, a->d_gu, xb, bf16, xperm, dims->k, xrows, a->offsets, A,
+                         2 * I, d, a->d_w13, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+    }
     const float *dxr = nullptr;
     if (a->w_router) {
         const float *logits = a->logits;

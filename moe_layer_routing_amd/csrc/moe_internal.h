@@ -153,13 +153,17 @@ hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, 
                               int32_t *tiles, hipStream_t s);
 hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
                              const void *wgt, float *out, int N, const int32_t *offsets,
-                             const Workspace &ws, hipStream_t s);
+                             const Workspace &ws, hipStream_t s, int K = 0);
 // Backward steps (backward.hip).
 hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float *y,
-                              const int32_t *inv, const float *topk_w, float scale, float *dy,
-                              float *dw, hipStream_t s);
-hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, float *dgu,
-                             hipStream_t s);
+                              const int32_t *inv, const float *topk_w, float scale, void *dy,
+                              float *dw, bool dy_bf16, hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, void *dgu,
+                             bool out_bf16, hipStream_t s);
+hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
+                             int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
+                             int C, float *out, hipStream_t s);
+hipError_t launch_transpose16(const void *src, void *dst, int E, int R, int C, hipStream_t s);
 hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
                          const float *dxr, float *dx, hipStream_t s);
 hipError_t launch_router_bwd(const moe_dims &dm, const float *logits, const float *dw,

@@ -40,7 +40,7 @@ def _close(gpu, ref, what, tol=GTOL):
     assert worst <= tol, f"{what}: {worst:.3e} > {tol}"
 
 
-def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True):
+def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=False):
     dims = dims_of(L)
     fb = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
     fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"])
@@ -56,7 +56,8 @@ def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True):
         del fb["x_perm"]
     ws = M.alloc_workspace(dims)
     M.forward(dims, fb, ws, routed_scale=scale)
-    bb = M.alloc_backward_buffers(dims, "cuda", router=router_grads)
+    gd = M.MOE_BF16 if g16 else M.MOE_F32
+    bb = M.alloc_backward_buffers(dims, "cuda", router=router_grads, grad_dtype=gd)
     bb.update(x=inp["x"], x_perm=fb.get("x_perm"), w13=fb["w13"], w2=fb["w2"],
               offsets=fb["offsets"], perm=fb["perm"], inv=fb["inv"], topk_w=fb["topk_w"],
               h=fb["h"], y=fb["y"], d_out=dev(dout))
@@ -64,19 +65,19 @@ def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True):
         bb["w_router"] = dev(L.w_router)
         bb["logit_bias"] = inp.get("logit_bias")
         bb["logits"] = fb.get("logits")          # replay: recomputed from x and w_router
-    M.backward(dims, bb, ws, routed_scale=scale)
+    M.backward(dims, bb, ws, routed_scale=scale, grad_dtype=gd)
     torch.cuda.synchronize()
     assert int(fb["d_err"].item()) == 0
     return fb, bb
 
 
-def _oracle(L, fb, dout, scale, slot=None):
+def _oracle(L, fb, dout, scale, slot=None, g16=False):
     offsets = host(fb["offsets"])
     counts = np.diff(offsets)
     w13, w2 = host(fb["w13"]), host(fb["w2"])
     be = oracle.backward_experts(L.x, host(fb["perm"]), host(fb["inv"]), counts,
                                  host(fb["topk_w"]), w13, w2, host(fb["h"]), host(fb["y"]),
-                                 dout, L.dtype, scale)
+                                 dout, L.dtype, scale, round_grads=g16)
     logits = host(fb["logits"]) if "logits" in fb else oracle.router_logits(
         L.x, L.w_router, L.logit_bias, L.dtype)
     br = oracle.backward_router(logits, be["dw"], L.x, L.w_router, L.dtype)
@@ -142,3 +143,56 @@ def test_backward_deterministic_and_batch_invariant():
     fs, bs = _run(Ls, inps, np.ascontiguousarray(dout[:64]), 2.5)
     for n in ("d_x", "d_topk_w", "d_logits", "d_x_router"):
         assert host(bs[n]).tobytes() == host(b1[n])[:64].tobytes(), n
+
+
+G16_CASES = [
+    # (T, d, E, k, I, mode, scale, placed, x_perm)
+    (300, 256, 16, 4, 192, "router", 2.5, False, False),
+    (517, 128, 32, 8, 128, "router", 1.0, True, True),
+    (40, 192, 8, 6, 64, "replay", 1.0, False, False),
+]
+
+
+@pytest.mark.parametrize("case", G16_CASES, ids=lambda c: f"T{c[0]}_d{c[1]}_E{c[2]}_k{c[3]}_"
+                                                          f"I{c[4]}_{c[5]}")
+def test_backward_bf16_operands_parity(case):
+    """bf16 gradient operands: dy and d_gu rounded once where they are formed, the data
+    gradients on the forward's bf16 GEMM (transposed weights), the weight gradients on the
+    bf16 weight-gradient kernel; against the oracle with the same rounding points. dy is
+    bitwise; d_gu within one bf16 rounding (its FP32 input dh is summed in another order);
+    every other gradient within 1e-3 * max(1, |ref|)."""
+    T, d, E, k, I, mode, scale, placed, xp = case
+    L = W.make_layer(T=T, d=d, E=E, k=k, I=I, dtype="bf16", mode=mode, seed=T + 3, bias="zipf",
+                     replay="uniform")
+    if mode == "replay":
+        L.w_router = W._normal(L.seed, W.TID_ROUTER, (E, d), 1.0 / np.sqrt(d), "bf16")
+    inp = upload(L)
+    rng = np.random.default_rng(T)
+    dout = W.f32_to_bf16_bits(rng.normal(0, 1, (T, d)).astype(np.float32))
+    slot = rng.permutation(E).astype(np.int32) if placed else None
+    fb, bb = _run(L, inp, dout, scale, slot, xp, g16=True)
+    be, br = _oracle(L, fb, dout, scale, slot, g16=True)
+    assert host(bb["d_y"]).tobytes() == W.f32_to_bf16_bits(be["dy"]).tobytes()
+    # the weights' transposes are exact
+    w2t = host(bb["w2_t"]).transpose(0, 2, 1)
+    assert w2t.tobytes() == np.ascontiguousarray(host(fb["w2"])).tobytes()
+    assert host(bb["w13_t"]).transpose(0, 2, 1).tobytes() == host(fb["w13"]).tobytes()
+    _close(as_f32(host(bb["d_gu"]), "bf16"), be["dgu"], "d_gu", tol=2.0 ** -7)
+    for n, r in (("d_topk_w", be["dw"]), ("gu", be["gu"]), ("d_h", be["dh"]),
+                 ("d_w2", be["dw2"]), ("d_logits", br["dl"]),
+                 ("d_w_router", br["dw_router"]), ("d_x_router", br["dx"])):
+        _close(host(bb[n]), r, n, tol=1e-3)
+    # downstream of the rounded d_gu, whose bf16 rounding can flip by one unit where the two
+    # sides' FP32 dh (summed in different orders) straddle a midpoint: the bf16 tolerance
+    for n, r in (("d_xp", be["dxp"]), ("d_w13", be["dw13"])):
+        _close(host(bb[n]), r, n, tol=2e-2)
+    _close(host(bb["d_x"]), be["dx"] + br["dx"], "d_x", tol=2e-2)
+    # and tightly, from the GPU's own rounded d_gu (float64 sums of the same operands)
+    dgu = as_f32(host(bb["d_gu"]), "bf16").astype(np.float64)
+    offs = host(fb["offsets"])
+    xr = as_f32(L.x, "bf16").astype(np.float64)[host(fb["perm"]) // k]
+    w13 = as_f32(host(fb["w13"]), "bf16").astype(np.float64)
+    ref_w13 = np.stack([dgu[offs[e]:offs[e + 1]].T @ xr[offs[e]:offs[e + 1]] for e in range(E)])
+    ref_xp = np.concatenate([dgu[offs[e]:offs[e + 1]] @ w13[e] for e in range(E)])
+    _close(host(bb["d_w13"]), ref_w13, "d_w13 (GPU d_gu)", tol=1e-4)
+    _close(host(bb["d_xp"]), ref_xp, "d_xp (GPU d_gu)", tol=1e-4)
