@@ -436,11 +436,15 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
+        // the MFMA block at raised wave priority: while one wave of a SIMD issues MFMAs the
+        // others' fragment reads and DMA issue wait (measured 0 to +1 %, same bytes)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b[t], acc[f][t], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // NS-slot ring: stages kt+1 .. kt+NS-1 are in flight while stage kt is computed. At
