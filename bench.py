@@ -521,8 +521,30 @@ def decode_sweep(args):
             times.append(hip.ms(ev[0], ev[4]))
             t13.append(hip.ms(ev[1], ev[2]))
             hip.destroy(ev)
+        # the same step captured once into a HIP graph and replayed (no launch overhead)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            M.forward(dims, b, ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            M.forward(dims, b, ws)
+        gtimes = []
+        for _ in range(args.steps):
+            scrub.sum()
+            ev = hip.create(2)
+            hip.record(ev[0], stream.cuda_stream)
+            graph.replay()
+            hip.record(ev[1], stream.cuda_stream)
+            torch.cuda.synchronize()
+            gtimes.append(hip.ms(ev[0], ev[1]))
+            hip.destroy(ev)
+        del graph
         assert int(b["d_err"].item()) == 0
         t_ms = float(np.median(times))
+        gr_ms = float(np.median(gtimes))
         g_ms = float(np.median(t13))
         active = int((b["counts"] > 0).sum().item())
         A = T * L.k
@@ -531,9 +553,12 @@ def decode_sweep(args):
         rows.append({"T": T, "ms": round(t_ms, 4), "p10_ms": round(float(np.percentile(times, 10)), 4),
                      "p90_ms": round(float(np.percentile(times, 90)), 4),
                      "tokens_per_s": round(T / (t_ms * 1e-3), 1),
+                     "graph_ms": round(gr_ms, 4),
+                     "graph_hbm_gbs": None,
                      "active_experts": active, "hbm_gbs": round(nbytes / (t_ms * 1e-3) / 1e9, 1),
                      "gate_up_ms": round(g_ms, 4), "gate_up_bytes": g_bytes,
                      "gate_up_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1)})
+        rows[-1]["graph_hbm_gbs"] = round(nbytes / (gr_ms * 1e-3) / 1e9, 1)
     top = rows[-1]
     rec = {
         "metric": METRIC + " (decode-shaped layer, HBM GB/s)",
