@@ -370,6 +370,47 @@ def backward_report(L, dims, inp, K, hip, stream):
     return out
 
 
+def ep_share_report(K, hip, stream, cfg="c3", ranks=8):
+    """One GPU's share of the packed-microbatch layer under expert parallelism (8 data-
+    parallel ranks x 8 expert-parallel ranks): the grouped FFN of the 16 experts rank 0
+    owns, over the rows the 8 ranks' batches route to them (each batch shaped like the
+    packed-microbatch layer, with its own seed). Synthetic bf16 rows and weights on the
+    device; TFLOP/s of 6*A*d*I against the bf16 peak."""
+    import torch
+
+    import moe_layer_routing_amd as M
+    import workloads as W
+    c = W.CONFIGS[cfg]
+    d, I, H = c["d"], c["inter"] if "inter" in c else c["I"], c["E"] // ranks
+    counts = W.ep_share_counts(cfg, ranks)
+    A = int(counts.sum())
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    std = 1.0 / np.sqrt(d)
+    x_perm = torch.randn((A, d), generator=g, device=dev).to(torch.bfloat16)
+    w13 = (torch.randn((H, 2 * I, d), generator=g, device=dev) * std).to(torch.bfloat16)
+    w2 = (torch.randn((H, d, I), generator=g, device=dev) * std).to(torch.bfloat16)
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+    h = torch.empty((A, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((A, d), dtype=torch.float32, device=dev)
+    dims = M.make_dims(A, d, H, 1, I, M.MOE_BF16)
+    ws = M.alloc_workspace(dims, dev)
+    M.grouped_ffn(dims, x_perm, offsets, w13, w2, h, y, workspace=ws)
+    ev = hip.create(2 * K)
+    for i in range(K):
+        hip.record(ev[2 * i], stream.cuda_stream)
+        M.grouped_ffn(dims, x_perm, offsets, w13, w2, h, y, workspace=ws)
+        hip.record(ev[2 * i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+    hip.destroy(ev)
+    flops = 6.0 * A * d * I
+    return {"workload": f"{cfg} under DP{ranks} x EP{ranks}: rank 0's {H} experts",
+            "rows": A, "rows_per_expert": counts.tolist(), "d": d, "inter": I,
+            "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def host_list(t):
     return [float(v) for v in t.cpu().tolist()]
 
@@ -700,7 +741,7 @@ def main():
     t2 = np.array([hip.ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)])
     hip.destroy(evs)
     hip.destroy(bnd)
-    stages = placement = variants = ranks = bwd = None
+    stages = placement = variants = ranks = bwd = ep_share = None
     if not args.no_reports:
         stages = stage_rates(L, dims, inp, K, hip, stream)
         if L.E % 8 == 0:
@@ -708,6 +749,7 @@ def main():
         if L.mode == "router":
             variants = variant_report(L, dims, inp, K, hip, stream)
         ranks = ranks_report(L, dims, inp, K, hip, stream)
+        ep_share = ep_share_report(K, hip, stream)
         if L.mode == "router":
             bwd = backward_report(L, dims, inp, K, hip, stream)
             bwd["forward_ms_for_reference"] = round(total_ms / K, 5)
@@ -764,6 +806,7 @@ def main():
         "router_variants": variants,
         "expert_parallel": ranks,
         "backward": bwd,
+        "ep_share": ep_share,
         "wall_s_timed": round(t_wall, 4),
     }
     if args.cpu_sample > 0:

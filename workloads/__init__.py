@@ -191,6 +191,22 @@ def replay_dirichlet(cu_seqlens: np.ndarray, E: int, k: int, seed: int):
     return _sort_slots(ids, w.astype(np.float32))
 
 
+def ep_share_counts(cfg: str = "c3", ranks: int = 8, seed0: int = 100) -> np.ndarray:
+    """Rows one expert-parallel rank receives: ``ranks`` data-parallel batches shaped like
+    ``cfg`` (each its own seed), each routed over all E experts; rank 0 owns experts
+    0 .. E/ranks - 1 and receives every batch's rows for them. Returns the per-local-expert
+    row counts (int64, length E / ranks)."""
+    c = CONFIGS[cfg]
+    E, k, T = c["E"], c["k"], c["T"]
+    H = E // ranks
+    tot = np.zeros(H, dtype=np.int64)
+    for r in range(ranks):
+        cu = packed_lengths(T, seed0 + r)
+        ids, _ = replay_dirichlet(cu, E, k, seed0 + r)
+        tot += np.bincount(ids.reshape(-1), minlength=E)[:H]
+    return tot
+
+
 def replay_hot(T: int, E: int, k: int, seed: int):
     """Imbalanced replay for E=256, k=8: one hot expert is in every token's set, four
     slots come from a 15-expert group, three from 224 tail experts (both uniform without
