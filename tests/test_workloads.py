@@ -1,5 +1,6 @@
 """Structural claims of the seeded workload generators."""
 import numpy as np
+import pytest
 
 import workloads as W
 
@@ -64,3 +65,35 @@ def test_c5_pool_prefix():
     a = W.make_config("c5", T=7, weights=False)
     b = W.make_config("c5", weights=False)
     np.testing.assert_array_equal(a.x, b.x[:7])
+
+
+def test_router_variant_inputs():
+    """Correction bias, frozen hash table and token ids: seeded, in range, the table's rows
+    k distinct experts, the token ids skewed (frequent ids repeat)."""
+    b1, b2 = W.correction_bias(64, 3), W.correction_bias(64, 3)
+    assert b1.dtype == np.float32 and (b1 == b2).all() and 0.02 < b1.std() < 0.08
+    tab = W.hash_table(5000, 64, 8, 3)
+    assert tab.shape == (5000, 8) and tab.dtype == np.int32
+    assert (tab >= 0).all() and (tab < 64).all()
+    assert all(len(set(r)) == 8 for r in tab.tolist())
+    assert (tab == W.hash_table(5000, 64, 8, 3)).all()
+    tok = W.token_ids(20000, 5000, 3)
+    assert tok.dtype == np.int32 and (tok >= 0).all() and (tok < 5000).all()
+    _, cnt = np.unique(tok, return_counts=True)
+    assert cnt.max() > 20 * 20000 / 5000                 # Zipf: a few ids dominate
+    L = W.make_layer(T=50, d=64, E=16, k=4, I=64, mode="router", seed=2)
+    W.set_router(L, "sqrt_softplus", bias=True, hash_vocab=300, routed_scale=2.5)
+    assert L.score == "sqrt_softplus" and L.routed_scale == 2.5
+    assert L.hash_table.shape == (300, 4) and L.token_ids.shape == (50,)
+    with pytest.raises(ValueError):
+        W.set_router(L, "tanh")
+
+
+def test_ep_share_counts():
+    """Rank 0's rows under 8 x 8 expert parallelism: 16 experts, about T*k rows in all
+    (each of 8 batches sends 1/8 of its T*k assignments on average), reproducible."""
+    c = W.ep_share_counts("c3", 8)
+    assert c.shape == (16,) and c.dtype == np.int64
+    T, k = W.CONFIGS["c3"]["T"], W.CONFIGS["c3"]["k"]
+    assert abs(int(c.sum()) - T * k) < 0.1 * T * k
+    assert (c == W.ep_share_counts("c3", 8)).all()
