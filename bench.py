@@ -609,7 +609,7 @@ def decode_sweep(args):
         "data": "synthetic",
         "config": {"workload": WORKLOADS["c5"], "name": "c5", "T": top["T"], "d": L.d,
                    "E": L.E, "k": L.k, "inter": L.I, "mode": "router", "evict_read_mb": 512},
-        "roofline": {"kernel": "grouped gate/up GEMM + SwiGLU (decode tiles), T=64",
+        "roofline": {"kernel": f"grouped gate/up GEMM + SwiGLU (decode tiles), T={top['T']}",
                      "bound": "hbm", "achieved": top["gate_up_gbs"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(top["gate_up_gbs"] / PEAK_HBM_GBS, 4),
                      "traffic": None,

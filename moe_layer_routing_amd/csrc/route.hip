@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
 // tokens' q·p in token order (starting from 0), then the four waves' sums in wave order.
 static_assert(kTopkTokPerBlock == 16, "4 waves x 4 tokens");
 
-template <int kFn, bool kHash>
+template <int kFn, bool kHash, int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
                                                          const int32_t *__restrict__ q,
                                                          int64_t T, int E, int k,
@@ -140,7 +140,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
     const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * 4;
     float qp[kRowVals];
     int err = 0;
-    route_rows<kFn, kHash>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr, qp, err);
+    if (t0 < T) {   // wave-uniform; a wave past the batch only contributes zeros
+        route_rows<kFn, kHash, NV>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr, qp,
+                                   err);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
+    }
     wave_raise(err, d_err);
     if (mass_part) {
         __shared__ float mpt[kTopkTokPerBlock][kMaxE];
@@ -254,8 +260,10 @@ template <int kFn, bool kHash>
 static void launch_topk_t(const moe_dims &dm, int64_t tblk, const float *logits,
                           const int32_t *q, int32_t *topk_idx, float *topk_w, float *mass_part,
                           int32_t *d_err, const RouteOpts &o, hipStream_t s) {
-    route_topk_kernel<kFn, kHash><<<dim3((unsigned)tblk), dim3(256), 0, s>>>(
-        logits, q, dm.T, dm.E, dm.k, topk_idx, topk_w, mass_part, d_err, o);
+    with_row_vals(dm.E, [&](auto nv) {
+        route_topk_kernel<kFn, kHash, decltype(nv)::value><<<dim3((unsigned)tblk), dim3(256), 0, s>>>(
+            logits, q, dm.T, dm.E, dm.k, topk_idx, topk_w, mass_part, d_err, o);
+    });
 }
 
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,

@@ -4,6 +4,8 @@
 #pragma once
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // Total order used for expert selection: larger logit first, equal logits -> lower id.
@@ -86,6 +88,7 @@ __device__ __forceinline__ float row_sum(float v) {
 // logit of an existing token. lse (optional) receives max + log(Z) per token.
 constexpr int kRowVals = kMaxE / 16;   // logits per lane
 
+template <int NV>
 __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
                                             const int32_t *__restrict__ q, int64_t t0,
                                             int64_t T, int E, int k,
@@ -97,44 +100,25 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
     const int64_t t = t0 + (lane >> 4);
     const bool tv = t < T;
     const int nv = (E + 15) >> 4;     // logits per lane actually used (uniform)
-    float lv[kRowVals];
-    uint32_t hi[kRowVals];
-    bool valid[kRowVals];
+    float lv[NV];
+    uint32_t hi[NV];                  // selection keys; 0 = absent or already taken
+    bool valid[NV];
+    uint32_t lmax = 0;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i) {
-        valid[i] = i < nv && c + 16 * i < E;
+    for (int i = 0; i < NV; ++i) {
+        valid[i] = c + 16 * i < E;
         lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
         if (tv && valid[i] && !__builtin_isfinite(lv[i])) err |= MOE_DERR_NONFINITE;
-        hi[i] = valid[i] ? ordered_bits(lv[i]) : 0u;
+        // a present expert's key is at least 1 (only the NaN with all bits set maps to 0)
+        hi[i] = valid[i] ? max(ordered_bits(lv[i]), 1u) : 0u;
+        lmax = max(lmax, hi[i]);
     }
-    uint32_t taken = 0, mkey[kMaxK];
-    int sel[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        sel[j] = 0;
-        mkey[j] = 0;
-        if (j < k) {
-            uint32_t best = 0;
-#pragma unroll
-            for (int i = 0; i < kRowVals; ++i)
-                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
-            const uint32_t m = row_max_u32(best);
-            int cand = 0x7fffffff;
-#pragma unroll
-            for (int i = kRowVals - 1; i >= 0; --i)
-                if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] == m) cand = c + 16 * i;
-            const int e = row_min_i32(cand);
-            sel[j] = e;
-            mkey[j] = m;
-            if ((e & 15) == c) taken |= 1u << (e >> 4);
-        }
-    }
-    // softmax over all E, renormalisation of the k selected probabilities
-    const float mx = from_ordered_bits(mkey[0]);
-    float z[kRowVals];
+    // softmax over all E: shift by the row maximum (the first round's logit)
+    const float mx = from_ordered_bits(row_max_u32(lmax));
+    float z[NV];
     float zl = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i) {
+    for (int i = 0; i < NV; ++i) {
         z[i] = valid[i] ? expf(lv[i] - mx) : 0.f;
         if (i < nv) zl = (i == 0) ? z[0] : zl + z[i];
     }
@@ -142,24 +126,41 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
     if (lse && tv && c == 0) lse[t] = mx + logf(Z);
     const float qt = (q && tv) ? static_cast<float>(q[t]) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i) qp[i] = (tv && valid[i]) ? qt * (z[i] / Z) : 0.f;
-    float ps[kMaxK];
+    for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-        ps[j] = (j < k) ? expf(from_ordered_bits(mkey[j]) - mx) / Z : 0.f;
-    float sum = ps[0];
+    for (int i = 0; i < NV; ++i) qp[i] = (tv && valid[i]) ? qt * (z[i] / Z) : 0.f;
+    // k rounds, as a loop (decode-sized launches fetch this code cold, so its size counts):
+    // the row's largest remaining key, ties to the lowest id; the owning lane clears the
+    // key. Each round's probability is recomputed from its logit and added left to right;
+    // lane c of the row keeps round c's id and probability.
+    int my_sel = 0;
+    float my_p = 0.f, sum = 0.f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+        uint32_t best = 0;
 #pragma unroll
-    for (int j = 1; j < kMaxK; ++j)
-        if (j < k) sum = sum + ps[j];
-    if (tv) {
+        for (int i = 0; i < NV; ++i) best = max(best, hi[i]);
+        const uint32_t m = row_max_u32(best);
+        int cand = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k && c == j) {
-                topk_idx[t * k + j] = sel[j];
-                topk_w[t * k + j] = ps[j] / sum;
-                if (lds_ids) lds_ids[t * k + j] = sel[j];
-            }
+        for (int i = NV - 1; i >= 0; --i)
+            if (hi[i] == m) cand = c + 16 * i;
+        const int e = row_min_i32(cand);
+        const float pj = expf(from_ordered_bits(m) - mx) / Z;
+        sum = (j == 0) ? pj : sum + pj;
+        if (c == j) {
+            my_sel = e;
+            my_p = pj;
         }
+        const bool own = (e & 15) == c;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (own && i == (e >> 4)) hi[i] = 0u;
+    }
+    if (tv && c < k) {
+        topk_idx[t * k + c] = my_sel;
+        topk_w[t * k + c] = my_p / sum;
+        if (lds_ids) lds_ids[t * k + c] = my_sel;
     }
 }
 
@@ -180,11 +181,12 @@ __device__ __forceinline__ float router_score(float l) {
 
 // Row-uniform value v[e] of the row's lane (e & 15), register e >> 4 (v >= 0 or NaN, so
 // its bits order like the value; non-owning lanes offer +0). 0 for e outside [0, 16 * nv).
-__device__ __forceinline__ float row_pick(const float (&v)[kRowVals], int e, int c, int nv) {
+template <int NV>
+__device__ __forceinline__ float row_pick(const float (&v)[NV], int e, int c, int nv) {
     const bool own = e >= 0 && (e & 15) == c && (e >> 4) < nv;
     uint32_t b = 0;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i)
+    for (int i = 0; i < NV; ++i)
         if (own && i == (e >> 4)) b = __float_as_uint(v[i]);
     return __uint_as_float(row_max_u32(b));
 }
@@ -202,7 +204,7 @@ __device__ __forceinline__ float row_pick(const float (&v)[kRowVals], int e, int
 //    sum: the bias never enters a weight.
 //  - qp: q[t] * prob[e], prob = p (softmax) or s[e] / (row sum of s) for the scored
 //    routers; lse: max logit + log(Z) with Z = row sum of exp(l - max).
-template <int kFn, bool kHash>
+template <int kFn, bool kHash, int NV>
 __device__ __forceinline__ void route_rows4_scored(
     const float *__restrict__ logits, const int32_t *__restrict__ q, int64_t t0, int64_t T,
     int E, int k, const RouteOpts &o, int32_t *__restrict__ topk_idx,
@@ -211,12 +213,12 @@ __device__ __forceinline__ void route_rows4_scored(
     const int64_t t = t0 + (lane >> 4);
     const bool tv = t < T;
     const int nv = (E + 15) >> 4;
-    float lv[kRowVals], v[kRowVals];
-    bool valid[kRowVals];
+    float lv[NV], v[NV];
+    bool valid[NV];
     uint32_t lmax = 0;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i) {
-        valid[i] = i < nv && c + 16 * i < E;
+    for (int i = 0; i < NV; ++i) {
+        valid[i] = c + 16 * i < E;
         lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
         if (tv && valid[i] && !__builtin_isfinite(lv[i])) err |= MOE_DERR_NONFINITE;
         if (valid[i]) lmax = max(lmax, ordered_bits(lv[i]));
@@ -226,7 +228,7 @@ __device__ __forceinline__ void route_rows4_scored(
     if (kFn == kScoreSoftmax || o.lse) {
         float zl = 0.f;
 #pragma unroll
-        for (int i = 0; i < kRowVals; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const float z = valid[i] ? expf(lv[i] - mx) : 0.f;
             if (i < nv) zl = (i == 0) ? z : zl + z;
             if constexpr (kFn == kScoreSoftmax) v[i] = z;
@@ -237,12 +239,12 @@ __device__ __forceinline__ void route_rows4_scored(
     float norm;
     if constexpr (kFn == kScoreSoftmax) {
 #pragma unroll
-        for (int i = 0; i < kRowVals; ++i) v[i] = valid[i] ? v[i] / Z : 0.f;
+        for (int i = 0; i < NV; ++i) v[i] = valid[i] ? v[i] / Z : 0.f;
         norm = 1.f;
     } else {
         float sl = 0.f;
 #pragma unroll
-        for (int i = 0; i < kRowVals; ++i) {
+        for (int i = 0; i < NV; ++i) {
             v[i] = valid[i] ? router_score<kFn>(lv[i]) : 0.f;
             if (i < nv) sl = (i == 0) ? v[0] : sl + v[i];
         }
@@ -250,18 +252,19 @@ __device__ __forceinline__ void route_rows4_scored(
     }
     const float qt = (q && tv) ? static_cast<float>(q[t]) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < kRowVals; ++i) {
+    for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
         if constexpr (kFn == kScoreSoftmax) qp[i] = (tv && valid[i]) ? qt * v[i] : 0.f;
         else qp[i] = (tv && valid[i]) ? qt * (v[i] / norm) : 0.f;
     }
 
-    int sel[kMaxK];
-    bool zero_w = false;
     if constexpr (kHash) {
+        int sel[kMaxK];
         const int32_t tok = tv ? o.token_ids[t] : 0;
         const bool bad_tok = tv && (tok < 0 || tok >= o.vocab);
         if (bad_tok) err |= MOE_DERR_IDX_RANGE;
-        zero_w = bad_tok;
+        bool zero_w = bad_tok;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             sel[j] = -1;
@@ -279,54 +282,66 @@ __device__ __forceinline__ void route_rows4_scored(
                     }
             }
         }
+        float vs[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) vs[j] = (j < k) ? row_pick(v, sel[j], c, nv) : 0.f;
+        float sum = vs[0];
+#pragma unroll
+        for (int j = 1; j < kMaxK; ++j)
+            if (j < k) sum = sum + vs[j];
+        if (tv) {
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k && c == j) {
+                    topk_idx[t * k + j] = sel[j];
+                    topk_w[t * k + j] = zero_w ? 0.f : vs[j] / sum;
+                    if (lds_ids) lds_ids[t * k + j] = sel[j];
+                }
+            }
+        }
     } else {
-        uint32_t hi[kRowVals];
+        uint32_t hi[NV];            // selection keys; 0 = absent or already taken
 #pragma unroll
-        for (int i = 0; i < kRowVals; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const float b = (o.corr_bias && valid[i]) ? o.corr_bias[c + 16 * i] : 0.f;
-            hi[i] = valid[i] ? ordered_bits(v[i] + b) : 0u;
+            hi[i] = valid[i] ? max(ordered_bits(v[i] + b), 1u) : 0u;
         }
-        uint32_t taken = 0;
+        // rounds as a loop (compact code, as route_rows4); lane c keeps round c's id and
+        // value, the weights' sum runs left to right over the rounds
+        int my_sel = 0;
+        float my_v = 0.f, sum = 0.f;
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            uint32_t best = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            sel[j] = 0;
-            if (j < k) {
-                uint32_t best = 0;
+            for (int i = 0; i < NV; ++i) best = max(best, hi[i]);
+            const uint32_t m = row_max_u32(best);
+            int cand = 0x7fffffff;
 #pragma unroll
-                for (int i = 0; i < kRowVals; ++i)
-                    if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] > best) best = hi[i];
-                const uint32_t m = row_max_u32(best);
-                int cand = 0x7fffffff;
-#pragma unroll
-                for (int i = kRowVals - 1; i >= 0; --i)
-                    if (i < nv && valid[i] && !((taken >> i) & 1u) && hi[i] == m) cand = c + 16 * i;
-                const int e = row_min_i32(cand);
-                sel[j] = e;
-                if ((e & 15) == c) taken |= 1u << (e >> 4);
+            for (int i = NV - 1; i >= 0; --i)
+                if (hi[i] == m) cand = c + 16 * i;
+            const int e = row_min_i32(cand);
+            const float vj = row_pick(v, e, c, nv);
+            sum = (j == 0) ? vj : sum + vj;
+            if (c == j) {
+                my_sel = e;
+                my_v = vj;
             }
+            const bool own = (e & 15) == c;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (own && i == (e >> 4)) hi[i] = 0u;
         }
-    }
-    float vs[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) vs[j] = (j < k) ? row_pick(v, sel[j], c, nv) : 0.f;
-    float sum = vs[0];
-#pragma unroll
-    for (int j = 1; j < kMaxK; ++j)
-        if (j < k) sum = sum + vs[j];
-    if (tv) {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k && c == j) {
-                topk_idx[t * k + j] = sel[j];
-                topk_w[t * k + j] = zero_w ? 0.f : vs[j] / sum;
-                if (lds_ids) lds_ids[t * k + j] = sel[j];
-            }
+        if (tv && c < k) {
+            topk_idx[t * k + c] = my_sel;
+            topk_w[t * k + c] = my_v / sum;
+            if (lds_ids) lds_ids[t * k + c] = my_sel;
         }
     }
 }
 
 // The row routine of a router variant (the plain softmax router is route_rows4).
-template <int kFn, bool kHash>
+template <int kFn, bool kHash, int NV>
 __device__ __forceinline__ void route_rows(const float *__restrict__ logits,
                                            const int32_t *__restrict__ q, int64_t t0,
                                            int64_t T, int E, int k, const RouteOpts &o,
@@ -334,10 +349,19 @@ __device__ __forceinline__ void route_rows(const float *__restrict__ logits,
                                            float *__restrict__ topk_w, int32_t *lds_ids,
                                            float (&qp)[kRowVals], int &err) {
     if constexpr (kFn == kScoreSoftmax && !kHash)
-        route_rows4(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, qp, err, o.lse);
+        route_rows4<NV>(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, qp, err, o.lse);
     else
-        route_rows4_scored<kFn, kHash>(logits, q, t0, T, E, k, o, topk_idx, topk_w, lds_ids,
+        route_rows4_scored<kFn, kHash, NV>(logits, q, t0, T, E, k, o, topk_idx, topk_w, lds_ids,
                                        qp, err);
+}
+
+// Logits per lane for E experts, as a template argument (4, 8 or 16 registers): the row
+// routines then hold and scan only as many values as E needs.
+template <class F>
+inline void with_row_vals(int E, F &&f) {
+    if (E <= 64) f(std::integral_constant<int, 4>{});
+    else if (E <= 128) f(std::integral_constant<int, 8>{});
+    else f(std::integral_constant<int, 16>{});
 }
 
 // OR a per-lane error mask over the wave and raise it once.

@@ -32,7 +32,7 @@ constexpr int kTailMaxA = kSmallT * kMaxK;
 static_assert(kTailWaves * kTailTokPerWave == kSmallT, "one wave per 4 tokens");
 static_assert(kTailMaxA / kWave <= kTailWaves, "one wave per 64 assignments");
 
-template <bool kReplay, int kFn, bool kHash>
+template <bool kReplay, int kFn, bool kHash, int NV>
 __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ q,
     const int32_t *__restrict__ idx_in, const float *__restrict__ w_in, int T, int E, int k,
@@ -78,8 +78,13 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
         }
     } else {
         float qp[kRowVals];
-        route_rows<kFn, kHash>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k, opts,
-                               topk_idx, topk_w, ids, qp, err);
+        if (wave * kTailTokPerWave < T) {   // waves past the batch hold zeros
+            route_rows<kFn, kHash, NV>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k,
+                                       opts, topk_idx, topk_w, ids, qp, err);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
+        }
         if (prob_mass) {
             const int row = wave * 4 + (lane >> 4), c = lane & 15;
 #pragma unroll
@@ -204,9 +209,15 @@ static void launch_tail_t(const moe_dims &dm, int bt, int cap, const float *logi
                           int32_t *offsets, int32_t *perm, int32_t *inv,
                           int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
                           const int32_t *slot_map, const RouteOpts &o, hipStream_t s) {
-    route_tail_kernel<kReplay, kFn, kHash><<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
-        logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w, prob_mass,
-        counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map, o);
+    auto go = [&](auto nv) {
+        route_tail_kernel<kReplay, kFn, kHash, decltype(nv)::value>
+            <<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
+                logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
+                prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map,
+                o);
+    };
+    if constexpr (kReplay) go(std::integral_constant<int, kRowVals>{});   // no top-k
+    else with_row_vals(dm.E, go);
 }
 
 hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
