@@ -73,6 +73,61 @@ def test_route(case):
     assert_close(host(mass), r_mass, L.dtype, "prob_mass")
 
 
+TIE_CASES = [
+    dict(T=200, E=65, k=8), dict(T=100, E=129, k=6), dict(T=300, E=128, k=8),
+    dict(T=64, E=128, k=8), dict(T=17, E=200, k=8), dict(T=5, E=64, k=4),
+    dict(T=90, E=64, k=8), dict(T=40, E=16, k=16 // 2),
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: f"T{c['T']}_E{c['E']}_k{c['k']}")
+def test_route_exact_ties_and_lane_widths(case):
+    """Exact ties (duplicated router rows give equal logits; all-zero tokens tie every
+    expert) must go to the lowest id, through the multi-block routing (moe_route) and,
+    for T <= 64, through the single-block tail inside moe_forward; E spans the 4 / 8 / 16
+    logits-per-lane code paths and their boundaries. Ids are compared exactly with the
+    oracle on the GPU's own logits, and the two paths must agree bitwise."""
+    T, E, k = case["T"], case["E"], case["k"]
+    L = W.make_layer(T=T, d=128, E=E, k=k, I=64, dtype="bf16", mode="router", seed=E + T)
+    rng = np.random.default_rng(E * 7 + T)
+    for _ in range(max(2, E // 8)):          # groups of equal router rows
+        src = int(rng.integers(E))
+        for dst in rng.choice(E, size=int(rng.integers(1, 4)), replace=False):
+            L.w_router[dst] = L.w_router[src]
+    L.x[rng.choice(T, size=max(1, T // 10), replace=False)] = 0   # every expert ties
+    L.logit_bias = None
+    _print("route ties", case)
+    dims = dims_of(L)
+    inp = upload(L)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.route(dims, inp["x"], inp["w_router"], None, idx, w, lg, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    g_lg = host(lg)
+    r_idx, r_w, _, r_err = oracle.route_from_logits(g_lg, k)
+    assert r_err == 0
+    # the cases really tie: some token has equal logits among its selected experts
+    ties = sum(len(np.unique(g_lg[t, r_idx[t]])) < k for t in range(T))
+    assert ties > 0
+    np.testing.assert_array_equal(host(idx), r_idx)
+    assert_close(host(w), r_w, "f32", "topk_w")
+    zero_rows = np.where(~L.x.any(axis=1))[0]
+    np.testing.assert_array_equal(host(idx)[zero_rows], np.tile(np.arange(k), (len(zero_rows), 1)))
+    # the fused forward (single-block tail for T <= 64) gives the same bytes
+    b = M.alloc_forward_buffers(dims, "cuda", router=True)
+    del b["x_perm"]
+    b.update(x=inp["x"], w_router=inp["w_router"], w13=inp["w13"], w2=inp["w2"])
+    M.forward(dims, b, M.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    assert int(b["d_err"].item()) == 0
+    assert host(b["logits"]).tobytes() == g_lg.tobytes()
+    assert host(b["topk_idx"]).tobytes() == host(idx).tobytes()
+    assert host(b["topk_w"]).tobytes() == host(w).tobytes()
+
+
 def test_route_nonfinite_flag():
     L = W.make_layer(T=70, d=128, E=16, k=4, I=64, dtype="bf16", mode="router", seed=7,
                      weights=False)
