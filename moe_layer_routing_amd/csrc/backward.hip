@@ -377,8 +377,10 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
     }
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wn = wv & 1, wc = wv >> 1;
-    constexpr int AR = kKc * BN / 4 / 256, BR = kKc * BC / 4 / 256;
-    static_assert(AR >= 1 && BR >= 1, "tile too small for 256 threads");
+    // float4 copies per thread and stage (threads past kKc * BN / 4 copy nothing)
+    constexpr int AR = (kKc * BN / 4 + 255) / 256, BR = (kKc * BC / 4 + 255) / 256;
+    constexpr int AQ = kKc * BN / 4, BQ = kKc * BC / 4;
+    static_assert(NF >= 1 && NC >= 1, "tile too small");
     float4 ra[AR], rb[BR];
     auto load = [&](int64_t p0) {
 #pragma unroll
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
             const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
             const int64_t p = p0 + r;
             ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p < r1)
+            if (q < AQ && p < r1)
                 ra[i] = *reinterpret_cast<const float4 *>(a + p * N + min(n0 + nc, N - 4));
         }
 #pragma unroll
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
             const int q = tid + 256 * i, r = q / (BC / 4), cc = (q % (BC / 4)) * 4;
             const int64_t p = p0 + r;
             rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p < r1) {
+            if (q < BQ && p < r1) {
                 int64_t row = p;
                 if (bperm) row = min<int64_t>((int64_t)max(bperm[p], 0) / bk, bT - 1);
                 const int64_t o = row * C + min(c0 + cc, C - 4);
@@ -412,12 +414,12 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 #pragma unroll
         for (int i = 0; i < AR; ++i) {
             const int q = tid + 256 * i, r = q / (BN / 4), nc = (q % (BN / 4)) * 4;
-            *reinterpret_cast<float4 *>(sa[s] + r * kAS + nc) = ra[i];
+            if (q < AQ) *reinterpret_cast<float4 *>(sa[s] + r * kAS + nc) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < BR; ++i) {
             const int q = tid + 256 * i, r = q / (BC / 4), cc = (q % (BC / 4)) * 4;
-            *reinterpret_cast<float4 *>(sb[s] + r * kBS + cc) = rb[i];
+            if (q < BQ) *reinterpret_cast<float4 *>(sb[s] + r * kBS + cc) = rb[i];
         }
     };
     f32x4_t acc[NF][NC];
@@ -468,33 +470,56 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 
 // ------------------------------------------------- bf16 weight gradient (MFMA 16x16x32)
 // out[e, n, c] = sum over the segment's rows p ascending of a[p, n] b[p, c], a and b bf16
-// (b gathered through bperm / bk when given), FP32 accumulation and output. The MFMA takes
-// 8 consecutive K values (rows p) per lane, so each 32-row stage is staged transposed: a
-// thread loads 8 consecutive features of one row (16 bytes, as stored) and writes them to
-// the feature-major LDS tile [feature][row] (8 two-byte writes). A wave's 64 lanes cover
-// 32 rows x 2 groups of 8 features, so each write instruction fills two 64-byte row spans
-// that the 80-byte row pitch puts in different banks (a 64-row stage measured slower: its
-// registers and LDS allow fewer blocks per CU). Block: BN x BC outputs, four waves of
-// (BN/2) x (BC/2); MFMA operand A = a^T (rows n, K = p), B = b (K = p, columns c): lane l
-// reads 16 bytes of feature row n + l%16 (or c + l%16) at rows 8(l/16) .. 8(l/16)+7 of the
-// stage; the result lane l holds column c + l%16 of rows n + 4(l/16) + 0..3.
-constexpr int kWgRows = 32;                  // rows (K) per stage
-constexpr int kWgPitch = 80;                 // LDS bytes per feature row (64 + 16 pad)
+// (b gathered through bperm / bk when given), FP32 accumulation and output. A 32-row stage
+// of each operand goes to LDS as stored (row-major: row p, features contiguous): 16 lanes
+// copy one row's 256 bytes, 16 bytes each. The MFMA wants 8 consecutive K values (rows p)
+// per lane; gfx950's transposing LDS read (ds_read_b64_tr_b16) delivers them: within each
+// 16-lane group, lane s names 4 consecutive features of one row, and lane i receives, in
+// slot j, the element that lane 4j + i/4 named at position i%4. With lane s of group g
+// naming row 8g + j0 + s/4 (j0 = 0, then 4) at features f0 + 4(s%4) .. +3, lane i gets
+// feature f0 + i at rows 8g + j0 + 0..3: two reads give the MFMA operand of feature f0 + i,
+// K = rows 8g .. 8g + 7 of the stage -- the same operand values, in the same K positions,
+// as a feature-major staging, so the results are the same bits.
+// LDS tile: 32 rows x 288-byte pitch (256 + 32); byte column b of row r lives at
+// b ^ 128 * bit3(r), so the 16 rows one read touches (8g + 0..3 for g = 0..3) fall on
+// distinct 32-byte bank groups within each 256-byte window.
+// Block: BN x BC outputs, four waves of (BN/2) x (BC/2); the result lane l holds column
+// c + l%16 of rows n + 4(l/16) + 0..3.
+#ifndef MOE_WG_ROWS
+#define MOE_WG_ROWS 32                       // rows (K) per stage
+#endif
+#ifndef MOE_WG_TILE
+#define MOE_WG_TILE 256, 256, 4, 2           // BN, BC, waves along n, waves along c
+#endif
 
-template <int BN, int BC>
-__global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restrict__ a,
-                                                         const uint16_t *__restrict__ b,
-                                                         const int32_t *__restrict__ bperm,
-                                                         int bk, int64_t bT,
-                                                         const int32_t *__restrict__ off,
-                                                         int64_t nrows, int N, int C, int nbn,
-                                                         int nbc, float *__restrict__ out) {
-    constexpr int WN = BN / 2, WC = BC / 2, NF = WN / 16, NC = WC / 16;
-    constexpr int AL = kWgRows * BN / 8 / 256, BL = kWgRows * BC / 8 / 256;  // loads / thread
-    static_assert(AL >= 1 && BL >= 1, "tile too small for 256 threads");
-    static_assert(BN == 128 && BC == 128 && kWgRows == 32, "load mapping: 16 groups x 32 rows");
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][BN * kWgPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][BC * kWgPitch];
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t lds_tr_operand(const uint8_t *p_lo, const uint8_t *p_hi) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(p_lo));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t *)(p_hi));
+    typedef short s16x8_t __attribute__((ext_vector_type(8)));
+    const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int BN, int BC, int WNW, int WCW, int kWgRows>
+__global__ __launch_bounds__(64 * WNW * WCW) void wgrad_bf16_kernel(
+    const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+    const int32_t *__restrict__ bperm, int bk, int64_t bT, const int32_t *__restrict__ off,
+    int64_t nrows, int N, int C, int nbn, int nbc, float *__restrict__ out) {
+    constexpr int NT = 64 * WNW * WCW;                    // threads
+    constexpr int WN = BN / WNW, WC = BC / WCW, NF = WN / 16, NC = WC / 16;
+    constexpr int PA = 2 * BN + 32, PB = 2 * BC + 32;     // LDS row pitches (bytes)
+    constexpr int LA = BN / 8, LB = BC / 8;               // 16-byte chunks per row
+    constexpr int AL = kWgRows * LA / NT, BL = kWgRows * LB / NT;   // loads per thread
+    static_assert(AL >= 1 && BL >= 1 && kWgRows * LA % NT == 0 && kWgRows * LB % NT == 0,
+                  "whole rows per load round");
+    static_assert(NF >= 1 && NC >= 1 && kWgRows % 32 == 0 && BN % 128 == 0 && BC % 128 == 0,
+                  "tile shape");
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kWgRows * PA];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kWgRows * PB];
     const int per_e = nbn * nbc;
     const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
     const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
@@ -504,12 +529,13 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restr
         r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
     }
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wn = wv & 1, wc = wv >> 1;
+    const int wn = wv % WNW, wc = wv / WNW;
+    // copy mapping: element q = tid + NT i is row q / L, features 8 (q % L) .. + 7
     u32x4_t ra[AL], rb[BL];
     auto load = [&](int64_t p0) {
 #pragma unroll
         for (int i = 0; i < AL; ++i) {
-            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            const int q = tid + NT * i, p = q / LA, g = q % LA;
             const int64_t row = p0 + p;
             ra[i] = u32x4_t{0u, 0u, 0u, 0u};
             if (row < r1)
@@ -517,7 +543,7 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restr
         }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
-            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
+            const int q = tid + NT * i, p = q / LB, g = q % LB;
             const int64_t row = p0 + p;
             rb[i] = u32x4_t{0u, 0u, 0u, 0u};
             if (row < r1) {
@@ -530,23 +556,13 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restr
     auto store = [&](int s) {
 #pragma unroll
         for (int i = 0; i < AL; ++i) {
-            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
-            uint8_t *d = sa[s] + (8 * g) * kWgPitch + 2 * p;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t w = ra[i][j >> 1];
-                *reinterpret_cast<uint16_t *>(d + j * kWgPitch) = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffff));
-            }
+            const int q = tid + NT * i, p = q / LA, g = q % LA;
+            *reinterpret_cast<u32x4_t *>(sa[s] + p * PA + ((16 * g) ^ (((p >> 3) & 1) << 7))) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
-            const int q = tid + 256 * i, p = q % kWgRows, g = q / kWgRows;
-            uint8_t *d = sb[s] + (8 * g) * kWgPitch + 2 * p;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t w = rb[i][j >> 1];
-                *reinterpret_cast<uint16_t *>(d + j * kWgPitch) = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffff));
-            }
+            const int q = tid + NT * i, p = q / LB, g = q % LB;
+            *reinterpret_cast<u32x4_t *>(sb[s] + p * PB + ((16 * g) ^ (((p >> 3) & 1) << 7))) = rb[i];
         }
     };
     f32x4_t acc[NF][NC];
@@ -555,6 +571,10 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restr
 #pragma unroll
         for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int r16 = lane & 15, g4 = lane >> 4;
+    // transposing reads: this lane names row 8 g4 + r16/4 (+4), features 4 (r16 % 4) + 0..3
+    // of the fragment; rows 8 g4 .. 8 g4 + 7 share bit 3, hence one swizzle per lane
+    const int tr_ra = (8 * g4 + (r16 >> 2)) * PA, tr_rb = (8 * g4 + (r16 >> 2)) * PB;
+    const int tr_col = 8 * (r16 & 3), tr_sw = (g4 & 1) << 7;
     const int64_t nk = (r1 - r0 + kWgRows - 1) / kWgRows;
     if (nk > 0) {
         load(r0);
@@ -564,16 +584,20 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(const uint16_t *__restr
             const int s = (int)(kt & 1);
             if (kt + 1 < nk) load(r0 + (kt + 1) * kWgRows);
 #pragma unroll
-            for (int kk = 0; kk < kWgRows / 32; ++kk) {
+            for (int kk = 0; kk < kWgRows / 32; ++kk) {     // 32-row MFMA K-steps, in order
                 bf16x8_t av[NF], bv[NC];
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    av[f] = *reinterpret_cast<const bf16x8_t *>(
-                        sa[s] + (wn * WN + f * 16 + r16) * kWgPitch + 64 * kk + 16 * g4);
+                for (int f = 0; f < NF; ++f) {
+                    const uint8_t *p = sa[s] + tr_ra + 32 * kk * PA +
+                                       ((2 * (wn * WN + f * 16) + tr_col) ^ tr_sw);
+                    av[f] = lds_tr_operand(p, p + 4 * PA);
+                }
 #pragma unroll
-                for (int t = 0; t < NC; ++t)
-                    bv[t] = *reinterpret_cast<const bf16x8_t *>(
-                        sb[s] + (wc * WC + t * 16 + r16) * kWgPitch + 64 * kk + 16 * g4);
+                for (int t = 0; t < NC; ++t) {
+                    const uint8_t *p = sb[s] + tr_rb + 32 * kk * PB +
+                                       ((2 * (wc * WC + t * 16) + tr_col) ^ tr_sw);
+                    bv[t] = lds_tr_operand(p, p + 4 * PB);
+                }
 #pragma unroll
                 for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -675,10 +699,12 @@ hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *d
 hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
                              int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
                              int C, float *out, hipStream_t s) {
-    constexpr int BN = 128, BC = 128;
+    constexpr int tile[4] = {MOE_WG_TILE};
+    constexpr int BN = tile[0], BC = tile[1], WNW = tile[2], WCW = tile[3], KR = MOE_WG_ROWS;
     if (N % 8 || C % 8 || nseg < 1) return hipErrorInvalidValue;
     const int nbn = (N + BN - 1) / BN, nbc = (C + BC - 1) / BC;
-    wgrad_bf16_kernel<BN, BC><<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(256), 0, s>>>(
+    wgrad_bf16_kernel<BN, BC, WNW, WCW, KR>
+        <<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(64 * WNW * WCW), 0, s>>>(
         static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), bperm, bk, bT, off,
         nrows, N, C, nbn, nbc, out);
     return hipGetLastError();
@@ -797,9 +823,19 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
 
 hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *x, float *dwr,
                                hipStream_t s) {
-    if (dm.E % 4 == 0)
-        return launch_wgrad(1, dl, x, dm.dtype == MOE_BF16, nullptr, 1, dm.T, nullptr, dm.T,
-                            dm.E, dm.d, dwr, s);
+    if (dm.E % 4 == 0 && dm.d % 4 == 0) {
+        // one segment of T rows and only E x d outputs: 32 x 32 tiles give E d / 1024
+        // blocks (each output is the same MFMA chain over ascending rows at any tile size)
+        const int nbn = (dm.E + 31) / 32, nbc = (dm.d + 31) / 32;
+        const dim3 grid((unsigned)((int64_t)nbn * nbc));
+        if (dm.dtype == MOE_BF16)
+            wgrad_kernel<true, 32, 32><<<grid, dim3(256), 0, s>>>(dl, x, nullptr, 1, dm.T, nullptr,
+                                                                  dm.T, dm.E, dm.d, nbn, nbc, dwr);
+        else
+            wgrad_kernel<false, 32, 32><<<grid, dim3(256), 0, s>>>(dl, x, nullptr, 1, dm.T, nullptr,
+                                                                   dm.T, dm.E, dm.d, nbn, nbc, dwr);
+        return hipGetLastError();
+    }
     const int64_t n = (int64_t)dm.E * dm.d;
     router_wgrad_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
         dl, x, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dwr);
