@@ -352,11 +352,11 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const float *__restrict__ ac
 // a[p, n] b[p, c]; a FP32 [rows, N], b [rows, C] (bf16 or FP32; row of b = bperm[p] / bk
 // when bperm is given: the gathered token rows), out FP32 [E, N, C]. Segment e = rows
 // [off[e], off[e+1]) (off NULL: one segment of nrows rows). Block: BN x BC outputs of one
-// expert, four waves of (BN/2) x (BC/2); K = the segment's rows in stages of kKc, the tail
+// expert, four waves of (BN/2) x (BC/2); K = the segment's rows in stages of KC, the tail
 // zero-filled. MFMA operand A = a (rows n, K = p), B = b (K = p, columns c): lane l holds
 // a[p0 + l/16][n + l%16] and b[p0 + l/16][c + l%16]; the result lane l holds column
 // c + l%16 of rows n + 4(l/16) + 0..3.
-template <bool kBBF16, int BN, int BC>
+template <bool kBBF16, int BN, int BC, int KC = kKc>
 __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
                                                     const void *__restrict__ b,
                                                     const int32_t *__restrict__ bperm, int bk,
@@ -365,8 +365,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
                                                     int nbc, float *__restrict__ out) {
     constexpr int WN = BN / 2, WC = BC / 2, NF = WN / 16, NC = WC / 16;
     constexpr int kAS = BN + 4, kBS = BC + 4;
-    __shared__ float sa[2][kKc * kAS];
-    __shared__ float sb[2][kKc * kBS];
+    __shared__ float sa[2][KC * kAS];
+    __shared__ float sb[2][KC * kBS];
     const int per_e = nbn * nbc;
     const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
     const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
@@ -377,9 +377,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
     }
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wn = wv & 1, wc = wv >> 1;
-    // float4 copies per thread and stage (threads past kKc * BN / 4 copy nothing)
-    constexpr int AR = (kKc * BN / 4 + 255) / 256, BR = (kKc * BC / 4 + 255) / 256;
-    constexpr int AQ = kKc * BN / 4, BQ = kKc * BC / 4;
+    // float4 copies per thread and stage (threads past KC * BN / 4 copy nothing)
+    constexpr int AR = (KC * BN / 4 + 255) / 256, BR = (KC * BC / 4 + 255) / 256;
+    constexpr int AQ = KC * BN / 4, BQ = KC * BC / 4;
     static_assert(NF >= 1 && NC >= 1, "tile too small");
     float4 ra[AR], rb[BR];
     auto load = [&](int64_t p0) {
@@ -428,16 +428,16 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 #pragma unroll
         for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int64_t nk = (r1 - r0 + kKc - 1) / kKc;
+    const int64_t nk = (r1 - r0 + KC - 1) / KC;
     if (nk > 0) {
         load(r0);
         store(0);
         __syncthreads();
         for (int64_t kt = 0; kt < nk; ++kt) {
             const int s = (int)(kt & 1);
-            if (kt + 1 < nk) load(r0 + (kt + 1) * kKc);
+            if (kt + 1 < nk) load(r0 + (kt + 1) * KC);
 #pragma unroll
-            for (int kk = 0; kk < kKc; kk += 4) {
+            for (int kk = 0; kk < KC; kk += 4) {
                 float av[NF], bv[NC];
 #pragma unroll
                 for (int f = 0; f < NF; ++f) av[f] = sa[s][(kk + g4) * kAS + wn * WN + f * 16 + r16];
@@ -828,12 +828,13 @@ hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *
         // blocks (each output is the same MFMA chain over ascending rows at any tile size)
         const int nbn = (dm.E + 31) / 32, nbc = (dm.d + 31) / 32;
         const dim3 grid((unsigned)((int64_t)nbn * nbc));
+        // and 64-row stages: a quarter of the barriers on the T-long chain
         if (dm.dtype == MOE_BF16)
-            wgrad_kernel<true, 32, 32><<<grid, dim3(256), 0, s>>>(dl, x, nullptr, 1, dm.T, nullptr,
-                                                                  dm.T, dm.E, dm.d, nbn, nbc, dwr);
+            wgrad_kernel<true, 32, 32, 64><<<grid, dim3(256), 0, s>>>(
+                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dwr);
         else
-            wgrad_kernel<false, 32, 32><<<grid, dim3(256), 0, s>>>(dl, x, nullptr, 1, dm.T, nullptr,
-                                                                   dm.T, dm.E, dm.d, nbn, nbc, dwr);
+            wgrad_kernel<false, 32, 32, 64><<<grid, dim3(256), 0, s>>>(
+                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dwr);
         return hipGetLastError();
     }
     const int64_t n = (int64_t)dm.E * dm.d;
