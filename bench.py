@@ -365,7 +365,7 @@ def backward_report(L, dims, inp, K, hip, stream):
             "tflops_overall": round(flops / (ms16 * 1e-3) / 1e12, 2),
             "frac_bf16_peak_overall": round(flops / (ms16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "dy and d_gu rounded once to bf16; bf16 MFMA for every gradient GEMM; "
-                    "includes the per-call transposes of w13 and w2"}
+                    "the data gradients read w2 and w13 K-major as stored"}
     assert int(fb["d_err"].item()) == 0
     return out
 

@@ -455,12 +455,10 @@ typedef struct moe_backward_args {
     /* MOE_F32 (0): the gradient GEMMs take FP32 operands, as above. MOE_BF16 (bf16 layers
      * only): d_y and d_gu are rounded once to bf16 where they are formed (RNE; the buffers
      * then hold bf16 [T*k,d] and [T*k,2I]), and every gradient GEMM consumes the rounded
-     * values on bf16 MFMA: dh and d_xp through the forward's grouped GEMM with the expert
-     * weights transposed into w2_t [E,I,d] and w13_t [E,d,2I] (dtype; caller buffers the
-     * library fills on every call), d_w2 and d_w13 on a bf16 weight-gradient kernel. */
+     * values on bf16 MFMA: dh and d_xp through the forward's grouped GEMM reading w2 and
+     * w13 as stored (K-major for these products), d_w2 and d_w13 on a bf16 weight-gradient
+     * kernel. */
     int32_t grad_dtype;
-    void *w13_t;
-    void *w2_t;
 } moe_backward_args;
 moe_status moe_backward(const moe_dims *dims, const moe_backward_args *args, void *stream);
 

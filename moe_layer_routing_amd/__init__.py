@@ -72,8 +72,7 @@ class BackwardArgs(ctypes.Structure):
                [(n, _P) for n in ("d_x", "d_w13", "d_w2", "d_topk_w", "d_logits", "d_w_router",
                                   "d_x_router", "d_y", "gu", "d_h", "d_gu", "d_xp",
                                   "workspace")] + \
-               [("workspace_bytes", ctypes.c_size_t), ("grad_dtype", ctypes.c_int32),
-                ("w13_t", _P), ("w2_t", _P)]
+               [("workspace_bytes", ctypes.c_size_t), ("grad_dtype", ctypes.c_int32)]
 
 
 # exported symbols and their signatures (argument types after the dims pointer)
@@ -344,8 +343,7 @@ def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=
 def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.0,
              stream=None, grad_dtype: int = MOE_F32):
     """Run moe_backward. ``bufs`` maps BackwardArgs field names to tensors (or None);
-    grad_dtype MOE_BF16 selects bf16 gradient operands (then d_y / d_gu are bf16 and w13_t,
-    w2_t are required)."""
+    grad_dtype MOE_BF16 selects bf16 gradient operands (then d_y / d_gu are bf16)."""
     a = BackwardArgs()
     for name, _ in BackwardArgs._fields_:
         if name in ("routed_scale", "workspace", "workspace_bytes", "grad_dtype"):
@@ -362,7 +360,7 @@ def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.
 def alloc_backward_buffers(dims: Dims, device="cuda", router: bool = True,
                            grad_dtype: int = MOE_F32) -> dict:
     """Allocate every output and intermediate of moe_backward for ``dims`` (with bf16
-    gradient operands: bf16 d_y / d_gu and the transposed-weight buffers)."""
+    gradient operands, d_y / d_gu are bf16)."""
     T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.inter
     A = T * k
     f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=device)
@@ -370,10 +368,6 @@ def alloc_backward_buffers(dims: Dims, device="cuda", router: bool = True,
         if grad_dtype == MOE_BF16 else f
     b = dict(d_x=f(T, d), d_w13=f(E, 2 * I, d), d_w2=f(E, d, I), d_topk_w=f(T, k),
              d_y=g(A, d), gu=f(A, 2 * I), d_h=f(A, I), d_gu=g(A, 2 * I), d_xp=f(A, d))
-    if grad_dtype == MOE_BF16:
-        sd = storage_dtype(dims.dtype)
-        b["w13_t"] = torch.empty((E, d, 2 * I), dtype=sd, device=device)
-        b["w2_t"] = torch.empty((E, I, d), dtype=sd, device=device)
     if router:
         b.update(d_logits=f(T, E), d_w_router=f(E, d), d_x_router=f(T, d))
     return b

@@ -492,8 +492,6 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 #define MOE_WG_TILE 256, 256, 4, 2           // BN, BC, waves along n, waves along c
 #endif
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ bf16x8_t lds_tr_operand(const uint8_t *p_lo, const uint8_t *p_hi) {
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4_t *)(p_lo));
@@ -624,41 +622,6 @@ __global__ __launch_bounds__(64 * WNW * WCW) void wgrad_bf16_kernel(
     }
 }
 
-// ------------------------------------------------------------- per-expert transpose
-// dst[e, c, r] = src[e, r, c] for 2-byte elements, through a 64 x 64 LDS tile: each thread
-// reads 8 consecutive elements of a source row (16 bytes) and writes 8 consecutive elements
-// of a destination row (16 bytes, gathered from 8 tile rows). R and C multiples of 64.
-__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ src,
-                                                          uint16_t *__restrict__ dst, int R,
-                                                          int Cn, int nbr, int nbc) {
-    __shared__ uint16_t tile[64][64 + 2];
-    const int per_e = nbr * nbc;
-    const int64_t e = blockIdx.x / per_e;
-    const int rem = blockIdx.x % per_e;
-    const int r0 = (rem / nbc) * 64, c0 = (rem % nbc) * 64;
-    const uint16_t *sp = src + e * (int64_t)R * Cn;
-    uint16_t *dp = dst + e * (int64_t)R * Cn;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = tid + 256 * i, r = q >> 3, c8 = (q & 7) * 8;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sp + (int64_t)(r0 + r) * Cn + c0 + c8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            tile[r][c8 + j] = (uint16_t)((j & 1) ? (v[j >> 1] >> 16) : (v[j >> 1] & 0xffff));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = tid + 256 * i, c = q >> 3, r8 = (q & 7) * 8;
-        u32x4_t v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = (uint32_t)tile[r8 + 2 * j][c] | ((uint32_t)tile[r8 + 2 * j + 1][c] << 16);
-        *reinterpret_cast<u32x4_t *>(dp + (int64_t)(c0 + c) * R + r0 + r8) = v;
-    }
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------------ launchers
@@ -710,14 +673,6 @@ hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32
     return hipGetLastError();
 }
 
-// dst[e] = src[e]^T for E matrices of R x C 2-byte elements.
-hipError_t launch_transpose16(const void *src, void *dst, int E, int R, int C, hipStream_t s) {
-    if (R % 64 || C % 64) return hipErrorInvalidValue;
-    const int nbr = R / 64, nbc = C / 64;
-    transpose16_kernel<<<dim3((unsigned)((int64_t)E * nbr * nbc)), dim3(256), 0, s>>>(
-        static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), R, C, nbr, nbc);
-    return hipGetLastError();
-}
 
 hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
                          const float *dxr, float *dx, hipStream_t s) {

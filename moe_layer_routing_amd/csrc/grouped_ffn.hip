@@ -338,23 +338,40 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // one wait + one s_barrier per stage.
 __device__ __forceinline__ int chunk_swizzle8(int r) { return r & 7; }
 
+// K-major weight stages: the 16 K-rows one transposing read touches (8g + 0..3, g = 0..3)
+// get distinct 32-byte bank groups within each half-wave (chunk XOR 2 * (bits 0-1 and 3 of
+// the row), limited to the row's chunks).
+template <int CPR>
+__device__ __forceinline__ int kmajor_swz(int r) {
+    return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) & (CPR - 1);
+}
+
 template <int NBW, int NW>
 __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase,
                                              const uint8_t *abase, const uint32_t (&off)[NBW],
-                                             uint32_t is_act_mask, int kt, int wv) {
+                                             uint32_t is_act_mask, int kt, uint32_t wstride,
+                                             int wv) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass never runs this; it cannot parse the builtin
-    const uint32_t ko = (uint32_t)kt * 128u;
+    const uint32_t ako = (uint32_t)kt * 128u, wko = (uint32_t)kt * wstride;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        const uint8_t *base = ((is_act_mask >> i) & 1u) ? abase : wbase;
+        const bool is_act = (is_act_mask >> i) & 1u;
         __builtin_amdgcn_global_load_lds(
-            base + off[i] + ko,
+            (is_act ? abase : wbase) + off[i] + (is_act ? ako : wko),
             (__attribute__((address_space(3))) void *)(slot + (wv + i * NW) * 1024), 16, 0, 0);
     }
 #endif
 }
 
-template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS>
+// kKMajor (plain mode only): the weights are stored K-major, wgt[e][k][n] (n contiguous),
+// as the data-gradient GEMMs of the backward read w2 and w13. A stage's 64 K-rows of the
+// BW features are copied as stored (2 BW bytes per K-row, 16-byte chunks swizzled by
+// kmajor_swz(k-row)), and the weight fragments come from gfx950's transposing LDS read
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives in slot j the element that
+// lane 4j + i/4 named at position i%4, so lane s naming K-row 8g + s/4 (then + 4) at
+// features f + 4(s%4) hands lane i feature f + i at K-rows 8g + 0..7 -- the operand a
+// row-major weight tile gives, in the same K positions, hence the same bits.
+template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS, bool kKMajor = false>
 __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
@@ -372,6 +389,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     static_assert(NBLK % NW == 0 && NBW <= 32 && NFh >= 1 && NT >= 1, "bad tile shape");
     static_assert(BW % 16 == 0 && (BW / 2) % 16 == 0, "16-row fragments");
     static_assert(NS >= 2 && NBW * (NS - 2) < 64, "ring depth");
+    static_assert(!kKMajor || (!kGateUp && BW >= 64 && BW <= 512), "K-major: plain mode");
+    constexpr int kCPR = BW / 8;                        // K-major: 16-byte chunks per K-row
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStageBytes];
 
@@ -395,7 +414,14 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     for (int i = 0; i < NBW; ++i) {
         const int row = (wv + i * NW) * 8 + rb;
         const int chunk = (lane & 7) ^ chunk_swizzle8(row);
-        if (row < BW) {
+        if (kKMajor && row < BW) {
+            // instruction block bi moves K-rows bi * (64 / kCPR) + lane / kCPR of the stage;
+            // lane chunk position p holds logical chunk p ^ kmajor_swz(k-row)
+            const int bi = wv + i * NW;
+            const int kr = bi * (64 / kCPR) + lane / kCPR;
+            const int lc = (lane % kCPR) ^ kmajor_swz<kCPR>(kr);
+            off[i] = (uint32_t)kr * (uint32_t)N * 2u + (uint32_t)min(n0 + 8 * lc, N - 8) * 2u;
+        } else if (row < BW) {
             int grow;
             if (kGateUp) {
                 const int half = row >= BW / 2;
@@ -428,11 +454,27 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto kstep = [&](const uint8_t *sb) {
+    // K-major weight fragment f of K-step kk: this lane names K-row 32 kk + 8 g4 + r16/4
+    // (then + 4) at features wrow(f) + 4 (r16 % 4) .. + 3
+    const int kmr = 8 * g4 + (r16 >> 2);
+    const int kms = kmajor_swz<kCPR>(kmr);           // equal for K-rows kmr and kmr + 4
+    auto kmajor_frag = [&](const uint8_t *stage, int kk, int f) {
+        const int byte = 2 * wrow(f) + 8 * (r16 & 3);
+        const int pb = (((byte >> 4) ^ kms) << 4) | (byte & 15);
+        const uint8_t *p = stage + (32 * kk + kmr) * (2 * BW) + pb;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t *)(p));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t *)(p + 4 * (2 * BW)));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto kstep = [&](const uint8_t *sb, const uint8_t *stage, int kk) {
         bf16x8_t a[NF], b[NT];
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-            a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 3) * 1024);
+        for (int f = 0; f < NF; ++f) {
+            if constexpr (kKMajor) a[f] = kmajor_frag(stage, kk, f);
+            else a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 3) * 1024);
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
@@ -454,10 +496,13 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     // a wave whose features or tokens are all padding issues no MFMAs (loop-invariant)
     const bool active = (n0 + wf * kWaveRows < N) && (wt * (BT / WT) < nrows);
     const int nk = K >> 6;
+    // bytes one stage advances in the weights: 64 K-values of a row, or 64 K-rows
+    const uint32_t wstride = kKMajor ? 64u * (uint32_t)N * 2u : 128u;
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
         if (st < nk)
-            dma_stage128<NBW, NW>(ring + st * kStageBytes, wbase, abase, off, is_act, st, wv);
+            dma_stage128<NBW, NW>(ring + st * kStageBytes, wbase, abase, off, is_act, st, wstride,
+                                  wv);
     if (NS - 2 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
     else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
@@ -465,10 +510,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
         uint8_t *cur = ring + (kt % NS) * kStageBytes;
         if (kt + NS - 1 < nk)
             dma_stage128<NBW, NW>(ring + ((kt + NS - 1) % NS) * kStageBytes, wbase, abase, off,
-                                  is_act, kt + NS - 1, wv);
+                                  is_act, kt + NS - 1, wstride, wv);
         if (active) {
-            kstep(cur + lane_off0);
-            kstep(cur + lane_off1);
+            kstep(cur + lane_off0, cur, 0);
+            kstep(cur + lane_off1, cur, 1);
         }
         if (kt + 1 < nk) {
             if (kt + NS - 1 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
@@ -536,14 +581,16 @@ struct IsDma128<C, std::void_t<decltype(C::kDma128)>> : std::true_type {};
 
 
 // gperm != nullptr: activation rows are gathered (token perm[p] / gk of act, gT rows).
-template <bool kBF16, bool kGateUp, class C>
+// kKMajor: weights stored wgt[e][k][n] (bf16 DMA kernel only).
+template <bool kBF16, bool kGateUp, class C, bool kKMajor = false>
 hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_t *tiles,
                        int64_t mtiles, int K, int N, hipStream_t s,
                        const int32_t *gperm = nullptr, int gk = 1, int64_t gT = 0) {
     constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
     const int nft = (N + feat - 1) / feat;
+    static_assert(!kKMajor || (IsDma128<C>::value && kBF16 && !kGateUp), "K-major weights");
     if constexpr (IsDma128<C>::value && kBF16) {
-        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE, C::NS>
+        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE, C::NS, kKMajor>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
                 K, N, nft, gperm, gk, gT);
@@ -597,6 +644,12 @@ hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, 
 #define MOE_FFN_HUGE_CFG13 Dma128Cfg<256, 256, 4, 4, 2, 4>
 #define MOE_FFN_HUGE_CFG2 Dma128Cfg<256, 256, 2, 4>
 #endif
+
+using PLAIN_CFG16 = Dma128Cfg<64, 16, 2, 1, 6>;
+using PLAIN_CFG32 = Dma128Cfg<64, 32, 2, 1, 6>;
+using PLAIN_CFG64 = Dma128Cfg<128, 64, 2, 2, 4>;
+using PLAIN_LARGE = MOE_FFN_LARGE_CFG2;
+using PLAIN_HUGE = MOE_FFN_HUGE_CFG2;
 
 template <bool kBF16>
 hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const int32_t *gperm,
@@ -654,31 +707,32 @@ hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, 
 // reproduces the forward's gate and up values bit for bit.
 hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
                              const void *wgt, float *out, int N, const int32_t *offsets,
-                             const Workspace &ws, hipStream_t s, int K) {
+                             const Workspace &ws, hipStream_t s, int K, bool kmajor) {
     const int64_t A = dm.T * dm.k;
     if (A == 0) return hipGetLastError();
     if (K == 0) K = dm.d;
+    if (kmajor && dm.dtype != MOE_BF16) return hipErrorInvalidValue;
     const int bt = select_tile_m(dm);
     const int64_t cap = max_m_tiles(A, dm.E, bt);
     build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
     const bool b = dm.dtype == MOE_BF16;
+#define MOE_PLAIN(CFG)                                                                          \
+    (kmajor ? launch_gemm<true, false, CFG, true>(act, wgt, out, ws.tiles, cap, K, N, s, gperm,  \
+                                                  dm.k, dm.T)                                   \
+     : b    ? launch_gemm<true, false, CFG>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k,  \
+                                            dm.T)                                               \
+            : launch_gemm<false, false, CFG>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, \
+                                             dm.T))
+    hipError_t e;
     switch (bt) {
-    case 16:
-        return b ? launch_gemm<true, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<64, 16, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
-    case 32:
-        return b ? launch_gemm<true, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<64, 32, 2, 1, 6>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
-    case 64:
-        return b ? launch_gemm<true, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, Dma128Cfg<128, 64, 2, 2, 4>>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
-    case 128:
-        return b ? launch_gemm<true, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, MOE_FFN_LARGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
-    default:
-        return b ? launch_gemm<true, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T)
-                 : launch_gemm<false, false, MOE_FFN_HUGE_CFG2>(act, wgt, out, ws.tiles, cap, K, N, s, gperm, dm.k, dm.T);
+    case 16: e = MOE_PLAIN(PLAIN_CFG16); break;
+    case 32: e = MOE_PLAIN(PLAIN_CFG32); break;
+    case 64: e = MOE_PLAIN(PLAIN_CFG64); break;
+    case 128: e = MOE_PLAIN(PLAIN_LARGE); break;
+    default: e = MOE_PLAIN(PLAIN_HUGE); break;
     }
+#undef MOE_PLAIN
+    return e;
 }
 
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,

@@ -448,10 +448,7 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     if (a->w_router) MOE_REQUIRE(a->d_logits && a->d_x_router, MOE_E_NULLPTR);
     MOE_REQUIRE(a->grad_dtype == MOE_F32 || a->grad_dtype == MOE_BF16, MOE_E_DTYPE);
     const bool g16 = a->grad_dtype == MOE_BF16;
-    if (g16) {
-        MOE_REQUIRE(dims->dtype == MOE_BF16, MOE_E_DTYPE);
-        MOE_REQUIRE(a->w13_t && a->w2_t, MOE_E_NULLPTR);
-    }
+    if (g16) MOE_REQUIRE(dims->dtype == MOE_BF16, MOE_E_DTYPE);
     if (!a->x_perm) {
         const int64_t x_bytes = dims->T * (int64_t)dims->d * (dims->dtype == MOE_BF16 ? 2 : 4);
         MOE_REQUIRE(x_bytes < (int64_t(1) << 32), MOE_E_SHAPE);
@@ -474,16 +471,15 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     const int32_t *xperm = a->x_perm ? nullptr : a->perm;
     const int64_t xrows = a->x_perm ? A : dims->T;
     if (g16) {
-        e = launch_transpose16(a->w2, a->w2_t, dims->E, d, I, s);
-        if (e != hipSuccess) return MOE_E_LAUNCH;
-        e = launch_transpose16(a->w13, a->w13_t, dims->E, 2 * I, d, s);
-        if (e != hipSuccess) return MOE_E_LAUNCH;
-        e = launch_plain_gemm(*dims, a->d_y, nullptr, a->w2_t, a->d_h, I, a->offsets, ws, s, d);
+        // data gradients on the forward's DMA GEMM with the weights read K-major as stored:
+        // dh = dy w2[e] (K = d rows of w2), dxp = dgu w13[e] (K = 2I rows of w13)
+        e = launch_plain_gemm(*dims, a->d_y, nullptr, a->w2, a->d_h, I, a->offsets, ws, s, d,
+                              /*kmajor=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, true, s);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        e = launch_plain_gemm(*dims, a->d_gu, nullptr, a->w13_t, a->d_xp, d, a->offsets, ws, s,
-                              2 * I);
+        e = launch_plain_gemm(*dims, a->d_gu, nullptr, a->w13, a->d_xp, d, a->offsets, ws, s,
+                              2 * I, /*kmajor=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         e = launch_wgrad_bf16(dims->E, a->d_y, a->h, nullptr, 1, A, a->offsets, A, d, I,
                               a->d_w2, s);

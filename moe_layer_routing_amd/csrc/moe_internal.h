@@ -21,6 +21,7 @@ constexpr int kMaxRanks = 16;         // ranks of the emulated expert-parallel o
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // bfloat16 widening (exact) and narrowing (round to nearest, ties to even; NaN kept quiet).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -148,12 +149,14 @@ hipError_t launch_shared_ffn(const moe_dims &dm, int R, int inter_shared, const 
                              const void *w13s, const void *w2s, void *h_s, float *y_s,
                              void *workspace, hipStream_t s);
 // Grouped-GEMM helpers shared with the backward: the token-tile list for tile height bt,
-// and the plain FP32-output GEMM (the forward's down launch) with N features over K = d.
+// and the plain FP32-output GEMM (the forward's down launch) with N features over K = d;
+// kmajor (bf16 only): the weights are stored wgt[e][k][n] instead of wgt[e][n][k].
 hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, int64_t cap,
                               int32_t *tiles, hipStream_t s);
 hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
                              const void *wgt, float *out, int N, const int32_t *offsets,
-                             const Workspace &ws, hipStream_t s, int K = 0);
+                             const Workspace &ws, hipStream_t s, int K = 0,
+                             bool kmajor = false);
 // Backward steps (backward.hip).
 hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float *y,
                               const int32_t *inv, const float *topk_w, float scale, void *dy,
@@ -163,7 +166,6 @@ hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *d
 hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
                              int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
                              int C, float *out, hipStream_t s);
-hipError_t launch_transpose16(const void *src, void *dst, int E, int R, int C, hipStream_t s);
 hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
                          const float *dxr, float *dx, hipStream_t s);
 hipError_t launch_router_bwd(const moe_dims &dm, const float *logits, const float *dw,

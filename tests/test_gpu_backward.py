@@ -157,7 +157,7 @@ G16_CASES = [
                                                           f"I{c[4]}_{c[5]}")
 def test_backward_bf16_operands_parity(case):
     """bf16 gradient operands: dy and d_gu rounded once where they are formed, the data
-    gradients on the forward's bf16 GEMM (transposed weights), the weight gradients on the
+    gradients on the forward's bf16 GEMM (weights read K-major), the weight gradients on the
     bf16 weight-gradient kernel; against the oracle with the same rounding points. dy is
     bitwise; d_gu within one bf16 rounding (its FP32 input dh is summed in another order);
     every other gradient within 1e-3 * max(1, |ref|)."""
@@ -173,10 +173,6 @@ def test_backward_bf16_operands_parity(case):
     fb, bb = _run(L, inp, dout, scale, slot, xp, g16=True)
     be, br = _oracle(L, fb, dout, scale, slot, g16=True)
     assert host(bb["d_y"]).tobytes() == W.f32_to_bf16_bits(be["dy"]).tobytes()
-    # the weights' transposes are exact
-    w2t = host(bb["w2_t"]).transpose(0, 2, 1)
-    assert w2t.tobytes() == np.ascontiguousarray(host(fb["w2"])).tobytes()
-    assert host(bb["w13_t"]).transpose(0, 2, 1).tobytes() == host(fb["w13"]).tobytes()
     _close(as_f32(host(bb["d_gu"]), "bf16"), be["dgu"], "d_gu", tol=2.0 ** -7)
     for n, r in (("d_topk_w", be["dw"]), ("gu", be["gu"]), ("d_h", be["dh"]),
                  ("d_w2", be["dw2"]), ("d_logits", br["dl"]),
