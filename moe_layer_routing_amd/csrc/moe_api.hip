@@ -42,6 +42,8 @@ Workspace carve_workspace(const moe_dims &d, void *base) {
     w.blk_hist = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * std::max<int64_t>(nchunks, 1) * E));
     w.blk_whist = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * std::max<int64_t>(nchunks, 1) * E));
     w.tiles = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (1 + 3 * tiles)));
+    w.logit_part = reinterpret_cast<float *>(
+        take(T * E <= kChainSumMax ? sizeof(float) * kLogitChains * T * E : 1));
     w.total = off;
     return w;
 }
@@ -397,16 +399,24 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dims->T >= 1 && dims->T <= kSmallT && !a->seq_counts) {
-        // small batch: logits, then the whole routing tail (and the tile list) in one block
+        // small batch: router logits, then the whole routing tail (top-k, statistics,
+        // permutation, tile list) in one block. For the smallest batches the logits' 16
+        // K-chains run as separate waves (the router weights then stream through 4x as many
+        // CUs) and the tail adds the partials; past kChainSumMax partial values per chain
+        // that sum costs the single block more than the wider logits launch saves.
         float *logits = a->logits ? a->logits : ws.logits;
-        if (!replay) {
+        const bool chains = !replay && dims->T * dims->E <= kChainSumMax;
+        if (chains) {
+            e = launch_router_logit_chains(*dims, a->x, a->w_router, ws.logit_part, s);
+            if (e != hipSuccess) return MOE_E_LAUNCH;
+        } else if (!replay) {
             e = launch_router_logits(*dims, a->x, a->w_router, a->logit_bias, logits, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
         }
         e = launch_small_tail(*dims, logits, a->token_mult, a->idx_in, a->w_in, a->topk_idx,
                               a->topk_w, a->prob_mass, a->counts, a->offsets, a->perm, a->inv,
                               a->weighted_counts, ws.tiles, a->d_err, s, a->slot_of_expert,
-                              ro);
+                              ro, chains ? ws.logit_part : nullptr, a->logit_bias);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         if (a->x_perm) {
             e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);

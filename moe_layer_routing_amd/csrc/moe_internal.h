@@ -90,6 +90,7 @@ struct Workspace {
     int32_t *blk_hist;        // [nchunks, E] per-chunk expert histogram -> chunk offsets
     uint64_t *blk_whist;      // [nchunks, E] per-chunk multiplicity-weighted histogram
     int32_t *tiles;           // [1 + 3*max_tiles] grouped-GEMM tile list
+    float *logit_part;        // [16, T, E] router-logit chain partials, T * E <= 2048 only
     size_t total;
 };
 
@@ -191,19 +192,28 @@ int select_tile_m(const moe_dims &dm);
 // Router logits only (the first step of launch_route).
 hipError_t launch_router_logits(const moe_dims &dm, const void *x, const void *w_router,
                                 const float *bias, float *logits, hipStream_t s);
+// The router logits' kLogitChains K-chains as separate waves: part[c][t][e] (chain c's
+// partial, the same bits as inside launch_router_logits); launch_small_tail adds them.
+constexpr int kLogitChains = 16;
+constexpr int64_t kChainSumMax = 2048;    // T * E up to which the small-batch path uses them
+hipError_t launch_router_logit_chains(const moe_dims &dm, const void *x, const void *w_router,
+                                      float *part, hipStream_t s);
 // Token-major row gather x -> x_perm through inv (part of launch_permute).
 hipError_t launch_gather(const moe_dims &dm, const void *x, const int32_t *inv, void *x_perm,
                          hipStream_t s);
 // Routing tail of a small batch (1 <= T <= kSmallT) in one block: top-k from logits (or,
 // with idx_in, replay validation), probability mass, counts, offsets, weighted counts,
 // perm / inv, and the token-tile list for tile height select_tile_m(dm). Every output is
-// bitwise the one the multi-kernel steps produce for the same T.
+// bitwise the one the multi-kernel steps produce for the same T. With logit_part (router
+// mode), the block first forms logits[t][e] = (part[0] + ... + part[15]) + bias[e] in chain
+// order, as launch_router_logits does, and writes them to logits.
 hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
                              const int32_t *idx_in, const float *w_in, int32_t *topk_idx,
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
                              hipStream_t s, const int32_t *slot_map = nullptr,
-                             const RouteOpts &opts = RouteOpts());
+                             const RouteOpts &opts = RouteOpts(),
+                             const float *logit_part = nullptr, const float *bias = nullptr);
 
 }  // namespace moe

@@ -31,24 +31,24 @@ namespace {
 // MFMA operand mapping (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4f32): the A operand
 // rows are experts, the B operand columns are tokens; lane l feeds row/column l%16 and
 // K-slice l/16; the result lane l holds column l%16 and rows 4*(l/16) + 0..3.
-constexpr int kLogitSplit = 16;
+constexpr int kLogitSplit = kLogitChains;
+static_assert(kLogitSplit == 16, "16 K-chains per logit");
 
+// Chain `chain` of the logits of token tile tb (16 tokens) and expert tiles et0 .. et0+EPB-1:
+// K-steps chain, chain+16, ... accumulated in that order into acc (one MFMA per step and
+// tile; the operands of up to kGroup steps are loaded before their MFMAs so that the loads
+// overlap). Every kernel that forms logits runs this routine, so a chain's partial is the
+// same bits whichever launch computes it.
 template <bool kBF16, int EPB>
-__global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
-    const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
-    float *__restrict__ logits, int64_t T, int d, int E) {
-    const int n_et = (E + 15) >> 4;
-    const int n_eg = (n_et + EPB - 1) / EPB;
-    const int et0 = (int)(blockIdx.x % n_eg) * EPB;
-    const int64_t tb = (int64_t)(blockIdx.x / n_eg) * 16;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void logit_chain(const void *__restrict__ x_,
+                                            const void *__restrict__ wr_, int64_t T, int d,
+                                            int E, int64_t tb, int et0, int chain,
+                                            f32x4_t (&acc)[EPB]) {
+    const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int64_t t_row = min<int64_t>(tb + r, T - 1);
-    f32x4_t acc[EPB];
 #pragma unroll
     for (int j = 0; j < EPB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // K-steps w, w+16, ... of this wave, accumulated in that order; the operands of up to
-    // kGroup steps are loaded before their MFMAs so that the loads overlap.
     constexpr int kGroup = EPB >= 4 ? 2 : (EPB == 2 ? 4 : 8);
     constexpr int kStride = kLogitSplit;
     if constexpr (kBF16) {
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
                     (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g * 8;
         const uint16_t *xp = static_cast<const uint16_t *>(x_) + t_row * d + g * 8;
         const int nsteps = d >> 5;
-        for (int s0 = wave; s0 < nsteps; s0 += kStride * kGroup) {
+        for (int s0 = chain; s0 < nsteps; s0 += kStride * kGroup) {
             bf16x8_t a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
                     (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g;
         const float *xp = static_cast<const float *>(x_) + t_row * d + g;
         const int nsteps = d >> 2;
-        for (int s0 = wave; s0 < nsteps; s0 += kStride * kGroup) {
+        for (int s0 = chain; s0 < nsteps; s0 += kStride * kGroup) {
             float a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
@@ -103,6 +103,19 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
                                                                       0, 0, 0);
         }
     }
+}
+
+template <bool kBF16, int EPB>
+__global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
+    const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E) {
+    const int n_et = (E + 15) >> 4;
+    const int n_eg = (n_et + EPB - 1) / EPB;
+    const int et0 = (int)(blockIdx.x % n_eg) * EPB;
+    const int64_t tb = (int64_t)(blockIdx.x / n_eg) * 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    f32x4_t acc[EPB];
+    logit_chain<kBF16, EPB>(x_, wr_, T, d, E, tb, et0, wave, acc);
     __shared__ float part[kLogitSplit][EPB][4][64];
 #pragma unroll
     for (int j = 0; j < EPB; ++j)
@@ -118,6 +131,36 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
         const int64_t t = tb + (l & 15);
         const int e = (et0 + j) * 16 + 4 * (l >> 4) + i;
         if (t < T && e < E && et0 + j < n_et) logits[t * E + e] = bias ? v + bias[e] : v;
+    }
+}
+
+// Small batches: the 16 chains of every (token tile, expert tile) run as separate waves of
+// kChainWaves-wave blocks (many more blocks than the single-block-per-tile kernel, so the
+// router weights stream through many CUs) and each writes its partial to
+// part[chain][t][e]; the routing tail then adds the 16 partials in chain order (and the
+// bias) exactly as route_logits_kernel does, so the logits are the same bits.
+constexpr int kChainWaves = 4;
+
+template <bool kBF16>
+__global__ __launch_bounds__(64 * kChainWaves) void route_logit_chains_kernel(
+    const void *__restrict__ x_, const void *__restrict__ wr_, float *__restrict__ part,
+    int64_t T, int d, int E) {
+    constexpr int kGroups = kLogitSplit / kChainWaves;
+    const int n_et = (E + 15) >> 4;
+    const int cg = (int)(blockIdx.x % kGroups);
+    const int tile = (int)(blockIdx.x / kGroups);
+    const int et0 = tile % n_et;
+    const int64_t tb = (int64_t)(tile / n_et) * 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int chain = cg * kChainWaves + wave;
+    f32x4_t acc[1];
+    logit_chain<kBF16, 1>(x_, wr_, T, d, E, tb, et0, chain, acc);
+    // lane l holds token tb + l%16, experts 16 et0 + 4 (l/16) + 0..3
+    const int64_t t = tb + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = et0 * 16 + 4 * (lane >> 4) + i;
+        if (t < T && e < E) part[((int64_t)chain * T + t) * E + e] = acc[0][i];
     }
 }
 
@@ -252,6 +295,19 @@ hipError_t launch_router_logits(const moe_dims &dm, const void *x, const void *w
     if (dm.T > 0) {
         if (dm.dtype == MOE_BF16) launch_logits_t<true>(dm, x, w_router, bias, logits, s);
         else launch_logits_t<false>(dm, x, w_router, bias, logits, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_router_logit_chains(const moe_dims &dm, const void *x, const void *w_router,
+                                      float *part, hipStream_t s) {
+    if (dm.T > 0) {
+        const int64_t tiles = ((dm.T + 15) / 16) * (int64_t)((dm.E + 15) / 16);
+        const dim3 grid((unsigned)(tiles * (kLogitSplit / kChainWaves))), block(64 * kChainWaves);
+        if (dm.dtype == MOE_BF16)
+            route_logit_chains_kernel<true><<<grid, block, 0, s>>>(x, w_router, part, dm.T, dm.d, dm.E);
+        else
+            route_logit_chains_kernel<false><<<grid, block, 0, s>>>(x, w_router, part, dm.T, dm.d, dm.E);
     }
     return hipGetLastError();
 }

@@ -34,13 +34,14 @@ static_assert(kTailMaxA / kWave <= kTailWaves, "one wave per 64 assignments");
 
 template <bool kReplay, int kFn, bool kHash, int NV>
 __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
-    const float *__restrict__ logits, const int32_t *__restrict__ q,
+    float *__restrict__ logits, const int32_t *__restrict__ q,
     const int32_t *__restrict__ idx_in, const float *__restrict__ w_in, int T, int E, int k,
     int bt, int cap, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     float *__restrict__ prob_mass, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int64_t *__restrict__ weighted_counts, int32_t *__restrict__ tiles,
-    int32_t *__restrict__ d_err, const int32_t *__restrict__ slot_map, RouteOpts opts) {
+    int32_t *__restrict__ d_err, const int32_t *__restrict__ slot_map, RouteOpts opts,
+    const float *__restrict__ part, const float *__restrict__ bias) {
     __shared__ int32_t ids[kTailMaxA];
     __shared__ int32_t wstart[kTailMaxA / kWave][kMaxE];  // per-wave counts -> run starts
     __shared__ int32_t eoff[kMaxE + 1];                    // counts -> exclusive offsets
@@ -52,6 +53,30 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     for (int i = tid; i < (kTailMaxA / kWave) * kMaxE; i += 64 * kTailWaves)
         (&wstart[0][0])[i] = 0;
     for (int i = tid; i < kMaxE; i += 64 * kTailWaves) wsum[i] = 0;
+    if (!kReplay && part) {
+        // router logits from the chain partials, in chain order, then the bias
+        // (two logits per thread and pass: their 32 partial loads are in flight together)
+        const int TE = T * E;
+        constexpr int kNT = 64 * kTailWaves;
+        for (int i0 = tid; i0 < TE; i0 += 2 * kNT) {
+            const int i1 = min(i0 + kNT, TE - 1);
+            float p0[kLogitChains], p1[kLogitChains];
+#pragma unroll
+            for (int c = 0; c < kLogitChains; ++c) {
+                p0[c] = part[(int64_t)c * TE + i0];
+                p1[c] = part[(int64_t)c * TE + i1];
+            }
+            float v0 = p0[0], v1 = p1[0];
+#pragma unroll
+            for (int c = 1; c < kLogitChains; ++c) {
+                v0 = v0 + p0[c];
+                v1 = v1 + p1[c];
+            }
+            logits[i0] = bias ? v0 + bias[i0 % E] : v0;
+            if (i0 + kNT < TE) logits[i1] = bias ? v1 + bias[i1 % E] : v1;
+        }
+        __syncthreads();   // the block's own global writes are visible to it after this
+    }
 
     // ---- top-k (or replay validation); ids also go to LDS
     int err = 0;
@@ -203,29 +228,33 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
 }  // namespace
 
 template <bool kReplay, int kFn, bool kHash>
-static void launch_tail_t(const moe_dims &dm, int bt, int cap, const float *logits,
+static void launch_tail_t(const moe_dims &dm, int bt, int cap, float *logits,
                           const int32_t *q, const int32_t *idx_in, const float *w_in,
                           int32_t *topk_idx, float *topk_w, float *prob_mass, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv,
                           int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                          const int32_t *slot_map, const RouteOpts &o, hipStream_t s) {
+                          const int32_t *slot_map, const RouteOpts &o, const float *part,
+                          const float *bias, hipStream_t s) {
     auto go = [&](auto nv) {
         route_tail_kernel<kReplay, kFn, kHash, decltype(nv)::value>
             <<<dim3(1), dim3(64 * kTailWaves), 0, s>>>(
                 logits, q, idx_in, w_in, (int)dm.T, dm.E, dm.k, bt, cap, topk_idx, topk_w,
                 prob_mass, counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map,
-                o);
+                o, part, bias);
     };
     if constexpr (kReplay) go(std::integral_constant<int, kRowVals>{});   // no top-k
     else with_row_vals(dm.E, go);
 }
 
-hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int32_t *q,
+hipError_t launch_small_tail(const moe_dims &dm, const float *logits_in, const int32_t *q,
                              const int32_t *idx_in, const float *w_in, int32_t *topk_idx,
                              float *topk_w, float *prob_mass, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv,
                              int64_t *weighted_counts, int32_t *tiles, int32_t *d_err,
-                             hipStream_t s, const int32_t *slot_map, const RouteOpts &o) {
+                             hipStream_t s, const int32_t *slot_map, const RouteOpts &o,
+                             const float *logit_part, const float *bias) {
+    // the block writes the logits itself when it forms them from chain partials
+    float *logits = const_cast<float *>(logits_in);
     if (dm.T < 1 || dm.T > kSmallT || dm.E > kMaxE || dm.k > kMaxK)
         return hipErrorInvalidValue;
     if (slot_map) {
@@ -235,7 +264,7 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits, const int3
     const int bt = select_tile_m(dm);
     const int cap = (int)max_m_tiles(dm.T * dm.k, dm.E, bt);
 #define MOE_TAIL_ARGS dm, bt, cap, logits, q, idx_in, w_in, topk_idx, topk_w, prob_mass, \
-        counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map, o, s
+        counts, offsets, perm, inv, weighted_counts, tiles, d_err, slot_map, o, logit_part, bias, s
     if (idx_in) {
         launch_tail_t<true, kScoreSoftmax, false>(MOE_TAIL_ARGS);
     } else {
