@@ -485,6 +485,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 // distinct 32-byte bank groups within each 256-byte window.
 // Block: BN x BC outputs, four waves of (BN/2) x (BC/2); the result lane l holds column
 // c + l%16 of rows n + 4(l/16) + 0..3.
+#ifndef MOE_WG_DMA
+#define MOE_WG_DMA 4                         // ring slots of the DMA-fed kernel (0: off)
+#endif
 #ifndef MOE_WG_ROWS
 #define MOE_WG_ROWS 32                       // rows (K) per stage
 #endif
@@ -622,6 +625,191 @@ __global__ __launch_bounds__(64 * WNW * WCW) void wgrad_bf16_kernel(
     }
 }
 
+// The same weight gradient with the stages copied global -> LDS by DMA (global_load_lds)
+// into an NS-slot ring, so NS - 1 stages are in flight without holding them in registers
+// (the register-staged kernel waits on L2 for most of its time). A 32-row stage of each
+// operand is 32 rows x 512 bytes (256 features), one 1 KB DMA instruction per 2 rows:
+// lane l moves 16-byte chunk (l % 32) ^ kmajor_swz(row) of row 2i + l/32, so row r's
+// chunk c sits at c ^ kmajor_swz(r) -- the layout the transposing fragment reads expect.
+// Rows past the segment are fetched from its last row and zeroed in the fragments of the
+// last stage (the products are 0 * 0, as in the register-staged kernel), so every output is
+// the same sequence of MFMAs on the same operand values: the same bits. With bperm, the
+// activation rows' token indices of stage s + 2 are loaded while stage s is issued (two
+// register sets), so a DMA never waits on its own index load.
+template <int NS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void wgrad_dma_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+                      const int32_t *__restrict__ bperm, int bk, int64_t bT,
+                      const int32_t *__restrict__ off, int64_t nrows, int N, int C, int nbn,
+                      int nbc, float *__restrict__ out) {
+    constexpr int BN = 256, BC = 256, KR = 32, WNW = 4, NW = 8;
+    constexpr int WN = BN / WNW, WC = BC / (NW / WNW), NF = WN / 16, NC = WC / 16;
+    constexpr int kOpBytes = KR * 2 * BN;               // one operand's stage: 16 KB
+    constexpr int kStage = 2 * kOpBytes;
+    static_assert(BN == BC && 2 * BN == 512, "512-byte rows: 2 rows per DMA instruction");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStage];
+    const int per_e = nbn * nbc;
+    const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
+    const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
+    int64_t r0 = 0, r1 = nrows;
+    if (off) {
+        r0 = min<int64_t>(max(off[e], 0), nrows);
+        r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
+    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wn = wv % WNW, wc = wv / WNW;
+    const int64_t nk = (r1 - r0 + KR - 1) / KR;
+    // DMA roles: instructions i = 0, 1 move a-rows 2 (wv + 8 i) + lane / 32, i = 2, 3 the
+    // b-rows 2 (wv + 8 (i - 2)) + lane / 32; the lane's chunk position is lane % 32
+    const int pc = lane & 31;
+    const int rA0 = 2 * wv + (lane >> 5), rA1 = rA0 + 16;      // rows of this lane's DMAs
+    const int colA0 = min(n0 + 8 * (pc ^ kmajor_swz<32>(rA0)), N - 8);
+    const int colA1 = min(n0 + 8 * (pc ^ kmajor_swz<32>(rA1)), N - 8);
+    const int colB0 = min(c0 + 8 * (pc ^ kmajor_swz<32>(rA0)), C - 8);
+    const int colB1 = min(c0 + 8 * (pc ^ kmajor_swz<32>(rA1)), C - 8);
+    auto row_of = [&](int64_t s, int r) { return min<int64_t>(r0 + s * KR + r, r1 - 1); };
+    auto src_of = [&](int32_t idx) {
+        return min<int64_t>((int64_t)max(idx, 0) / bk, bT - 1);
+    };
+    // token indices (bperm) of the wave's four b-rows 2 wv + {0, 1, 16, 17} of a stage:
+    // wave-uniform, so they come through the scalar unit (lgkmcnt, not the vmcnt that
+    // paces the DMA ring); the half-wave picks its row's value
+    int32_t ix[2][4];
+    auto load_idx = [&](int64_t s, int32_t (&dst)[4]) {
+        const int64_t sc = min<int64_t>(s, nk - 1);            // past the end: any valid row
+        dst[0] = bperm[row_of(sc, 2 * wv)];
+        dst[1] = bperm[row_of(sc, 2 * wv + 1)];
+        dst[2] = bperm[row_of(sc, 2 * wv + 16)];
+        dst[3] = bperm[row_of(sc, 2 * wv + 17)];
+    };
+    auto issue = [&](int64_t s, const int32_t (&idx)[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        uint8_t *slot = ring + (int)(s % NS) * kStage;
+        const int64_t pa0 = row_of(s, rA0), pa1 = row_of(s, rA1);
+        const bool hi = lane >= 32;
+        const int64_t pb0 = bperm ? src_of(hi ? idx[1] : idx[0]) : pa0;
+        const int64_t pb1 = bperm ? src_of(hi ? idx[3] : idx[2]) : pa1;
+        __builtin_amdgcn_global_load_lds(a + pa0 * N + colA0,
+            (__attribute__((address_space(3))) void *)(slot + wv * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a + pa1 * N + colA1,
+            (__attribute__((address_space(3))) void *)(slot + (wv + 8) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b + pb0 * C + colB0,
+            (__attribute__((address_space(3))) void *)(slot + kOpBytes + wv * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b + pb1 * C + colB1,
+            (__attribute__((address_space(3))) void *)(slot + kOpBytes + (wv + 8) * 1024), 16, 0, 0);
+#endif
+    };
+
+    f32x4_t acc[NF][NC];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g4 = lane >> 4;
+    // transposing reads: this lane names row 8 g4 + r16/4 (+4) at features 4 (r16 % 4) .. +3
+    // of a fragment; both rows share kmajor_swz
+    const int trow = (8 * g4 + (r16 >> 2)) * (2 * BN);
+    const int tsw = kmajor_swz<32>(8 * g4 + (r16 >> 2));
+    auto frag_ptr = [&](const uint8_t *base, int feat0) {
+        const int byte = 2 * feat0 + 8 * (r16 & 3);
+        return base + trow + ((((byte >> 4) ^ tsw) << 4) | (byte & 15));
+    };
+    auto compute = [&](const uint8_t *slot, int valid) {
+        i32x2_t alo[NF], ahi[NF], blo[NC], bhi[NC];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const uint8_t *p = frag_ptr(slot, wn * WN + f * 16);
+            alo[f] = tr_read(p);
+            ahi[f] = tr_read(p + 4 * (2 * BN));
+        }
+#pragma unroll
+        for (int t = 0; t < NC; ++t) {
+            const uint8_t *p = frag_ptr(slot + kOpBytes, wc * WC + t * 16);
+            blo[t] = tr_read(p);
+            bhi[t] = tr_read(p + 4 * (2 * BN));
+        }
+        tr_fence();
+        bf16x8_t av[NF], bv[NC];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) av[f] = tr_take(alo[f], ahi[f]);
+#pragma unroll
+        for (int t = 0; t < NC; ++t) bv[t] = tr_take(blo[t], bhi[t]);
+        if (valid < KR) {   // last stage: rows 8 g4 + j (j < 8) at or past `valid` hold 0
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (8 * g4 + j >= valid) {
+#pragma unroll
+                    for (int f = 0; f < NF; ++f) av[f][j] = (__bf16)0.0f;
+#pragma unroll
+                    for (int t = 0; t < NC; ++t) bv[t][j] = (__bf16)0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int t = 0; t < NC; ++t)
+                acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], bv[t], acc[f][t], 0, 0, 0);
+    };
+
+    if (nk > 0) {
+        // prologue: stages 0 .. NS-2 (their index loads waited on in place), then the
+        // index sets of stages NS-1 and NS
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) {
+            if (st < nk) {
+                int32_t idx[4] = {0, 0, 0, 0};
+                if (bperm) load_idx(st, idx);
+                issue(st, idx);
+            }
+        }
+        if (bperm) {
+            load_idx(NS - 1, ix[(NS - 1) & 1]);
+            load_idx(NS, ix[NS & 1]);
+        }
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        // iteration kt issues stage kt + NS - 1 (index set of its parity) and reloads that
+        // set with stage kt + NS + 1's indices
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t k2 = kt + h;
+                if (k2 >= nk) break;
+                constexpr int par = (NS - 1) & 1;     // parity of kt + NS - 1 for even kt
+                const bool issuing = k2 + NS - 1 < nk;
+                if (issuing) {
+                    issue(k2 + NS - 1, ix[par ^ h]);
+                    if (bperm) load_idx(k2 + NS + 1, ix[par ^ h]);
+                }
+                compute(ring + (int)(k2 % NS) * kStage,
+                        (int)min<int64_t>(KR, r1 - (r0 + k2 * KR)));
+                if (k2 + 1 < nk) {
+                    // stage kt + 1's DMA was followed by NS - 2 iterations of 4 DMAs each
+                    // (the index loads are scalar: lgkmcnt, which this also drains)
+                    if (issuing) wait_vm_lgkm0<(NS - 2) * 4>();
+                    else wait_vm_lgkm0<0>();
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+        const int cc = c0 + wc * WC + t * 16 + r16;
+        if (cc >= C) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + wn * WN + f * 16 + g4 * 4 + i;
+                if (n < N) out[((int64_t)e * N + n) * C + cc] = acc[f][t][i];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ launchers
@@ -662,9 +850,19 @@ hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *d
 hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
                              int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
                              int C, float *out, hipStream_t s) {
+    if (N % 8 || C % 8 || nseg < 1) return hipErrorInvalidValue;
+#if MOE_WG_DMA
+    {
+        constexpr int NS = MOE_WG_DMA;
+        const int nbn = (N + 255) / 256, nbc = (C + 255) / 256;
+        wgrad_dma_kernel<NS><<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(512), 0, s>>>(
+            static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), bperm, bk, bT,
+            off, nrows, N, C, nbn, nbc, out);
+        return hipGetLastError();
+    }
+#endif
     constexpr int tile[4] = {MOE_WG_TILE};
     constexpr int BN = tile[0], BC = tile[1], WNW = tile[2], WCW = tile[3], KR = MOE_WG_ROWS;
-    if (N % 8 || C % 8 || nseg < 1) return hipErrorInvalidValue;
     const int nbn = (N + BN - 1) / BN, nbc = (C + BC - 1) / BC;
     wgrad_bf16_kernel<BN, BC, WNW, WCW, KR>
         <<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(64 * WNW * WCW), 0, s>>>(

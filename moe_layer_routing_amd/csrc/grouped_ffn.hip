@@ -320,12 +320,6 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     }
 }
 
-// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 immediate encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
 
 // ------------------------------------------------------------------------------------
 // Same GEMM with 128-byte K stages (64 bf16 per row): every DMA lane group of 8 covers one
@@ -338,13 +332,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // one wait + one s_barrier per stage.
 __device__ __forceinline__ int chunk_swizzle8(int r) { return r & 7; }
 
-// K-major weight stages: the 16 K-rows one transposing read touches (8g + 0..3, g = 0..3)
-// get distinct 32-byte bank groups within each half-wave (chunk XOR 2 * (bits 0-1 and 3 of
-// the row), limited to the row's chunks).
-template <int CPR>
-__device__ __forceinline__ int kmajor_swz(int r) {
-    return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) & (CPR - 1);
-}
 
 template <int NBW, int NW>
 __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase,
@@ -458,26 +445,37 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     // (then + 4) at features wrow(f) + 4 (r16 % 4) .. + 3
     const int kmr = 8 * g4 + (r16 >> 2);
     const int kms = kmajor_swz<kCPR>(kmr);           // equal for K-rows kmr and kmr + 4
-    auto kmajor_frag = [&](const uint8_t *stage, int kk, int f) {
+    auto kmajor_ptr = [&](const uint8_t *stage, int kk, int f) {
         const int byte = 2 * wrow(f) + 8 * (r16 & 3);
         const int pb = (((byte >> 4) ^ kms) << 4) | (byte & 15);
-        const uint8_t *p = stage + (32 * kk + kmr) * (2 * BW) + pb;
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t *)(p));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t *)(p + 4 * (2 * BW)));
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return stage + (32 * kk + kmr) * (2 * BW) + pb;
     };
     auto kstep = [&](const uint8_t *sb, const uint8_t *stage, int kk) {
         bf16x8_t a[NF], b[NT];
+        if constexpr (kKMajor) {
+            // transposing reads from inline assembly (no compiler wait on the DMA ring),
+            // the token fragments as usual, then one lgkmcnt(0) for both
+            i32x2_t lo[NF], hi[NF];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if constexpr (kKMajor) a[f] = kmajor_frag(stage, kk, f);
-            else a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 3) * 1024);
+            for (int f = 0; f < NF; ++f) {
+                const uint8_t *p = kmajor_ptr(stage, kk, f);
+                lo[f] = tr_read(p);
+                hi[f] = tr_read(p + 4 * (2 * BW));
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
+            tr_fence();
+#pragma unroll
+            for (int f = 0; f < NF; ++f) a[f] = tr_take(lo[f], hi[f]);
+        } else {
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+                a[f] = *reinterpret_cast<const bf16x8_t *>(sb + (wrow(f) >> 3) * 1024);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
         }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            b[t] = *reinterpret_cast<const bf16x8_t *>(sb + (trow(t) >> 3) * 1024);
         // the MFMA block at raised wave priority: while one wave of a SIMD issues MFMAs the
         // others' fragment reads and DMA issue wait (measured 0 to +1 %, same bytes)
         __builtin_amdgcn_s_setprio(1);

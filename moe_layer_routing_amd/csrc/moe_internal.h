@@ -23,6 +23,43 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 immediate encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Row-major (K-major) LDS tiles read with ds_read_b64_tr_b16: the 16 rows one transposing
+// read touches (8g + 0..3, g = 0..3) get distinct 32-byte bank groups within each
+// half-wave when 16-byte chunk c of row r is stored at c ^ kmajor_swz(r) (XOR 2 * (bits
+// 0-1 and 3 of the row), limited to the row's CPR chunks).
+template <int CPR>
+__device__ __forceinline__ int kmajor_swz(int r) {
+    return (2 * ((r & 3) | (((r >> 3) & 1) << 2))) & (CPR - 1);
+}
+
+// Transposing LDS reads issued from inline assembly. The compiler, not knowing which LDS
+// bytes the ds_read_b64_tr_b16 intrinsic reads, waits for every outstanding global->LDS
+// DMA (vmcnt(0)) before it, which would stall a DMA ring on its newest stage; these reads
+// carry no such wait. The caller issues a batch of them, then tr_fence() (lgkmcnt(0)) and
+// tr_take() on every result before use, which ties the results to the fence.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ i32x2_t tr_read(const uint8_t *p) {
+    i32x2_t v;
+    const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) const uint8_t *)(p));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+__device__ __forceinline__ void tr_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ bf16x8_t tr_take(i32x2_t &lo, i32x2_t &hi) {
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const i32x4_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // bfloat16 widening (exact) and narrowing (round to nearest, ties to even; NaN kept quiet).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
