@@ -470,172 +470,23 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
 
 // ------------------------------------------------- bf16 weight gradient (MFMA 16x16x32)
 // out[e, n, c] = sum over the segment's rows p ascending of a[p, n] b[p, c], a and b bf16
-// (b gathered through bperm / bk when given), FP32 accumulation and output. A 32-row stage
-// of each operand goes to LDS as stored (row-major: row p, features contiguous): 16 lanes
-// copy one row's 256 bytes, 16 bytes each. The MFMA wants 8 consecutive K values (rows p)
-// per lane; gfx950's transposing LDS read (ds_read_b64_tr_b16) delivers them: within each
-// 16-lane group, lane s names 4 consecutive features of one row, and lane i receives, in
-// slot j, the element that lane 4j + i/4 named at position i%4. With lane s of group g
-// naming row 8g + j0 + s/4 (j0 = 0, then 4) at features f0 + 4(s%4) .. +3, lane i gets
-// feature f0 + i at rows 8g + j0 + 0..3: two reads give the MFMA operand of feature f0 + i,
-// K = rows 8g .. 8g + 7 of the stage -- the same operand values, in the same K positions,
-// as a feature-major staging, so the results are the same bits.
-// LDS tile: 32 rows x 288-byte pitch (256 + 32); byte column b of row r lives at
-// b ^ 128 * bit3(r), so the 16 rows one read touches (8g + 0..3 for g = 0..3) fall on
-// distinct 32-byte bank groups within each 256-byte window.
-// Block: BN x BC outputs, four waves of (BN/2) x (BC/2); the result lane l holds column
+// (b gathered through bperm / bk when given), FP32 accumulation and output.
+// Stages of 32 rows x 512 bytes (256 features) per operand are copied global -> LDS by DMA
+// (global_load_lds) into an NS-slot ring, NS - 1 stages in flight: one 1 KB DMA
+// instruction per 2 rows, lane l moving 16-byte chunk (l % 32) ^ kmajor_swz(row) of row
+// 2i + l/32, so row r's chunk c sits at c ^ kmajor_swz(r).
+// The MFMA wants 8 consecutive K values (rows p) per lane; gfx950's transposing LDS read
+// (ds_read_b64_tr_b16) delivers them: within each 16-lane group, lane s names 4
+// consecutive features of one row, and lane i receives, in slot j, the element that lane
+// 4j + i/4 named at position i % 4. With lane s of group g naming row 8g + j0 + s/4
+// (j0 = 0, then 4) at features f0 + 4(s % 4) .. +3, lane i gets feature f0 + i at rows
+// 8g + j0 + 0..3: two reads give the MFMA operand of feature f0 + i, K = rows 8g .. 8g + 7
+// of the stage. Rows past the segment are fetched from its last row and zeroed in the
+// fragments of the last stage (their products are 0 * 0). With bperm, the activation
+// rows' token indices of stage s + 2 are loaded while stage s is issued (two register
+// sets; wave-uniform, so through the scalar unit, whose lgkmcnt does not pace the ring).
+// Block: 256 x 256 outputs on 8 waves of 64 x 128; the result lane l holds column
 // c + l%16 of rows n + 4(l/16) + 0..3.
-#ifndef MOE_WG_DMA
-#define MOE_WG_DMA 4                         // ring slots of the DMA-fed kernel (0: off)
-#endif
-#ifndef MOE_WG_ROWS
-#define MOE_WG_ROWS 32                       // rows (K) per stage
-#endif
-#ifndef MOE_WG_TILE
-#define MOE_WG_TILE 256, 256, 4, 2           // BN, BC, waves along n, waves along c
-#endif
-
-__device__ __forceinline__ bf16x8_t lds_tr_operand(const uint8_t *p_lo, const uint8_t *p_hi) {
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(p_lo));
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t *)(p_hi));
-    typedef short s16x8_t __attribute__((ext_vector_type(8)));
-    const s16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
-template <int BN, int BC, int WNW, int WCW, int kWgRows>
-__global__ __launch_bounds__(64 * WNW * WCW) void wgrad_bf16_kernel(
-    const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
-    const int32_t *__restrict__ bperm, int bk, int64_t bT, const int32_t *__restrict__ off,
-    int64_t nrows, int N, int C, int nbn, int nbc, float *__restrict__ out) {
-    constexpr int NT = 64 * WNW * WCW;                    // threads
-    constexpr int WN = BN / WNW, WC = BC / WCW, NF = WN / 16, NC = WC / 16;
-    constexpr int PA = 2 * BN + 32, PB = 2 * BC + 32;     // LDS row pitches (bytes)
-    constexpr int LA = BN / 8, LB = BC / 8;               // 16-byte chunks per row
-    constexpr int AL = kWgRows * LA / NT, BL = kWgRows * LB / NT;   // loads per thread
-    static_assert(AL >= 1 && BL >= 1 && kWgRows * LA % NT == 0 && kWgRows * LB % NT == 0,
-                  "whole rows per load round");
-    static_assert(NF >= 1 && NC >= 1 && kWgRows % 32 == 0 && BN % 128 == 0 && BC % 128 == 0,
-                  "tile shape");
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kWgRows * PA];
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kWgRows * PB];
-    const int per_e = nbn * nbc;
-    const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
-    const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
-    int64_t r0 = 0, r1 = nrows;
-    if (off) {
-        r0 = min<int64_t>(max(off[e], 0), nrows);
-        r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
-    }
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wn = wv % WNW, wc = wv / WNW;
-    // copy mapping: element q = tid + NT i is row q / L, features 8 (q % L) .. + 7
-    u32x4_t ra[AL], rb[BL];
-    auto load = [&](int64_t p0) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) {
-            const int q = tid + NT * i, p = q / LA, g = q % LA;
-            const int64_t row = p0 + p;
-            ra[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (row < r1)
-                ra[i] = *reinterpret_cast<const u32x4_t *>(a + row * N + min(n0 + 8 * g, N - 8));
-        }
-#pragma unroll
-        for (int i = 0; i < BL; ++i) {
-            const int q = tid + NT * i, p = q / LB, g = q % LB;
-            const int64_t row = p0 + p;
-            rb[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (row < r1) {
-                int64_t src = row;
-                if (bperm) src = min<int64_t>((int64_t)max(bperm[row], 0) / bk, bT - 1);
-                rb[i] = *reinterpret_cast<const u32x4_t *>(b + src * C + min(c0 + 8 * g, C - 8));
-            }
-        }
-    };
-    auto store = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) {
-            const int q = tid + NT * i, p = q / LA, g = q % LA;
-            *reinterpret_cast<u32x4_t *>(sa[s] + p * PA + ((16 * g) ^ (((p >> 3) & 1) << 7))) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < BL; ++i) {
-            const int q = tid + NT * i, p = q / LB, g = q % LB;
-            *reinterpret_cast<u32x4_t *>(sb[s] + p * PB + ((16 * g) ^ (((p >> 3) & 1) << 7))) = rb[i];
-        }
-    };
-    f32x4_t acc[NF][NC];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int t = 0; t < NC; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int r16 = lane & 15, g4 = lane >> 4;
-    // transposing reads: this lane names row 8 g4 + r16/4 (+4), features 4 (r16 % 4) + 0..3
-    // of the fragment; rows 8 g4 .. 8 g4 + 7 share bit 3, hence one swizzle per lane
-    const int tr_ra = (8 * g4 + (r16 >> 2)) * PA, tr_rb = (8 * g4 + (r16 >> 2)) * PB;
-    const int tr_col = 8 * (r16 & 3), tr_sw = (g4 & 1) << 7;
-    const int64_t nk = (r1 - r0 + kWgRows - 1) / kWgRows;
-    if (nk > 0) {
-        load(r0);
-        store(0);
-        __syncthreads();
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const int s = (int)(kt & 1);
-            if (kt + 1 < nk) load(r0 + (kt + 1) * kWgRows);
-#pragma unroll
-            for (int kk = 0; kk < kWgRows / 32; ++kk) {     // 32-row MFMA K-steps, in order
-                bf16x8_t av[NF], bv[NC];
-#pragma unroll
-                for (int f = 0; f < NF; ++f) {
-                    const uint8_t *p = sa[s] + tr_ra + 32 * kk * PA +
-                                       ((2 * (wn * WN + f * 16) + tr_col) ^ tr_sw);
-                    av[f] = lds_tr_operand(p, p + 4 * PA);
-                }
-#pragma unroll
-                for (int t = 0; t < NC; ++t) {
-                    const uint8_t *p = sb[s] + tr_rb + 32 * kk * PB +
-                                       ((2 * (wc * WC + t * 16) + tr_col) ^ tr_sw);
-                    bv[t] = lds_tr_operand(p, p + 4 * PB);
-                }
-#pragma unroll
-                for (int f = 0; f < NF; ++f)
-#pragma unroll
-                    for (int t = 0; t < NC; ++t)
-                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], bv[t], acc[f][t],
-                                                                            0, 0, 0);
-            }
-            if (kt + 1 < nk) store(s ^ 1);
-            __syncthreads();
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < NC; ++t) {
-        const int cc = c0 + wc * WC + t * 16 + r16;
-        if (cc >= C) continue;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = n0 + wn * WN + f * 16 + g4 * 4 + i;
-                if (n < N) out[((int64_t)e * N + n) * C + cc] = acc[f][t][i];
-            }
-        }
-    }
-}
-
-// The same weight gradient with the stages copied global -> LDS by DMA (global_load_lds)
-// into an NS-slot ring, so NS - 1 stages are in flight without holding them in registers
-// (the register-staged kernel waits on L2 for most of its time). A 32-row stage of each
-// operand is 32 rows x 512 bytes (256 features), one 1 KB DMA instruction per 2 rows:
-// lane l moves 16-byte chunk (l % 32) ^ kmajor_swz(row) of row 2i + l/32, so row r's
-// chunk c sits at c ^ kmajor_swz(r) -- the layout the transposing fragment reads expect.
-// Rows past the segment are fetched from its last row and zeroed in the fragments of the
-// last stage (the products are 0 * 0, as in the register-staged kernel), so every output is
-// the same sequence of MFMAs on the same operand values: the same bits. With bperm, the
-// activation rows' token indices of stage s + 2 are loaded while stage s is issued (two
-// register sets), so a DMA never waits on its own index load.
 template <int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void wgrad_dma_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
@@ -851,21 +702,9 @@ hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32
                              int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
                              int C, float *out, hipStream_t s) {
     if (N % 8 || C % 8 || nseg < 1) return hipErrorInvalidValue;
-#if MOE_WG_DMA
-    {
-        constexpr int NS = MOE_WG_DMA;
-        const int nbn = (N + 255) / 256, nbc = (C + 255) / 256;
-        wgrad_dma_kernel<NS><<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(512), 0, s>>>(
-            static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), bperm, bk, bT,
-            off, nrows, N, C, nbn, nbc, out);
-        return hipGetLastError();
-    }
-#endif
-    constexpr int tile[4] = {MOE_WG_TILE};
-    constexpr int BN = tile[0], BC = tile[1], WNW = tile[2], WCW = tile[3], KR = MOE_WG_ROWS;
-    const int nbn = (N + BN - 1) / BN, nbc = (C + BC - 1) / BC;
-    wgrad_bf16_kernel<BN, BC, WNW, WCW, KR>
-        <<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(64 * WNW * WCW), 0, s>>>(
+    constexpr int NS = 4;   // ring slots: 3 stages in flight
+    const int nbn = (N + 255) / 256, nbc = (C + 255) / 256;
+    wgrad_dma_kernel<NS><<<dim3((unsigned)((int64_t)nseg * nbn * nbc)), dim3(512), 0, s>>>(
         static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), bperm, bk, bT, off,
         nrows, N, C, nbn, nbc, out);
     return hipGetLastError();
