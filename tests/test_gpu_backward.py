@@ -146,10 +146,14 @@ def test_backward_deterministic_and_batch_invariant():
 
 
 G16_CASES = [
-    # (T, d, E, k, I, mode, scale, placed, x_perm)
+    # (T, d, E, k, I, mode, scale, placed, x_perm); the token-tile heights (16 .. 256) select
+    # every launch shape of the K-major data-gradient GEMM
     (300, 256, 16, 4, 192, "router", 2.5, False, False),
     (517, 128, 32, 8, 128, "router", 1.0, True, True),
     (40, 192, 8, 6, 64, "replay", 1.0, False, False),
+    (12, 128, 16, 4, 128, "router", 1.0, False, False),      # 16-row tiles
+    (30, 192, 16, 4, 64, "router", 1.0, False, True),        # 32-row tiles
+    (2100, 128, 4, 2, 128, "router", 1.0, False, False),     # 256-row tiles, long segments
 ]
 
 
