@@ -437,10 +437,10 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     e = launch_permute(*dims, a->topk_idx, a->x, a->x_perm, a->perm, a->inv, a->counts,
                        a->offsets, a->cu_seqlens, a->seq_counts ? a->num_seqs : 0,
                        a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s,
-                       a->slot_of_expert);
+                       a->slot_of_expert, select_tile_m(*dims));   // tile list with the scan
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
-                           a->prof_events, s, a->x, a->perm);
+                           a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     return to_status(finish_layer(dims, a, scale, s));
 }

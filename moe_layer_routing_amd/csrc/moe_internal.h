@@ -163,7 +163,8 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
-                          hipStream_t s, const int32_t *slot_map = nullptr);
+                          hipStream_t s, const int32_t *slot_map = nullptr,
+                          int tiles_bt = 0);   // > 0: also write ws.tiles for this tile height
 // Raises MOE_DERR_SLOTMAP unless map[0..E-1] is a permutation of 0..E-1 (one block).
 hipError_t launch_check_slot_map(const int32_t *map, int E, int32_t *d_err, hipStream_t s);
 // x_perm == nullptr: gather token rows of x through perm inside the gate/up GEMM.

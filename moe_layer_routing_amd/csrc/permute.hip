@@ -50,14 +50,20 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
     }
 }
 
-// One block: counts, offsets, and each chunk's starting position per expert.
+// One block: counts, offsets, and each chunk's starting position per expert; with tiles,
+// also the grouped GEMM's token-tile list for tile height bt (ceil(count / bt) tiles per
+// expert in expert order, at most cap; tiles[0] = their number), as build_tiles_kernel
+// forms it from the offsets.
 __global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ blk_hist,
                                                    const uint64_t *__restrict__ blk_whist,
                                                    int64_t nchunks, int E, bool have_q,
                                                    int32_t *__restrict__ counts,
                                                    int32_t *__restrict__ offsets,
-                                                   int64_t *__restrict__ weighted_counts) {
+                                                   int64_t *__restrict__ weighted_counts,
+                                                   int bt, int64_t cap,
+                                                   int32_t *__restrict__ tiles) {
     __shared__ int32_t cnt[kMaxE + 1];
+    __shared__ int32_t tpre[kMaxE + 1];
     const int e = threadIdx.x;
     int32_t run = 0;
     if (e < E) {
@@ -74,19 +80,33 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ blk_his
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int32_t acc = 0;
+        int32_t acc = 0, tacc = 0;
         for (int i = 0; i < E; ++i) {
             const int32_t c = cnt[i];
             cnt[i] = acc;
             acc += c;
+            tpre[i] = tacc;
+            tacc += (c + bt - 1) / bt;
         }
         cnt[E] = acc;
+        if (tiles) tiles[0] = (int32_t)min<int64_t>(tacc, cap);
     }
     __syncthreads();
     if (e < E) {
         const int32_t off = cnt[e];
         offsets[e] = off;
         for (int64_t b = 0; b < nchunks; ++b) blk_hist[b * E + e] += off;
+        if (tiles) {
+            const int32_t c = cnt[e + 1] - off, nt = (c + bt - 1) / bt;
+            for (int i = 0; i < nt; ++i) {
+                const int64_t slot = (int64_t)tpre[e] + i;
+                if (slot >= cap) break;
+                int32_t *d = tiles + 1 + 3 * slot;
+                d[0] = e;
+                d[1] = off + i * bt;
+                d[2] = min(bt, c - i * bt);
+            }
+        }
     }
     if (e == 0) offsets[E] = cnt[E];
 }
@@ -271,7 +291,7 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
-                          hipStream_t s, const int32_t *slot_map) {
+                          hipStream_t s, const int32_t *slot_map, int tiles_bt) {
     const int64_t T = dm.T, A = dm.T * dm.k;
     const int E = dm.E, k = dm.k;
     const int64_t nchunks = perm_chunks(A);
@@ -284,8 +304,11 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
         hist_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
             topk_idx, A, k, E, token_mult, ws.blk_hist,
             (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err, slot_map);
-    scan_kernel<<<dim3(1), dim3(256), 0, s>>>(ws.blk_hist, ws.blk_whist, nchunks, E, have_q,
-                                              counts, offsets, weighted_counts);
+    // the forward's tile list comes with the scan (tiles_bt > 0)
+    const int bt = tiles_bt > 0 ? tiles_bt : 1;
+    scan_kernel<<<dim3(1), dim3(256), 0, s>>>(
+        ws.blk_hist, ws.blk_whist, nchunks, E, have_q, counts, offsets, weighted_counts, bt,
+        tiles_bt > 0 ? max_m_tiles(A, E, bt) : 0, tiles_bt > 0 ? ws.tiles : nullptr);
     if (nchunks > 0)
         scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
                                                                      ws.blk_hist, perm, inv,
