@@ -68,7 +68,7 @@ __device__ __forceinline__ void store_b(uint16_t *p, const uint16_t (&b)[V]) {
 // Features per lane: fewer as R grows, so that the R partials of every feature a lane
 // holds, and the FP64 tree over them, stay in registers at a useful occupancy.
 template <int R>
-constexpr int ranks_vec() { return R <= 4 ? 4 : 2; }
+constexpr int ranks_vec() { return R <= 8 ? 4 : 2; }
 
 // One wave per (token, slice of 128 V features); lane l takes features slice*128V + V*l
 // and slice*128V + 64V + V*l (two chunks). For each chunk: the k weighted expert rows
