@@ -697,7 +697,7 @@ hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *d
     return hipGetLastError();
 }
 
-// bf16 weight gradient over segments (see wgrad_bf16_kernel); N and C multiples of 8.
+// bf16 weight gradient over segments (see wgrad_dma_kernel); N and C multiples of 8.
 hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32_t *bperm,
                              int bk, int64_t bT, const int32_t *off, int64_t nrows, int N,
                              int C, float *out, hipStream_t s) {
