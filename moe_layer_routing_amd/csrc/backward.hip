@@ -764,35 +764,49 @@ hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
 }
 
 // dx_r[t, c] = sum over e ascending of dl[t, e] w_router[e, c]; each thread takes four
-// consecutive features of one token (one dl value serves four products).
+// consecutive features of kRdxTok consecutive tokens, so each router-weight load serves
+// 4 x kRdxTok products (the weights were re-read from L2 once per token before).
+constexpr int kRdxTok = 4;
 __global__ __launch_bounds__(256) void router_dx_kernel(const float *__restrict__ dl,
                                                         const void *__restrict__ wr, bool bf16,
                                                         int64_t T, int E, int d,
                                                         float *__restrict__ dx) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= T * d) return;
-    const int64_t t = i / d;
-    const int c = (int)(i - t * d);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (token group, quad)
+    const int nq = d / 4;
+    const int64_t tg = q / nq;
+    const int c = (int)(q - tg * nq) * 4;
+    const int64_t t0 = tg * kRdxTok;
+    if (t0 >= T) return;
+    float a[kRdxTok][4];
+#pragma unroll
+    for (int u = 0; u < kRdxTok; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) a[u][v] = 0.f;
     for (int e = 0; e < E; ++e) {
-        const float g = dl[t * E + e];
-        float w0, w1, w2, w3;
+        float w[4];
         if (bf16) {
             const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(wr) + (int64_t)e * d + c);
-            w0 = bf16_to_f32((uint16_t)(v.x & 0xffff));
-            w1 = bf16_to_f32((uint16_t)(v.x >> 16));
-            w2 = bf16_to_f32((uint16_t)(v.y & 0xffff));
-            w3 = bf16_to_f32((uint16_t)(v.y >> 16));
+            w[0] = bf16_to_f32((uint16_t)(v.x & 0xffff));
+            w[1] = bf16_to_f32((uint16_t)(v.x >> 16));
+            w[2] = bf16_to_f32((uint16_t)(v.y & 0xffff));
+            w[3] = bf16_to_f32((uint16_t)(v.y >> 16));
         } else {
             const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(wr) + (int64_t)e * d + c);
-            w0 = v.x; w1 = v.y; w2 = v.z; w3 = v.w;
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
         }
-        a0 = a0 + g * w0;
-        a1 = a1 + g * w1;
-        a2 = a2 + g * w2;
-        a3 = a3 + g * w3;
+#pragma unroll
+        for (int u = 0; u < kRdxTok; ++u) {
+            const int64_t t = min<int64_t>(t0 + u, T - 1);
+            const float g = dl[t * E + e];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a[u][v] = a[u][v] + g * w[v];
+        }
     }
-    *reinterpret_cast<float4 *>(dx + i) = make_float4(a0, a1, a2, a3);
+#pragma unroll
+    for (int u = 0; u < kRdxTok; ++u)
+        if (t0 + u < T)
+            *reinterpret_cast<float4 *>(dx + (t0 + u) * d + c) =
+                make_float4(a[u][0], a[u][1], a[u][2], a[u][3]);
 }
 
 // dw_router[e, c] = sum over t ascending of dl[t, e] x[t, c] when E is not a multiple of 4
@@ -837,7 +851,7 @@ hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *
 
 hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
                             float *dx, hipStream_t s) {
-    const int64_t n = dm.T * dm.d / 4;
+    const int64_t n = (dm.T + kRdxTok - 1) / kRdxTok * (dm.d / 4);
     if (n == 0) return hipGetLastError();
     router_dx_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
         dl, w_router, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dx);
