@@ -99,22 +99,41 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict
                                                          const float *__restrict__ dh,
                                                          int64_t A, int I,
                                                          void *__restrict__ dguv) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // four consecutive features per thread (I is a multiple of 4): 16-byte loads, 8- or
+    // 16-byte stores; the per-element arithmetic is unchanged
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= A * I) return;
     const int64_t p = i / I;
     const int n = (int)(i - p * I);
-    const float g = gu[p * 2 * I + n], u = gu[p * 2 * I + I + n], d = dh[i];
-    const float e = expf(-g);
-    const float sg = 1.0f / (1.0f + e);
-    const float silu = g / (1.0f + e);
-    const float dsilu = sg * (1.0f + g * (1.0f - sg));
-    const float dg = (d * u) * dsilu, du = d * silu;
+    const float4 g4 = *reinterpret_cast<const float4 *>(gu + p * 2 * I + n);
+    const float4 u4 = *reinterpret_cast<const float4 *>(gu + p * 2 * I + I + n);
+    const float4 d4 = *reinterpret_cast<const float4 *>(dh + i);
+    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+    float dg[4], du[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float g = gv[q], u = uv[q], d = dv[q];
+        const float e = expf(-g);
+        const float sg = 1.0f / (1.0f + e);
+        const float silu = g / (1.0f + e);
+        const float dsilu = sg * (1.0f + g * (1.0f - sg));
+        dg[q] = (d * u) * dsilu;
+        du[q] = d * silu;
+    }
     if constexpr (kOutBF16) {
-        static_cast<uint16_t *>(dguv)[p * 2 * I + n] = f32_to_bf16(dg);
-        static_cast<uint16_t *>(dguv)[p * 2 * I + I + n] = f32_to_bf16(du);
+        uint16_t *o = static_cast<uint16_t *>(dguv) + p * 2 * I + n;
+        uint2 pg, pu;
+        pg.x = (uint32_t)f32_to_bf16(dg[0]) | ((uint32_t)f32_to_bf16(dg[1]) << 16);
+        pg.y = (uint32_t)f32_to_bf16(dg[2]) | ((uint32_t)f32_to_bf16(dg[3]) << 16);
+        pu.x = (uint32_t)f32_to_bf16(du[0]) | ((uint32_t)f32_to_bf16(du[1]) << 16);
+        pu.y = (uint32_t)f32_to_bf16(du[2]) | ((uint32_t)f32_to_bf16(du[3]) << 16);
+        *reinterpret_cast<uint2 *>(o) = pg;
+        *reinterpret_cast<uint2 *>(o + I) = pu;
     } else {
-        static_cast<float *>(dguv)[p * 2 * I + n] = dg;
-        static_cast<float *>(dguv)[p * 2 * I + I + n] = du;
+        float *o = static_cast<float *>(dguv) + p * 2 * I + n;
+        *reinterpret_cast<float4 *>(o) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+        *reinterpret_cast<float4 *>(o + I) = make_float4(du[0], du[1], du[2], du[3]);
     }
 }
 
@@ -687,7 +706,7 @@ hipError_t launch_combine_bwd(const moe_dims &dm, const void *dout, const float 
 
 hipError_t launch_swiglu_bwd(const moe_dims &dm, const float *gu, const float *dh, void *dgu,
                              bool out_bf16, hipStream_t s) {
-    const int64_t n = dm.T * dm.k * dm.inter;
+    const int64_t n = dm.T * dm.k * dm.inter / 4;     // four features per thread
     if (n == 0) return hipGetLastError();
     const dim3 grid((unsigned)((n + 255) / 256));
     if (out_bf16)
