@@ -32,12 +32,6 @@ namespace {
 
 constexpr int kKc = 16;   // K elements per LDS stage of the FP32 gradient GEMMs
 
-template <bool kBF16>
-__device__ __forceinline__ float ld_elem(const void *p, int64_t i) {
-    if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
-    else return static_cast<const float *>(p)[i];
-}
-
 // ------------------------------------------------------------------ combine backward
 // One wave per token: lane l takes features 4l, 4l + 256, ... of every slot's y row;
 // dy = (s w_j) dout; the partial dot products <dout, y_j> are summed per lane in feature
@@ -61,13 +55,29 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         acc[j] = 0.f;
     }
     for (int c = lane * 4; c < d; c += 256) {
+        // issue every slot's y load before the first use, so k rows are in flight at once
         float g[4];
+        if constexpr (kBF16) {
+            const uint2 raw = *reinterpret_cast<const uint2 *>(
+                static_cast<const uint16_t *>(dout) + t * d + c);
+            g[0] = bf16_to_f32((uint16_t)(raw.x & 0xffffu));
+            g[1] = bf16_to_f32((uint16_t)(raw.x >> 16));
+            g[2] = bf16_to_f32((uint16_t)(raw.y & 0xffffu));
+            g[3] = bf16_to_f32((uint16_t)(raw.y >> 16));
+        } else {
+            const float4 raw = *reinterpret_cast<const float4 *>(static_cast<const float *>(dout) + t * d + c);
+            g[0] = raw.x;
+            g[1] = raw.y;
+            g[2] = raw.z;
+            g[3] = raw.w;
+        }
+        float4 yv[kMaxK];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) g[q] = ld_elem<kBF16>(dout, t * d + c + q);
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) yv[j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             if (j < k) {
-                const float4 yv = *reinterpret_cast<const float4 *>(y + src[j] + c);
                 if constexpr (kDyBF16) {
                     uint2 pk;
                     pk.x = (uint32_t)f32_to_bf16(ws[j] * g[0]) | ((uint32_t)f32_to_bf16(ws[j] * g[1]) << 16);
@@ -77,10 +87,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
                     *reinterpret_cast<float4 *>(static_cast<float *>(dyv) + src[j] + c) =
                         make_float4(ws[j] * g[0], ws[j] * g[1], ws[j] * g[2], ws[j] * g[3]);
                 }
-                acc[j] = acc[j] + g[0] * yv.x;
-                acc[j] = acc[j] + g[1] * yv.y;
-                acc[j] = acc[j] + g[2] * yv.z;
-                acc[j] = acc[j] + g[3] * yv.w;
+                acc[j] = acc[j] + g[0] * yv[j].x;
+                acc[j] = acc[j] + g[1] * yv[j].y;
+                acc[j] = acc[j] + g[2] * yv[j].z;
+                acc[j] = acc[j] + g[3] * yv[j].w;
             }
         }
     }
@@ -147,15 +157,29 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const float *__restrict__ d
     if (i >= T * d) return;
     const int64_t t = i / d;
     const int c = (int)(i - t * d);
+    // all k slot indices, then all k row loads, are issued before the slot-order sum
+    // consumes them (vmcnt retires in order: a wait for an index placed after a row load
+    // would wait for that row as well)
+    int32_t pi[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) pi[j] = (j < k) ? inv[t * k + j] : 0;
+    float4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            const int32_t p = (pi[j] < 0 || pi[j] >= A) ? 0 : pi[j];
+            v[j] = *reinterpret_cast<const float4 *>(dxp + (int64_t)p * d + c);
+        }
+    }
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-        int32_t p = inv[t * k + j];
-        p = (p < 0 || p >= A) ? 0 : p;
-        const float4 v = *reinterpret_cast<const float4 *>(dxp + (int64_t)p * d + c);
-        a0 = a0 + v.x;
-        a1 = a1 + v.y;
-        a2 = a2 + v.z;
-        a3 = a3 + v.w;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            a0 = a0 + v[j].x;
+            a1 = a1 + v[j].y;
+            a2 = a2 + v[j].z;
+            a3 = a3 + v[j].w;
+        }
     }
     if (dxr) {
         const float4 r = *reinterpret_cast<const float4 *>(dxr + i);
