@@ -541,7 +541,10 @@ void wgrad_dma_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict
     constexpr int kOpBytes = KR * 2 * BN;               // one operand's stage: 16 KB
     constexpr int kStage = 2 * kOpBytes;
     static_assert(BN == BC && 2 * BN == 512, "512-byte rows: 2 rows per DMA instruction");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStage];
+    // the epilogue reuses the ring for two passes of 128 output rows of kOutStride floats
+    constexpr int kOutStride = BC + 4;
+    constexpr int kRing = NS * kStage, kOut = 128 * kOutStride * 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing > kOut ? kRing : kOut];
     const int per_e = nbn * nbc;
     const int e = blockIdx.x / per_e, rem = blockIdx.x % per_e;
     const int n0 = (rem / nbc) * BN, c0 = (rem % nbc) * BC;
@@ -689,18 +692,33 @@ void wgrad_dma_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict
             }
         }
     }
+    // epilogue through LDS, in two passes of 128 rows x 256 columns (rows f = 2 pass, 2 pass
+    // + 1 of every wave); a row stride of 260 floats puts the four 4-row groups of one
+    // scalar LDS store in different banks; each row then leaves as 64 lanes x 16 bytes
+    static_assert(NF == 4 && WNW * 32 == 128 && (NW / WNW) * WC == BC, "epilogue tiling");
+    float *stage = reinterpret_cast<float *>(ring);
+    __syncthreads();   // every wave is past its last fragment read
 #pragma unroll
-    for (int t = 0; t < NC; ++t) {
-        const int cc = c0 + wc * WC + t * 16 + r16;
-        if (cc >= C) continue;
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
+        for (int fh = 0; fh < 2; ++fh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = n0 + wn * WN + f * 16 + g4 * 4 + i;
-                if (n < N) out[((int64_t)e * N + n) * C + cc] = acc[f][t][i];
-            }
+            for (int t = 0; t < NC; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    stage[(wn * 32 + fh * 16 + g4 * 4 + i) * kOutStride + wc * WC + t * 16 + r16] =
+                        acc[2 * pass + fh][t][i];
+        __syncthreads();
+        const int cc = c0 + 4 * lane;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int lr = wv + 8 * q;                         // staged row 0 .. 127
+            const int n = n0 + (lr >> 5) * WN + 32 * pass + (lr & 31);
+            const float4 v = *reinterpret_cast<const float4 *>(stage + lr * kOutStride + 4 * lane);
+            if (n < N && cc < C)
+                *reinterpret_cast<float4 *>(out + ((int64_t)e * N + n) * C + cc) = v;
         }
+        if (pass == 0) __syncthreads();
     }
 }
 
