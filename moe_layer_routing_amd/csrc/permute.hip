@@ -62,40 +62,73 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ blk_his
                                                    int64_t *__restrict__ weighted_counts,
                                                    int bt, int64_t cap,
                                                    int32_t *__restrict__ tiles) {
+    static_assert(kMaxE == 256, "one thread per expert, 256 threads");
     __shared__ int32_t cnt[kMaxE + 1];
     __shared__ int32_t tpre[kMaxE + 1];
     const int e = threadIdx.x;
     int32_t run = 0;
+    // chunk counts are read kScanBatch at a time, all loads before the stores of the batch,
+    // so the chain costs nchunks / kScanBatch memory round trips instead of nchunks
+    constexpr int kScanBatch = 16;
     if (e < E) {
         uint64_t wsum = 0;
-        for (int64_t b = 0; b < nchunks; ++b) {
-            const int32_t c = blk_hist[b * E + e];
-            blk_hist[b * E + e] = run;
-            run += c;
-            if (have_q && weighted_counts) wsum += blk_whist[b * E + e];
+        for (int64_t b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+            int32_t c[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                c[j] = (b0 + j < nchunks) ? blk_hist[(b0 + j) * E + e] : 0;
+            if (have_q && weighted_counts) {
+#pragma unroll
+                for (int j = 0; j < kScanBatch; ++j)
+                    wsum += (b0 + j < nchunks) ? blk_whist[(b0 + j) * E + e] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) {
+                if (b0 + j < nchunks) {
+                    blk_hist[(b0 + j) * E + e] = run;
+                    run += c[j];
+                }
+            }
         }
         counts[e] = run;
-        cnt[e] = run;
         if (weighted_counts) weighted_counts[e] = have_q ? (int64_t)wsum : (int64_t)run;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0, tacc = 0;
-        for (int i = 0; i < E; ++i) {
-            const int32_t c = cnt[i];
-            cnt[i] = acc;
-            acc += c;
-            tpre[i] = tacc;
-            tacc += (c + bt - 1) / bt;
+    // exclusive prefix sums over the experts of the counts and of the tile counts: a
+    // Hillis-Steele scan over the 256 threads (E <= 256; experts past E count 0, so entry E
+    // of the exclusive sum is the total)
+    const int32_t c_e = (e < E) ? run : 0;
+    const int32_t nt_e = (e < E) ? (c_e + bt - 1) / bt : 0;
+    int32_t xs = c_e, ys = nt_e;
+    for (int sh = 1; sh < 256; sh <<= 1) {
+        __syncthreads();
+        cnt[e] = xs;
+        tpre[e] = ys;
+        __syncthreads();
+        if (e >= sh) {
+            xs += cnt[e - sh];
+            ys += tpre[e - sh];
         }
-        cnt[E] = acc;
-        if (tiles) tiles[0] = (int32_t)min<int64_t>(tacc, cap);
+    }
+    __syncthreads();
+    cnt[e] = xs - c_e;
+    tpre[e] = ys - nt_e;
+    if (e == 255) {
+        cnt[256] = xs;
+        if (tiles) tiles[0] = (int32_t)min<int64_t>(ys, cap);
     }
     __syncthreads();
     if (e < E) {
         const int32_t off = cnt[e];
         offsets[e] = off;
-        for (int64_t b = 0; b < nchunks; ++b) blk_hist[b * E + e] += off;
+        for (int64_t b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+            int32_t c[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                c[j] = (b0 + j < nchunks) ? blk_hist[(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                if (b0 + j < nchunks) blk_hist[(b0 + j) * E + e] = c[j] + off;
+        }
         if (tiles) {
             const int32_t c = cnt[e + 1] - off, nt = (c + bt - 1) / bt;
             for (int i = 0; i < nt; ++i) {
