@@ -326,7 +326,8 @@ def backward_report(L, dims, inp, K, hip, stream):
     fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"], w_router=inp["w_router"],
               logit_bias=inp["logit_bias"])
     M.forward(dims, fb, ws)
-    bb = M.alloc_backward_buffers(dims, dev, router=True)
+    # bf16 layers: no gu buffer, the gate/up recomputation forms d_gu in its epilogue
+    bb = M.alloc_backward_buffers(dims, dev, router=True, keep_gu=(L.dtype != "bf16"))
     g = torch.Generator(device=dev).manual_seed(L.seed)
     dout = torch.randn((L.T, L.d), generator=g, device=dev).to(fb["out"].dtype)
     bb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"], w_router=inp["w_router"],
@@ -354,7 +355,8 @@ def backward_report(L, dims, inp, K, hip, stream):
            "frac_overall": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
            "forward_ms_for_reference": None}
     if L.dtype == "bf16":
-        b16 = M.alloc_backward_buffers(dims, dev, router=True, grad_dtype=M.MOE_BF16)
+        b16 = M.alloc_backward_buffers(dims, dev, router=True, grad_dtype=M.MOE_BF16,
+                                       keep_gu=False)
         b16.update({n: bb[n] for n in ("x", "w13", "w2", "w_router", "logit_bias", "logits",
                                        "offsets", "perm", "inv", "topk_w", "h", "y", "d_out")})
         del bb
@@ -365,7 +367,7 @@ def backward_report(L, dims, inp, K, hip, stream):
             "tflops_overall": round(flops / (ms16 * 1e-3) / 1e12, 2),
             "frac_bf16_peak_overall": round(flops / (ms16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "dy and d_gu rounded once to bf16; bf16 MFMA for every gradient GEMM; "
-                    "the data gradients read w2 and w13 K-major as stored"}
+                    "the data gradients read w2 and w13 K-major as stored; the gate/up recomputation forms d_gu in its epilogue (no gu buffer)"}
     assert int(fb["d_err"].item()) == 0
     return out
 

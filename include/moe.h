@@ -419,7 +419,9 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *args, void 
  * h [T*k,I] dtype, y [T*k,d] f32), d_out [T,d] dtype; outputs FP32: d_x [T,d],
  * d_w13 [E,2I,d], d_w2 [E,d,I], d_topk_w [T,k], and with w_router: d_logits [T,E],
  * d_w_router [E,d] (optional), d_x_router [T,d]; FP32 intermediates d_y [T*k,d],
- * gu [T*k,2I], d_h [T*k,I], d_gu [T*k,2I], d_xp [T*k,d]; x_perm [T*k,d] or NULL (the
+ * gu [T*k,2I] (may be NULL for a bf16 layer: the recomputation then runs after d_h and
+ * forms d_gu in its epilogue with the same arithmetic, so every gradient has the same bits
+ * and gu is not written), d_h [T*k,I], d_gu [T*k,2I], d_xp [T*k,d]; x_perm [T*k,d] or NULL (the
  * recomputation gathers x through perm; x must then be under 4 GiB); workspace of
  * moe_workspace_size() bytes. */
 typedef struct moe_backward_args {

@@ -358,16 +358,19 @@ def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.
 
 
 def alloc_backward_buffers(dims: Dims, device="cuda", router: bool = True,
-                           grad_dtype: int = MOE_F32) -> dict:
+                           grad_dtype: int = MOE_F32, keep_gu: bool = True) -> dict:
     """Allocate every output and intermediate of moe_backward for ``dims`` (with bf16
-    gradient operands, d_y / d_gu are bf16)."""
+    gradient operands, d_y / d_gu are bf16). ``keep_gu=False`` (bf16 layers) leaves out the
+    recomputed pre-activations gu: the recomputation then forms d_gu itself."""
     T, d, E, k, I = dims.T, dims.d, dims.E, dims.k, dims.inter
     A = T * k
     f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=device)
     g = (lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=device)) \
         if grad_dtype == MOE_BF16 else f
     b = dict(d_x=f(T, d), d_w13=f(E, 2 * I, d), d_w2=f(E, d, I), d_topk_w=f(T, k),
-             d_y=g(A, d), gu=f(A, 2 * I), d_h=f(A, I), d_gu=g(A, 2 * I), d_xp=f(A, d))
+             d_y=g(A, d), d_h=f(A, I), d_gu=g(A, 2 * I), d_xp=f(A, d))
+    if keep_gu:
+        b["gu"] = f(A, 2 * I)
     if router:
         b.update(d_logits=f(T, E), d_w_router=f(E, d), d_x_router=f(T, d))
     return b

@@ -122,29 +122,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict
     const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
     float dg[4], du[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float g = gv[q], u = uv[q], d = dv[q];
-        const float e = expf(-g);
-        const float sg = 1.0f / (1.0f + e);
-        const float silu = g / (1.0f + e);
-        const float dsilu = sg * (1.0f + g * (1.0f - sg));
-        dg[q] = (d * u) * dsilu;
-        du[q] = d * silu;
-    }
-    if constexpr (kOutBF16) {
-        uint16_t *o = static_cast<uint16_t *>(dguv) + p * 2 * I + n;
-        uint2 pg, pu;
-        pg.x = (uint32_t)f32_to_bf16(dg[0]) | ((uint32_t)f32_to_bf16(dg[1]) << 16);
-        pg.y = (uint32_t)f32_to_bf16(dg[2]) | ((uint32_t)f32_to_bf16(dg[3]) << 16);
-        pu.x = (uint32_t)f32_to_bf16(du[0]) | ((uint32_t)f32_to_bf16(du[1]) << 16);
-        pu.y = (uint32_t)f32_to_bf16(du[2]) | ((uint32_t)f32_to_bf16(du[3]) << 16);
-        *reinterpret_cast<uint2 *>(o) = pg;
-        *reinterpret_cast<uint2 *>(o + I) = pu;
-    } else {
-        float *o = static_cast<float *>(dguv) + p * 2 * I + n;
-        *reinterpret_cast<float4 *>(o) = make_float4(dg[0], dg[1], dg[2], dg[3]);
-        *reinterpret_cast<float4 *>(o + I) = make_float4(du[0], du[1], du[2], du[3]);
-    }
+    for (int q = 0; q < 4; ++q) swiglu_grad(gv[q], uv[q], dv[q], dg[q], du[q]);
+    store_dgu4<kOutBF16>(dguv, p * 2 * I + n, I, dg, du);
 }
 
 // ------------------------------------------------------------ dx: slot-order sum

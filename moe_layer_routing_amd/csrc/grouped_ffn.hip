@@ -358,12 +358,13 @@ __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase
 // lane 4j + i/4 named at position i%4, so lane s naming K-row 8g + s/4 (then + 4) at
 // features f + 4(s%4) hands lane i feature f + i at K-rows 8g + 0..7 -- the operand a
 // row-major weight tile gives, in the same K positions, hence the same bits.
-template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS, bool kKMajor = false>
+template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS, bool kKMajor = false,
+          int kGrad = 0>
 __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
     const int32_t *__restrict__ tiles, int K, int N, int nft,
-    const int32_t *__restrict__ gperm, int gk, int64_t gT) {
+    const int32_t *__restrict__ gperm, int gk, int64_t gT, const float *__restrict__ dh) {
     constexpr int NW = WF * WT;
     constexpr int NBLK = (BW + BT) / 8;                // 8-row LDS blocks per stage
     constexpr int NBW = NBLK / NW;                     // DMA instructions per wave per stage
@@ -526,7 +527,22 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
         const int m = wt * (BT / WT) + t * 16 + r16;
         if (m >= nrows) continue;
         const int64_t row = (int64_t)p0 + m;
-        if constexpr (kGateUp) {
+        if constexpr (kGateUp && kGrad != 0) {
+            // backward: the SwiGLU derivative of the recomputed gate and up values with
+            // dh [rows][N]; d_gu [rows][2N] (bf16 for kGrad 1, FP32 for kGrad 2)
+#pragma unroll
+            for (int f = 0; f < NFh; ++f) {
+                const int feat = n0 + wf * kWaveRows + f * 16 + g4 * 4;
+                if (feat >= N) continue;
+                const float4 d4 = *reinterpret_cast<const float4 *>(dh + row * N + feat);
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+                float dg[4], du[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    swiglu_grad(acc[f][t][i], acc[f + NFh][t][i], dv[i], dg[i], du[i]);
+                store_dgu4<kGrad == 1>(out, row * 2 * N + feat, N, dg, du);
+            }
+        } else if constexpr (kGateUp) {
 #pragma unroll
             for (int f = 0; f < NFh; ++f) {
                 const int feat = n0 + wf * kWaveRows + f * 16 + g4 * 4;
@@ -580,18 +596,21 @@ struct IsDma128<C, std::void_t<decltype(C::kDma128)>> : std::true_type {};
 
 // gperm != nullptr: activation rows are gathered (token perm[p] / gk of act, gT rows).
 // kKMajor: weights stored wgt[e][k][n] (bf16 DMA kernel only).
-template <bool kBF16, bool kGateUp, class C, bool kKMajor = false>
+template <bool kBF16, bool kGateUp, class C, bool kKMajor = false, int kGrad = 0>
 hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_t *tiles,
                        int64_t mtiles, int K, int N, hipStream_t s,
-                       const int32_t *gperm = nullptr, int gk = 1, int64_t gT = 0) {
+                       const int32_t *gperm = nullptr, int gk = 1, int64_t gT = 0,
+                       const float *dh = nullptr) {
     constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
     const int nft = (N + feat - 1) / feat;
     static_assert(!kKMajor || (IsDma128<C>::value && kBF16 && !kGateUp), "K-major weights");
+    static_assert(kGrad == 0 || (IsDma128<C>::value && kBF16 && kGateUp), "fused SwiGLU grad");
     if constexpr (IsDma128<C>::value && kBF16) {
-        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE, C::NS, kKMajor>
+        grouped_gemm_dma128_kernel<kGateUp, C::BW, C::BT, C::WF, C::WT, C::WPE, C::NS, kKMajor,
+                                   kGrad>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
-                K, N, nft, gperm, gk, gT);
+                K, N, nft, gperm, gk, gT, dh);
     } else if constexpr (IsDma128<C>::value) {
         // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
         // same token tiles
@@ -730,6 +749,39 @@ hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t 
     default: e = MOE_PLAIN(PLAIN_HUGE); break;
     }
 #undef MOE_PLAIN
+    return e;
+}
+
+// The backward's gate/up recomputation fused with the SwiGLU derivative (bf16 layers): each
+// (row, feature)'s gate and up values are the forward's (the forward's gate/up launch shape
+// for the tile height, the same MFMA sequence), and the epilogue forms
+// d_gu[p, n] = (dh u) silu'(g), d_gu[p, I + n] = dh silu(g) with the elementwise kernel's
+// arithmetic, so g and u never reach memory. d_gu is bf16 (dgu_bf16) or FP32.
+hipError_t launch_gate_up_grad(const moe_dims &dm, const void *act, const int32_t *gperm,
+                               const void *w13, const float *dh, void *dgu, bool dgu_bf16,
+                               const int32_t *offsets, const Workspace &ws, hipStream_t s) {
+    const int64_t A = dm.T * dm.k;
+    if (A == 0) return hipGetLastError();
+    if (dm.dtype != MOE_BF16) return hipErrorInvalidValue;
+    const int bt = select_tile_m(dm);
+    const int64_t cap = max_m_tiles(A, dm.E, bt);
+    build_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(offsets, dm.E, A, bt, cap, ws.tiles);
+    using GugLarge = MOE_FFN_LARGE_CFG13;
+    using GugHuge = MOE_FFN_HUGE_CFG13;
+#define MOE_GUG(CFG)                                                                            \
+    (dgu_bf16 ? launch_gemm<true, true, CFG, false, 1>(act, w13, dgu, ws.tiles, cap, dm.d,       \
+                                                       dm.inter, s, gperm, dm.k, dm.T, dh)      \
+              : launch_gemm<true, true, CFG, false, 2>(act, w13, dgu, ws.tiles, cap, dm.d,       \
+                                                       dm.inter, s, gperm, dm.k, dm.T, dh))
+    hipError_t e;
+    switch (bt) {
+    case 16: e = MOE_GUG(PLAIN_CFG16); break;
+    case 32: e = MOE_GUG(PLAIN_CFG32); break;
+    case 64: e = MOE_GUG(PLAIN_CFG64); break;
+    case 128: e = MOE_GUG(GugLarge); break;
+    default: e = MOE_GUG(GugHuge); break;
+    }
+#undef MOE_GUG
     return e;
 }
 

@@ -453,8 +453,10 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     if (dims->T == 0) return MOE_OK;
     MOE_REQUIRE(a->x && a->w13 && a->w2 && a->offsets && a->perm && a->inv && a->topk_w &&
                     a->h && a->y && a->d_out && a->d_x && a->d_w13 && a->d_w2 &&
-                    a->d_topk_w && a->d_y && a->gu && a->d_h && a->d_gu && a->d_xp,
+                    a->d_topk_w && a->d_y && a->d_h && a->d_gu && a->d_xp,
                 MOE_E_NULLPTR);
+    // gu may be omitted on bf16 layers: the recomputation then forms d_gu in its epilogue
+    MOE_REQUIRE(a->gu || dims->dtype == MOE_BF16, MOE_E_NULLPTR);
     if (a->w_router) MOE_REQUIRE(a->d_logits && a->d_x_router, MOE_E_NULLPTR);
     MOE_REQUIRE(a->grad_dtype == MOE_F32 || a->grad_dtype == MOE_BF16, MOE_E_DTYPE);
     const bool g16 = a->grad_dtype == MOE_BF16;
@@ -474,19 +476,28 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     hipError_t e = launch_combine_bwd(*dims, a->d_out, a->y, a->inv, a->topk_w, scale, a->d_y,
                                       a->d_topk_w, g16, s);
     if (e != hipSuccess) return MOE_E_LAUNCH;
-    e = launch_plain_gemm(*dims, a->x_perm ? a->x_perm : a->x, a->x_perm ? nullptr : a->perm,
-                          a->w13, a->gu, 2 * I, a->offsets, ws, s);
-    if (e != hipSuccess) return MOE_E_LAUNCH;
     const void *xb = a->x_perm ? a->x_perm : a->x;
     const int32_t *xperm = a->x_perm ? nullptr : a->perm;
     const int64_t xrows = a->x_perm ? A : dims->T;
+    // with gu, the gate/up pre-activations are recomputed into it and the SwiGLU derivative
+    // is its own kernel; without, the recomputation runs after dh and forms d_gu itself
+    const bool fused = a->gu == nullptr;
+    if (!fused) {
+        e = launch_plain_gemm(*dims, xb, xperm, a->w13, a->gu, 2 * I, a->offsets, ws, s);
+        if (e != hipSuccess) return MOE_E_LAUNCH;
+    }
+    auto swiglu_grad = [&](bool out_bf16) {
+        return fused ? launch_gate_up_grad(*dims, xb, xperm, a->w13, a->d_h, a->d_gu, out_bf16,
+                                           a->offsets, ws, s)
+                     : launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, out_bf16, s);
+    };
     if (g16) {
         // data gradients on the forward's DMA GEMM with the weights read K-major as stored:
         // dh = dy w2[e] (K = d rows of w2), dxp = dgu w13[e] (K = 2I rows of w13)
         e = launch_plain_gemm(*dims, a->d_y, nullptr, a->w2, a->d_h, I, a->offsets, ws, s, d,
                               /*kmajor=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, true, s);
+        e = swiglu_grad(true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         e = launch_plain_gemm(*dims, a->d_gu, nullptr, a->w13, a->d_xp, d, a->offsets, ws, s,
                               2 * I, /*kmajor=*/true);
@@ -500,7 +511,7 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     } else {
         e = launch_dgrad(*dims, a->d_y, a->w2, bf16, d, I, a->offsets, a->d_h, ws, s);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        e = launch_swiglu_bwd(*dims, a->gu, a->d_h, a->d_gu, false, s);
+        e = swiglu_grad(false);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         e = launch_dgrad(*dims, a->d_gu, a->w13, bf16, 2 * I, d, a->offsets, a->d_xp, ws, s);
         if (e != hipSuccess) return MOE_E_LAUNCH;

@@ -71,6 +71,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// SwiGLU derivative of one element, h = silu(g) u: dg = (d u) silu'(g), du = d silu(g),
+// with silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g)). One definition serves the
+// elementwise backward kernel and the fused gate/up recomputation, so both give the same bits.
+__device__ __forceinline__ void swiglu_grad(float g, float u, float d, float &dg, float &du) {
+    const float e = expf(-g);
+    const float sg = 1.0f / (1.0f + e);
+    const float silu = g / (1.0f + e);
+    const float dsilu = sg * (1.0f + g * (1.0f - sg));
+    dg = (d * u) * dsilu;
+    du = d * silu;
+}
+
+// four consecutive features of d_gu's gate part at o and of its up part at o + I
+template <bool kBF16>
+__device__ __forceinline__ void store_dgu4(void *dgu, int64_t o, int I, const float (&dg)[4],
+                                           const float (&du)[4]) {
+    if constexpr (kBF16) {
+        uint16_t *q = static_cast<uint16_t *>(dgu) + o;
+        uint2 pg, pu;
+        pg.x = (uint32_t)f32_to_bf16(dg[0]) | ((uint32_t)f32_to_bf16(dg[1]) << 16);
+        pg.y = (uint32_t)f32_to_bf16(dg[2]) | ((uint32_t)f32_to_bf16(dg[3]) << 16);
+        pu.x = (uint32_t)f32_to_bf16(du[0]) | ((uint32_t)f32_to_bf16(du[1]) << 16);
+        pu.y = (uint32_t)f32_to_bf16(du[2]) | ((uint32_t)f32_to_bf16(du[3]) << 16);
+        *reinterpret_cast<uint2 *>(q) = pg;
+        *reinterpret_cast<uint2 *>(q + I) = pu;
+    } else {
+        float *q = static_cast<float *>(dgu) + o;
+        *reinterpret_cast<float4 *>(q) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+        *reinterpret_cast<float4 *>(q + I) = make_float4(du[0], du[1], du[2], du[3]);
+    }
+}
+
 // Error word update: one atomic OR, taken only when a check failed.
 __device__ __forceinline__ void raise_err(int32_t *d_err, int32_t bits) {
     if (d_err && bits) atomicOr(d_err, bits);
@@ -192,6 +224,9 @@ hipError_t launch_shared_ffn(const moe_dims &dm, int R, int inter_shared, const 
 // kmajor (bf16 only): the weights are stored wgt[e][k][n] instead of wgt[e][n][k].
 hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, int64_t cap,
                               int32_t *tiles, hipStream_t s);
+hipError_t launch_gate_up_grad(const moe_dims &dm, const void *act, const int32_t *gperm,
+                               const void *w13, const float *dh, void *dgu, bool dgu_bf16,
+                               const int32_t *offsets, const Workspace &ws, hipStream_t s);
 hipError_t launch_plain_gemm(const moe_dims &dm, const void *act, const int32_t *gperm,
                              const void *wgt, float *out, int N, const int32_t *offsets,
                              const Workspace &ws, hipStream_t s, int K = 0,

@@ -40,7 +40,8 @@ def _close(gpu, ref, what, tol=GTOL):
     assert worst <= tol, f"{what}: {worst:.3e} > {tol}"
 
 
-def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=False):
+def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=False,
+         fused=False):
     dims = dims_of(L)
     fb = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
     fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"])
@@ -57,7 +58,8 @@ def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=Fa
     ws = M.alloc_workspace(dims)
     M.forward(dims, fb, ws, routed_scale=scale)
     gd = M.MOE_BF16 if g16 else M.MOE_F32
-    bb = M.alloc_backward_buffers(dims, "cuda", router=router_grads, grad_dtype=gd)
+    bb = M.alloc_backward_buffers(dims, "cuda", router=router_grads, grad_dtype=gd,
+                                  keep_gu=not fused)
     bb.update(x=inp["x"], x_perm=fb.get("x_perm"), w13=fb["w13"], w2=fb["w2"],
               offsets=fb["offsets"], perm=fb["perm"], inv=fb["inv"], topk_w=fb["topk_w"],
               h=fb["h"], y=fb["y"], d_out=dev(dout))
@@ -196,3 +198,30 @@ def test_backward_bf16_operands_parity(case):
     ref_xp = np.concatenate([dgu[offs[e]:offs[e + 1]] @ w13[e] for e in range(E)])
     _close(host(bb["d_w13"]), ref_w13, "d_w13 (GPU d_gu)", tol=1e-4)
     _close(host(bb["d_xp"]), ref_xp, "d_xp (GPU d_gu)", tol=1e-4)
+
+
+FUSED_CASES = [  # T, d, E, k, I, g16, x_perm: tile heights 16 .. 256, both gradient dtypes
+    (12, 128, 16, 4, 128, True, False), (30, 192, 16, 4, 64, True, True),
+    (300, 256, 8, 2, 192, False, False), (2100, 128, 4, 2, 128, True, False),
+    (1500, 256, 4, 4, 320, False, True), (4096, 128, 2, 2, 64, True, False)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"T{c[0]}_d{c[1]}_E{c[2]}_k{c[3]}_"
+                                                            f"I{c[4]}_g16{int(c[5])}_xp{int(c[6])}")
+def test_backward_fused_swiglu_grad_bitwise(case):
+    """Without gu (bf16 layers) the gate/up recomputation runs after dh and forms d_gu in its
+    epilogue: every gradient is bitwise the one of the path that materialises gu and runs
+    the elementwise SwiGLU derivative."""
+    T, d, E, k, I, g16, xp = case
+    L = W.make_layer(T=T, d=d, E=E, k=k, I=I, dtype="bf16", mode="router", seed=T + 5,
+                     bias="zipf")
+    inp = upload(L)
+    rng = np.random.default_rng(T + 1)
+    dout = W.f32_to_bf16_bits(rng.normal(0, 1, (T, d)).astype(np.float32))
+    _, b1 = _run(L, inp, dout, 1.0, None, xp, g16=g16)
+    _, b2 = _run(L, inp, dout, 1.0, None, xp, g16=g16, fused=True)
+    assert "gu" not in b2
+    for n in sorted(b1):
+        if n.startswith("d_"):
+            assert host(b1[n]).tobytes() == host(b2[n]).tobytes(), n
