@@ -521,6 +521,39 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
         }
     }
 
+    if constexpr (!kGateUp && BT >= 128) {
+        // plain FP32 output of the large tiles, staged through the ring: one wave row of
+        // tokens (RP rows) per pass, row stride BW + 4 floats; then every thread stores
+        // consecutive 16-byte pieces of whole output rows (instead of 64-byte row pieces
+        // from the result lanes). The values are the accumulators, unchanged.
+        constexpr int RP = BT / WT, kLd = BW + 4, kRow4 = BW / 4;
+        static_assert(RP * kLd * 4 <= NS * kStageBytes, "staging fits the ring");
+        float *stg = reinterpret_cast<float *>(ring);
+        float *outf = static_cast<float *>(out);
+        __syncthreads();   // every wave is past its last fragment read; no DMA is pending
+#pragma unroll 1
+        for (int q = 0; q < WT; ++q) {
+            if (wt == q) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+                        *reinterpret_cast<float4 *>(stg + (t * 16 + r16) * kLd + wf * kWaveRows +
+                                                    f * 16 + g4 * 4) =
+                            make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]);
+            }
+            __syncthreads();
+            for (int idx = tid; idx < RP * kRow4; idx += 64 * NW) {
+                const int r = idx / kRow4, c = (idx % kRow4) * 4;
+                const int m = q * RP + r;
+                if (m < nrows && n0 + c < N)
+                    *reinterpret_cast<float4 *>(outf + ((int64_t)p0 + m) * N + n0 + c) =
+                        *reinterpret_cast<const float4 *>(stg + r * kLd + c);
+            }
+            __syncthreads();
+        }
+        return;
+    }
     // epilogue (same arithmetic and layout as grouped_gemm_kernel)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
