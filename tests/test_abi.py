@@ -106,3 +106,28 @@ def test_host_checks_reject_before_any_launch(M):
     # cu_seqlens without seq_counts
     assert L.moe_permute(ctypes.byref(good), fake, fake, fake, fake, fake, fake, fake, fake, 2,
                          None, None, None, None, ws, 1 << 30, None) == 1
+
+
+def test_backward_gu_optional_only_on_bf16_layers(M):
+    """moe_backward may be called without gu on a bf16 layer (the recomputation then forms
+    d_gu itself): the pointer checks pass and the call stops at the too-small workspace,
+    still before any launch. An FP32 layer without gu is rejected as a missing pointer."""
+    L = M.lib()
+    optional = {"x_perm", "w_router", "logit_bias", "logits", "d_logits", "d_w_router",
+                "d_x_router", "gu"}
+
+    def args(gu):
+        a = M.BackwardArgs()
+        for n, t in a._fields_:
+            if t is ctypes.c_void_p and n not in optional:
+                setattr(a, n, 0x2000)
+        a.gu = 0x2000 if gu else None
+        a.workspace, a.workspace_bytes = 0x1000, 16
+        a.grad_dtype = M.MOE_F32
+        return a
+
+    for dtype, gu, status in ((M.MOE_BF16, False, 4), (M.MOE_BF16, True, 4),
+                              (M.MOE_F32, False, 1), (M.MOE_F32, True, 4)):
+        dims = M.make_dims(16, 128, 8, 2, 128, dtype)
+        a = args(gu)
+        assert L.moe_backward(ctypes.byref(dims), ctypes.byref(a), None) == status, (dtype, gu)
