@@ -19,6 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# A test may point the wrapper at another build of the same source (the sanitizer build).
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 
 ERR_IDX_RANGE, ERR_IDX_DUP, ERR_NONFINITE, ERR_SEQLENS = 1, 2, 4, 8
 
@@ -37,9 +39,12 @@ def build() -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build()
+            L = ctypes.CDLL(_LIB)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.orc_router_logits.argtypes = [P, P, P, I64, I32, I32, I32, P]
         L.orc_router_logits.restype = None
@@ -72,12 +77,12 @@ def lib():
                                              I64, I32, I32, I32, I32, I32, I32] + [P] * 9
         L.orc_backward_experts_r.restype = None
         L.orc_backward_router.argtypes = [P, P, P, P, I64, I32, I32, I32, I32, P, P, P]
-        L.orc_backward_router.restype = None
+        L.orc_backward_router.restype = I32
         L.orc_round_f64_bf16.argtypes = [P, P, I64]
         L.orc_round_f64_bf16.restype = None
         L.orc_combine_ranks.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, P,
                                         ctypes.c_float, I32, P, P]
-        L.orc_combine_ranks.restype = None
+        L.orc_combine_ranks.restype = I32
         L.orc_round_bf16.argtypes = [P, P, I64]
         L.orc_round_bf16.restype = None
         L.orc_place_lpt.argtypes = [P, I32, I32, P, P]
@@ -345,12 +350,11 @@ def combine_ranks(y, inv, w, idx, E: int, R: int, dtype: str, slot_of_expert=Non
     ys = _c(y_shared, np.float32)
     T, k = w.shape
     d = y.shape[1]
-    if E % R or R > 64:
-        raise ValueError("R must divide E (and be at most 64)")
     parts = np.empty((R, T, d), dtype=_store_dtype(dtype))
     out = np.empty((T, d), dtype=_store_dtype(dtype))
-    lib().orc_combine_ranks(_p(y), _p(inv), _p(w), _p(idx), _p(sm), T, k, d, E, R, _p(ys),
-                            scale, _dt(dtype), _p(parts), _p(out))
+    if lib().orc_combine_ranks(_p(y), _p(inv), _p(w), _p(idx), _p(sm), T, k, d, E, R, _p(ys),
+                               scale, _dt(dtype), _p(parts), _p(out)) < 0:
+        raise ValueError("combine_ranks: need 1 <= k <= E <= 256, d >= 1 and R dividing E")
     return parts, out
 
 
@@ -389,9 +393,11 @@ def backward_router(logits, dw, x, w_router, dtype: str) -> dict:
     d = x.shape[1]
     r = dict(dl=np.empty((T, E), np.float32), dw_router=np.empty((E, d), np.float32),
              dx=np.empty((T, d), np.float32))
-    lib().orc_backward_router(_p(logits), _p(_c(dw, np.float32)), _p(np.ascontiguousarray(x)),
-                              _p(np.ascontiguousarray(w_router)), T, E, k, d, _dt(dtype),
-                              _p(r["dl"]), _p(r["dw_router"]), _p(r["dx"]))
+    if lib().orc_backward_router(_p(logits), _p(_c(dw, np.float32)),
+                                 _p(np.ascontiguousarray(x)), _p(np.ascontiguousarray(w_router)),
+                                 T, E, k, d, _dt(dtype), _p(r["dl"]), _p(r["dw_router"]),
+                                 _p(r["dx"])) < 0:
+        raise ValueError("backward_router: need 1 <= k <= E <= 256 and d >= 1")
     return r
 
 

@@ -446,7 +446,7 @@ int orc_route_scored(const float *logits, const int32_t *q, int64_t T, int E, in
     for (int64_t t = 0; t < T; ++t) {
         const float *l = logits + t * (int64_t)E;
         float v[256], key[256];
-        int32_t sel[8];
+        int32_t sel[256];
         for (int e = 0; e < E; ++e)
             if (!isfinite(l[e])) err |= ORC_ERR_NONFINITE;
         float m = l[0];
@@ -614,20 +614,21 @@ void orc_round_f64_bf16(const double *in, uint16_t *out, int64_t n) {
  *    FP64, an odd last contributor carried to the next level unchanged, repeated until one
  *    value remains, which is rounded once to the output type.
  * partials (optional, [R, T, d], output type) receives the rank partials. */
-void orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const int32_t *idx,
-                       const int32_t *slot_map, int64_t T, int k, int d, int E, int R,
-                       const float *ys, float scale, int dt, void *partials, void *out) {
+int orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const int32_t *idx,
+                      const int32_t *slot_map, int64_t T, int k, int d, int E, int R,
+                      const float *ys, float scale, int dt, void *partials, void *out) {
+    if (E < 1 || E > 256 || k < 1 || k > E || d < 1 || R < 1 || R > E || E % R) return -1;
     const int H = E / R;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
-        int owner[8];
+        int owner[256];
         for (int j = 0; j < k; ++j) {
             int e = idx[t * k + j];
             int v = (e >= 0 && e < E) ? (slot_map ? slot_map[e] : e) : -1;
             owner[j] = (v >= 0 && v < E) ? v / H : -1;
         }
         for (int o = 0; o < d; ++o) {
-            double lvl[64];
+            double lvl[256];
             for (int r = 0; r < R; ++r) {
                 float acc = 0.0f;
                 for (int j = 0; j < k; ++j) {
@@ -658,6 +659,7 @@ void orc_combine_ranks(const float *y, const int32_t *inv, const float *w, const
             else ((float *)out)[t * (int64_t)d + o] = (float)lvl[0];
         }
     }
+    return 0;
 }
 
 /* Backward of the expert path of the layer (the derivative of the forward definitions
@@ -799,13 +801,14 @@ void orc_backward_experts_r(const void *x, const int32_t *perm, const int32_t *i
  * function is that gradient in both modes.
  *   dw_router[e,c] = sum over t ascending of dl[t,e] * x[t,c];
  *   dx_r[t,c]      = sum over e ascending of dl[t,e] * w_router[e,c]. */
-void orc_backward_router(const float *logits, const float *dw, const void *x,
-                         const void *w_router, int64_t T, int E, int k, int d, int dt,
-                         float *dl, float *dw_router, float *dx_r) {
+int orc_backward_router(const float *logits, const float *dw, const void *x,
+                        const void *w_router, int64_t T, int E, int k, int d, int dt,
+                        float *dl, float *dw_router, float *dx_r) {
+    if (E < 1 || E > 256 || k < 1 || k > E || d < 1) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         const float *l = logits + t * (int64_t)E;
-        int sel[8];
+        int sel[256];
         unsigned char taken[256];
         memset(taken, 0, sizeof(taken));
         for (int j = 0; j < k; ++j) {
@@ -828,7 +831,7 @@ void orc_backward_router(const float *logits, const float *dw, const void *x,
         for (int j = 1; j < k; ++j) s = s + p[sel[j]];
         float a = 0.0f;
         for (int j = 0; j < k; ++j) a = a + dw[t * k + j] * (p[sel[j]] / s);
-        float dp[8], c = 0.0f;
+        float dp[256], c = 0.0f;
         for (int j = 0; j < k; ++j) {
             dp[j] = (dw[t * k + j] - a) / s;
             c = c + dp[j] * p[sel[j]];
@@ -855,4 +858,5 @@ void orc_backward_router(const float *logits, const float *dw, const void *x,
                 acc = acc + dl[t * E + e] * orc_load(w_router, (int64_t)e * d + c, dt);
             dx_r[t * d + c] = acc;
         }
+    return 0;
 }
