@@ -2,13 +2,17 @@
 
 One step = route -> permute (+ load statistics) -> grouped SwiGLU GEMMs -> combine for one
 batch of synthetic tokens (moe_forward), with inputs already resident in HBM. Default
-workload: the training-shaped bf16 layer (T=4096, d=2048, E=64, top-8, I=1408, router
-logits with a per-expert Zipf(1.1) log bias).
+workload: the packed RL microbatch (T=16384 tokens in variable-length sequences, d=4096,
+E=128, top-8, I=1536, bf16, routing replay), the largest single-GPU layer; the
+training-shaped layer (T=4096, d=2048, E=64, I=1408, router with a Zipf(1.1) log bias,
+with its backward and router-variant reports) and the heavily imbalanced replay layer
+(T=32768, d=2048, E=256, I=768) are timed in the same run under "other_configs".
 
-Prints ONE JSON line with the throughput (tokens/s), a roofline entry for the dominant
-kernel (the fused gate/up + SwiGLU grouped GEMM, timed live with HIP events recorded by
-the library around it on the launch stream) and the CPU oracle timed on a bounded sample
-of the same workload.
+Prints ONE JSON line with the throughput (tokens/s from the median step), a roofline entry
+for the dominant kernel (the fused gate/up + SwiGLU grouped GEMM, timed live with HIP events
+recorded by the library around it on the launch stream), the bf16 peak derived from the
+device's CU count and clock next to the published one, and the CPU oracle timed on a
+bounded sample of the same workload. Progress lines go to stderr.
 """
 from __future__ import annotations
 
@@ -27,8 +31,18 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X; grouped-GEMM TFLOP/s as % bf16 MFMA peak"
 PEAK_FP32_TFLOPS = 157.3
-PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published figure
 PEAK_HBM_GBS = 8000.0
+# dense bf16 MFMA work per compute unit per clock on gfx950: four SIMDs, each retiring one
+# v_mfma_f32_16x16x32_bf16 (16*16*32*2 = 16384 FLOP) every 16 cycles = 1024 FLOP/clk
+BF16_FLOP_PER_CLK_CU = 4096
+# hipDeviceAttribute_t values (hip_runtime_api.h, ROCm 7)
+_HIP_ATTR_CLOCK_KHZ, _HIP_ATTR_CU_COUNT = 5, 63
+
+
+def log(msg: str):
+    """Progress of the run itself, on stderr (stdout carries the one JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 WORKLOADS = {
     "c2": "training-shaped bf16 MoE layer: T=4096 tokens, d=2048, E=64 experts, top-8, SwiGLU "
@@ -72,6 +86,23 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+    def attribute(self, attr: int, dev: int = 0) -> int:
+        v = ctypes.c_int()
+        assert self.rt.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr),
+                                             ctypes.c_int(dev)) == 0
+        return v.value
+
+
+def derived_peak(hip) -> dict:
+    """The bf16 dense MFMA peak from this device's own figures: compute units x peak clock
+    x bf16 FLOP per clock per CU, next to the published 2.5 PFLOP/s."""
+    cus = hip.attribute(_HIP_ATTR_CU_COUNT)
+    mhz = hip.attribute(_HIP_ATTR_CLOCK_KHZ) / 1000.0
+    tf = cus * mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12
+    return {"compute_units": cus, "peak_clock_mhz": mhz,
+            "bf16_flop_per_clk_per_cu": BF16_FLOP_PER_CLK_CU,
+            "derived_bf16_tflops": round(tf, 1), "published_bf16_tflops": PEAK_BF16_TFLOPS}
 
 
 def cpu_baseline(L, sample_tokens: int):
@@ -661,46 +692,18 @@ def gemm_traffic(config: str):
     return int(fields["gate/up bytes per launch"])
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-sample", type=int, default=4096,
-                    help="tokens of the workload the CPU oracle runs (0 = skip)")
-    ap.add_argument("--tile-m", type=int, default=0)
-    ap.add_argument("--decode-t", default="1,2,4,8,16,32,64",
-                    help="batch sizes of the decode-shaped sweep (--config c5)")
-    ap.add_argument("--no-reports", action="store_true",
-                    help="time the layer steps only (no stage, placement, router-variant, "
-                         "expert-parallel or backward reports): for counter passes, whose "
-                         "per-dispatch averages must see the step's kernels alone")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB MiB five times (the "
-                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(expert-parallel sharding is a design note only); run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
-
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.config == "c5":
-        decode_sweep(args)
-        return
-
+def run_layer(cfg: str, args, hip, reports: bool, cpu_sample: int):
+    """Times K whole moe_forward steps of workload ``cfg`` (inputs resident in HBM, the
+    library's HIP events around both grouped GEMMs of every step) and, with ``reports``,
+    the per-stage and NEXT-row reports. Returns the record fields of that workload."""
     import torch
 
     import moe_layer_routing_amd as M
     import workloads as W
-    L = W.make_config(args.config)
+    t0 = time.perf_counter()
+    L = W.make_config(cfg)
+    log(f"{cfg}: inputs generated ({time.perf_counter() - t0:.1f} s)")
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     dims = M.make_dims(L.T, L.d, L.E, L.k, L.I, M.MOE_BF16 if L.dtype == "bf16" else M.MOE_F32,
                        args.tile_m)
     inp = upload(L, dev)
@@ -718,7 +721,6 @@ def main():
         b["cu_seqlens"] = inp["cu_seqlens"]
     ws = M.alloc_workspace(dims, dev)
     stream = torch.cuda.current_stream()
-    hip = HipEvents()
 
     for _ in range(args.warmup):
         M.forward(dims, b, ws)
@@ -743,45 +745,36 @@ def main():
     t2 = np.array([hip.ms(evs[3 * i + 1], evs[3 * i + 2]) for i in range(K)])
     hip.destroy(evs)
     hip.destroy(bnd)
-    stages = placement = variants = ranks = bwd = ep_share = None
-    if not args.no_reports:
-        stages = stage_rates(L, dims, inp, K, hip, stream)
+    log(f"{cfg}: {K} timed steps, median {float(np.median(step_ms)):.4f} ms")
+    out = {}
+    if reports:
+        out["stages_hbm"] = stage_rates(L, dims, inp, K, hip, stream)
         if L.E % 8 == 0:
-            placement = placement_report(L, dims, inp, host_counts, K, hip, stream)
+            out["placement"] = placement_report(L, dims, inp, host_counts, K, hip, stream)
+        out["expert_parallel"] = ranks_report(L, dims, inp, K, hip, stream)
         if L.mode == "router":
-            variants = variant_report(L, dims, inp, K, hip, stream)
-        ranks = ranks_report(L, dims, inp, K, hip, stream)
-        ep_share = ep_share_report(K, hip, stream)
-        if L.mode == "router":
-            bwd = backward_report(L, dims, inp, K, hip, stream)
-            bwd["forward_ms_for_reference"] = round(total_ms / K, 5)
+            out["router_variants"] = variant_report(L, dims, inp, K, hip, stream)
+            out["backward"] = backward_report(L, dims, inp, K, hip, stream)
+            out["backward"]["forward_ms_for_reference"] = round(float(np.median(step_ms)), 5)
+        log(f"{cfg}: stage and NEXT-row reports done")
 
     A = L.T * L.k
-    ms_step = total_ms / K
-    tokens_per_s = L.T / (ms_step * 1e-3)
+    med = float(np.median(step_ms))
     flops13 = 4.0 * A * L.d * L.I
     flops2 = 2.0 * A * L.I * L.d
     t13_avg = float(t13.mean())
     t2_avg = float(t2.mean())
     ach13 = flops13 / (t13_avg * 1e-3) / 1e12
     ach_ffn = (flops13 + flops2) / ((t13_avg + t2_avg) * 1e-3) / 1e12
-
-    rec = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+    out.update({
+        "tokens_per_s": round(L.T / (med * 1e-3), 1),
+        "ms_per_step_mean": round(total_ms / K, 5),
+        "step_ms": {"median": round(med, 5),
+                    "p10": round(float(np.percentile(step_ms, 10)), 5),
+                    "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "config": {"workload": WORKLOADS[cfg], "name": cfg, "T": L.T, "d": L.d, "E": L.E,
+                   "k": L.k, "inter": L.I, "mode": L.mode, "tile_m": args.tile_m or "auto"},
         "dtype": "bf16" if L.dtype == "bf16" else "f32",
-        "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "name": args.config, "T": L.T, "d": L.d,
-                   "E": L.E, "k": L.k, "inter": L.I, "mode": L.mode,
-                   "tile_m": args.tile_m or "auto"},
         "roofline": {
             "kernel": "grouped_gemm_dma128_kernel<gate/up + SwiGLU, fused gather>",
             "bound": "mfma",
@@ -789,7 +782,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach13 / PEAK_BF16_TFLOPS, 4),
-            "traffic": gemm_traffic(args.config) if not args.tile_m else None,
+            "traffic": gemm_traffic(cfg) if not args.tile_m else None,
             "algorithmic": f"4*T*k*d*I = {flops13:.4g} FLOP per launch",
             "avg_launch_ms": round(t13_avg, 5),
         },
@@ -800,27 +793,111 @@ def main():
             "down_ms": round(t2_avg, 5),
             "down_tflops": round(flops2 / (t2_avg * 1e-3) / 1e12, 2),
         },
-        "step_ms": {"median": round(float(np.median(step_ms)), 5),
-                    "p10": round(float(np.percentile(step_ms, 10)), 5),
-                    "p90": round(float(np.percentile(step_ms, 90)), 5)},
-        "stages_hbm": stages,
-        "placement": placement,
-        "router_variants": variants,
-        "expert_parallel": ranks,
-        "backward": bwd,
-        "ep_share": ep_share,
         "wall_s_timed": round(t_wall, 4),
-    }
-    if args.cpu_sample > 0:
-        tps, secs, threads = cpu_baseline(L, args.cpu_sample)
-        rec["cpu_baseline"] = {
+    })
+    if cpu_sample > 0:
+        tps, secs, threads = cpu_baseline(L, cpu_sample)
+        out["cpu_baseline"] = {
             "value": round(tps, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
-            "sample": f"first {min(args.cpu_sample, L.T)} of the {L.T} tokens, every stage "
+            "sample": f"first {min(cpu_sample, L.T)} of the {L.T} tokens, every stage "
                       f"({secs:.1f} s)",
         }
-    else:
-        rec["cpu_baseline"] = None
+        log(f"{cfg}: oracle sample done ({secs:.1f} s)")
+    del b, inp, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS),
+                    help="headline workload (default: the packed-microbatch layer, the "
+                         "largest that the metric is quoted on)")
+    ap.add_argument("--extra", default="c2,c4",
+                    help="further workloads timed in the same run and reported under "
+                         "'other_configs' (comma list, '' for none)")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
+                    help="tokens of the workload the CPU oracle runs (0 = skip)")
+    ap.add_argument("--tile-m", type=int, default=0)
+    ap.add_argument("--decode-t", default="1,2,4,8,16,32,64",
+                    help="batch sizes of the decode-shaped sweep (--config c5)")
+    ap.add_argument("--no-reports", action="store_true",
+                    help="time the layer steps only (no stage, placement, router-variant, "
+                         "expert-parallel or backward reports, no extra workloads): for "
+                         "counter passes, whose per-dispatch averages must see the step's "
+                         "kernels alone")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(expert-parallel sharding is a design note only); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.config == "c5":
+        decode_sweep(args)
+        return
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+    head = run_layer(args.config, args, hip, not args.no_reports, args.cpu_sample)
+    extra = {}
+    if not args.no_reports:
+        head["ep_share"] = ep_share_report(args.steps, hip, stream)
+        log("expert-parallel share done")
+        for cfg in [c for c in args.extra.split(",") if c and c != args.config]:
+            if cfg == "c5":
+                continue
+            r = run_layer(cfg, args, hip, reports=(cfg == "c2"), cpu_sample=0)
+            extra[cfg] = {n: r[n] for n in ("tokens_per_s", "step_ms", "grouped_gemm",
+                                            "roofline", "router_variants", "backward",
+                                            "placement", "stages_hbm", "expert_parallel")
+                          if n in r}
+            extra[cfg]["workload"] = r["config"]["workload"]
+
+    rec = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["step_ms"]["median"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "peak": derived_peak(hip),
+        "grouped_gemm": head["grouped_gemm"],
+        "step_ms": head["step_ms"],
+        "ms_per_step_mean": head["ms_per_step_mean"],
+        "stages_hbm": head.get("stages_hbm"),
+        "placement": head.get("placement"),
+        "expert_parallel": head.get("expert_parallel"),
+        "router_variants": head.get("router_variants"),
+        "backward": head.get("backward"),
+        "ep_share": head.get("ep_share"),
+        "other_configs": extra or None,
+        "wall_s_timed": head["wall_s_timed"],
+        "cpu_baseline": head.get("cpu_baseline"),
+    }
     print(json.dumps(rec), flush=True)
 
 

@@ -40,9 +40,10 @@ def _rng(seed: int, tid: int, chunk: int = 0) -> np.random.Generator:
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + r) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    # 32-bit arithmetic suffices: a finite value's bits are at most 0xFF7FFFFF, so adding
+    # at most 0x8000 cannot wrap; NaN patterns (which may wrap) are replaced below
+    out = ((u + (((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF))) >> 16).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = ((a.view(np.uint32)[nan] >> 16) | 0x40).astype(np.uint16)
