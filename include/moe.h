@@ -58,7 +58,8 @@ typedef enum moe_status {
     MOE_E_SHAPE = 2,     /* a size is outside the supported range */
     MOE_E_DTYPE = 3,     /* dtype is not MOE_F32 or MOE_BF16 */
     MOE_E_WORKSPACE = 4, /* workspace NULL or smaller than moe_workspace_size() */
-    MOE_E_LAUNCH = 5     /* the HIP runtime rejected a launch or an event record */
+    MOE_E_LAUNCH = 5,    /* the HIP runtime rejected a launch or an event record */
+    MOE_E_SCRATCH = 6    /* moe_forward_noalloc: the layer needs more than the static scratch */
 } moe_status;
 
 /* bits OR-ed into *d_err by device-side checks */
@@ -389,6 +390,23 @@ typedef struct moe_forward_args {
  * the entry point above defines it, enqueued on `stream` with no host synchronisation
  * (graph-capturable). */
 moe_status moe_forward(const moe_dims *dims, const moe_forward_args *args, void *stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same layer, bitwise
+ * the same outputs, with the workspace (and the shared expert's, after it at a 256-byte
+ * boundary) taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends; args->workspace,
+ * workspace_bytes, shared_workspace and shared_workspace_bytes are ignored. The caller
+ * still passes every input and output. No hipMalloc, hipFree or allocating library call.
+ * The array of the current device is used (the stream must belong to that device); its
+ * address is looked up on the first call on each device. Every call on one GPU shares the
+ * one array, which keeps the last call's contents (no step needs it cleared): calls that
+ * overlap on one GPU (other streams, other threads) race, and the caller must serialise
+ * them. Returns MOE_E_SCRATCH, enqueuing nothing, when moe_workspace_size(dims) (plus the
+ * shared expert's workspace) exceeds MOE_NOALLOC_SCRATCH_BYTES; otherwise as moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_dims *dims, const moe_forward_args *args,
+                               void *stream);
 
 /* Backward of the layer [EX][SW][RT][TRR]: the derivative of the forward definitions,
  * every reduction in one fixed order (results bitwise identical run to run; every per-token

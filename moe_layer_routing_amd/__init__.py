@@ -17,9 +17,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20     # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 DERR_IDX_RANGE, DERR_IDX_DUP, DERR_NONFINITE, DERR_SEQLENS, DERR_SLOTMAP = 1, 2, 4, 8, 16
 STATUS = {0: "MOE_OK", 1: "MOE_E_NULLPTR", 2: "MOE_E_SHAPE", 3: "MOE_E_DTYPE",
-          4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH"}
+          4: "MOE_E_WORKSPACE", 5: "MOE_E_LAUNCH", 6: "MOE_E_SCRATCH"}
 
 
 class MoeError(RuntimeError):
@@ -88,6 +89,8 @@ _SIGS = {
                         ctypes.c_int),
     "moe_combine": ([ctypes.POINTER(Dims)] + [_P] * 4 + [_P], ctypes.c_int),
     "moe_forward": ([ctypes.POINTER(Dims), ctypes.POINTER(ForwardArgs), _P], ctypes.c_int),
+    "moe_forward_noalloc": ([ctypes.POINTER(Dims), ctypes.POINTER(ForwardArgs), _P],
+                            ctypes.c_int),
     "moe_permute_placed": ([ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                             ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
                            ctypes.c_int),
@@ -311,6 +314,27 @@ def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=
     """Run moe_forward. ``bufs`` maps ForwardArgs field names to tensors (or None);
     ``prof_events`` is None or a sequence of three raw hipEvent_t handles; ``router`` is
     None or the keyword arguments of router_opts; ``routed_scale`` 0 means no factor."""
+    keep = _forward_args(bufs, workspace, prof_events, router, routed_scale, ranks,
+                         inter_shared, shared_workspace)
+    _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(keep[0]), _stream(stream)),
+           "moe_forward")
+
+
+def forward_noalloc(dims, bufs: dict, prof_events=None, stream=None,
+                    router: Optional[dict] = None, routed_scale: float = 0.0, ranks: int = 0,
+                    inter_shared: int = 0):
+    """Run moe_forward_noalloc: moe_forward with the library's static per-GPU scratch as
+    its workspace (the caller allocates no workspace). Same ``bufs`` as ``forward``."""
+    keep = _forward_args(bufs, None, prof_events, router, routed_scale, ranks, inter_shared,
+                         None)
+    _check(lib().moe_forward_noalloc(ctypes.byref(dims), ctypes.byref(keep[0]),
+                                     _stream(stream)), "moe_forward_noalloc")
+
+
+def _forward_args(bufs, workspace, prof_events, router, routed_scale, ranks, inter_shared,
+                  shared_workspace):
+    """ForwardArgs for ``bufs``, plus the ctypes objects it points into (kept alive by the
+    caller for the duration of the call)."""
     a = ForwardArgs()
     for name, _ in ForwardArgs._fields_:
         if name in ("num_seqs", "workspace", "workspace_bytes", "prof_events", "router",
@@ -330,14 +354,14 @@ def forward(dims, bufs: dict, workspace: torch.Tensor, prof_events=None, stream=
         a.shared_workspace_bytes = shared_workspace.numel()
     cu = bufs.get("cu_seqlens")
     a.num_seqs = 0 if cu is None else cu.numel() - 1
-    a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel()
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel()
     ev_arr = None
     if prof_events is not None:
         ev_arr = (ctypes.c_void_p * 3)(*prof_events)
         a.prof_events = ctypes.cast(ev_arr, ctypes.c_void_p)
-    _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(a), _stream(stream)),
-           "moe_forward")
+    return a, ropts, ev_arr
 
 
 def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.0,

@@ -1,6 +1,7 @@
 // moe_api.hip -- the C ABI: argument checks, workspace carving, launches.
 // Nothing here allocates, synchronises the host or throws.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "moe_internal.h"
@@ -69,6 +70,7 @@ const char *moe_status_string(moe_status s) {
     case MOE_E_DTYPE: return "unsupported dtype";
     case MOE_E_WORKSPACE: return "workspace missing or too small";
     case MOE_E_LAUNCH: return "HIP launch failed";
+    case MOE_E_SCRATCH: return "layer needs more workspace than the static scratch holds";
     }
     return "unknown status";
 }
@@ -347,12 +349,12 @@ moe_status moe_shared_ffn(const moe_dims *dims, int32_t ranks, int32_t inter_sha
 // The layer's output step: the plain combine, or (ranks >= 1) the shared expert's shards
 // and the rank partials with their FP64 tree.
 static hipError_t finish_layer(const moe_dims *dims, const moe_forward_args *a, float scale,
-                               hipStream_t s) {
+                               void *shared_work, hipStream_t s) {
     if (!a->ranks) return launch_combine(*dims, a->y, a->inv, a->topk_w, a->out, s, scale);
     if (a->w13_shared) {
         const hipError_t e = launch_shared_ffn(*dims, a->ranks, a->inter_shared, a->x,
                                                a->w13_shared, a->w2_shared, a->h_shared,
-                                               a->y_shared, a->shared_workspace, s);
+                                               a->y_shared, shared_work, s);
         if (e != hipSuccess) return e;
     }
     return launch_combine_ranks(*dims, a->ranks, a->y, a->inv, a->topk_w, a->topk_idx,
@@ -360,7 +362,10 @@ static hipError_t finish_layer(const moe_dims *dims, const moe_forward_args *a, 
                                 a->partials, a->out, s);
 }
 
-moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *stream) {
+// moe_forward with the workspace (and the shared expert's) given explicitly.
+static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, void *work,
+                               size_t work_bytes, void *shared_work, size_t shared_bytes,
+                               void *stream) {
     moe_status st = check_common(dims);
     if (st != MOE_OK) return st;
     MOE_REQUIRE(a, MOE_E_NULLPTR);
@@ -388,14 +393,13 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     if (a->w13_shared) {
         MOE_REQUIRE(a->ranks >= 1 && shared_ok(dims, a->ranks, a->inter_shared), MOE_E_SHAPE);
         MOE_REQUIRE(a->w2_shared && a->h_shared && a->y_shared, MOE_E_NULLPTR);
-        MOE_REQUIRE(a->shared_workspace && a->shared_workspace_bytes >=
-                                               shared_workspace_bytes(*dims, a->ranks,
-                                                                      a->inter_shared),
+        MOE_REQUIRE(shared_work && shared_bytes >= shared_workspace_bytes(*dims, a->ranks,
+                                                                         a->inter_shared),
                     MOE_E_WORKSPACE);
     }
-    st = check_ws(dims, a->workspace, a->workspace_bytes);
+    st = check_ws(dims, work, work_bytes);
     if (st != MOE_OK) return st;
-    const Workspace ws = carve_workspace(*dims, a->workspace);
+    const Workspace ws = carve_workspace(*dims, work);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dims->T >= 1 && dims->T <= kSmallT && !a->seq_counts) {
@@ -425,7 +429,7 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                                a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
         if (e != hipSuccess) return MOE_E_LAUNCH;
-        return to_status(finish_layer(dims, a, scale, s));
+        return to_status(finish_layer(dims, a, scale, shared_work, s));
     }
     if (replay)
         e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
@@ -442,7 +446,61 @@ moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *st
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                            a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
     if (e != hipSuccess) return MOE_E_LAUNCH;
-    return to_status(finish_layer(dims, a, scale, s));
+    return to_status(finish_layer(dims, a, scale, shared_work, s));
+}
+
+moe_status moe_forward(const moe_dims *dims, const moe_forward_args *a, void *stream) {
+    if (!a) return check_common(dims) != MOE_OK ? check_common(dims) : MOE_E_NULLPTR;
+    return forward_impl(dims, a, a->workspace, a->workspace_bytes, a->shared_workspace,
+                        a->shared_workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free forward
+// The workspace of moe_forward_noalloc: one array per GPU, held from the code object's load
+// until the process ends. Host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or nullptr when it cannot be had.
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    // a concurrent first call stores the same address
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const moe_dims *dims, const moe_forward_args *a, void *stream) {
+    moe_status st = check_common(dims);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(a, MOE_E_NULLPTR);
+    // the layer's workspace, then the shared expert's, carved from the one array
+    const size_t work = carve_workspace(*dims, nullptr).total;
+    size_t shared = 0;
+    if (a->w13_shared) {
+        MOE_REQUIRE(a->ranks >= 1 && shared_ok(dims, a->ranks, a->inter_shared), MOE_E_SHAPE);
+        shared = shared_workspace_bytes(*dims, a->ranks, a->inter_shared);
+    }
+    const size_t shared_off = align_up(work, 256);
+    MOE_REQUIRE(shared_off + shared <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_E_SCRATCH);
+    uint8_t *base = static_cast<uint8_t *>(scratch_ptr());
+    MOE_REQUIRE(base != nullptr, MOE_E_LAUNCH);
+    return forward_impl(dims, a, base, work, shared ? base + shared_off : nullptr, shared,
+                        stream);
 }
 
 moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *stream) {

@@ -77,7 +77,7 @@ def test_workspace_size(M):
 
 def test_status_strings(M):
     L = M.lib()
-    for s in range(6):
+    for s in range(7):
         assert L.moe_status_string(s)
 
 
@@ -131,3 +131,20 @@ def test_backward_gu_optional_only_on_bf16_layers(M):
         dims = M.make_dims(16, 128, 8, 2, 128, dtype)
         a = args(gu)
         assert L.moe_backward(ctypes.byref(dims), ctypes.byref(a), None) == status, (dtype, gu)
+
+
+def test_noalloc_rejects_layers_beyond_its_scratch(M):
+    """moe_forward_noalloc's host checks: a layer whose workspace exceeds the static scratch
+    is refused with MOE_E_SCRATCH before any HIP call; NULL args with MOE_E_NULLPTR."""
+    L = M.lib()
+    big = M.make_dims(100000, 128, 256, 8, 128, M.MOE_BF16)
+    assert M.workspace_size(big) > M.NOALLOC_SCRATCH_BYTES
+    a = M.ForwardArgs()
+    assert L.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(a), None) == 6
+    assert L.moe_forward_noalloc(ctypes.byref(big), None, None) == 1
+    bad = M.make_dims(16, 128, 8, 9, 128, M.MOE_BF16)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), ctypes.byref(a), None) == 2
+    # the header's limit is the binding's
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
+    assert M.NOALLOC_SCRATCH_BYTES == 64 << 20
