@@ -49,7 +49,7 @@ __device__ __forceinline__ void logit_chain(const void *__restrict__ x_,
     const int64_t t_row = min<int64_t>(tb + r, T - 1);
 #pragma unroll
     for (int j = 0; j < EPB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int kGroup = EPB >= 4 ? 2 : (EPB == 2 ? 4 : 8);
+    constexpr int kGroup = EPB >= 8 ? 2 : (EPB == 1 ? 8 : 4);
     constexpr int kStride = kLogitSplit;
     if constexpr (kBF16) {
         const uint16_t *wp[EPB];
@@ -105,18 +105,22 @@ __device__ __forceinline__ void logit_chain(const void *__restrict__ x_,
     }
 }
 
+// The logits of block `blk` of a launch with n_eg expert-tile groups: the 16 chains of EPB
+// expert tiles of one token tile, one chain per wave, added in chain order (then the bias).
 template <bool kBF16, int EPB>
-__global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
-    const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
-    float *__restrict__ logits, int64_t T, int d, int E) {
+__device__ __forceinline__ void logits_block(const void *__restrict__ x_,
+                                             const void *__restrict__ wr_,
+                                             const float *__restrict__ bias,
+                                             float *__restrict__ logits, int64_t T, int d,
+                                             int E, int64_t blk,
+                                             float (&part)[kLogitSplit][EPB][4][64]) {
     const int n_et = (E + 15) >> 4;
     const int n_eg = (n_et + EPB - 1) / EPB;
-    const int et0 = (int)(blockIdx.x % n_eg) * EPB;
-    const int64_t tb = (int64_t)(blockIdx.x / n_eg) * 16;
+    const int et0 = (int)(blk % n_eg) * EPB;
+    const int64_t tb = (blk / n_eg) * 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     f32x4_t acc[EPB];
     logit_chain<kBF16, EPB>(x_, wr_, T, d, E, tb, et0, wave, acc);
-    __shared__ float part[kLogitSplit][EPB][4][64];
 #pragma unroll
     for (int j = 0; j < EPB; ++j)
 #pragma unroll
@@ -132,6 +136,14 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
         const int e = (et0 + j) * 16 + 4 * (l >> 4) + i;
         if (t < T && e < E && et0 + j < n_et) logits[t * E + e] = bias ? v + bias[e] : v;
     }
+}
+
+template <bool kBF16, int EPB>
+__global__ __launch_bounds__(64 * kLogitSplit) void route_logits_kernel(
+    const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E) {
+    __shared__ float part[kLogitSplit][EPB][4][64];
+    logits_block<kBF16, EPB>(x_, wr_, bias, logits, T, d, E, blockIdx.x, part);
 }
 
 // Small batches: the 16 chains of every (token tile, expert tile) run as separate waves of
@@ -170,20 +182,23 @@ __global__ __launch_bounds__(64 * kChainWaves) void route_logit_chains_kernel(
 // tokens' q·p in token order (starting from 0), then the four waves' sums in wave order.
 static_assert(kTopkTokPerBlock == 16, "4 waves x 4 tokens");
 
+// Top-k of the 16 tokens of group `grp` (waves 0..3 of the block, 4 tokens each) and the
+// group's probability-mass partial; every thread of the block (nthr of them) reaches the
+// one barrier.
 template <int kFn, bool kHash, int NV>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
-                                                         const int32_t *__restrict__ q,
-                                                         int64_t T, int E, int k,
-                                                         int32_t *__restrict__ topk_idx,
-                                                         float *__restrict__ topk_w,
-                                                         float *__restrict__ mass_part,
-                                                         int32_t *__restrict__ d_err,
-                                                         RouteOpts opts) {
+__device__ __forceinline__ void topk_group(const float *__restrict__ logits,
+                                           const int32_t *__restrict__ q, int64_t T, int E,
+                                           int k, int32_t *__restrict__ topk_idx,
+                                           float *__restrict__ topk_w,
+                                           float *__restrict__ mass_part,
+                                           int32_t *__restrict__ d_err, const RouteOpts &opts,
+                                           int64_t grp, int nthr,
+                                           float (&mpt)[kTopkTokPerBlock][kMaxE]) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t0 = (int64_t)blockIdx.x * kTopkTokPerBlock + wave * 4;
+    const int64_t t0 = grp * kTopkTokPerBlock + wave * 4;
     float qp[kRowVals];
     int err = 0;
-    if (t0 < T) {   // wave-uniform; a wave past the batch only contributes zeros
+    if (wave < 4 && t0 < T) {   // wave-uniform; a wave past the batch only contributes zeros
         route_rows<kFn, kHash, NV>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr, qp,
                                    err);
     } else {
@@ -192,13 +207,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
     }
     wave_raise(err, d_err);
     if (mass_part) {
-        __shared__ float mpt[kTopkTokPerBlock][kMaxE];
         const int row = wave * 4 + (lane >> 4), c = lane & 15;
+        if (wave < 4) {
 #pragma unroll
-        for (int i = 0; i < kRowVals; ++i)
-            if (c + 16 * i < E) mpt[row][c + 16 * i] = qp[i];
+            for (int i = 0; i < kRowVals; ++i)
+                if (c + 16 * i < E) mpt[row][c + 16 * i] = qp[i];
+        }
         __syncthreads();
-        for (int e = threadIdx.x; e < E; e += 256) {
+        for (int e = threadIdx.x; e < E; e += nthr) {
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -208,9 +224,41 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
                 m = m + mpt[4 * w + 3][e];
                 v = (w == 0) ? m : v + m;
             }
-            mass_part[(int64_t)blockIdx.x * E + e] = v;
+            mass_part[grp * E + e] = v;
         }
     }
+}
+
+template <int kFn, bool kHash, int NV>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits,
+                                                         const int32_t *__restrict__ q,
+                                                         int64_t T, int E, int k,
+                                                         int32_t *__restrict__ topk_idx,
+                                                         float *__restrict__ topk_w,
+                                                         float *__restrict__ mass_part,
+                                                         int32_t *__restrict__ d_err,
+                                                         RouteOpts opts) {
+    __shared__ float mpt[kTopkTokPerBlock][kMaxE];
+    topk_group<kFn, kHash, NV>(logits, q, T, E, k, topk_idx, topk_w, mass_part, d_err, opts,
+                               blockIdx.x, 256, mpt);
+}
+
+// Logits and top-k in one launch, when one block holds every expert of its token tile
+// (EPB >= E/16): block b forms the logits of tokens 16b .. 16b+15 (as route_logits_kernel
+// does) and then routes the same 16 tokens (as route_topk_kernel's block b does), reading
+// the logits it has just written; every output is the bits of the two-kernel path.
+template <bool kBF16, int EPB, int kFn, bool kHash, int NV>
+__global__ __launch_bounds__(64 * kLogitSplit) void route_fused_kernel(
+    const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
+    float *__restrict__ logits, int64_t T, int d, int E, const int32_t *__restrict__ q, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    float *__restrict__ mass_part, int32_t *__restrict__ d_err, RouteOpts opts) {
+    __shared__ float part[kLogitSplit][EPB][4][64];
+    __shared__ float mpt[kTopkTokPerBlock][kMaxE];
+    logits_block<kBF16, EPB>(x_, wr_, bias, logits, T, d, E, blockIdx.x, part);
+    __syncthreads();   // the block's own global writes are visible to it after this
+    topk_group<kFn, kHash, NV>(logits, q, T, E, k, topk_idx, topk_w, mass_part, d_err, opts,
+                               blockIdx.x, 64 * kLogitSplit, mpt);
 }
 
 // prob_mass[e]: one block per expert; thread i adds the partials of blocks i, i+256, ...
@@ -322,6 +370,31 @@ static void launch_topk_t(const moe_dims &dm, int64_t tblk, const float *logits,
     });
 }
 
+// Logits + top-k in one launch for the plain softmax router when the logits launch would
+// give every block all expert tiles of its token tile anyway (EPB >= number of tiles).
+template <bool kBF16>
+static bool launch_fused_t(const moe_dims &dm, const void *x, const void *w_router,
+                           const float *bias, float *logits, const int32_t *q,
+                           int32_t *topk_idx, float *topk_w, float *mass_part, int32_t *d_err,
+                           const RouteOpts &o, hipStream_t s) {
+    const int n_et = (dm.E + 15) / 16;
+    const int epb = logits_epb(dm.T, dm.E);
+    if (!o.plain() || epb < n_et) return false;
+    const dim3 grid((unsigned)((dm.T + 15) / 16)), block(64 * kLogitSplit);
+#define MOE_FUSED(EPB, NV)                                                                    \
+    route_fused_kernel<kBF16, EPB, kScoreSoftmax, false, NV><<<grid, block, 0, s>>>(          \
+        x, w_router, bias, logits, dm.T, dm.d, dm.E, q, dm.k, topk_idx, topk_w, mass_part,   \
+        d_err, o)
+    switch (epb) {
+    case 1: MOE_FUSED(1, 4); break;
+    case 2: MOE_FUSED(2, 4); break;
+    case 4: MOE_FUSED(4, 4); break;
+    default: MOE_FUSED(8, 8); break;
+    }
+#undef MOE_FUSED
+    return true;
+}
+
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                         const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
                         float *mass_part, float *prob_mass, const int32_t *token_mult,
@@ -329,10 +402,21 @@ hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
     const int64_t T = dm.T;
     const int E = dm.E;
     if (T > 0) {
-        const hipError_t le = launch_router_logits(dm, x, w_router, bias, logits, s);
-        if (le != hipSuccess) return le;
         const int64_t tblk = (T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
         float *mp = prob_mass ? mass_part : nullptr;
+        const bool fused =
+            dm.dtype == MOE_BF16
+                ? launch_fused_t<true>(dm, x, w_router, bias, logits, token_mult, topk_idx,
+                                       topk_w, mp, d_err, o, s)
+                : launch_fused_t<false>(dm, x, w_router, bias, logits, token_mult, topk_idx,
+                                        topk_w, mp, d_err, o, s);
+        if (fused) {
+            if (prob_mass)
+                mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
+            return hipGetLastError();
+        }
+        const hipError_t le = launch_router_logits(dm, x, w_router, bias, logits, s);
+        if (le != hipSuccess) return le;
         const bool h = o.hash_table != nullptr;
         switch (o.fn * 2 + (h ? 1 : 0)) {
         case 0: launch_topk_t<kScoreSoftmax, false>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
