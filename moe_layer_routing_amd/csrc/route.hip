@@ -36,71 +36,116 @@ static_assert(kLogitSplit == 16, "16 K-chains per logit");
 
 // Chain `chain` of the logits of token tile tb (16 tokens) and expert tiles et0 .. et0+EPB-1:
 // K-steps chain, chain+16, ... accumulated in that order into acc (one MFMA per step and
-// tile; the operands of up to kGroup steps are loaded before their MFMAs so that the loads
-// overlap). Every kernel that forms logits runs this routine, so a chain's partial is the
+// tile). Every kernel that forms logits runs this routine, so a chain's partial is the
 // same bits whichever launch computes it.
+//
+// Operand loads: a fragment is 16 rows x one K-step. Loaded in the MFMA layout (lane l:
+// row l%16, K-slice l/16) every lane of a 4-lane group would touch a different row, and
+// the memory pipeline serves such a load as 64 separate pieces; so lane l loads row l/4,
+// K-slice l%4 (each 4-lane group reads one row's contiguous K-step) and a cross-lane
+// permutation (ds_bpermute: lane l takes lane 4(l%16) + l/16's value) puts every value in
+// the lane the MFMA reads it from. The MFMA operands are unchanged, value for value.
+// Steps go in groups of kGroup whose loads are all issued before the first MFMA of the
+// group; a chain's last steps that do not fill a group follow one at a time, in order.
+__device__ __forceinline__ int to_mfma_lane(int v, int src) {
+    return __builtin_amdgcn_ds_bpermute(src, v);
+}
+
 template <bool kBF16, int EPB>
 __device__ __forceinline__ void logit_chain(const void *__restrict__ x_,
                                             const void *__restrict__ wr_, int64_t T, int d,
                                             int E, int64_t tb, int et0, int chain,
                                             f32x4_t (&acc)[EPB]) {
     const int lane = threadIdx.x & 63;
-    const int r = lane & 15, g = lane >> 4;
-    const int64_t t_row = min<int64_t>(tb + r, T - 1);
+    const int rc = lane >> 2, gc = lane & 3;                  // the lane's load row / slice
+    const int src = 4 * (4 * (lane & 15) + (lane >> 4));       // byte address of its source
+    const int64_t t_row = min<int64_t>(tb + rc, T - 1);
 #pragma unroll
     for (int j = 0; j < EPB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     constexpr int kGroup = EPB >= 8 ? 2 : (EPB == 1 ? 8 : 4);
     constexpr int kStride = kLogitSplit;
     if constexpr (kBF16) {
+        auto lay = [&](bf16x8_t v) {
+            int4 q = __builtin_bit_cast(int4, v);
+            q.x = to_mfma_lane(q.x, src);
+            q.y = to_mfma_lane(q.y, src);
+            q.z = to_mfma_lane(q.z, src);
+            q.w = to_mfma_lane(q.w, src);
+            return __builtin_bit_cast(bf16x8_t, q);
+        };
         const uint16_t *wp[EPB];
 #pragma unroll
         for (int j = 0; j < EPB; ++j)
             wp[j] = static_cast<const uint16_t *>(wr_) +
-                    (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g * 8;
-        const uint16_t *xp = static_cast<const uint16_t *>(x_) + t_row * d + g * 8;
+                    (int64_t)min((et0 + j) * 16 + rc, E - 1) * d + gc * 8;
+        const uint16_t *xp = static_cast<const uint16_t *>(x_) + t_row * d + gc * 8;
         const int nsteps = d >> 5;
-        for (int s0 = chain; s0 < nsteps; s0 += kStride * kGroup) {
+        int s0 = chain;
+        for (; s0 + kStride * (kGroup - 1) < nsteps; s0 += kStride * kGroup) {
             bf16x8_t a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                const int st = min(s0 + kStride * i, nsteps - 1);
+                const int st = s0 + kStride * i;
                 b[i] = *reinterpret_cast<const bf16x8_t *>(xp + st * 32);
 #pragma unroll
                 for (int j = 0; j < EPB; ++j)
                     a[i][j] = *reinterpret_cast<const bf16x8_t *>(wp[j] + st * 32);
             }
+            __builtin_amdgcn_sched_barrier(0);   // the group's loads are all in flight
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                if (s0 + kStride * i < nsteps)
+            for (int i = 0; i < kGroup; ++i) {
+                const bf16x8_t bi = lay(b[i]);
 #pragma unroll
-                    for (int j = 0; j < EPB; ++j)
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][j], b[i], acc[j],
-                                                                         0, 0, 0);
+                for (int j = 0; j < EPB; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lay(a[i][j]), bi, acc[j],
+                                                                     0, 0, 0);
+            }
+        }
+        for (; s0 < nsteps; s0 += kStride) {
+            const bf16x8_t bi = lay(*reinterpret_cast<const bf16x8_t *>(xp + s0 * 32));
+#pragma unroll
+            for (int j = 0; j < EPB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    lay(*reinterpret_cast<const bf16x8_t *>(wp[j] + s0 * 32)), bi, acc[j], 0,
+                    0, 0);
         }
     } else {
+        auto lay = [&](float v) {
+            return __builtin_bit_cast(float, to_mfma_lane(__builtin_bit_cast(int, v), src));
+        };
         const float *wp[EPB];
 #pragma unroll
         for (int j = 0; j < EPB; ++j)
             wp[j] = static_cast<const float *>(wr_) +
-                    (int64_t)min((et0 + j) * 16 + r, E - 1) * d + g;
-        const float *xp = static_cast<const float *>(x_) + t_row * d + g;
+                    (int64_t)min((et0 + j) * 16 + rc, E - 1) * d + gc;
+        const float *xp = static_cast<const float *>(x_) + t_row * d + gc;
         const int nsteps = d >> 2;
-        for (int s0 = chain; s0 < nsteps; s0 += kStride * kGroup) {
+        int s0 = chain;
+        for (; s0 + kStride * (kGroup - 1) < nsteps; s0 += kStride * kGroup) {
             float a[kGroup][EPB], b[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                const int st = min(s0 + kStride * i, nsteps - 1);
+                const int st = s0 + kStride * i;
                 b[i] = xp[st * 4];
 #pragma unroll
                 for (int j = 0; j < EPB; ++j) a[i][j] = wp[j][st * 4];
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                if (s0 + kStride * i < nsteps)
+            for (int i = 0; i < kGroup; ++i) {
+                const float bi = lay(b[i]);
 #pragma unroll
-                    for (int j = 0; j < EPB; ++j)
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][j], b[i], acc[j],
-                                                                      0, 0, 0);
+                for (int j = 0; j < EPB; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(lay(a[i][j]), bi, acc[j],
+                                                                  0, 0, 0);
+            }
+        }
+        for (; s0 < nsteps; s0 += kStride) {
+            const float bi = lay(xp[s0 * 4]);
+#pragma unroll
+            for (int j = 0; j < EPB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(lay(wp[j][s0 * 4]), bi, acc[j],
+                                                              0, 0, 0);
         }
     }
 }
@@ -118,7 +163,7 @@ __device__ __forceinline__ void logits_block(const void *__restrict__ x_,
     const int n_eg = (n_et + EPB - 1) / EPB;
     const int et0 = (int)(blk % n_eg) * EPB;
     const int64_t tb = (blk / n_eg) * 16;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     f32x4_t acc[EPB];
     logit_chain<kBF16, EPB>(x_, wr_, T, d, E, tb, et0, wave, acc);
 #pragma unroll
@@ -163,7 +208,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void route_logit_chains_kernel(
     const int tile = (int)(blockIdx.x / kGroups);
     const int et0 = tile % n_et;
     const int64_t tb = (int64_t)(tile / n_et) * 16;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int chain = cg * kChainWaves + wave;
     f32x4_t acc[1];
     logit_chain<kBF16, 1>(x_, wr_, T, d, E, tb, et0, chain, acc);
