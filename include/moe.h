@@ -425,7 +425,10 @@ moe_status moe_forward_noalloc(const moe_dims *dims, const moe_forward_args *arg
  *     x, w_router and logit_bias when logits is NULL), p = softmax, s' = sum of the chosen
  *     p left to right; a = sum_j d_topk_w[t,j] p_j / s', dp_j = (d_topk_w[t,j] - a) / s',
  *     c = sum_j dp_j p_j; d_logits[t,e] = p_e (dp_e - c) (dp_e = 0 for experts not chosen);
- *     d_w_router = d_logits^T x; d_x_router = d_logits w_router.
+ *     d_w_router = d_logits^T x; d_x_router = d_logits w_router. For T >= 512 and E, d
+ *     multiples of 4, d_w_router's sum over t runs as S = min(8, T/256) segments of
+ *     ceil(T/S) ascending rows, each its own ascending sum, the S partials then added in
+ *     segment order (the partials are staged in d_x, which the call writes last).
  *     Under routing replay this is the gradient of w - sg[w] + w* ("Total Router Recall"):
  *     the forward value is the replayed w*, the router's gradient flows through its own
  *     weights at its own choice, slot by slot.
@@ -441,7 +444,7 @@ moe_status moe_forward_noalloc(const moe_dims *dims, const moe_forward_args *arg
  * forms d_gu in its epilogue with the same arithmetic, so every gradient has the same bits
  * and gu is not written), d_h [T*k,I], d_gu [T*k,2I], d_xp [T*k,d]; x_perm [T*k,d] or NULL (the
  * recomputation gathers x through perm; x must then be under 4 GiB); workspace of
- * moe_workspace_size() bytes. */
+ * moe_workspace_size() bytes. No output or intermediate may overlap an input. */
 typedef struct moe_backward_args {
     const void *x;
     const void *x_perm;

@@ -373,7 +373,8 @@ __global__ __launch_bounds__(256) void dgrad_kernel(const float *__restrict__ ac
 // Weight gradient: out[e, n, c] = sum over the segment's rows p ascending of
 // a[p, n] b[p, c]; a FP32 [rows, N], b [rows, C] (bf16 or FP32; row of b = bperm[p] / bk
 // when bperm is given: the gathered token rows), out FP32 [E, N, C]. Segment e = rows
-// [off[e], off[e+1]) (off NULL: one segment of nrows rows). Block: BN x BC outputs of one
+// [off[e], off[e+1]) (off NULL: segments of seg_rows rows, or with seg_rows 0 one segment
+// of nrows rows). Block: BN x BC outputs of one
 // expert, four waves of (BN/2) x (BC/2); K = the segment's rows in stages of KC, the tail
 // zero-filled. MFMA operand A = a (rows n, K = p), B = b (K = p, columns c): lane l holds
 // a[p0 + l/16][n + l%16] and b[p0 + l/16][c + l%16]; the result lane l holds column
@@ -384,7 +385,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
                                                     const int32_t *__restrict__ bperm, int bk,
                                                     int64_t bT, const int32_t *__restrict__ off,
                                                     int64_t nrows, int N, int C, int nbn,
-                                                    int nbc, float *__restrict__ out) {
+                                                    int nbc, float *__restrict__ out,
+                                                    int64_t seg_rows = 0) {
     constexpr int WN = BN / 2, WC = BC / 2, NF = WN / 16, NC = WC / 16;
     constexpr int kAS = BN + 4, kBS = BC + 4;
     __shared__ float sa[2][KC * kAS];
@@ -396,6 +398,9 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const float *__restrict__ a,
     if (off) {
         r0 = min<int64_t>(max(off[e], 0), nrows);
         r1 = min<int64_t>(max<int64_t>(off[e + 1], r0), nrows);
+    } else if (seg_rows > 0) {
+        r0 = min<int64_t>((int64_t)e * seg_rows, nrows);
+        r1 = min<int64_t>(r0 + seg_rows, nrows);
     }
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wn = wv & 1, wc = wv >> 1;
@@ -867,20 +872,46 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float *__restri
     dwr[i] = acc;
 }
 
+// dwr[i] = part[0][i] + part[1][i] + ... + part[S-1][i], left to right.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float *__restrict__ part, int S,
+                                                        int64_t n, float *__restrict__ out) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 acc = *reinterpret_cast<const float4 *>(part + i);
+    for (int j = 1; j < S; ++j) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)j * n + i);
+        acc.x = acc.x + v.x;
+        acc.y = acc.y + v.y;
+        acc.z = acc.z + v.z;
+        acc.w = acc.w + v.w;
+    }
+    *reinterpret_cast<float4 *>(out + i) = acc;
+}
+
 hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *x, float *dwr,
-                               hipStream_t s) {
+                               float *scratch, int64_t scratch_floats, hipStream_t s) {
     if (dm.E % 4 == 0 && dm.d % 4 == 0) {
-        // one segment of T rows and only E x d outputs: 32 x 32 tiles give E d / 1024
-        // blocks (each output is the same MFMA chain over ascending rows at any tile size)
+        // only E x d outputs, over a T-long sum: 32 x 32 tiles (E d / 1024 blocks) with
+        // 64-row stages, and, when the scratch holds them, the rows split into S ascending
+        // segments of at least 256 rows whose partials are then added in segment order
+        const int64_t n = (int64_t)dm.E * dm.d;
+        int S = (int)std::max<int64_t>(1, std::min<int64_t>(kRouterWgradSplit, dm.T / 256));
+        if (!scratch || scratch_floats < S * n) S = 1;
+        const int64_t seg = (dm.T + S - 1) / S;
+        float *dst = S > 1 ? scratch : dwr;
         const int nbn = (dm.E + 31) / 32, nbc = (dm.d + 31) / 32;
-        const dim3 grid((unsigned)((int64_t)nbn * nbc));
-        // and 64-row stages: a quarter of the barriers on the T-long chain
+        const dim3 grid((unsigned)((int64_t)S * nbn * nbc));
         if (dm.dtype == MOE_BF16)
             wgrad_kernel<true, 32, 32, 64><<<grid, dim3(256), 0, s>>>(
-                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dwr);
+                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dst,
+                S > 1 ? seg : 0);
         else
             wgrad_kernel<false, 32, 32, 64><<<grid, dim3(256), 0, s>>>(
-                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dwr);
+                dl, x, nullptr, 1, dm.T, nullptr, dm.T, dm.E, dm.d, nbn, nbc, dst,
+                S > 1 ? seg : 0);
+        if (S > 1)
+            sum_parts_kernel<<<dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s>>>(
+                scratch, S, n, dwr);
         return hipGetLastError();
     }
     const int64_t n = (int64_t)dm.E * dm.d;

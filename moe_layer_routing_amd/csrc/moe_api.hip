@@ -591,7 +591,10 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
         e = launch_router_bwd(*dims, logits, a->d_topk_w, a->d_logits, s);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         if (a->d_w_router) {
-            e = launch_router_wgrad(*dims, a->d_logits, a->x, a->d_w_router, s);
+            // d_x is written last (the slot-order sum below): its T x d floats serve as
+            // the scratch of the router weight gradient's row segments
+            e = launch_router_wgrad(*dims, a->d_logits, a->x, a->d_w_router, a->d_x,
+                                    dims->T * (int64_t)dims->d, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
         }
         e = launch_router_dx(*dims, a->d_logits, a->w_router, a->d_x_router, s);

@@ -17,6 +17,7 @@ constexpr int kPermChunk = 2048;   // flat assignments per permute block (fixed,
 constexpr int kTopkTokPerBlock = 16;  // 4 waves x 4 tokens
 constexpr int kSmallT = 64;           // largest batch the single-block routing tail takes
 constexpr int kMaxRanks = 16;         // ranks of the emulated expert-parallel output
+constexpr int kRouterWgradSplit = 8;  // row segments of the router weight gradient
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -250,8 +251,9 @@ hipError_t launch_dgrad(const moe_dims &dm, const float *act, const void *wgt, b
 hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
                         const int32_t *bperm, int bk, int64_t bT, const int32_t *off,
                         int64_t nrows, int N, int C, float *out, hipStream_t s);
+// scratch: scratch_floats floats the call may overwrite (NULL: no row split)
 hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *x, float *dwr,
-                               hipStream_t s);
+                               float *scratch, int64_t scratch_floats, hipStream_t s);
 hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
                             float *dx, hipStream_t s);
 // Objective statistics (one block): out[3] = z_loss, aux_loss, S; optional bias update.

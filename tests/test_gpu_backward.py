@@ -94,6 +94,7 @@ CASES = [
     (257, 128, 24, 4, 128, "f32", "router", 1.5, False, False),
     (300, 128, 16, 4, 128, "bf16", "replay", 1.0, False, False),    # router grads recomputed
     (123, 192, 10, 3, 64, "f32", "replay", 1.0, True, True),        # E % 4 != 0
+    (1100, 128, 16, 4, 128, "f32", "router", 1.0, False, False),    # d_w_router in 4 segments
 ]
 
 
