@@ -700,7 +700,7 @@ void wgrad_dma_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict
             const int n = n0 + (lr >> 5) * WN + 32 * pass + (lr & 31);
             const float4 v = *reinterpret_cast<const float4 *>(stage + lr * kOutStride + 4 * lane);
             if (n < N && cc < C)
-                *reinterpret_cast<float4 *>(out + ((int64_t)e * N + n) * C + cc) = v;
+                store_nt(out + ((int64_t)e * N + n) * C + cc, v);
         }
         if (pass == 0) __syncthreads();
     }

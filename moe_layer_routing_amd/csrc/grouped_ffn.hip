@@ -547,8 +547,8 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
                 const int r = idx / kRow4, c = (idx % kRow4) * 4;
                 const int m = q * RP + r;
                 if (m < nrows && n0 + c < N)
-                    *reinterpret_cast<float4 *>(outf + ((int64_t)p0 + m) * N + n0 + c) =
-                        *reinterpret_cast<const float4 *>(stg + r * kLd + c);
+                    store_nt(outf + ((int64_t)p0 + m) * N + n0 + c,
+                             *reinterpret_cast<const float4 *>(stg + r * kLd + c));
             }
             __syncthreads();
         }
