@@ -127,47 +127,59 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float *__restrict
 }
 
 // ------------------------------------------------------------ dx: slot-order sum
+// One wave per (token, 512-feature slice); lane l takes features s*512 + 4l and
+// s*512 + 256 + 4l. The token's k slot indices are loaded first, then every row load of
+// both chunks (and the router part) is issued before the sums consume them.
+constexpr int kDxSlice = 512;
 __global__ __launch_bounds__(256) void dx_sum_kernel(const float *__restrict__ dxp,
                                                      const int32_t *__restrict__ inv,
                                                      const float *__restrict__ dxr,
                                                      int64_t T, int k, int d, int64_t A,
                                                      float *__restrict__ dx) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= T * d) return;
-    const int64_t t = i / d;
-    const int c = (int)(i - t * d);
-    // all k slot indices, then all k row loads, are issued before the slot-order sum
-    // consumes them (vmcnt retires in order: a wait for an index placed after a row load
-    // would wait for that row as well)
-    int32_t pi[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) pi[j] = (j < k) ? inv[t * k + j] : 0;
-    float4 v[kMaxK];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nslice = (d + kDxSlice - 1) / kDxSlice;
+    const int64_t W = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t t = W / nslice;
+    if (t >= T) return;
+    const int c0 = (int)(W % nslice) * kDxSlice + lane * 4;
+    int64_t src[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            const int32_t p = (pi[j] < 0 || pi[j] >= A) ? 0 : pi[j];
-            v[j] = *reinterpret_cast<const float4 *>(dxp + (int64_t)p * d + c);
-        }
+        int32_t p = (j < k) ? inv[t * k + j] : 0;
+        p = (p < 0 || p >= A) ? 0 : p;
+        src[j] = (int64_t)p * d;
     }
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float4 v[2][kMaxK], r[2];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            a0 = a0 + v[j].x;
-            a1 = a1 + v[j].y;
-            a2 = a2 + v[j].z;
-            a3 = a3 + v[j].w;
+    for (int u = 0; u < 2; ++u) {
+        const int c = min(c0 + 256 * u, d - 4);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) v[u][j] = *reinterpret_cast<const float4 *>(dxp + src[j] + c);
+        if (dxr) r[u] = *reinterpret_cast<const float4 *>(dxr + t * d + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = c0 + 256 * u;
+        if (c >= d) break;
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                a0 = a0 + v[u][j].x;
+                a1 = a1 + v[u][j].y;
+                a2 = a2 + v[u][j].z;
+                a3 = a3 + v[u][j].w;
+            }
         }
+        if (dxr) {
+            a0 = a0 + r[u].x;
+            a1 = a1 + r[u].y;
+            a2 = a2 + r[u].z;
+            a3 = a3 + r[u].w;
+        }
+        *reinterpret_cast<float4 *>(dx + t * d + c) = make_float4(a0, a1, a2, a3);
     }
-    if (dxr) {
-        const float4 r = *reinterpret_cast<const float4 *>(dxr + i);
-        a0 = a0 + r.x;
-        a1 = a1 + r.y;
-        a2 = a2 + r.z;
-        a3 = a3 + r.w;
-    }
-    *reinterpret_cast<float4 *>(dx + i) = make_float4(a0, a1, a2, a3);
 }
 
 // ------------------------------------------------------------------ router backward
@@ -758,9 +770,9 @@ hipError_t launch_wgrad_bf16(int nseg, const void *a, const void *b, const int32
 
 hipError_t launch_dx_sum(const moe_dims &dm, const float *dxp, const int32_t *inv,
                          const float *dxr, float *dx, hipStream_t s) {
-    const int64_t n = dm.T * dm.d / 4;
-    if (n == 0) return hipGetLastError();
-    dx_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+    if (dm.T == 0) return hipGetLastError();
+    const int64_t waves = dm.T * ((dm.d + kDxSlice - 1) / kDxSlice);
+    dx_sum_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s>>>(
         dxp, inv, dxr, dm.T, dm.k, dm.d, dm.T * dm.k, dx);
     return hipGetLastError();
 }
@@ -808,50 +820,97 @@ hipError_t launch_wgrad(int nseg, const float *a, const void *b, bool bbf16,
     return hipGetLastError();
 }
 
-// dx_r[t, c] = sum over e ascending of dl[t, e] w_router[e, c]; each thread takes four
-// consecutive features of kRdxTok consecutive tokens, so each router-weight load serves
-// 4 x kRdxTok products (the weights were re-read from L2 once per token before).
-constexpr int kRdxTok = 4;
+// dx_r[t, c] = sum over e of dl[t, e] w_router[e, c] on FP32 MFMA (16x16x4): a block of
+// 4 waves covers 64 tokens x 64 features, wave w tokens 16w .. 16w+15; A = 16 router-weight
+// features x 4 experts, B = 4 experts x 16 tokens, K = the experts ascending, 4 per step.
+// Each 64-expert chunk of dl (64 tokens) and of the weights (64 features, widened to FP32)
+// is copied to LDS with coalesced loads first; the result goes through LDS so that every
+// output row leaves as 16 lanes x 16 bytes.
+constexpr int kRdxT = 64, kRdxC = 64, kRdxE = 64, kRdxLd = kRdxE + 1, kRdxOut = kRdxC + 4;
 __global__ __launch_bounds__(256) void router_dx_kernel(const float *__restrict__ dl,
                                                         const void *__restrict__ wr, bool bf16,
                                                         int64_t T, int E, int d,
                                                         float *__restrict__ dx) {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (token group, quad)
-    const int nq = d / 4;
-    const int64_t tg = q / nq;
-    const int c = (int)(q - tg * nq) * 4;
-    const int64_t t0 = tg * kRdxTok;
-    if (t0 >= T) return;
-    float a[kRdxTok][4];
+    __shared__ float sdl[kRdxT * kRdxLd];      // [token][expert of the chunk]
+    __shared__ float sw[kRdxE * kRdxOut];      // [expert of the chunk][feature]
+    __shared__ float sout[kRdxT * kRdxOut];    // [token][feature]
+    const int ncb = (d + kRdxC - 1) / kRdxC;
+    const int64_t t0 = (int64_t)(blockIdx.x / ncb) * kRdxT;
+    const int c0 = (int)(blockIdx.x % ncb) * kRdxC;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    f32x4_t acc[kRdxC / 16];
 #pragma unroll
-    for (int u = 0; u < kRdxTok; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) a[u][v] = 0.f;
-    for (int e = 0; e < E; ++e) {
-        float w[4];
-        if (bf16) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(wr) + (int64_t)e * d + c);
-            w[0] = bf16_to_f32((uint16_t)(v.x & 0xffff));
-            w[1] = bf16_to_f32((uint16_t)(v.x >> 16));
-            w[2] = bf16_to_f32((uint16_t)(v.y & 0xffff));
-            w[3] = bf16_to_f32((uint16_t)(v.y >> 16));
+    for (int f = 0; f < kRdxC / 16; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int e0 = 0; e0 < E; e0 += kRdxE) {
+        const int ne = min(kRdxE, E - e0);
+        __syncthreads();   // the previous chunk's LDS reads are done
+        if (E % 4 == 0) {   // 16-byte loads of dl rows
+            for (int i = tid; i < kRdxT * kRdxE / 4; i += 256) {
+                const int tt = i / (kRdxE / 4), ee = (i % (kRdxE / 4)) * 4;
+                const int64_t t = t0 + tt;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t < T && ee < ne) v = *reinterpret_cast<const float4 *>(dl + t * E + e0 + ee);
+                float *q = sdl + tt * kRdxLd + ee;
+                q[0] = v.x;
+                q[1] = v.y;
+                q[2] = v.z;
+                q[3] = v.w;
+            }
         } else {
-            const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(wr) + (int64_t)e * d + c);
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            for (int i = tid; i < kRdxT * kRdxE; i += 256) {
+                const int tt = i / kRdxE, ee = i % kRdxE;
+                const int64_t t = t0 + tt;
+                sdl[tt * kRdxLd + ee] = (t < T && ee < ne) ? dl[t * E + e0 + ee] : 0.f;
+            }
         }
+        // router weights: 8 features (16 or 32 bytes) per load; d is a multiple of 64
+        for (int i = tid; i < kRdxE * kRdxC / 8; i += 256) {
+            const int ee = i / (kRdxC / 8), cc = (i % (kRdxC / 8)) * 8;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (ee < ne) {
+                const int64_t o = (int64_t)(e0 + ee) * d + c0 + cc;
+                if (bf16) {
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(wr) + o);
+                    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int u = 0; u < kRdxTok; ++u) {
-            const int64_t t = min<int64_t>(t0 + u, T - 1);
-            const float g = dl[t * E + e];
+                    for (int q = 0; q < 4; ++q) {
+                        v[2 * q] = bf16_to_f32((uint16_t)(wv[q] & 0xffffu));
+                        v[2 * q + 1] = bf16_to_f32((uint16_t)(wv[q] >> 16));
+                    }
+                } else {
+                    const float4 x0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(wr) + o);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(wr) + o + 4);
+                    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+                    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                }
+            }
+            *reinterpret_cast<float4 *>(sw + ee * kRdxOut + cc) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4 *>(sw + ee * kRdxOut + cc + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        __syncthreads();
+        for (int k0 = 0; k0 < ne; k0 += 4) {
+            const float b = sdl[(16 * wave + r) * kRdxLd + k0 + g];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a[u][v] = a[u][v] + g * w[v];
+            for (int f = 0; f < kRdxC / 16; ++f) {
+                const float a = sw[(k0 + g) * kRdxOut + 16 * f + r];
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[f], 0, 0, 0);
+            }
         }
     }
+    // result lane l: token 16 wave + l%16, features 16 f + 4 (l/16) + 0..3
 #pragma unroll
-    for (int u = 0; u < kRdxTok; ++u)
-        if (t0 + u < T)
-            *reinterpret_cast<float4 *>(dx + (t0 + u) * d + c) =
-                make_float4(a[u][0], a[u][1], a[u][2], a[u][3]);
+    for (int f = 0; f < kRdxC / 16; ++f)
+        *reinterpret_cast<float4 *>(sout + (16 * wave + r) * kRdxOut + 16 * f + 4 * g) =
+            make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+    __syncthreads();
+    for (int i = tid; i < kRdxT * (kRdxC / 4); i += 256) {
+        const int tt = i / (kRdxC / 4), cc = (i % (kRdxC / 4)) * 4;
+        const int64_t t = t0 + tt;
+        if (t < T && c0 + cc < d)
+            *reinterpret_cast<float4 *>(dx + t * d + c0 + cc) =
+                *reinterpret_cast<const float4 *>(sout + tt * kRdxOut + cc);
+    }
 }
 
 // dw_router[e, c] = sum over t ascending of dl[t, e] x[t, c] when E is not a multiple of 4
@@ -922,9 +981,9 @@ hipError_t launch_router_wgrad(const moe_dims &dm, const float *dl, const void *
 
 hipError_t launch_router_dx(const moe_dims &dm, const float *dl, const void *w_router,
                             float *dx, hipStream_t s) {
-    const int64_t n = (dm.T + kRdxTok - 1) / kRdxTok * (dm.d / 4);
-    if (n == 0) return hipGetLastError();
-    router_dx_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+    if (dm.T == 0) return hipGetLastError();
+    const int64_t blocks = (dm.T + kRdxT - 1) / kRdxT * ((dm.d + kRdxC - 1) / kRdxC);
+    router_dx_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
         dl, w_router, dm.dtype == MOE_BF16, dm.T, dm.E, dm.d, dx);
     return hipGetLastError();
 }
