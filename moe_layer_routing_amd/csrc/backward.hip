@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         float4 yv[kMaxK];
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
-            if (j < k) yv[j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
+            if (j < k) yv[j] = load_nt(y + src[j] + c);
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
             if (j < k) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const float *__restrict__ d
         const int c = min(c0 + 256 * u, d - 4);
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j)
-            if (j < k) v[u][j] = *reinterpret_cast<const float4 *>(dxp + src[j] + c);
+            if (j < k) v[u][j] = load_nt(dxp + src[j] + c);
         if (dxr) r[u] = *reinterpret_cast<const float4 *>(dxr + t * d + c);
     }
 #pragma unroll

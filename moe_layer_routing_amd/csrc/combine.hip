@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
             const int c = min(c0 + 256 * u, d - 4);
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j)
-                if (j < k) v[u][j] = *reinterpret_cast<const float4 *>(y + src[j] + c);
+                if (j < k) v[u][j] = load_nt(y + src[j] + c);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {

@@ -27,6 +27,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_nt(float *p, float4 v) {
     __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(p));
 }
+// 16-byte load with the nontemporal hint, for rows read once (the combine's gathered y rows)
+__device__ __forceinline__ float4 load_nt(const float *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
