@@ -333,7 +333,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
 __device__ __forceinline__ int chunk_swizzle8(int r) { return r & 7; }
 
 
-template <int NBW, int NW>
+template <int NBW, int NW, bool kWeightNT = false>
 __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase,
                                              const uint8_t *abase, const uint32_t (&off)[NBW],
                                              uint32_t is_act_mask, int kt, uint32_t wstride,
@@ -342,10 +342,13 @@ __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase
     const uint32_t ako = (uint32_t)kt * 128u, wko = (uint32_t)kt * wstride;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        const bool is_act = (is_act_mask >> i) & 1u;
-        __builtin_amdgcn_global_load_lds(
-            (is_act ? abase : wbase) + off[i] + (is_act ? ako : wko),
-            (__attribute__((address_space(3))) void *)(slot + (wv + i * NW) * 1024), 16, 0, 0);
+        const bool is_act = (is_act_mask >> i) & 1u;   // wave-uniform
+        auto *dst = (__attribute__((address_space(3))) void *)(slot + (wv + i * NW) * 1024);
+        if (kWeightNT && !is_act)   // weight rows read once: nontemporal (cache policy nt)
+            __builtin_amdgcn_global_load_lds(wbase + off[i] + wko, dst, 16, 0, 2);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (is_act ? abase : wbase) + off[i] + (is_act ? ako : wko), dst, 16, 0, 0);
     }
 #endif
 }
@@ -500,7 +503,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
         if (st < nk)
-            dma_stage128<NBW, NW>(ring + st * kStageBytes, wbase, abase, off, is_act, st, wstride,
+            dma_stage128<NBW, NW, (BT < 128)>(ring + st * kStageBytes, wbase, abase, off, is_act, st, wstride,
                                   wv);
     if (NS - 2 < nk) wait_vm_lgkm0<NBW * (NS - 2)>();
     else wait_vm_lgkm0<0>();
@@ -508,7 +511,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     for (int kt = 0; kt < nk; ++kt) {
         uint8_t *cur = ring + (kt % NS) * kStageBytes;
         if (kt + NS - 1 < nk)
-            dma_stage128<NBW, NW>(ring + ((kt + NS - 1) % NS) * kStageBytes, wbase, abase, off,
+            dma_stage128<NBW, NW, (BT < 128)>(ring + ((kt + NS - 1) % NS) * kStageBytes, wbase, abase, off,
                                   is_act, kt + NS - 1, wstride, wv);
         if (active) {
             kstep(cur + lane_off0, cur, 0);
