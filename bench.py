@@ -399,6 +399,37 @@ def backward_report(L, dims, inp, K, hip, stream):
             "frac_bf16_peak_overall": round(flops / (ms16 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "dy and d_gu rounded once to bf16; bf16 MFMA for every gradient GEMM; "
                     "the data gradients read w2 and w13 K-major as stored; the gate/up recomputation forms d_gu in its epilogue (no gu buffer)"}
+        # the forward keeps g and u (FP32) and the backward reads them instead of
+        # recomputing: forward and backward timed over K calls each
+        gu = torch.empty((L.T * L.k, 2 * L.I), dtype=torch.float32, device=dev)
+        fb["gu"] = gu
+        M.forward(dims, fb, ws)
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            M.forward(dims, fb, ws)
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        fwd_gu = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+        hip.destroy(ev)
+        b16["gu"] = gu
+        M.backward(dims, b16, ws, grad_dtype=M.MOE_BF16, gu_saved=True)
+        ev = hip.create(2 * K)
+        for i in range(K):
+            hip.record(ev[2 * i], stream.cuda_stream)
+            M.backward(dims, b16, ws, grad_dtype=M.MOE_BF16, gu_saved=True)
+            hip.record(ev[2 * i + 1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        bwd_gu = float(np.median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(K)]))
+        hip.destroy(ev)
+        del fb["gu"], b16["gu"], gu
+        flops_saved = 12.0 * L.T * L.k * L.d * L.I      # no recomputation
+        out["bf16_operands_saved_gu"] = {
+            "forward_ms": round(fwd_gu, 5), "backward_ms": round(bwd_gu, 5),
+            "tflops_backward": round(flops_saved / (bwd_gu * 1e-3) / 1e12, 2),
+            "note": "the forward also stores g and u (FP32, 8*T*k*inter bytes); the backward "
+                    "reads them instead of recomputing the gate/up GEMM (12*T*k*d*I FLOP "
+                    "left); the same gradients bit for bit"}
     assert int(fb["d_err"].item()) == 0
     return out
 

@@ -384,6 +384,13 @@ typedef struct moe_forward_args {
     float *y_shared;               /* [R, T, d] f32 */
     void *shared_workspace;
     size_t shared_workspace_bytes;
+    /* NULL, or FP32 [T*k, 2*inter]: the gate/up GEMM also stores its pre-activations for
+     * a later moe_backward (gu_saved = 1), which then skips their recomputation: row p
+     * (expert row order, as h) holds g at columns [0, inter) and u at [inter, 2*inter),
+     * the FP32 values h[p,:] = round(silu(g) * u) is formed from ("SwiGLU: rounding
+     * after the multiply"). Memory for compute: 8*T*k*inter bytes kept between the
+     * forward and the backward. */
+    float *gu;
 } moe_forward_args;
 
 /* The whole layer: route (or replay) -> permute -> grouped FFN -> combine, each step as
@@ -482,6 +489,11 @@ typedef struct moe_backward_args {
      * w13 as stored (K-major for these products), d_w2 and d_w13 on a bf16 weight-gradient
      * kernel. */
     int32_t grad_dtype;
+    /* 1: gu holds the forward's pre-activations (moe_forward_args.gu of the same step):
+     * the recomputation is skipped and the SwiGLU derivative reads them, so every
+     * gradient is bitwise the one of the recomputing call. 0: gu (if given) is written by
+     * the recomputation. */
+    int32_t gu_saved;
 } moe_backward_args;
 moe_status moe_backward(const moe_dims *dims, const moe_backward_args *args, void *stream);
 

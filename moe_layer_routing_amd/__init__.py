@@ -54,7 +54,7 @@ class ForwardArgs(ctypes.Structure):
                 ("ranks", ctypes.c_int32), ("partials", _P), ("w13_shared", _P),
                 ("w2_shared", _P), ("inter_shared", ctypes.c_int32), ("h_shared", _P),
                 ("y_shared", _P), ("shared_workspace", _P),
-                ("shared_workspace_bytes", ctypes.c_size_t)]
+                ("shared_workspace_bytes", ctypes.c_size_t), ("gu", _P)]
 
 
 class RouterOpts(ctypes.Structure):
@@ -73,7 +73,8 @@ class BackwardArgs(ctypes.Structure):
                [(n, _P) for n in ("d_x", "d_w13", "d_w2", "d_topk_w", "d_logits", "d_w_router",
                                   "d_x_router", "d_y", "gu", "d_h", "d_gu", "d_xp",
                                   "workspace")] + \
-               [("workspace_bytes", ctypes.c_size_t), ("grad_dtype", ctypes.c_int32)]
+               [("workspace_bytes", ctypes.c_size_t), ("grad_dtype", ctypes.c_int32),
+                ("gu_saved", ctypes.c_int32)]
 
 
 # exported symbols and their signatures (argument types after the dims pointer)
@@ -365,16 +366,18 @@ def _forward_args(bufs, workspace, prof_events, router, routed_scale, ranks, int
 
 
 def backward(dims, bufs: dict, workspace: torch.Tensor, routed_scale: float = 0.0,
-             stream=None, grad_dtype: int = MOE_F32):
+             stream=None, grad_dtype: int = MOE_F32, gu_saved: bool = False):
     """Run moe_backward. ``bufs`` maps BackwardArgs field names to tensors (or None);
-    grad_dtype MOE_BF16 selects bf16 gradient operands (then d_y / d_gu are bf16)."""
+    grad_dtype MOE_BF16 selects bf16 gradient operands (then d_y / d_gu are bf16);
+    gu_saved: bufs["gu"] holds the forward's pre-activations (forward with bufs["gu"])."""
     a = BackwardArgs()
     for name, _ in BackwardArgs._fields_:
-        if name in ("routed_scale", "workspace", "workspace_bytes", "grad_dtype"):
+        if name in ("routed_scale", "workspace", "workspace_bytes", "grad_dtype", "gu_saved"):
             continue
         setattr(a, name, _ptr(bufs.get(name)))
     a.routed_scale = routed_scale
     a.grad_dtype = grad_dtype
+    a.gu_saved = int(bool(gu_saved))
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel()
     _check(lib().moe_backward(ctypes.byref(dims), ctypes.byref(a), _stream(stream)),

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
     const int32_t *__restrict__ tiles, int K, int N, int nft,
-    const int32_t *__restrict__ gperm, int gk, int64_t gT) {
+    const int32_t *__restrict__ gperm, int gk, int64_t gT, float *__restrict__ gu_out) {
     constexpr int NTHR = 64 * WF * WT;
     constexpr int kRowBytes = SRB;                     // K bytes of one row per stage
     constexpr int kLdsStride = kRowBytes + 16;         // padded LDS row (bank spread)
@@ -307,6 +307,13 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_kernel(
                     *reinterpret_cast<float4 *>(static_cast<float *>(out) + row * N + feat) =
                         make_float4(hv[0], hv[1], hv[2], hv[3]);
                 }
+                if (gu_out) {   // the pre-activations g and u, FP32 [rows][2N], as computed
+                    store_nt(gu_out + row * 2 * N + feat,
+                             make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]));
+                    store_nt(gu_out + row * 2 * N + N + feat,
+                             make_float4(acc[f + NFh][t][0], acc[f + NFh][t][1],
+                                         acc[f + NFh][t][2], acc[f + NFh][t][3]));
+                }
             }
         } else {
 #pragma unroll
@@ -367,7 +374,8 @@ __global__ __launch_bounds__(64 * WF * WT)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
     const int32_t *__restrict__ tiles, int K, int N, int nft,
-    const int32_t *__restrict__ gperm, int gk, int64_t gT, const float *__restrict__ dh) {
+    const int32_t *__restrict__ gperm, int gk, int64_t gT, const float *__restrict__ dh,
+    float *__restrict__ gu_out = nullptr) {
     constexpr int NW = WF * WT;
     constexpr int NBLK = (BW + BT) / 8;                // 8-row LDS blocks per stage
     constexpr int NBW = NBLK / NW;                     // DMA instructions per wave per stage
@@ -595,6 +603,13 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
                 pk.x = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
                 pk.y = (uint32_t)f32_to_bf16(hv[2]) | ((uint32_t)f32_to_bf16(hv[3]) << 16);
                 *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + row * N + feat) = pk;
+                if (gu_out) {   // the pre-activations g and u, FP32 [rows][2N], as computed
+                    store_nt(gu_out + row * 2 * N + feat,
+                             make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]));
+                    store_nt(gu_out + row * 2 * N + N + feat,
+                             make_float4(acc[f + NFh][t][0], acc[f + NFh][t][1],
+                                         acc[f + NFh][t][2], acc[f + NFh][t][3]));
+                }
             }
         } else {
 #pragma unroll
@@ -636,7 +651,7 @@ template <bool kBF16, bool kGateUp, class C, bool kKMajor = false, int kGrad = 0
 hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_t *tiles,
                        int64_t mtiles, int K, int N, hipStream_t s,
                        const int32_t *gperm = nullptr, int gk = 1, int64_t gT = 0,
-                       const float *dh = nullptr) {
+                       const float *dh = nullptr, float *gu_out = nullptr) {
     constexpr int feat = kGateUp ? C::BW / 2 : C::BW;
     const int nft = (N + feat - 1) / feat;
     static_assert(!kKMajor || (IsDma128<C>::value && kBF16 && !kGateUp), "K-major weights");
@@ -646,7 +661,7 @@ hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_
                                    kGrad>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
-                K, N, nft, gperm, gk, gT, dh);
+                K, N, nft, gperm, gk, gT, dh, gu_out);
     } else if constexpr (IsDma128<C>::value) {
         // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
         // same token tiles
@@ -655,12 +670,12 @@ hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_
             typename std::conditional<(C::BT == 64), Cfg<128, 64, 2, 2, 1, 128, 2>,
                                       Cfg<256, C::BT, 2, 2, 1, 64, 1>>::type>::type;
         return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s, gperm, gk,
-                                              gT);
+                                              gT, nullptr, gu_out);
     } else {
         grouped_gemm_kernel<kBF16, kGateUp, C::BW, C::BT, C::WF, C::WT, C::PF, C::SRB, C::WPE>
             <<<dim3((unsigned)(mtiles * nft)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(act), static_cast<const uint8_t *>(wgt), out, tiles,
-                K, N, nft, gperm, gk, gT);
+                K, N, nft, gperm, gk, gT, gu_out);
     }
     return hipGetLastError();
 }
@@ -669,12 +684,12 @@ hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_
 template <bool kBF16, class C13, class C2>
 hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, const void *w13,
                    const void *w2, void *h, float *y, const int32_t *tiles, int64_t mtiles,
-                   void *const *ev, hipStream_t s) {
+                   void *const *ev, hipStream_t s, float *gu_out) {
     static_assert(C13::BT == C2::BT, "both GEMMs walk the same token tiles");
     if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[0]), s) != hipSuccess)
         return hipErrorInvalidValue;
     hipError_t e = launch_gemm<kBF16, true, C13>(act13, w13, h, tiles, mtiles, dm.d, dm.inter, s,
-                                                 gperm, dm.k, dm.T);
+                                                 gperm, dm.k, dm.T, nullptr, gu_out);
     if (e != hipSuccess) return e;
     if (ev && hipEventRecord(static_cast<hipEvent_t>(ev[1]), s) != hipSuccess)
         return hipErrorInvalidValue;
@@ -707,28 +722,29 @@ using PLAIN_HUGE = MOE_FFN_HUGE_CFG2;
 template <bool kBF16>
 hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const int32_t *gperm,
                         const void *w13, const void *w2, void *h, float *y,
-                        const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s) {
+                        const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s,
+                        float *gu_out) {
     // Decode-shaped launches stream the weights: narrow 64-row weight slices (many blocks per
     // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block.
     switch (bt) {
     case 16: {
         using C = Dma128Cfg<64, 16, 2, 1, 6>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out);
     }
     case 32: {
         using C = Dma128Cfg<64, 32, 2, 1, 6>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out);
     }
     case 64: {
         using C = Dma128Cfg<128, 64, 2, 2, 4>;
-        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s);
+        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out);
     }
     case 128:
         return run_ffn<kBF16, MOE_FFN_LARGE_CFG13, MOE_FFN_LARGE_CFG2>(dm, x_perm, gperm, w13, w2, h, y,
-                                                                       tiles, mtiles, ev, s);
+                                                                       tiles, mtiles, ev, s, gu_out);
     default:
         return run_ffn<kBF16, MOE_FFN_HUGE_CFG13, MOE_FFN_HUGE_CFG2>(dm, x_perm, gperm, w13, w2, h, y,
-                                                                     tiles, mtiles, ev, s);
+                                                                     tiles, mtiles, ev, s, gu_out);
     }
 }
 
@@ -824,7 +840,8 @@ hipError_t launch_gate_up_grad(const moe_dims &dm, const void *act, const int32_
 hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int32_t *offsets,
                               const void *w13, const void *w2, void *h, float *y,
                               const Workspace &ws, void *const *prof_events, hipStream_t s,
-                              const void *x, const int32_t *perm, bool tiles_ready) {
+                              const void *x, const int32_t *perm, bool tiles_ready,
+                              float *gu_out) {
     const int64_t A = dm.T * dm.k;
     const int bt = select_tile_m(dm);
     const int64_t cap = max_m_tiles(A, dm.E, bt);
@@ -842,9 +859,9 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
     const int32_t *gperm = x_perm ? nullptr : perm;
     if (dm.dtype == MOE_BF16)
         return dispatch_ffn<true>(dm, bt, act13, gperm, w13, w2, h, y, ws.tiles, cap, prof_events,
-                                  s);
+                                  s, gu_out);
     return dispatch_ffn<false>(dm, bt, act13, gperm, w13, w2, h, y, ws.tiles, cap, prof_events,
-                               s);
+                               s, gu_out);
 }
 
 }  // namespace moe

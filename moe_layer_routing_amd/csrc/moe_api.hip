@@ -427,7 +427,7 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
             if (e != hipSuccess) return MOE_E_LAUNCH;
         }
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
-                               a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
+                               a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu);
         if (e != hipSuccess) return MOE_E_LAUNCH;
         return to_status(finish_layer(dims, a, scale, shared_work, s));
     }
@@ -444,7 +444,7 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
                        a->slot_of_expert, select_tile_m(*dims));   // tile list with the scan
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
-                           a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true);
+                           a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     return to_status(finish_layer(dims, a, scale, shared_work, s));
 }
@@ -517,6 +517,8 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     MOE_REQUIRE(a->gu || dims->dtype == MOE_BF16, MOE_E_NULLPTR);
     if (a->w_router) MOE_REQUIRE(a->d_logits && a->d_x_router, MOE_E_NULLPTR);
     MOE_REQUIRE(a->grad_dtype == MOE_F32 || a->grad_dtype == MOE_BF16, MOE_E_DTYPE);
+    MOE_REQUIRE(a->gu_saved == 0 || a->gu_saved == 1, MOE_E_SHAPE);
+    if (a->gu_saved) MOE_REQUIRE(a->gu != nullptr, MOE_E_NULLPTR);
     const bool g16 = a->grad_dtype == MOE_BF16;
     if (g16) MOE_REQUIRE(dims->dtype == MOE_BF16, MOE_E_DTYPE);
     if (!a->x_perm) {
@@ -539,8 +541,9 @@ moe_status moe_backward(const moe_dims *dims, const moe_backward_args *a, void *
     const int64_t xrows = a->x_perm ? A : dims->T;
     // with gu, the gate/up pre-activations are recomputed into it and the SwiGLU derivative
     // is its own kernel; without, the recomputation runs after dh and forms d_gu itself
+    // with gu saved by the forward, the SwiGLU derivative reads it as it stands
     const bool fused = a->gu == nullptr;
-    if (!fused) {
+    if (!fused && !a->gu_saved) {
         e = launch_plain_gemm(*dims, xb, xperm, a->w13, a->gu, 2 * I, a->offsets, ws, s);
         if (e != hipSuccess) return MOE_E_LAUNCH;
     }

@@ -216,7 +216,7 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                               const void *w13, const void *w2, void *h, float *y,
                               const Workspace &ws, void *const *prof_events, hipStream_t s,
                               const void *x = nullptr, const int32_t *perm = nullptr,
-                              bool tiles_ready = false);
+                              bool tiles_ready = false, float *gu_out = nullptr);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s, float scale = 1.0f);
 // Rank partial outputs and their FP64 pairwise tree (1 <= R <= kMaxRanks, R divides E).

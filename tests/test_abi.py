@@ -45,7 +45,8 @@ def test_library_exports_every_declared_symbol(M):
 def test_struct_layouts_match_header(M, tmp_path):
     """Field offsets of the ctypes mirrors equal what a C compiler makes of the header."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', 'int main(void){']
-    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs)):
+    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs),
+                      ("moe_backward_args", M.BackwardArgs), ("moe_router_opts", M.RouterOpts)):
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in py._fields_:
             lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
@@ -56,7 +57,8 @@ def test_struct_layouts_match_header(M, tmp_path):
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
                                                  check=True).stdout.splitlines())
-    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs)):
+    for cname, py in (("moe_dims", M.Dims), ("moe_forward_args", M.ForwardArgs),
+                      ("moe_backward_args", M.BackwardArgs), ("moe_router_opts", M.RouterOpts)):
         assert int(got[cname]) == ctypes.sizeof(py)
         for f, _ in py._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, f
@@ -131,6 +133,12 @@ def test_backward_gu_optional_only_on_bf16_layers(M):
         dims = M.make_dims(16, 128, 8, 2, 128, dtype)
         a = args(gu)
         assert L.moe_backward(ctypes.byref(dims), ctypes.byref(a), None) == status, (dtype, gu)
+    # pre-activations saved by the forward: gu must be there, and the flag is 0 or 1
+    dims = M.make_dims(16, 128, 8, 2, 128, M.MOE_BF16)
+    for gu, flag, status in ((False, 1, 1), (True, 1, 4), (True, 2, 2)):
+        a = args(gu)
+        a.gu_saved = flag
+        assert L.moe_backward(ctypes.byref(dims), ctypes.byref(a), None) == status, (gu, flag)
 
 
 def test_noalloc_rejects_layers_beyond_its_scratch(M):

@@ -41,9 +41,11 @@ def _close(gpu, ref, what, tol=GTOL):
 
 
 def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=False,
-         fused=False):
+         fused=False, saved_gu=False):
     dims = dims_of(L)
     fb = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
+    if saved_gu:   # the forward stores the pre-activations; the backward reads them
+        fb["gu"] = torch.empty((L.T * L.k, 2 * L.I), dtype=torch.float32, device="cuda")
     fb.update(x=inp["x"], w13=inp["w13"], w2=inp["w2"])
     if L.mode == "router":
         fb["w_router"], fb["logit_bias"] = inp["w_router"], inp["logit_bias"]
@@ -63,11 +65,13 @@ def _run(L, inp, dout, scale, slot=None, x_perm=False, router_grads=True, g16=Fa
     bb.update(x=inp["x"], x_perm=fb.get("x_perm"), w13=fb["w13"], w2=fb["w2"],
               offsets=fb["offsets"], perm=fb["perm"], inv=fb["inv"], topk_w=fb["topk_w"],
               h=fb["h"], y=fb["y"], d_out=dev(dout))
+    if saved_gu:
+        bb["gu"] = fb["gu"]
     if router_grads:
         bb["w_router"] = dev(L.w_router)
         bb["logit_bias"] = inp.get("logit_bias")
         bb["logits"] = fb.get("logits")          # replay: recomputed from x and w_router
-    M.backward(dims, bb, ws, routed_scale=scale, grad_dtype=gd)
+    M.backward(dims, bb, ws, routed_scale=scale, grad_dtype=gd, gu_saved=saved_gu)
     torch.cuda.synchronize()
     assert int(fb["d_err"].item()) == 0
     return fb, bb
@@ -223,6 +227,39 @@ def test_backward_fused_swiglu_grad_bitwise(case):
     _, b1 = _run(L, inp, dout, 1.0, None, xp, g16=g16)
     _, b2 = _run(L, inp, dout, 1.0, None, xp, g16=g16, fused=True)
     assert "gu" not in b2
+    for n in sorted(b1):
+        if n.startswith("d_"):
+            assert host(b1[n]).tobytes() == host(b2[n]).tobytes(), n
+
+
+SAVED_CASES = [
+    # (T, d, E, k, I, dtype, g16, x_perm): token-tile heights 16 .. 256, both layer dtypes
+    (12, 128, 16, 4, 128, "bf16", True, False), (40, 192, 8, 6, 64, "bf16", False, True),
+    (300, 256, 8, 2, 192, "bf16", True, False), (2100, 128, 4, 2, 128, "bf16", False, False),
+    (4096, 128, 2, 2, 64, "bf16", True, True), (257, 128, 24, 4, 128, "f32", False, False),
+    (48, 128, 8, 2, 64, "f32", False, True)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SAVED_CASES, ids=lambda c: f"T{c[0]}_d{c[1]}_E{c[2]}_k{c[3]}_"
+                                                            f"I{c[4]}_{c[5]}_g16{int(c[6])}_xp{int(c[7])}")
+def test_backward_saved_preactivations_bitwise(case):
+    """The forward stores g and u (moe_forward_args.gu) and the backward reads them
+    (gu_saved): the saved values are bitwise the recomputed ones, every gradient is
+    bitwise the recomputing call's, and the forward's own outputs are unchanged."""
+    T, d, E, k, I, dtype, g16, xp = case
+    L = W.make_layer(T=T, d=d, E=E, k=k, I=I, dtype=dtype, mode="router", seed=T + 9,
+                     bias="zipf")
+    inp = upload(L)
+    rng = np.random.default_rng(T + 3)
+    dout = rng.normal(0, 1, (T, d)).astype(np.float32)
+    if dtype == "bf16":
+        dout = W.f32_to_bf16_bits(dout)
+    f1, b1 = _run(L, inp, dout, 1.5, None, xp, g16=g16)                  # recomputes into gu
+    f2, b2 = _run(L, inp, dout, 1.5, None, xp, g16=g16, saved_gu=True)   # reads the saved gu
+    for n in ("out", "h", "y", "topk_idx", "topk_w", "perm", "inv"):
+        assert host(f1[n]).tobytes() == host(f2[n]).tobytes(), n
+    assert host(f2["gu"]).tobytes() == host(b1["gu"]).tobytes(), "gu"
     for n in sorted(b1):
         if n.startswith("d_"):
             assert host(b1[n]).tobytes() == host(b2[n]).tobytes(), n
