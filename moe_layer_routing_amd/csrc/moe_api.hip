@@ -434,14 +434,20 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
     if (replay)
         e = launch_replay(*dims, a->idx_in, a->w_in, a->topk_idx, a->topk_w, a->d_err, s);
     else
+        // the probability mass is reduced by the permutation's histogram launch
         e = launch_route(*dims, a->x, a->w_router, a->logit_bias,
                          a->logits ? a->logits : ws.logits, a->topk_idx, a->topk_w,
-                         ws.mass_part, a->prob_mass, a->token_mult, a->d_err, s, ro);
+                         ws.mass_part, a->prob_mass, a->token_mult, a->d_err, s, ro,
+                         /*defer_mass=*/dims->T > 0);
     if (e != hipSuccess) return MOE_E_LAUNCH;
+    const bool mass_here = !replay && a->prob_mass && dims->T > 0;
     e = launch_permute(*dims, a->topk_idx, a->x, a->x_perm, a->perm, a->inv, a->counts,
                        a->offsets, a->cu_seqlens, a->seq_counts ? a->num_seqs : 0,
                        a->seq_counts, a->token_mult, a->weighted_counts, a->d_err, ws, s,
-                       a->slot_of_expert, select_tile_m(*dims));   // tile list with the scan
+                       a->slot_of_expert, select_tile_m(*dims),   // tile list with the scan
+                       mass_here ? ws.mass_part : nullptr,
+                       (dims->T + kTopkTokPerBlock - 1) / kTopkTokPerBlock,
+                       mass_here ? a->prob_mass : nullptr);
     if (e != hipSuccess) return MOE_E_LAUNCH;
     e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                            a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu);

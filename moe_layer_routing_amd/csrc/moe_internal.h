@@ -120,6 +120,30 @@ __device__ __forceinline__ void raise_err(int32_t *d_err, int32_t bits) {
     if (d_err && bits) atomicOr(d_err, bits);
 }
 
+// prob_mass[e] from the per-block partials, by one wave: the sum of 256 virtual threads
+// (virtual thread i adds the partials of blocks i, i+256, ... in order) followed by a fixed
+// binary tree over them (step s: i += i + s for i < s, s = 128 .. 1). Lane l holds
+// virtual threads l, l+64, l+128, l+192; the steps 128 and 64 stay inside the lane and the
+// rest pair lane l with lane l + s. The order depends only on the number of partials (i.e.
+// on T).
+__device__ __forceinline__ void mass_reduce_wave(const float *__restrict__ part, int64_t nblk,
+                                                 int E, int e, float *__restrict__ mass) {
+    const int lane = threadIdx.x & 63;
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float acc = 0.f;
+        for (int64_t b = lane + 64 * u; b < nblk; b += 256) acc = acc + part[b * E + e];
+        v[u] = acc;
+    }
+    v[0] = v[0] + v[2];   // s = 128
+    v[1] = v[1] + v[3];
+    float x = v[0] + v[1];   // s = 64
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = x + __shfl_down(x, s, 64);
+    if (lane == 0) mass[e] = x;
+}
+
 // Physical slot of routed expert id e under a placement map (identity when map is null):
 // -1 for an id outside [0, E) (*bits gets MOE_DERR_IDX_RANGE) or a map entry outside [0, E)
 // (*bits gets MOE_DERR_SLOTMAP).
@@ -199,7 +223,8 @@ struct RouteOpts {
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                         const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
                         float *mass_part, float *prob_mass, const int32_t *token_mult,
-                        int32_t *d_err, hipStream_t s, const RouteOpts &opts = RouteOpts());
+                        int32_t *d_err, hipStream_t s, const RouteOpts &opts = RouteOpts(),
+                        bool defer_mass = false);   // true: prob_mass is left to launch_permute
 hipError_t launch_replay(const moe_dims &dm, const int32_t *idx_in, const float *w_in,
                          int32_t *topk_idx, float *topk_w, int32_t *d_err, hipStream_t s);
 hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const void *x,
@@ -208,7 +233,9 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
                           hipStream_t s, const int32_t *slot_map = nullptr,
-                          int tiles_bt = 0);   // > 0: also write ws.tiles for this tile height
+                          int tiles_bt = 0,    // > 0: also write ws.tiles for this tile height
+                          const float *mass_part = nullptr, int64_t mass_nblk = 0,
+                          float *prob_mass = nullptr);   // the mass launch_route deferred
 // Raises MOE_DERR_SLOTMAP unless map[0..E-1] is a permutation of 0..E-1 (one block).
 hipError_t launch_check_slot_map(const int32_t *map, int E, int32_t *d_err, hipStream_t s);
 // x_perm == nullptr: gather token rows of x through perm inside the gate/up GEMM.

@@ -18,15 +18,25 @@ namespace {
 
 constexpr int kSubChunk = kPermChunk / 4;  // per wave
 
+// Also (when given): zeroes seq_counts (nzero entries, over the grid) for the scatter
+// kernel's per-sequence histogram, and forms prob_mass from the router's per-block
+// partials (wave w of block b reduces expert 4b + w, then every 4 * grid further).
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ idx, int64_t A,
                                                    int k, int E,
                                                    const int32_t *__restrict__ q,
                                                    int32_t *__restrict__ blk_hist,
                                                    uint64_t *__restrict__ blk_whist,
                                                    int32_t *__restrict__ d_err,
-                                                   const int32_t *__restrict__ slot) {
+                                                   const int32_t *__restrict__ slot,
+                                                   int32_t *__restrict__ zero, int64_t nzero,
+                                                   const float *__restrict__ mass_part,
+                                                   int64_t mass_nblk,
+                                                   float *__restrict__ prob_mass) {
     __shared__ int32_t hist[kMaxE];
     __shared__ unsigned long long whist[kMaxE];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nzero;
+         i += (int64_t)gridDim.x * 256)
+        zero[i] = 0;
     for (int e = threadIdx.x; e < E; e += 256) {
         hist[e] = 0;
         whist[e] = 0;
@@ -48,6 +58,9 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
         blk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
         if (blk_whist) blk_whist[(int64_t)blockIdx.x * E + e] = whist[e];
     }
+    if (prob_mass)   // one wave per expert
+        for (int e = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); e < E; e += gridDim.x * 4)
+            mass_reduce_wave(mass_part, mass_nblk, E, e, prob_mass);
 }
 
 // One block: counts, offsets, and each chunk's starting position per expert; with tiles,
@@ -148,13 +161,52 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ blk_his
 // a first pass counts each wave's experts, a second pass walks 64 assignments at a time
 // and places each one after the earlier lanes that hold the same expert (found with
 // ballots over the bits of the id).
+// With seq_counts: also the per-sequence counts of the chunk's assignments (for each
+// sequence s overlapping it, an LDS histogram of its assignments cu[s]*k .. cu[s+1]*k in
+// the chunk, whose non-zero bins are added to seq_counts[s] with integer atomics: any
+// order, the same sums; seq_counts was zeroed by the histogram kernel).
+__device__ __forceinline__ void seq_hist_chunk(const int32_t *__restrict__ idx, int64_t a_lo,
+                                               int64_t a_hi, int k, int E,
+                                               const int32_t *__restrict__ cu, int S,
+                                               int32_t *__restrict__ seq_counts,
+                                               const int32_t *__restrict__ slot,
+                                               int32_t *hist) {
+    // first sequence whose assignments end past a_lo (empty sequences are skipped)
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)cu[mid + 1] * k <= a_lo) lo = mid + 1;
+        else hi = mid;
+    }
+    for (int s = lo; s < S && (int64_t)cu[s] * k < a_hi; ++s) {
+        const int64_t a0 = max<int64_t>(a_lo, (int64_t)cu[s] * k);
+        const int64_t a1 = min<int64_t>(a_hi, (int64_t)cu[s + 1] * k);
+        if (a1 <= a0) continue;
+        for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+        __syncthreads();
+        for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
+            int bits = 0;
+            const int e = slot_of(slot, idx[a], E, bits);
+            if (e >= 0) atomicAdd(&hist[e], 1);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += 256)
+            if (hist[e]) atomicAdd(&seq_counts[(int64_t)s * E + e], hist[e]);
+        __syncthreads();
+    }
+}
+
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
                                                       int64_t A, int E,
                                                       const int32_t *__restrict__ blk_off,
                                                       int32_t *__restrict__ perm,
                                                       int32_t *__restrict__ inv,
-                                                      const int32_t *__restrict__ slot) {
+                                                      const int32_t *__restrict__ slot,
+                                                      int k, const int32_t *__restrict__ cu,
+                                                      int S, int32_t *__restrict__ seq_counts,
+                                                      int32_t *__restrict__ d_err) {
     __shared__ int32_t cur[4][kMaxE];
+    __shared__ int32_t shist[kMaxE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int i = threadIdx.x; i < 4 * kMaxE; i += 256) (&cur[0][0])[i] = 0;
     __syncthreads();
@@ -200,6 +252,21 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
+    if (seq_counts) {
+        // validate cu_seqlens: 0 = c_0 <= c_1 <= ... <= c_S = T
+        const int64_t T = A / k;
+        int bad = 0;
+        for (int s = threadIdx.x; s < S; s += 256)
+            if (cu[s + 1] < cu[s]) bad = 1;
+        if (threadIdx.x == 0 && (cu[0] != 0 || (int64_t)cu[S] != T)) bad = 1;
+        if (__syncthreads_or(bad)) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) raise_err(d_err, MOE_DERR_SEQLENS);
+            return;
+        }
+        const int64_t a_lo = (int64_t)blockIdx.x * kPermChunk;
+        seq_hist_chunk(idx, a_lo, min<int64_t>(a_lo + kPermChunk, A), k, E, cu, S, seq_counts,
+                       slot, shist);
+    }
 }
 
 // Token-major gather: each wave reads one token's row once and writes it to its k rows.
@@ -232,55 +299,6 @@ __global__ void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * 256)
         p[i] = v;
-}
-
-constexpr int kSeqTok = 256;  // tokens per block in the per-sequence histogram
-
-// Per-sequence counts over packed microbatches. Block b owns tokens [b*256, b*256+256);
-// for each sequence overlapping that range it histograms in LDS and adds the non-zero
-// bins to seq_counts with integer atomics (any order, same sums).
-__global__ __launch_bounds__(256) void seq_hist_kernel(const int32_t *__restrict__ idx,
-                                                       int64_t T, int k, int E,
-                                                       const int32_t *__restrict__ cu,
-                                                       int S,
-                                                       int32_t *__restrict__ seq_counts,
-                                                       int32_t *__restrict__ d_err,
-                                                       const int32_t *__restrict__ slot) {
-    __shared__ int32_t hist[kMaxE];
-    // validate cu_seqlens: 0 = c_0 <= c_1 <= ... <= c_S = T
-    int bad = 0;
-    for (int s = threadIdx.x; s < S; s += 256)
-        if (cu[s + 1] < cu[s]) bad = 1;
-    if (threadIdx.x == 0 && (cu[0] != 0 || (int64_t)cu[S] != T)) bad = 1;
-    if (__syncthreads_or(bad)) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) raise_err(d_err, MOE_DERR_SEQLENS);
-        return;
-    }
-    const int64_t t0 = (int64_t)blockIdx.x * kSeqTok;
-    const int64_t t1 = min<int64_t>(t0 + kSeqTok, T);
-    // first sequence whose end is past t0 (empty sequences are skipped naturally)
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((int64_t)cu[mid + 1] <= t0) lo = mid + 1;
-        else hi = mid;
-    }
-    for (int s = lo; s < S && (int64_t)cu[s] < t1; ++s) {
-        const int64_t a0 = max<int64_t>(t0, cu[s]) * k;
-        const int64_t a1 = min<int64_t>(t1, cu[s + 1]) * k;
-        if (a1 <= a0) continue;
-        for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
-        __syncthreads();
-        for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
-            int bits = 0;
-            const int e = slot_of(slot, idx[a], E, bits);
-            if (e >= 0) atomicAdd(&hist[e], 1);
-        }
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += 256)
-            if (hist[e]) atomicAdd(&seq_counts[(int64_t)s * E + e], hist[e]);
-        __syncthreads();
-    }
 }
 
 // MOE_DERR_SLOTMAP unless map is a permutation of 0..E-1 (E <= kMaxE).
@@ -324,7 +342,8 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
                           int32_t *offsets, const int32_t *cu_seqlens, int32_t num_seqs,
                           int32_t *seq_counts, const int32_t *token_mult,
                           int64_t *weighted_counts, int32_t *d_err, const Workspace &ws,
-                          hipStream_t s, const int32_t *slot_map, int tiles_bt) {
+                          hipStream_t s, const int32_t *slot_map, int tiles_bt,
+                          const float *mass_part, int64_t mass_nblk, float *prob_mass) {
     const int64_t T = dm.T, A = dm.T * dm.k;
     const int E = dm.E, k = dm.k;
     const int64_t nchunks = perm_chunks(A);
@@ -333,30 +352,33 @@ hipError_t launch_permute(const moe_dims &dm, const int32_t *topk_idx, const voi
         const hipError_t me = launch_check_slot_map(slot_map, E, d_err, s);
         if (me != hipSuccess) return me;
     }
+    // per-sequence counts ride on the histogram (zeroing) and scatter (counting) launches
+    const bool seqs = seq_counts && num_seqs > 0 && T > 0;
+    if (seq_counts && num_seqs > 0 && T == 0) {
+        const int64_t n = (int64_t)num_seqs * E;
+        fill_i32_kernel<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256),
+                          0, s>>>(seq_counts, n, 0);
+    }
     if (nchunks > 0)
         hist_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
             topk_idx, A, k, E, token_mult, ws.blk_hist,
-            (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err, slot_map);
+            (weighted_counts && have_q) ? ws.blk_whist : nullptr, d_err, slot_map,
+            seqs ? seq_counts : nullptr, seqs ? (int64_t)num_seqs * E : 0, mass_part,
+            mass_nblk, prob_mass);
+    else if (prob_mass)
+        return hipErrorInvalidValue;   // a deferred mass needs the histogram launch
     // the forward's tile list comes with the scan (tiles_bt > 0)
     const int bt = tiles_bt > 0 ? tiles_bt : 1;
     scan_kernel<<<dim3(1), dim3(256), 0, s>>>(
         ws.blk_hist, ws.blk_whist, nchunks, E, have_q, counts, offsets, weighted_counts, bt,
         tiles_bt > 0 ? max_m_tiles(A, E, bt) : 0, tiles_bt > 0 ? ws.tiles : nullptr);
     if (nchunks > 0)
-        scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(topk_idx, A, E,
-                                                                     ws.blk_hist, perm, inv,
-                                                                     slot_map);
+        scatter_kernel<<<dim3((unsigned)nchunks), dim3(256), 0, s>>>(
+            topk_idx, A, E, ws.blk_hist, perm, inv, slot_map, k, cu_seqlens, num_seqs,
+            seqs ? seq_counts : nullptr, d_err);
     if (x_perm) {
         const hipError_t ge = launch_gather(dm, x, inv, x_perm, s);
         if (ge != hipSuccess) return ge;
-    }
-    if (seq_counts && num_seqs > 0) {
-        const int64_t n = (int64_t)num_seqs * E;
-        fill_i32_kernel<<<dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256),
-                          0, s>>>(seq_counts, n, 0);
-        if (T > 0)
-            seq_hist_kernel<<<dim3((unsigned)((T + kSeqTok - 1) / kSeqTok)), dim3(256), 0, s>>>(
-                topk_idx, T, k, E, cu_seqlens, num_seqs, seq_counts, d_err, slot_map);
     }
     return hipGetLastError();
 }

@@ -306,24 +306,12 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_fused_kernel(
                                blockIdx.x, 64 * kLogitSplit, mpt);
 }
 
-// prob_mass[e]: one block per expert; thread i adds the partials of blocks i, i+256, ...
-// in order, then a fixed binary tree over the 256 threads. The order depends only on the
-// number of partials (i.e. on T).
+// prob_mass[e]: one wave per expert (mass_reduce_wave), four per block.
 __global__ __launch_bounds__(256) void mass_reduce_kernel(const float *__restrict__ part,
                                                           int64_t nblk, int E,
                                                           float *__restrict__ mass) {
-    __shared__ float red[256];
-    const int e = blockIdx.x;
-    float acc = 0.f;
-    for (int64_t b = threadIdx.x; b < nblk; b += 256) acc = acc + part[b * E + e];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-#pragma unroll
-    for (int s = 128; s >= 1; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + s];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) mass[e] = red[0];
+    const int e = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (e < E) mass_reduce_wave(part, nblk, E, e, mass);
 }
 
 // ------------------------------------------------------------------------ replay
@@ -443,12 +431,13 @@ static bool launch_fused_t(const moe_dims &dm, const void *x, const void *w_rout
 hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                         const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
                         float *mass_part, float *prob_mass, const int32_t *token_mult,
-                        int32_t *d_err, hipStream_t s, const RouteOpts &o) {
+                        int32_t *d_err, hipStream_t s, const RouteOpts &o, bool defer_mass) {
     const int64_t T = dm.T;
     const int E = dm.E;
     if (T > 0) {
         const int64_t tblk = (T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
         float *mp = prob_mass ? mass_part : nullptr;
+        if (defer_mass) prob_mass = nullptr;   // the caller's next launch reduces mass_part
         const bool fused =
             dm.dtype == MOE_BF16
                 ? launch_fused_t<true>(dm, x, w_router, bias, logits, token_mult, topk_idx,
@@ -457,7 +446,7 @@ hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
                                         topk_w, mp, d_err, o, s);
         if (fused) {
             if (prob_mass)
-                mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
+                mass_reduce_kernel<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
             return hipGetLastError();
         }
         const hipError_t le = launch_router_logits(dm, x, w_router, bias, logits, s);
@@ -472,9 +461,9 @@ hipError_t launch_route(const moe_dims &dm, const void *x, const void *w_router,
         default: launch_topk_t<kScoreSqrtSoftplus, true>(dm, tblk, logits, token_mult, topk_idx, topk_w, mp, d_err, o, s); break;
         }
         if (prob_mass)
-            mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
+            mass_reduce_kernel<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(mass_part, tblk, E, prob_mass);
     } else if (prob_mass) {
-        mass_reduce_kernel<<<dim3(E), dim3(256), 0, s>>>(mass_part, 0, E, prob_mass);
+        mass_reduce_kernel<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(mass_part, 0, E, prob_mass);
     }
     return hipGetLastError();
 }

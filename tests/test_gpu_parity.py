@@ -193,6 +193,20 @@ def test_permute_c4_ids():
     _check_permute(L)
 
 
+@pytest.mark.parametrize("T,k", [(1000, 3), (3001, 7), (700, 5)])
+def test_permute_sequences_across_chunk_edges(T, k):
+    """Per-sequence counts when 2048-assignment chunks split tokens (k does not divide
+    2048) and sequences span several chunks, with empty sequences in between."""
+    L = W.make_layer(T=T, d=64, E=24, k=k, I=64, dtype="bf16", mode="replay", seed=T + k,
+                     weights=False, replay="uniform", seqs=True)
+    cu = L.cu_seqlens.copy()
+    # two empty sequences: repeat an inner boundary twice
+    mid = len(cu) // 2
+    L.cu_seqlens = np.ascontiguousarray(np.insert(cu, mid, [cu[mid], cu[mid]])).astype(np.int32)
+    L.token_mult = W.token_multiplicities(L.T, 2)
+    _check_permute(L)
+
+
 def test_permute_all_tokens_one_expert_set():
     L = W.make_layer(T=5000, d=64, E=40, k=3, I=64, dtype="bf16", mode="replay", seed=15,
                      weights=False, replay="uniform")
