@@ -48,6 +48,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     __shared__ int32_t toff[kMaxE + 1];                    // tile starts
     __shared__ unsigned long long wsum[kMaxE];
     __shared__ float mpt[kSmallT][kMaxE];                  // q·p per token, router mode
+    __shared__ float lgl[kChainSumMax];                    // logits formed here (T*E <= 2048)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int A = T * k;
     for (int i = tid; i < (kTailMaxA / kWave) * kMaxE; i += 64 * kTailWaves)
@@ -72,11 +73,19 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
                 v0 = v0 + p0[c];
                 v1 = v1 + p1[c];
             }
-            logits[i0] = bias ? v0 + bias[i0 % E] : v0;
-            if (i0 + kNT < TE) logits[i1] = bias ? v1 + bias[i1 % E] : v1;
+            const float l0 = bias ? v0 + bias[i0 % E] : v0;
+            const float l1 = bias ? v1 + bias[i1 % E] : v1;
+            logits[i0] = l0;
+            lgl[i0] = l0;
+            if (i0 + kNT < TE) {
+                logits[i1] = l1;
+                lgl[i1] = l1;
+            }
         }
-        __syncthreads();   // the block's own global writes are visible to it after this
+        __syncthreads();
     }
+    // the top-k reads the logits it formed from LDS (the same values as the global copy)
+    const float *lg = (!kReplay && part) ? lgl : logits;
 
     // ---- top-k (or replay validation); ids also go to LDS
     int err = 0;
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     } else {
         float qp[kRowVals];
         if (wave * kTailTokPerWave < T) {   // waves past the batch hold zeros
-            route_rows<kFn, kHash, NV>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k,
+            route_rows<kFn, kHash, NV>(lg, q, (int64_t)wave * kTailTokPerWave, T, E, k,
                                        opts, topk_idx, topk_w, ids, qp, err);
         } else {
 #pragma unroll
@@ -257,6 +266,7 @@ hipError_t launch_small_tail(const moe_dims &dm, const float *logits_in, const i
     float *logits = const_cast<float *>(logits_in);
     if (dm.T < 1 || dm.T > kSmallT || dm.E > kMaxE || dm.k > kMaxK)
         return hipErrorInvalidValue;
+    if (logit_part && dm.T * dm.E > kChainSumMax) return hipErrorInvalidValue;   // LDS copy
     if (slot_map) {
         const hipError_t me = launch_check_slot_map(slot_map, dm.E, d_err, s);
         if (me != hipSuccess) return me;
