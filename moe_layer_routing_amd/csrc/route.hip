@@ -158,7 +158,8 @@ __device__ __forceinline__ void logits_block(const void *__restrict__ x_,
                                              const float *__restrict__ bias,
                                              float *__restrict__ logits, int64_t T, int d,
                                              int E, int64_t blk,
-                                             float (&part)[kLogitSplit][EPB][4][64]) {
+                                             float (&part)[kLogitSplit][EPB][4][64],
+                                             float *lds_rows = nullptr) {
     const int n_et = (E + 15) >> 4;
     const int n_eg = (n_et + EPB - 1) / EPB;
     const int et0 = (int)(blk % n_eg) * EPB;
@@ -179,7 +180,11 @@ __device__ __forceinline__ void logits_block(const void *__restrict__ x_,
         for (int w = 1; w < kLogitSplit; ++w) v = v + part[w][j][i][l];
         const int64_t t = tb + (l & 15);
         const int e = (et0 + j) * 16 + 4 * (l >> 4) + i;
-        if (t < T && e < E && et0 + j < n_et) logits[t * E + e] = bias ? v + bias[e] : v;
+        if (t < T && e < E && et0 + j < n_et) {
+            const float lv = bias ? v + bias[e] : v;
+            logits[t * E + e] = lv;
+            if (lds_rows) lds_rows[(l & 15) * E + e] = lv;   // the block's own copy
+        }
     }
 }
 
@@ -238,14 +243,20 @@ __device__ __forceinline__ void topk_group(const float *__restrict__ logits,
                                            float *__restrict__ mass_part,
                                            int32_t *__restrict__ d_err, const RouteOpts &opts,
                                            int64_t grp, int nthr,
-                                           float (&mpt)[kTopkTokPerBlock][kMaxE]) {
+                                           float (&mpt)[kTopkTokPerBlock][kMaxE],
+                                           const float *lds_rows = nullptr) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t0 = grp * kTopkTokPerBlock + wave * 4;
     float qp[kRowVals];
     int err = 0;
     if (wave < 4 && t0 < T) {   // wave-uniform; a wave past the batch only contributes zeros
-        route_rows<kFn, kHash, NV>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr, qp,
-                                   err);
+        // lds_rows: the group's 16 logit rows as this block formed them (same values)
+        if (lds_rows)
+            route_rows<kFn, kHash, NV>(lds_rows, q, t0, T, E, k, opts, topk_idx, topk_w,
+                                       nullptr, qp, err, grp * kTopkTokPerBlock);
+        else
+            route_rows<kFn, kHash, NV>(logits, q, t0, T, E, k, opts, topk_idx, topk_w, nullptr,
+                                       qp, err);
     } else {
 #pragma unroll
         for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
@@ -291,19 +302,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
 // Logits and top-k in one launch, when one block holds every expert of its token tile
 // (EPB >= E/16): block b forms the logits of tokens 16b .. 16b+15 (as route_logits_kernel
 // does) and then routes the same 16 tokens (as route_topk_kernel's block b does), reading
-// the logits it has just written; every output is the bits of the two-kernel path.
+// the logits from the copy it kept in LDS (the values it wrote to memory); every output is
+// the bits of the two-kernel path.
 template <bool kBF16, int EPB, int kFn, bool kHash, int NV>
 __global__ __launch_bounds__(64 * kLogitSplit) void route_fused_kernel(
     const void *__restrict__ x_, const void *__restrict__ wr_, const float *__restrict__ bias,
     float *__restrict__ logits, int64_t T, int d, int E, const int32_t *__restrict__ q, int k,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
     float *__restrict__ mass_part, int32_t *__restrict__ d_err, RouteOpts opts) {
+    static_assert(kFn == kScoreSoftmax && !kHash, "the fused launch routes the softmax router");
     __shared__ float part[kLogitSplit][EPB][4][64];
     __shared__ float mpt[kTopkTokPerBlock][kMaxE];
-    logits_block<kBF16, EPB>(x_, wr_, bias, logits, T, d, E, blockIdx.x, part);
-    __syncthreads();   // the block's own global writes are visible to it after this
+    __shared__ float rows[kTopkTokPerBlock * 16 * EPB];   // the block's logits (E <= 16 EPB)
+    logits_block<kBF16, EPB>(x_, wr_, bias, logits, T, d, E, blockIdx.x, part, rows);
+    __syncthreads();
     topk_group<kFn, kHash, NV>(logits, q, T, E, k, topk_idx, topk_w, mass_part, d_err, opts,
-                               blockIdx.x, 64 * kLogitSplit, mpt);
+                               blockIdx.x, 64 * kLogitSplit, mpt, rows);
 }
 
 // prob_mass[e]: one wave per expert (mass_reduce_wave), four per block.

@@ -95,7 +95,8 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
                                             int32_t *__restrict__ topk_idx,
                                             float *__restrict__ topk_w, int32_t *lds_ids,
                                             float (&qp)[kRowVals], int &err,
-                                            float *__restrict__ lse = nullptr) {
+                                            float *__restrict__ lse = nullptr,
+                                            int64_t row0 = 0) {
     const int lane = threadIdx.x & 63, c = lane & 15;
     const int64_t t = t0 + (lane >> 4);
     const bool tv = t < T;
@@ -107,7 +108,7 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         valid[i] = c + 16 * i < E;
-        lv[i] = (tv && valid[i]) ? logits[t * E + c + 16 * i] : 0.f;
+        lv[i] = (tv && valid[i]) ? logits[(t - row0) * E + c + 16 * i] : 0.f;
         if (tv && valid[i] && !__builtin_isfinite(lv[i])) err |= MOE_DERR_NONFINITE;
         // a present expert's key is at least 1 (only the NaN with all bits set maps to 0)
         hi[i] = valid[i] ? max(ordered_bits(lv[i]), 1u) : 0u;
@@ -347,9 +348,12 @@ __device__ __forceinline__ void route_rows(const float *__restrict__ logits,
                                            int64_t T, int E, int k, const RouteOpts &o,
                                            int32_t *__restrict__ topk_idx,
                                            float *__restrict__ topk_w, int32_t *lds_ids,
-                                           float (&qp)[kRowVals], int &err) {
+                                           float (&qp)[kRowVals], int &err, int64_t row0 = 0) {
+    // logits holds the rows of tokens row0 .. (the softmax router may read a block's own
+    // copy of its rows; the scored variants always read the full array, row0 = 0)
     if constexpr (kFn == kScoreSoftmax && !kHash)
-        route_rows4<NV>(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, qp, err, o.lse);
+        route_rows4<NV>(logits, q, t0, T, E, k, topk_idx, topk_w, lds_ids, qp, err, o.lse,
+                        row0);
     else
         route_rows4_scored<kFn, kHash, NV>(logits, q, t0, T, E, k, o, topk_idx, topk_w, lds_ids,
                                        qp, err);
