@@ -35,6 +35,14 @@ __device__ __forceinline__ float4 load_nt(const float *p) {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// Block barrier for hand-overs through LDS only: each wave waits for its own LDS
+// operations, then s_barrier. __syncthreads also waits for the wave's outstanding global
+// stores (about a microsecond of write latency); a block whose later steps never read back
+// what it stored to memory does not need that.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt with vmcnt(N), lgkmcnt(0), expcnt untouched (gfx9 immediate encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {

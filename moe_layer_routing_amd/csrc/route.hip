@@ -269,7 +269,7 @@ __device__ __forceinline__ void topk_group(const float *__restrict__ logits,
             for (int i = 0; i < kRowVals; ++i)
                 if (c + 16 * i < E) mpt[row][c + 16 * i] = qp[i];
         }
-        __syncthreads();
+        lds_barrier();   // (the top-k's stores to memory are not read back here)
         for (int e = threadIdx.x; e < E; e += nthr) {
             float v = 0.f;
 #pragma unroll
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(64 * kLogitSplit) void route_fused_kernel(
     __shared__ float mpt[kTopkTokPerBlock][kMaxE];
     __shared__ float rows[kTopkTokPerBlock * 16 * EPB];   // the block's logits (E <= 16 EPB)
     logits_block<kBF16, EPB>(x_, wr_, bias, logits, T, d, E, blockIdx.x, part, rows);
-    __syncthreads();
+    lds_barrier();   // the top-k reads the LDS copy, not the logits just stored
     topk_group<kFn, kHash, NV>(logits, q, T, E, k, topk_idx, topk_w, mass_part, d_err, opts,
                                blockIdx.x, 64 * kLogitSplit, mpt, rows);
 }

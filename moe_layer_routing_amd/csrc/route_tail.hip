@@ -3,8 +3,9 @@
 // Decode-sized batches spend most of their routing time in kernel boundaries: every step
 // of the multi-kernel path (top-k, probability-mass reduction, histogram, scan, stable
 // scatter, tile list) is a launch plus a memory round trip for a few hundred bytes. This
-// kernel runs those steps back to back in one 1024-thread block, with the ids, counts and
-// offsets kept in LDS. It computes the same functions as the multi-kernel path, in the
+// kernel runs those steps back to back in one 1024-thread block, with the logits, ids,
+// counts and offsets kept in LDS; no step reads back what an earlier one stored to memory,
+// so its barriers wait only for LDS traffic. It computes the same functions as the multi-kernel path, in the
 // same floating-point order, so each output is bitwise the one that path gives for the
 // same T:
 //   * top-k: wave w routes tokens 4w .. 4w+3 (one per 16-lane row) with the routine the
@@ -82,10 +83,8 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
                 lgl[i1] = l1;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
-    // the top-k reads the logits it formed from LDS (the same values as the global copy)
-    const float *lg = (!kReplay && part) ? lgl : logits;
 
     // ---- top-k (or replay validation); ids also go to LDS
     int err = 0;
@@ -113,8 +112,14 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
     } else {
         float qp[kRowVals];
         if (wave * kTailTokPerWave < T) {   // waves past the batch hold zeros
-            route_rows<kFn, kHash, NV>(lg, q, (int64_t)wave * kTailTokPerWave, T, E, k,
-                                       opts, topk_idx, topk_w, ids, qp, err);
+            // logits formed here are read from the LDS copy (the values stored to memory);
+            // a separate call, so that its reads are LDS reads, which wait for nothing else
+            if (part)
+                route_rows<kFn, kHash, NV>(lgl, q, (int64_t)wave * kTailTokPerWave, T, E, k,
+                                           opts, topk_idx, topk_w, ids, qp, err);
+            else
+                route_rows<kFn, kHash, NV>(logits, q, (int64_t)wave * kTailTokPerWave, T, E, k,
+                                           opts, topk_idx, topk_w, ids, qp, err);
         } else {
 #pragma unroll
             for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
         }
     }
     wave_raise(err, d_err);
-    __syncthreads();
+    lds_barrier();
 
     // ---- per-wave expert counts and in-wave stable ranks
     const int nwv = (A + kWave - 1) / kWave;
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
             atomicAdd(&wsum[e0], (unsigned long long)(uint32_t)q[a / k]);
     }
     wave_raise(err, d_err);
-    __syncthreads();
+    lds_barrier();
 
     // ---- per expert: run starts of each wave, totals, weighted counts, probability mass
     if (tid < E) {
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
             prob_mass[tid] = (P[0] + P[2]) + (P[1] + P[3]);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- exclusive scans over experts (wave 0; lane l holds experts 4l .. 4l+3)
     if (wave == 0) {
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(64 * kTailWaves) void route_tail_kernel(
             toff[E] = tx;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- outputs: offsets, perm / inv, tile list
     if (tid <= E) offsets[tid] = eoff[tid];
