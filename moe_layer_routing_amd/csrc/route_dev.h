@@ -130,46 +130,72 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
     for (int i = 0; i < kRowVals; ++i) qp[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) qp[i] = (tv && valid[i]) ? qt * (z[i] / Z) : 0.f;
-    // Selection. Each lane first sorts its own NV (key, id) pairs, largest key first and
-    // equal keys by ascending id (Batcher's odd-even merge network on the 64-bit composite
-    // key << 32 | ~id). Then k rounds, as a loop (decode-sized launches fetch this code
-    // cold, so its size counts): the row's largest head key m, the lowest id among the
-    // lanes whose head equals m (a lane's head is its lowest id of its largest key), and the
-    // owning lane drops its head. That is the row's largest remaining key with ties to the
-    // lowest id, as before. Lane c of the row keeps round c's key and id; the
+    // Selection: k rounds, as a loop (decode-sized launches fetch this code cold, so its
+    // size counts), each taking the row's largest remaining key with ties to the lowest id.
+    // With 4 or 8 keys per lane, each lane first sorts its own (key, id) pairs, largest key
+    // first and equal keys by ascending id (Batcher's odd-even merge network on the 64-bit
+    // composite key << 32 | ~id); a round then takes the row maximum m of the lanes' head
+    // keys and the lowest id among the heads equal to m (a lane's head is its lowest id of
+    // its largest key), and the owning lane drops its head. With 16 keys per lane (E > 128)
+    // the sorted lists do not fit the 1024-thread tail's registers, so a round takes the
+    // maximum over all of the lane's keys and the owner clears the taken key in place (a
+    // present expert's key is >= 1). Lane c of the row keeps round c's key and id; the
     // probabilities are formed after the loop, one per lane, and added left to right.
-    uint64_t kv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        kv[i] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(c + 16 * i);
-#pragma unroll
-    for (int pw = 1; pw < NV; pw <<= 1)
-#pragma unroll
-        for (int kk = pw; kk >= 1; kk >>= 1)
-#pragma unroll
-            for (int j = kk % pw; j + kk < NV; j += 2 * kk)
-#pragma unroll
-                for (int i = 0; i < kk; ++i)
-                    if ((i + j) / (2 * pw) == (i + j + kk) / (2 * pw)) {
-                        const uint64_t a = kv[i + j], b = kv[i + j + kk];
-                        kv[i + j] = b > a ? b : a;
-                        kv[i + j + kk] = b > a ? a : b;
-                    }
     int my_sel = 0;
     uint32_t my_key = 0;
-#pragma unroll 1
-    for (int j = 0; j < k; ++j) {
-        const uint32_t head = (uint32_t)(kv[0] >> 32);
-        const uint32_t m = row_max_u32(head);
-        const int e = row_min_i32(head == m ? (int)~(uint32_t)kv[0] : 0x7fffffff);
-        if (c == j) {
-            my_sel = e;
-            my_key = m;
-        }
-        if ((e & 15) == c) {   // the owner drops its head
+    if constexpr (NV <= 8) {
+        uint64_t kv[NV];
 #pragma unroll
-            for (int i = 0; i + 1 < NV; ++i) kv[i] = kv[i + 1];
-            kv[NV - 1] = 0;
+        for (int i = 0; i < NV; ++i)
+            kv[i] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(c + 16 * i);
+#pragma unroll
+        for (int pw = 1; pw < NV; pw <<= 1)
+#pragma unroll
+            for (int kk = pw; kk >= 1; kk >>= 1)
+#pragma unroll
+                for (int j = kk % pw; j + kk < NV; j += 2 * kk)
+#pragma unroll
+                    for (int i = 0; i < kk; ++i)
+                        if ((i + j) / (2 * pw) == (i + j + kk) / (2 * pw)) {
+                            const uint64_t a = kv[i + j], b = kv[i + j + kk];
+                            kv[i + j] = b > a ? b : a;
+                            kv[i + j + kk] = b > a ? a : b;
+                        }
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            const uint32_t head = (uint32_t)(kv[0] >> 32);
+            const uint32_t m = row_max_u32(head);
+            const int e = row_min_i32(head == m ? (int)~(uint32_t)kv[0] : 0x7fffffff);
+            if (c == j) {
+                my_sel = e;
+                my_key = m;
+            }
+            if ((e & 15) == c) {   // the owner drops its head
+#pragma unroll
+                for (int i = 0; i + 1 < NV; ++i) kv[i] = kv[i + 1];
+                kv[NV - 1] = 0;
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            uint32_t best = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) best = max(best, hi[i]);
+            const uint32_t m = row_max_u32(best);
+            int cand = 0x7fffffff;
+#pragma unroll
+            for (int i = NV - 1; i >= 0; --i)
+                if (hi[i] == m) cand = c + 16 * i;
+            const int e = row_min_i32(cand);
+            if (c == j) {
+                my_sel = e;
+                my_key = m;
+            }
+            const bool own = (e & 15) == c;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (own && i == (e >> 4)) hi[i] = 0u;
         }
     }
     // round c's probability (lanes c < k), then the left-to-right sum over the row's rounds
