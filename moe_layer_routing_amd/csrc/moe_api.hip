@@ -426,9 +426,16 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
             e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
         }
+        // the smallest batches run the down GEMM and the plain combine as one launch
+        const bool dc = !a->ranks && down_combine_small_ok(*dims);
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
-                               a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu);
+                               a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu,
+                               /*gate_up_only=*/dc);
         if (e != hipSuccess) return MOE_E_LAUNCH;
+        if (dc)
+            return to_status(launch_down_combine_small(*dims, a->h, a->w2, a->y, ws.tiles, a->inv,
+                                                       a->topk_w, scale, a->out, a->prof_events,
+                                                       s));
         return to_status(finish_layer(dims, a, scale, shared_work, s));
     }
     if (replay)

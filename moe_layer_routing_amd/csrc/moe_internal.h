@@ -251,7 +251,16 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                               const void *w13, const void *w2, void *h, float *y,
                               const Workspace &ws, void *const *prof_events, hipStream_t s,
                               const void *x = nullptr, const int32_t *perm = nullptr,
-                              bool tiles_ready = false, float *gu_out = nullptr);
+                              bool tiles_ready = false, float *gu_out = nullptr,
+                              bool gate_up_only = false);
+// Decode-sized bf16 layers (T*k <= 16, 16-row tiles, d/16 >= 256 blocks, inter % 768 == 0):
+// the down GEMM and the plain weighted combine in one launch (y is still written); records
+// prof_events[2] after it.
+bool down_combine_small_ok(const moe_dims &dm);
+hipError_t launch_down_combine_small(const moe_dims &dm, const void *h, const void *w2, float *y,
+                                     const int32_t *tiles, const int32_t *inv,
+                                     const float *topk_w, float scale, void *out,
+                                     void *const *prof_events, hipStream_t s);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s, float scale = 1.0f);
 // Rank partial outputs and their FP64 pairwise tree (1 <= R <= kMaxRanks, R divides E).

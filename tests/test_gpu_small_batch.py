@@ -141,3 +141,42 @@ def test_small_and_large_paths_agree_per_row():
     small, _ = run_forward(L64, inp64, stats=False)
     for n in ("logits", "topk_idx", "topk_w", "out"):
         assert host(small[n]).tobytes() == host(big[n])[:64].tobytes(), n
+
+
+DC_CASES = [
+    dict(T=1, E=16, k=8, I=768, mode="router", scale=None),
+    dict(T=2, E=16, k=8, I=768, mode="router", scale=None),
+    dict(T=1, E=12, k=3, I=1536, mode="router", scale=2.5),
+    dict(T=5, E=16, k=3, I=768, mode="replay", scale=None),
+    dict(T=16, E=16, k=1, I=768, mode="replay", scale=0.75),
+]
+
+
+@pytest.mark.parametrize("case", DC_CASES,
+                         ids=lambda c: f"T{c['T']}_E{c['E']}_k{c['k']}_I{c['I']}_{c['mode']}")
+def test_decode_down_combine_launch_matches_steps(case):
+    """At most 16 expert rows, d/16 >= 256 feature blocks and inter a multiple of 768:
+    moe_forward runs the down GEMM and the combine as one launch. Its y and output rows
+    (and every other output) are bitwise those of moe_grouped_ffn + moe_combine(_scaled)
+    after the separate routing and permutation steps; the routed scaling factor too."""
+    L = W.make_layer(T=case["T"], d=4096, E=case["E"], k=case["k"], I=case["I"],
+                     dtype="bf16", mode=case["mode"], seed=70 + case["T"] + case["k"],
+                     bias="zipf", replay="dirichlet")
+    inp = upload(L)
+    dims = dims_of(L)
+    ref = _steps(L, inp, mult=False)
+    if case["scale"] is not None:
+        M.combine(dims, ref["y"], ref["inv"], ref["topk_w"], ref["out"],
+                  routed_scale=case["scale"])
+    b = M.alloc_forward_buffers(dims, "cuda", router=(L.mode == "router"), weighted=True)
+    for n in ("x", "w13", "w2"):
+        b[n] = inp[n]
+    if L.mode == "router":
+        b["w_router"], b["logit_bias"] = inp["w_router"], inp["logit_bias"]
+    else:
+        b["idx_in"], b["w_in"] = inp["idx_in"], inp["w_in"]
+    M.forward(dims, b, M.alloc_workspace(dims), routed_scale=case["scale"] or 0.0)
+    torch.cuda.synchronize()
+    assert int(b["d_err"].item()) == 0
+    for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "h", "y", "out"):
+        assert host(b[n]).tobytes() == host(ref[n]).tobytes(), n
