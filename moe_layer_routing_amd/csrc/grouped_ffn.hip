@@ -869,7 +869,12 @@ int select_tile_m(const moe_dims &dm) {
     return 256;
 }
 
-int64_t max_m_tiles(int64_t A, int E, int tile_m) { return (A + tile_m - 1) / tile_m + E; }
+// Token tiles of any routing of A rows: sum over the active experts of ceil(c_e / tile_m)
+// <= A / tile_m + (active experts), and at most min(E, A) experts are active. (The bound
+// sizes the launch grids, so decode-sized batches do not launch blocks for 128 experts.)
+int64_t max_m_tiles(int64_t A, int E, int tile_m) {
+    return (A + tile_m - 1) / tile_m + std::min<int64_t>(E, A);
+}
 
 hipError_t launch_build_tiles(const int32_t *offsets, int E, int64_t A, int bt, int64_t cap,
                               int32_t *tiles, hipStream_t s) {

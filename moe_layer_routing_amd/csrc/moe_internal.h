@@ -208,6 +208,7 @@ struct Workspace {
 };
 
 int64_t perm_chunks(int64_t A);
+// Most token tiles any routing of A rows over E experts can produce at tile height tile_m.
 int64_t max_m_tiles(int64_t A, int E, int tile_m);
 Workspace carve_workspace(const moe_dims &d, void *base);
 
