@@ -766,11 +766,15 @@ hipError_t launch_gemm(const void *act, const void *wgt, void *out, const int32_
                 K, N, nft, gperm, gk, gT, dh, gu_out);
     } else if constexpr (IsDma128<C>::value) {
         // the DMA kernel is bf16-only: FP32 layers use the register-staged kernel with the
-        // same token tiles
+        // same token tiles (the 256-token gate/up tile takes 128 weight rows: with 256 its
+        // gate and up accumulators do not fit the registers)
         using F = typename std::conditional<
             (C::BT <= 32), Cfg<128, C::BT, 4, 1, 1, 128, 3>,
-            typename std::conditional<(C::BT == 64), Cfg<128, 64, 2, 2, 1, 128, 2>,
-                                      Cfg<256, C::BT, 2, 2, 1, 64, 1>>::type>::type;
+            typename std::conditional<
+                (C::BT == 64), Cfg<128, 64, 2, 2, 1, 128, 2>,
+                typename std::conditional<(kGateUp && C::BT == 256),
+                                          Cfg<128, 256, 2, 2, 1, 64, 1>,
+                                          Cfg<256, C::BT, 2, 2, 1, 64, 1>>::type>::type>::type;
         return launch_gemm<kBF16, kGateUp, F>(act, wgt, out, tiles, mtiles, K, N, s, gperm, gk,
                                               gT, nullptr, gu_out);
     } else {
