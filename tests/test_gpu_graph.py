@@ -24,10 +24,13 @@ OUTS = ("out", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "h", "y
         "weighted_counts", "prob_mass", "logits", "d_err")
 
 
-@pytest.mark.parametrize("T,mode", [(1, "router"), (48, "router"), (700, "router"),
-                                    (300, "replay")])
-def test_graph_replay_matches_eager(T, mode):
-    L = W.make_layer(T=T, d=256, E=32, k=8, I=128, dtype="bf16", mode=mode, seed=T,
+@pytest.mark.parametrize("T,mode,d", [(1, "router", 256), (48, "router", 256),
+                                      (700, "router", 256), (300, "replay", 256),
+                                      # d/16 >= 256: the one-launch down GEMM + combine
+                                      (1, "router", 4096), (2, "replay", 4096)])
+def test_graph_replay_matches_eager(T, mode, d):
+    E, I = (32, 128) if d == 256 else (16, 768)
+    L = W.make_layer(T=T, d=d, E=E, k=8, I=I, dtype="bf16", mode=mode, seed=T,
                      bias="zipf", replay="uniform")
     L.token_mult = W.token_multiplicities(T, 1)
     inp = upload(L)

@@ -81,6 +81,17 @@ def test_noalloc_equals_forward_on_shrinking_calls():
         _compare(L, upload(L), fused_gather=False)
 
 
+def test_noalloc_decode_shaped_calls():
+    """Decode-sized calls with d = 4096 (T = 64, then 2 and 1: the last two run the down
+    GEMM and the combine as one launch) on the same scratch."""
+    assert torch.cuda.is_available()
+    for T in (64, 2, 1):
+        L = W.make_layer(T=T, d=4096, E=16, k=8, I=768, dtype="bf16", mode="router", seed=74,
+                         mult=True, bias="zipf")
+        L.name = "noalloc-decode"
+        _compare(L, upload(L))
+
+
 def test_noalloc_training_shaped_layer_twice():
     """The training-shaped layer (T=4096, d=2048, E=64, I=1408), then its first 1024
     tokens: the second, smaller call follows the first on the same scratch."""
