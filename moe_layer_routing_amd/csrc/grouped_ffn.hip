@@ -692,7 +692,8 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_small_kernel(
         // lane l reads row l % 16 (rows past the tile repeat its last row), K-slice l / 16
         const uint16_t *hp = h + (int64_t)(p0 + min(lane & 15, nrows - 1)) * I + (lane >> 4) * 8;
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // two register sets: group s0 + kDcGroup is in flight while group s0 is multiplied
+        // two register sets: the loads of the next group are issued before this group's
+        // MFMAs, so a wave has up to 2 x kDcGroup K-steps in flight
         DcGroup g0, g1;
         dc_load(g0, wp, hp, 0);
         for (int s0 = 0; s0 < nsteps; s0 += 2 * kDcGroup) {
@@ -701,7 +702,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_small_kernel(
             if (s0 + 2 * kDcGroup < nsteps) dc_load(g0, wp, hp, s0 + 2 * kDcGroup);
             dc_mfma(acc, g1, src);
         }
-    // lane l holds token row l % 16 of the tile, features 4 (l / 16) + 0..3
+        // lane l holds token row l % 16 of the tile, features 4 (l / 16) + 0..3
         const int col = lane & 15, fr = 4 * (lane >> 4);
         if (col < nrows) {
             const int p = p0 + col;
