@@ -637,7 +637,10 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 // the block's 16 features of each token is summed over the token's k slots in slot order
 // with the combine kernel's arithmetic ("0 train-infer mismatch ...", "The experts:
 // keeping the route weight inside the accumulator"), scaled and rounded once.
-constexpr int kDcRows = 16, kDcFeat = 16, kDcWaves = 8, kDcGroup = 12;
+// (up to 64 rows measured the same at T = 4 and 8, where the tiled down GEMM and the
+// combine kernel already stream well; the one-launch form pays off at T <= 2)
+constexpr int kDcRows = 16, kDcTile = 16, kDcFeat = 16, kDcWaves = 8, kDcGroup = 12;
+constexpr int kDcMaxTiles = kDcRows / kDcTile + kDcRows;   // max_m_tiles(kDcRows, E, 16)
 constexpr int kDcMinBlocks = 256;   // d / 16 blocks must fill the 256 CUs
 
 __device__ __forceinline__ bf16x8_t dc_lay(bf16x8_t v, int src) {
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void down_combine_small_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int f0 = blockIdx.x * kDcFeat;
     const int A = T * k;
-    const int ntiles = min(tiles[0], kDcRows);
+    const int ntiles = min(tiles[0], kDcMaxTiles);
     const int rc = lane >> 2, gc = lane & 3;                   // the lane's load row / slice
     const int src = 4 * (4 * (lane & 15) + (lane >> 4));       // byte address of its source
     const int nsteps = I >> 5;
@@ -984,7 +987,7 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
 
 bool down_combine_small_ok(const moe_dims &dm) {
     return dm.dtype == MOE_BF16 && dm.T >= 1 && dm.T * dm.k <= kDcRows &&
-           select_tile_m(dm) == kDcRows && dm.d % kDcFeat == 0 &&
+           select_tile_m(dm) == kDcTile && dm.d % kDcFeat == 0 &&
            dm.d / kDcFeat >= kDcMinBlocks && dm.inter % (64 * kDcGroup) == 0;
 }
 
