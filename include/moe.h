@@ -332,7 +332,10 @@ moe_status moe_shared_ffn(const moe_dims *dims, int32_t ranks, int32_t inter_sha
  * of x through perm (identical results; x must then be smaller than 4 GiB, else
  * MOE_E_SHAPE).
  * prof_events: NULL, or three hipEvent_t handles recorded on `stream` before the
- * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing).
+ * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing). A bf16 layer
+ * with at most 16 expert rows (T*k <= 16), d/16 >= 256 and inter a multiple of 768 runs
+ * the down GEMM and the plain combine as one launch (same outputs, y included); the third
+ * event then follows that launch.
  * slot_of_expert: NULL, or a device placement map as in moe_permute_placed (w13 and w2
  * then hold the experts in slot order; counts/offsets/statistics are per slot; topk_idx
  * stays in logical ids).
