@@ -68,3 +68,30 @@ def test_no_packed_fp32_arithmetic():
                             "--cuda-device-only", os.path.join(CSRC, f), "-o", "-"],
                            check=True, capture_output=True, text=True)
         assert not re.search(r"v_pk_(add|mul|fma)_f32", r.stdout), f
+
+
+def _asm_of(src_name, tmp_path):
+    from moe_layer_routing_amd import _build
+    out = tmp_path / (src_name + ".s")
+    subprocess.run([_build.HIPCC, *[f for f in _build.FLAGS if f not in ("-shared", "-fPIC")],
+                    "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-S", "--cuda-device-only",
+                    os.path.join(CSRC, src_name), "-o", str(out)], check=True,
+                   capture_output=True)
+    return out.read_text()
+
+
+def test_decode_kernels_have_no_scratch(gemm_asm, tmp_path):
+    """The one-block routing tail (every router variant and register width) and the
+    decode-sized down GEMM + combine run on the decode path's critical chain; register
+    spills there are pure latency, so they must compile without scratch."""
+    checked = []
+    for asm, key in ((_asm_of("route_tail.hip", tmp_path), "route_tail_kernel"),
+                     (gemm_asm, "down_combine_small_kernel")):
+        for name, b in _kernels(asm):
+            if key not in name:
+                continue
+            priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", b).group(1))
+            assert priv == 0, f"{name}: scratch {priv} B"
+            checked.append(name)
+    assert sum("route_tail_kernel" in n for n in checked) >= 10
+    assert any("down_combine_small_kernel" in n for n in checked)
