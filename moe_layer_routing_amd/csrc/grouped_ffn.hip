@@ -22,7 +22,7 @@
 // 4*(l/16)+0..3) every lane stores 4 consecutive features of one token row.
 #include <type_traits>
 
-#include "moe_internal.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -368,14 +368,17 @@ __device__ __forceinline__ void dma_stage128(uint8_t *slot, const uint8_t *wbase
 // lane 4j + i/4 named at position i%4, so lane s naming K-row 8g + s/4 (then + 4) at
 // features f + 4(s%4) hands lane i feature f + i at K-rows 8g + 0..7 -- the operand a
 // row-major weight tile gives, in the same K positions, hence the same bits.
-template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS, bool kKMajor = false,
-          int kGrad = 0>
-__global__ __launch_bounds__(64 * WF * WT)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
-    const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
-    const int32_t *__restrict__ tiles, int K, int N, int nft,
-    const int32_t *__restrict__ gperm, int gk, int64_t gT, const float *__restrict__ dh,
-    float *__restrict__ gu_out = nullptr) {
+//
+// dma128_tile computes one block's tile: feature tile ft of expert e's weights against the
+// output's token rows p0 .. p0 + nrows - 1, whose activation rows start at abase (or are
+// gathered through gperm); ring is the block's LDS ring of NS stages.
+template <bool kGateUp, int BW, int BT, int WF, int WT, int NS, bool kKMajor, int kGrad>
+__device__ __forceinline__ void dma128_tile(uint8_t *ring, const uint8_t *__restrict__ abase,
+                                            const uint8_t *__restrict__ wgt,
+                                            void *__restrict__ out, int K, int N, int e, int p0,
+                                            int nrows, int ft, const int32_t *__restrict__ gperm,
+                                            int gk, int64_t gT, const float *__restrict__ dh,
+                                            float *__restrict__ gu_out) {
     constexpr int NW = WF * WT;
     constexpr int NBLK = (BW + BT) / 8;                // 8-row LDS blocks per stage
     constexpr int NBW = NBLK / NW;                     // DMA instructions per wave per stage
@@ -391,11 +394,6 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     static_assert(!kKMajor || (!kGateUp && BW >= 64 && BW <= 512), "K-major: plain mode");
     constexpr int kCPR = BW / 8;                        // K-major: 16-byte chunks per K-row
 
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * kStageBytes];
-
-    int mt, ft;
-    if (!block_tile(tiles[0], nft, mt, ft)) return;
-    const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wf = wv % WF, wt = wv / WF;
@@ -403,7 +401,6 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     const int64_t rows_per_expert = kGateUp ? 2 * (int64_t)N : (int64_t)N;
     const uint32_t krow = (uint32_t)K * 2u;
     const uint8_t *wbase = wgt + (int64_t)e * rows_per_expert * krow;
-    const uint8_t *abase = gperm ? act : act + (int64_t)p0 * krow;
 
     // DMA sources (byte offsets from wbase / abase) of this lane's row in each block
     const int rb = lane >> 3;
@@ -623,6 +620,114 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
     }
 }
 
+template <bool kGateUp, int BW, int BT, int WF, int WT, int WPE, int NS, bool kKMajor = false,
+          int kGrad = 0>
+__global__ __launch_bounds__(64 * WF * WT)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
+    const uint8_t *__restrict__ act, const uint8_t *__restrict__ wgt, void *__restrict__ out,
+    const int32_t *__restrict__ tiles, int K, int N, int nft,
+    const int32_t *__restrict__ gperm, int gk, int64_t gT, const float *__restrict__ dh,
+    float *__restrict__ gu_out = nullptr) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * ((BW + BT) / 8) * 1024];
+    int mt, ft;
+    if (!block_tile(tiles[0], nft, mt, ft)) return;
+    const int e = tiles[1 + 3 * mt], p0 = tiles[2 + 3 * mt], nrows = tiles[3 + 3 * mt];
+    const uint8_t *abase = gperm ? act : act + (int64_t)p0 * ((uint32_t)K * 2u);
+    dma128_tile<kGateUp, BW, BT, WF, WT, NS, kKMajor, kGrad>(ring, abase, wgt, out, K, N, e, p0,
+                                                              nrows, ft, gperm, gk, gT, dh,
+                                                              gu_out);
+}
+
+// One-token decode step with the plain softmax router: the gate/up launch routes the token
+// itself. Every block forms the E router logits from the K-chain partials (chain order, then
+// the bias: the routing tail's sums) and runs the tail's softmax + top-k + renormalisation
+// routine on them ("0 train-infer mismatch ...", "The router: matching expert ids and
+// weights"), so every block holds the same k experts with the tail's bits. Token tile mt is
+// the mt-th smallest selected id (the stable counting sort puts the k rows in expert order,
+// one 16-row tile each, row mt), and the block computes feature tile ft of it; block 0
+// also stores every output of the routing tail for T = 1 (logits, ids and weights, the
+// probability mass 0 + q p_e, counts, offsets, perm / inv, weighted counts, tile list,
+// error bits). The tail's launch and its boundary leave the step: the partials come
+// straight from the logit-chain launch before this one.
+template <class C, int NV>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_kernel(
+    const uint8_t *__restrict__ x, const uint8_t *__restrict__ w13, void *__restrict__ h,
+    int K, int N, int nft, int E, int k, DecodeRoute r, float *__restrict__ gu_out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NS * ((C::BW + C::BT) / 8) * 1024];
+    __shared__ float lgl[kMaxE / 2];
+    __shared__ float selw[kMaxK];
+    __shared__ int32_t sel[kMaxK], sorted[kMaxK];
+    const int tid = threadIdx.x;
+    const bool lead = blockIdx.x == 0;
+    for (int e = tid; e < E; e += C::kThreads) {
+        float p[kLogitChains];
+#pragma unroll
+        for (int c = 0; c < kLogitChains; ++c) p[c] = r.part[c * E + e];
+        float v = p[0];
+#pragma unroll
+        for (int c = 1; c < kLogitChains; ++c) v = v + p[c];
+        const float l = r.bias ? v + r.bias[e] : v;
+        lgl[e] = l;
+        if (lead) r.logits[e] = l;
+    }
+    lds_barrier();
+    if (tid < kWave) {
+        float qp[kRowVals];
+        int err = 0;
+        route_rows4<NV>(lgl, r.q, 0, 1, E, k, sel, selw, nullptr, qp, err,
+                        lead ? r.lse : nullptr);
+        if (lead) {
+            wave_raise(err, r.d_err);
+            if (r.prob_mass && tid < 16) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (tid + 16 * i < E) r.prob_mass[tid + 16 * i] = 0.f + qp[i];
+            }
+        }
+    }
+    lds_barrier();
+    if (tid < k) {
+        const int ej = sel[tid];
+        int rank = 0;
+        for (int i = 0; i < k; ++i) rank += sel[i] < ej;
+        sorted[rank] = ej;
+        if (lead) {
+            r.topk_idx[tid] = ej;
+            r.topk_w[tid] = selw[tid];
+            r.perm[rank] = tid;
+            r.inv[tid] = rank;
+            int32_t *d = r.tiles + 1 + 3 * rank;
+            d[0] = ej;
+            d[1] = rank;
+            d[2] = 1;
+        }
+    }
+    if (lead) {
+        if (tid == 0) {
+            r.tiles[0] = k;
+            r.offsets[E] = k;
+        }
+        for (int e = tid; e < E; e += C::kThreads) {
+            int before = 0;
+            bool chosen = false;
+            for (int i = 0; i < k; ++i) {
+                before += sel[i] < e;
+                chosen |= sel[i] == e;
+            }
+            r.counts[e] = chosen;
+            r.offsets[e] = before;
+            if (r.weighted_counts)
+                r.weighted_counts[e] = !chosen ? 0 : r.q ? (int64_t)(uint32_t)r.q[0] : 1;
+        }
+    }
+    lds_barrier();
+    int mt, ft;
+    block_tile(k, nft, mt, ft);   // the grid is exactly k x nft blocks
+    dma128_tile<true, C::BW, C::BT, C::WF, C::WT, C::NS, false, 0>(
+        ring, x, w13, h, K, N, sorted[mt], mt, 1, ft, nullptr, 1, 1, nullptr, gu_out);
+}
+
 // ------------------------------------------------------------------------------------
 // Decode-sized layers (at most kDcRows expert rows, so one 16-row token tile per active
 // expert): the down GEMM and the weighted combine in one launch. Block b owns output
@@ -824,7 +929,14 @@ hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, 
 #define MOE_FFN_HUGE_CFG2 Dma128Cfg<256, 256, 2, 4>
 #endif
 
-using PLAIN_CFG16 = Dma128Cfg<64, 16, 2, 1, 6>;
+#ifndef MOE_FFN_CFG16
+#define MOE_FFN_CFG16 Dma128Cfg<64, 16, 2, 1, 6>
+#endif
+using PLAIN_CFG16 = MOE_FFN_CFG16;
+#ifndef MOE_SELF_ROUTE_CFG
+#define MOE_SELF_ROUTE_CFG Dma128Cfg<32, 16, 1, 1, 6>
+#endif
+using SELF_ROUTE_CFG = MOE_SELF_ROUTE_CFG;
 using PLAIN_CFG32 = Dma128Cfg<64, 32, 2, 1, 6>;
 using PLAIN_CFG64 = Dma128Cfg<128, 64, 2, 2, 4>;
 using PLAIN_LARGE = MOE_FFN_LARGE_CFG2;
@@ -839,7 +951,7 @@ hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const in
     // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block.
     switch (bt) {
     case 16: {
-        using C = Dma128Cfg<64, 16, 2, 1, 6>;
+        using C = PLAIN_CFG16;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out,
                                     gate_up_only);
     }
@@ -983,6 +1095,32 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
                                   s, gu_out, gate_up_only);
     return dispatch_ffn<false>(dm, bt, act13, gperm, w13, w2, h, y, ws.tiles, cap, prof_events,
                                s, gu_out, gate_up_only);
+}
+
+bool decode_self_route_ok(const moe_dims &dm) {
+    return dm.dtype == MOE_BF16 && dm.T == 1 && dm.E >= dm.k && dm.E <= kMaxE / 2 &&
+           dm.k >= 1 && dm.k <= kMaxK && select_tile_m(dm) == 16;
+}
+
+hipError_t launch_decode_self_route(const moe_dims &dm, const DecodeRoute &r, const void *x,
+                                    const void *w13, void *h, float *gu_out,
+                                    void *const *prof_events, hipStream_t s) {
+    if (!decode_self_route_ok(dm)) return hipErrorInvalidValue;
+    using C = SELF_ROUTE_CFG;
+    const int nft = (dm.inter + C::BW / 2 - 1) / (C::BW / 2);
+    if (prof_events && hipEventRecord(static_cast<hipEvent_t>(prof_events[0]), s) != hipSuccess)
+        return hipErrorInvalidValue;
+    auto go = [&](auto nv) {
+        gate_up_self_route_kernel<C, decltype(nv)::value>
+            <<<dim3((unsigned)(dm.k * nft)), dim3(C::kThreads), 0, s>>>(
+                static_cast<const uint8_t *>(x), static_cast<const uint8_t *>(w13), h, dm.d,
+                dm.inter, nft, dm.E, dm.k, r, gu_out);
+    };
+    if (dm.E <= 64) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 8>{});
+    if (prof_events && hipEventRecord(static_cast<hipEvent_t>(prof_events[1]), s) != hipSuccess)
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 bool down_combine_small_ok(const moe_dims &dm) {

@@ -410,9 +410,37 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
         // that sum costs the single block more than the wider logits launch saves.
         float *logits = a->logits ? a->logits : ws.logits;
         const bool chains = !replay && dims->T * dims->E <= kChainSumMax;
+        // the smallest batches run the down GEMM and the plain combine as one launch
+        const bool dc = !a->ranks && down_combine_small_ok(*dims);
         if (chains) {
             e = launch_router_logit_chains(*dims, a->x, a->w_router, ws.logit_part, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
+            // one token, plain softmax router: the gate/up launch routes it (no tail launch)
+            if (dc && ro.plain() && !a->slot_of_expert && !a->x_perm &&
+                decode_self_route_ok(*dims)) {
+                DecodeRoute r;
+                r.part = ws.logit_part;
+                r.bias = a->logit_bias;
+                r.q = a->token_mult;
+                r.logits = logits;
+                r.topk_w = a->topk_w;
+                r.prob_mass = a->prob_mass;
+                r.lse = ro.lse;
+                r.topk_idx = a->topk_idx;
+                r.counts = a->counts;
+                r.offsets = a->offsets;
+                r.perm = a->perm;
+                r.inv = a->inv;
+                r.tiles = ws.tiles;
+                r.d_err = a->d_err;
+                r.weighted_counts = a->weighted_counts;
+                e = launch_decode_self_route(*dims, r, a->x, a->w13, a->h, a->gu,
+                                             a->prof_events, s);
+                if (e != hipSuccess) return MOE_E_LAUNCH;
+                return to_status(launch_down_combine_small(*dims, a->h, a->w2, a->y, ws.tiles,
+                                                           a->inv, a->topk_w, scale, a->out,
+                                                           a->prof_events, s));
+            }
         } else if (!replay) {
             e = launch_router_logits(*dims, a->x, a->w_router, a->logit_bias, logits, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
@@ -426,8 +454,6 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
             e = launch_gather(*dims, a->x, a->inv, a->x_perm, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
         }
-        // the smallest batches run the down GEMM and the plain combine as one launch
-        const bool dc = !a->ranks && down_combine_small_ok(*dims);
         e = launch_grouped_ffn(*dims, a->x_perm, a->offsets, a->w13, a->w2, a->h, a->y, ws,
                                a->prof_events, s, a->x, a->perm, /*tiles_ready=*/true, a->gu,
                                /*gate_up_only=*/dc);

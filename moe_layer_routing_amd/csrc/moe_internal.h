@@ -262,6 +262,24 @@ hipError_t launch_down_combine_small(const moe_dims &dm, const void *h, const vo
                                      const int32_t *tiles, const int32_t *inv,
                                      const float *topk_w, float scale, void *out,
                                      void *const *prof_events, hipStream_t s);
+// One-token bf16 decode step with the plain softmax router (T = 1, E <= 128, 16-row tiles):
+// the gate/up launch (gathered from x, records prof_events[0] and [1] around it) forms the
+// logits from the logit-chain partials and routes the token in every block, with the
+// routing tail's arithmetic; block 0 writes every output launch_small_tail writes for
+// T = 1 without a placement map (pointers as there; prob_mass, weighted_counts, lse and q
+// may be null). The tile list it writes serves the down GEMM launch after it.
+struct DecodeRoute {
+    const float *part;   // [kLogitChains][E] chain partials
+    const float *bias;   // [E] or null
+    const int32_t *q;    // [1] token multiplicity or null
+    float *logits, *topk_w, *prob_mass, *lse;
+    int32_t *topk_idx, *counts, *offsets, *perm, *inv, *tiles, *d_err;
+    int64_t *weighted_counts;
+};
+bool decode_self_route_ok(const moe_dims &dm);
+hipError_t launch_decode_self_route(const moe_dims &dm, const DecodeRoute &r, const void *x,
+                                    const void *w13, void *h, float *gu_out,
+                                    void *const *prof_events, hipStream_t s);
 hipError_t launch_combine(const moe_dims &dm, const float *y, const int32_t *inv,
                           const float *topk_w, void *out, hipStream_t s, float scale = 1.0f);
 // Rank partial outputs and their FP64 pairwise tree (1 <= R <= kMaxRanks, R divides E).

@@ -137,13 +137,13 @@ def test_c5_batch_invariance():
     inp = upload(L)
     ref_out = ref_idx = ref_w = None
 
-    def run(x_rows, tile_m=0):
+    def run(x_rows, tile_m=0, fused=False):
         L2 = W.make_config("c5", T=len(x_rows), weights=False)
         L2.x = np.ascontiguousarray(x_rows)
         L2.w13, L2.w2 = L.w13, L.w2
         inp2 = dict(inp)
         inp2["x"] = dev(L2.x)
-        b, _ = run_forward(L2, inp2, tile_m=tile_m, stats=False)
+        b, _ = run_forward(L2, inp2, tile_m=tile_m, stats=False, fused_gather=fused)
         assert int(b["d_err"].item()) == 0
         return host(b["out"]), host(b["topk_idx"]), host(b["topk_w"]), b
 
@@ -153,6 +153,16 @@ def test_c5_batch_invariance():
         assert out.tobytes() == ref_out[:T].tobytes(), T
         assert idx.tobytes() == ref_idx[:T].tobytes(), T
         assert w.tobytes() == ref_w[:T].tobytes(), T
+    # one token with the gather fused into the gate/up GEMM (the decode step's launches:
+    # the gate/up launch routes the token itself) and for T = 2 (routing tail): same bits
+    for rows in (pool[0:1], pool[17:18], pool[63:64], pool[40:42]):
+        t0 = int(np.flatnonzero((pool == rows[0]).all(axis=1))[0])
+        T = len(rows)
+        out, idx, w, b1 = run(rows, fused=True)
+        assert out.tobytes() == ref_out[t0:t0 + T].tobytes(), (t0, T)
+        assert idx.tobytes() == ref_idx[t0:t0 + T].tobytes(), (t0, T)
+        assert w.tobytes() == ref_w[t0:t0 + T].tobytes(), (t0, T)
+        assert host(b1["logits"]).tobytes() == host(b64["logits"])[t0:t0 + T].tobytes()
     out, idx, _, _ = run(pool[::-1])
     assert out.tobytes() == ref_out[::-1].tobytes()
     for tm in (16, 32, 64, 128, 256):

@@ -180,3 +180,88 @@ def test_decode_down_combine_launch_matches_steps(case):
     assert int(b["d_err"].item()) == 0
     for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "h", "y", "out"):
         assert host(b[n]).tobytes() == host(ref[n]).tobytes(), n
+
+
+SR_CASES = [
+    dict(E=16, k=8, I=768, mult=True, scale=None, lse=True),
+    dict(E=12, k=3, I=1536, mult=False, scale=2.5, lse=False),
+    dict(E=8, k=8, I=768, mult=True, scale=None, lse=False),     # every expert selected
+    dict(E=33, k=1, I=768, mult=True, scale=0.5, lse=True),
+]
+SR_OUTS = ("logits", "topk_idx", "topk_w", "prob_mass", "counts", "offsets", "perm", "inv",
+           "weighted_counts", "gu", "h", "y", "out", "d_err")
+
+
+def _decode_one(L, inp, fused, mult, scale, lse):
+    """One-token moe_forward; fused: no x_perm (the gate/up launch gathers, and with the
+    plain softmax router routes the token itself), else the routing tail + gather path."""
+    dims = dims_of(L)
+    b = M.alloc_forward_buffers(dims, "cuda", router=True, weighted=True)
+    for n in ("x", "w13", "w2", "w_router", "logit_bias"):
+        b[n] = inp[n]
+    if mult:
+        b["token_mult"] = inp["token_mult"]
+    if fused:
+        del b["x_perm"]
+    b["gu"] = torch.empty((L.k, 2 * L.I), dtype=torch.float32, device="cuda")
+    lse_t = torch.full((1,), 7.0, dtype=torch.float32, device="cuda") if lse else None
+    M.forward(dims, b, M.alloc_workspace(dims), routed_scale=scale or 0.0,
+              router=dict(score="softmax", lse=lse_t) if lse else None)
+    torch.cuda.synchronize()
+    return b, lse_t
+
+
+@pytest.mark.parametrize("case", SR_CASES,
+                         ids=lambda c: f"E{c['E']}_k{c['k']}_I{c['I']}_q{int(c['mult'])}")
+def test_decode_self_route_matches_tail(case):
+    """T = 1, plain softmax router, gather fused (the decode step's launch shape): the
+    gate/up launch forms the logits from the chain partials and selects the experts in
+    every block. Every output is bitwise the routing-tail path's (tail launch, gather,
+    gate/up from x_perm), the routing outputs the multi-kernel steps', and the oracle
+    agrees on the GPU logits."""
+    L = W.make_layer(T=1, d=4096, E=case["E"], k=case["k"], I=case["I"], dtype="bf16",
+                     mode="router", seed=90 + case["E"] + case["k"], bias="zipf")
+    L.token_mult = np.array([3], dtype=np.int32)
+    inp = upload(L)
+    args = (case["mult"], case["scale"], case["lse"])
+    ref, lse_r = _decode_one(L, inp, False, *args)
+    got, lse_g = _decode_one(L, inp, True, *args)
+    assert int(got["d_err"].item()) == 0
+    for n in SR_OUTS:
+        assert host(got[n]).tobytes() == host(ref[n]).tobytes(), n
+    if case["lse"]:
+        assert host(lse_g).tobytes() == host(lse_r).tobytes()
+    steps = _steps(L, inp, case["mult"])
+    for n in ("logits", "topk_idx", "topk_w", "prob_mass", "counts", "offsets", "perm", "inv",
+              "weighted_counts", "h", "y"):
+        assert host(got[n]).tobytes() == host(steps[n]).tobytes(), n
+    lg = host(got["logits"])
+    q = L.token_mult if case["mult"] else None
+    idx_o, w_o, mass_o, err_o = oracle.route_from_logits(lg, L.k, q)
+    assert err_o == 0
+    np.testing.assert_array_equal(host(got["topk_idx"]), idx_o)
+    assert_close(host(got["topk_w"]), w_o, "f32", "topk_w")
+    assert_close(host(got["prob_mass"]), mass_o, "f32", "prob_mass")
+    L.routed_scale = case["scale"] or 1.0
+    _, _, rout = oracle.forward_tokens(L, [0], host(got["topk_idx"]), host(got["topk_w"]))
+    assert_close(as_f32(host(got["out"]), "bf16"), as_f32(rout, "bf16"), "bf16", "out")
+
+
+def test_decode_self_route_nonfinite_logit():
+    """An infinite router logit (a +inf bias) on the one-token path: the same error bit
+    and the same (NaN-carrying) outputs as the routing tail."""
+    L = W.make_layer(T=1, d=4096, E=16, k=4, I=768, dtype="bf16", mode="router", seed=97,
+                     bias="zipf")
+    L.logit_bias = L.logit_bias.copy()
+    L.logit_bias[5] = np.inf
+    inp = upload(L)
+    ref, _ = _decode_one(L, inp, False, False, None, False)
+    got, _ = _decode_one(L, inp, True, False, None, False)
+    assert int(got["d_err"].item()) == int(ref["d_err"].item())
+    assert int(got["d_err"].item()) & M.DERR_NONFINITE
+    for n in ("topk_idx", "counts", "offsets", "perm", "inv", "weighted_counts"):
+        assert host(got[n]).tobytes() == host(ref[n]).tobytes(), n
+    assert int(host(got["topk_idx"])[0, 0]) == 5
+    for n in ("logits", "topk_w", "prob_mass", "out"):
+        np.testing.assert_array_equal(host(got[n]).view(np.uint8), host(ref[n]).view(np.uint8),
+                                      err_msg=n)

@@ -81,11 +81,13 @@ def _asm_of(src_name, tmp_path):
 
 
 def test_decode_kernels_have_no_scratch(gemm_asm, tmp_path):
-    """The one-block routing tail (every router variant and register width) and the
-    decode-sized down GEMM + combine run on the decode path's critical chain; register
-    spills there are pure latency, so they must compile without scratch."""
+    """The one-block routing tail (every router variant and register width), the
+    self-routing one-token gate/up GEMM and the decode-sized down GEMM + combine run on the
+    decode path's critical chain; register spills there are pure latency, so they must
+    compile without scratch."""
     checked = []
     for asm, key in ((_asm_of("route_tail.hip", tmp_path), "route_tail_kernel"),
+                     (gemm_asm, "gate_up_self_route_kernel"),
                      (gemm_asm, "down_combine_small_kernel")):
         for name, b in _kernels(asm):
             if key not in name:
@@ -95,3 +97,20 @@ def test_decode_kernels_have_no_scratch(gemm_asm, tmp_path):
             checked.append(name)
     assert sum("route_tail_kernel" in n for n in checked) >= 10
     assert any("down_combine_small_kernel" in n for n in checked)
+    assert sum("gate_up_self_route_kernel" in n for n in checked) == 2   # 4 and 8 per lane
+
+
+def test_dma_ring_reads_wait_only_for_their_stage(gemm_asm):
+    """The DMA GEMM kernels keep NS-2 stages of global->LDS copies in flight while the
+    fragment reads of the current stage run; the hand-placed vmcnt waits order them. A
+    compiler-inserted vmcnt(0) in front of a fragment read would drain the whole ring every
+    stage (measured: the decode gate/up launch 39 -> 69 us), so none may appear there."""
+    names = re.findall(r"^(_Z\w*(?:dma128_kernel|self_route_kernel)\w*):", gemm_asm, re.M)
+    assert len(names) >= 20
+    for n in names:
+        body = re.search("^" + n + r":[^\n]*\n(.*?)^\s*s_endpgm", gemm_asm, re.S | re.M).group(1)
+        lines = body.splitlines()
+        for i, line in enumerate(lines):
+            if "s_waitcnt vmcnt(0)" in line:
+                nxt = " ".join(lines[i + 1:i + 3])
+                assert "ds_read" not in nxt, f"{n}: vmcnt(0) before a fragment read"
