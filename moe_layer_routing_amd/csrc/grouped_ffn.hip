@@ -640,15 +640,16 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 
 // One-token decode step with the plain softmax router: the gate/up launch routes the token
 // itself. Every block forms the E router logits from the K-chain partials (chain order, then
-// the bias: the routing tail's sums) and runs the tail's softmax + top-k + renormalisation
-// routine on them ("0 train-infer mismatch ...", "The router: matching expert ids and
-// weights"), so every block holds the same k experts with the tail's bits. Token tile mt is
-// the mt-th smallest selected id (the stable counting sort puts the k rows in expert order,
-// one 16-row tile each, row mt), and the block computes feature tile ft of it; block 0
-// also stores every output of the routing tail for T = 1 (logits, ids and weights, the
-// probability mass 0 + q p_e, counts, offsets, perm / inv, weighted counts, tile list,
-// error bits). The tail's launch and its boundary leave the step: the partials come
-// straight from the logit-chain launch before this one.
+// the bias: the routing tail's sums). The last block runs the tail's softmax + top-k +
+// renormalisation routine on them ("0 train-infer mismatch ...", "The router: matching
+// expert ids and weights") and stores every output of the routing tail for T = 1 (logits,
+// ids and weights, lse, the probability mass 0 + q p_e, counts, offsets, perm / inv,
+// weighted counts, tile list, error bits); it computes no GEMM tile. The GEMM blocks run only
+// that routine's selection rounds on the same keys (select_row4), so they hold the same k
+// ids. Token tile mt is the mt-th smallest selected id (the stable counting sort puts the
+// k rows in expert order, one 16-row tile each, row mt), and block (mt, ft) computes
+// feature tile ft of it. The tail's launch and its boundary leave the step: the partials
+// come straight from the logit-chain launch before this one.
 template <class C, int NV>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_kernel(
@@ -659,7 +660,7 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
     __shared__ float selw[kMaxK];
     __shared__ int32_t sel[kMaxK], sorted[kMaxK];
     const int tid = threadIdx.x;
-    const bool lead = blockIdx.x == 0;
+    const bool router = blockIdx.x == gridDim.x - 1;   // the block that writes the routing
     for (int e = tid; e < E; e += C::kThreads) {
         float p[kLogitChains];
 #pragma unroll
@@ -669,15 +670,14 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
         for (int c = 1; c < kLogitChains; ++c) v = v + p[c];
         const float l = r.bias ? v + r.bias[e] : v;
         lgl[e] = l;
-        if (lead) r.logits[e] = l;
+        if (router) r.logits[e] = l;
     }
     lds_barrier();
-    if (tid < kWave) {
-        float qp[kRowVals];
-        int err = 0;
-        route_rows4<NV>(lgl, r.q, 0, 1, E, k, sel, selw, nullptr, qp, err,
-                        lead ? r.lse : nullptr);
-        if (lead) {
+    if (router) {
+        if (tid < kWave) {
+            float qp[kRowVals];
+            int err = 0;
+            route_rows4<NV>(lgl, r.q, 0, 1, E, k, sel, selw, nullptr, qp, err, r.lse);
             wave_raise(err, r.d_err);
             if (r.prob_mass && tid < 16) {
 #pragma unroll
@@ -685,14 +685,11 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
                     if (tid + 16 * i < E) r.prob_mass[tid + 16 * i] = 0.f + qp[i];
             }
         }
-    }
-    lds_barrier();
-    if (tid < k) {
-        const int ej = sel[tid];
-        int rank = 0;
-        for (int i = 0; i < k; ++i) rank += sel[i] < ej;
-        sorted[rank] = ej;
-        if (lead) {
+        lds_barrier();
+        if (tid < k) {
+            const int ej = sel[tid];
+            int rank = 0;
+            for (int i = 0; i < k; ++i) rank += sel[i] < ej;
             r.topk_idx[tid] = ej;
             r.topk_w[tid] = selw[tid];
             r.perm[rank] = tid;
@@ -702,8 +699,6 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
             d[1] = rank;
             d[2] = 1;
         }
-    }
-    if (lead) {
         if (tid == 0) {
             r.tiles[0] = k;
             r.offsets[E] = k;
@@ -720,10 +715,23 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
             if (r.weighted_counts)
                 r.weighted_counts[e] = !chosen ? 0 : r.q ? (int64_t)(uint32_t)r.q[0] : 1;
         }
+        return;
+    }
+    // the GEMM blocks need the ids only: the selection rounds without the softmax
+    if (tid < kWave) {
+        const int e = select_row4<NV>(lgl, E, k);
+        if (tid < k) sel[tid] = e;
+    }
+    lds_barrier();
+    if (tid < k) {
+        const int ej = sel[tid];
+        int rank = 0;
+        for (int i = 0; i < k; ++i) rank += sel[i] < ej;
+        sorted[rank] = ej;
     }
     lds_barrier();
     int mt, ft;
-    block_tile(k, nft, mt, ft);   // the grid is exactly k x nft blocks
+    block_tile(k, nft, mt, ft);   // blocks 0 .. k nft - 1 are the GEMM's
     dma128_tile<true, C::BW, C::BT, C::WF, C::WT, C::NS, false, 0>(
         ring, x, w13, h, K, N, sorted[mt], mt, 1, ft, nullptr, 1, 1, nullptr, gu_out);
 }
@@ -1112,7 +1120,7 @@ hipError_t launch_decode_self_route(const moe_dims &dm, const DecodeRoute &r, co
         return hipErrorInvalidValue;
     auto go = [&](auto nv) {
         gate_up_self_route_kernel<C, decltype(nv)::value>
-            <<<dim3((unsigned)(dm.k * nft)), dim3(C::kThreads), 0, s>>>(
+            <<<dim3((unsigned)(dm.k * nft + 1)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(x), static_cast<const uint8_t *>(w13), h, dm.d,
                 dm.inter, nft, dm.E, dm.k, r, gu_out);
     };

@@ -75,6 +75,69 @@ __device__ __forceinline__ float row_sum(float v) {
     return v;
 }
 
+// The k selection rounds of route_rows4 over one 16-lane row: lane c holds the keys hi[i]
+// of experts c + 16 i (0 = absent; a present expert's key is >= 1). Lane j < k receives
+// round j's id and key.
+template <int NV>
+__device__ __forceinline__ void topk_rounds(uint32_t (&hi)[NV], int c, int k, int &my_sel,
+                                            uint32_t &my_key) {
+    if constexpr (NV <= 8) {
+        uint64_t kv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            kv[i] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(c + 16 * i);
+#pragma unroll
+        for (int pw = 1; pw < NV; pw <<= 1)
+#pragma unroll
+            for (int kk = pw; kk >= 1; kk >>= 1)
+#pragma unroll
+                for (int j = kk % pw; j + kk < NV; j += 2 * kk)
+#pragma unroll
+                    for (int i = 0; i < kk; ++i)
+                        if ((i + j) / (2 * pw) == (i + j + kk) / (2 * pw)) {
+                            const uint64_t a = kv[i + j], b = kv[i + j + kk];
+                            kv[i + j] = b > a ? b : a;
+                            kv[i + j + kk] = b > a ? a : b;
+                        }
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            const uint32_t head = (uint32_t)(kv[0] >> 32);
+            const uint32_t m = row_max_u32(head);
+            const int e = row_min_i32(head == m ? (int)~(uint32_t)kv[0] : 0x7fffffff);
+            if (c == j) {
+                my_sel = e;
+                my_key = m;
+            }
+            if ((e & 15) == c) {   // the owner drops its head
+#pragma unroll
+                for (int i = 0; i + 1 < NV; ++i) kv[i] = kv[i + 1];
+                kv[NV - 1] = 0;
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int j = 0; j < k; ++j) {
+            uint32_t best = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) best = max(best, hi[i]);
+            const uint32_t m = row_max_u32(best);
+            int cand = 0x7fffffff;
+#pragma unroll
+            for (int i = NV - 1; i >= 0; --i)
+                if (hi[i] == m) cand = c + 16 * i;
+            const int e = row_min_i32(cand);
+            if (c == j) {
+                my_sel = e;
+                my_key = m;
+            }
+            const bool own = (e & 15) == c;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (own && i == (e >> 4)) hi[i] = 0u;
+        }
+    }
+}
+
 // Softmax + top-k + renormalisation ("0 train-infer mismatch ...", "The router: matching
 // expert ids and weights") of four consecutive tokens t0 .. t0+3, one per 16-lane row of
 // the calling wave: lane c of row r holds token t0+r's logits of experts c, c+16, c+32, ...
@@ -143,61 +206,7 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
     // probabilities are formed after the loop, one per lane, and added left to right.
     int my_sel = 0;
     uint32_t my_key = 0;
-    if constexpr (NV <= 8) {
-        uint64_t kv[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            kv[i] = ((uint64_t)hi[i] << 32) | (uint32_t)~(uint32_t)(c + 16 * i);
-#pragma unroll
-        for (int pw = 1; pw < NV; pw <<= 1)
-#pragma unroll
-            for (int kk = pw; kk >= 1; kk >>= 1)
-#pragma unroll
-                for (int j = kk % pw; j + kk < NV; j += 2 * kk)
-#pragma unroll
-                    for (int i = 0; i < kk; ++i)
-                        if ((i + j) / (2 * pw) == (i + j + kk) / (2 * pw)) {
-                            const uint64_t a = kv[i + j], b = kv[i + j + kk];
-                            kv[i + j] = b > a ? b : a;
-                            kv[i + j + kk] = b > a ? a : b;
-                        }
-#pragma unroll 1
-        for (int j = 0; j < k; ++j) {
-            const uint32_t head = (uint32_t)(kv[0] >> 32);
-            const uint32_t m = row_max_u32(head);
-            const int e = row_min_i32(head == m ? (int)~(uint32_t)kv[0] : 0x7fffffff);
-            if (c == j) {
-                my_sel = e;
-                my_key = m;
-            }
-            if ((e & 15) == c) {   // the owner drops its head
-#pragma unroll
-                for (int i = 0; i + 1 < NV; ++i) kv[i] = kv[i + 1];
-                kv[NV - 1] = 0;
-            }
-        }
-    } else {
-#pragma unroll 1
-        for (int j = 0; j < k; ++j) {
-            uint32_t best = 0;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) best = max(best, hi[i]);
-            const uint32_t m = row_max_u32(best);
-            int cand = 0x7fffffff;
-#pragma unroll
-            for (int i = NV - 1; i >= 0; --i)
-                if (hi[i] == m) cand = c + 16 * i;
-            const int e = row_min_i32(cand);
-            if (c == j) {
-                my_sel = e;
-                my_key = m;
-            }
-            const bool own = (e & 15) == c;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (own && i == (e >> 4)) hi[i] = 0u;
-        }
-    }
+    topk_rounds<NV>(hi, c, k, my_sel, my_key);
     // round c's probability (lanes c < k), then the left-to-right sum over the row's rounds
     const float my_p = expf(from_ordered_bits(my_key) - mx) / Z;
     const int rbase = lane & ~15;
@@ -214,6 +223,24 @@ __device__ __forceinline__ void route_rows4(const float *__restrict__ logits,
         topk_w[t * k + c] = my_p / sum;
         if (lds_ids) lds_ids[t * k + c] = my_sel;
     }
+}
+
+// The ids route_rows4 selects for the one token whose E logits are at `logits` (every
+// 16-lane row of the calling wave forms the same keys; lane j < k of each row returns
+// round j's id): the selection alone, without the softmax, the weights or the mass.
+template <int NV>
+__device__ __forceinline__ int select_row4(const float *__restrict__ logits, int E, int k) {
+    const int c = threadIdx.x & 15;
+    uint32_t hi[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const bool valid = c + 16 * i < E;
+        hi[i] = valid ? max(ordered_bits(logits[c + 16 * i]), 1u) : 0u;
+    }
+    int my_sel = 0;
+    uint32_t my_key = 0;
+    topk_rounds<NV>(hi, c, k, my_sel, my_key);
+    return my_sel;
 }
 
 // Scores of the learned routers: the function evaluated in FP64 and rounded once to FP32.
