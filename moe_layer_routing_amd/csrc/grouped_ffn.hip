@@ -941,6 +941,10 @@ hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, 
 #define MOE_FFN_CFG16 Dma128Cfg<64, 16, 2, 1, 6>
 #endif
 using PLAIN_CFG16 = MOE_FFN_CFG16;
+#ifndef MOE_FFN_DOWN_CFG16
+#define MOE_FFN_DOWN_CFG16 Dma128Cfg<64, 16, 2, 1, 4>
+#endif
+using DOWN_CFG16 = MOE_FFN_DOWN_CFG16;
 #ifndef MOE_SELF_ROUTE_CFG
 #define MOE_SELF_ROUTE_CFG Dma128Cfg<32, 16, 1, 1, 6>
 #endif
@@ -956,13 +960,13 @@ hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const in
                         const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s,
                         float *gu_out, bool gate_up_only) {
     // Decode-shaped launches stream the weights: narrow 64-row weight slices (many blocks per
-    // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block.
+    // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block. The down GEMM
+    // of 16-row tiles (192 KB of weights per block at I = 1536) takes 4-slot rings, so four
+    // blocks fit a CU (T = 64 decode step 0.754 -> 0.749 ms, T = 4 and 16 1-2 % faster).
     switch (bt) {
-    case 16: {
-        using C = PLAIN_CFG16;
-        return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out,
-                                    gate_up_only);
-    }
+    case 16:
+        return run_ffn<kBF16, PLAIN_CFG16, DOWN_CFG16>(dm, x_perm, gperm, w13, w2, h, y, tiles,
+                                                       mtiles, ev, s, gu_out, gate_up_only);
     case 32: {
         using C = Dma128Cfg<64, 32, 2, 1, 6>;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out,
