@@ -938,19 +938,25 @@ hipError_t run_ffn(const moe_dims &dm, const void *act13, const int32_t *gperm, 
 #endif
 
 #ifndef MOE_FFN_CFG16
-#define MOE_FFN_CFG16 Dma128Cfg<64, 16, 2, 1, 6>
+#define MOE_FFN_CFG16 Dma128Cfg<64, 16, 2, 1, 5, 2>
 #endif
 using PLAIN_CFG16 = MOE_FFN_CFG16;
 #ifndef MOE_FFN_DOWN_CFG16
-#define MOE_FFN_DOWN_CFG16 Dma128Cfg<64, 16, 2, 1, 4>
+#define MOE_FFN_DOWN_CFG16 Dma128Cfg<64, 16, 2, 1, 4, 2>
 #endif
 using DOWN_CFG16 = MOE_FFN_DOWN_CFG16;
 #ifndef MOE_SELF_ROUTE_CFG
 #define MOE_SELF_ROUTE_CFG Dma128Cfg<32, 16, 1, 1, 6>
 #endif
 using SELF_ROUTE_CFG = MOE_SELF_ROUTE_CFG;
-using PLAIN_CFG32 = Dma128Cfg<64, 32, 2, 1, 6>;
-using PLAIN_CFG64 = Dma128Cfg<128, 64, 2, 2, 4>;
+#ifndef MOE_FFN_CFG32
+#define MOE_FFN_CFG32 Dma128Cfg<64, 32, 2, 1, 4, 2>
+#endif
+#ifndef MOE_FFN_CFG64
+#define MOE_FFN_CFG64 Dma128Cfg<128, 64, 2, 2, 3, 2>
+#endif
+using PLAIN_CFG32 = MOE_FFN_CFG32;
+using PLAIN_CFG64 = MOE_FFN_CFG64;
 using PLAIN_LARGE = MOE_FFN_LARGE_CFG2;
 using PLAIN_HUGE = MOE_FFN_HUGE_CFG2;
 
@@ -960,20 +966,24 @@ hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const in
                         const int32_t *tiles, int64_t mtiles, void *const *ev, hipStream_t s,
                         float *gu_out, bool gate_up_only) {
     // Decode-shaped launches stream the weights: narrow 64-row weight slices (many blocks per
-    // active expert) and 6-slot rings keep ~50 KB of DMA in flight per block. The down GEMM
-    // of 16-row tiles (192 KB of weights per block at I = 1536) takes 4-slot rings, so four
-    // blocks fit a CU (T = 64 decode step 0.754 -> 0.749 ms, T = 4 and 16 1-2 % faster).
+    // active expert). Their kernels are compiled for two waves per SIMD (WPE 2: compiled for
+    // one, they declared over 256 registers and so held a CU to two 2-wave blocks whatever
+    // the LDS), and the rings are sized so that several blocks share a CU: the 16-row
+    // gate/up 5 slots (three blocks), its down GEMM 4 (four), the 32-row tiles 4 (three),
+    // the 64-row tiles 3 (two). Measured on the decode-shaped layer against one wave per
+    // SIMD and 6 / 6 / 4-slot rings: T = 2 0.122 -> 0.114 ms, T = 4 and 16 2 % and T = 64
+    // 1 % faster; tiles forced to 32 / 64 rows at T = 64 3-4 % / 11 % faster.
     switch (bt) {
     case 16:
         return run_ffn<kBF16, PLAIN_CFG16, DOWN_CFG16>(dm, x_perm, gperm, w13, w2, h, y, tiles,
                                                        mtiles, ev, s, gu_out, gate_up_only);
     case 32: {
-        using C = Dma128Cfg<64, 32, 2, 1, 6>;
+        using C = PLAIN_CFG32;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out,
                                     gate_up_only);
     }
     case 64: {
-        using C = Dma128Cfg<128, 64, 2, 2, 4>;
+        using C = PLAIN_CFG64;
         return run_ffn<kBF16, C, C>(dm, x_perm, gperm, w13, w2, h, y, tiles, mtiles, ev, s, gu_out,
                                     gate_up_only);
     }
@@ -990,15 +1000,25 @@ hipError_t dispatch_ffn(const moe_dims &dm, int bt, const void *x_perm, const in
 
 }  // namespace
 
+// Automatic token-tile height. Below 128 mean rows per expert the GEMMs mostly stream the
+// active experts' weights, once per token tile, so the tile is the smallest that holds
+// 1.5x the mean rows (no expert has more than T): most experts then take a single tile.
+// (Measured on a d=4096, E=128, top-8 layer: T = 256 and 512 went from 1.12 / 1.17 ms to
+// 0.84 / 0.87 ms, T = 1024 and 1536 from 1.29 / 1.74 ms to 0.94 / 1.00 ms; a tile at the
+// mean left about half the experts with a second tile.) From 128 mean rows on, 256-row
+// tiles: half the weight passes of 128-row tiles outweigh their padding (uniform routing,
+// d = 4096 / E = 128 and d = 2048 / E = 64, 128 to 768 rows per expert: 6-13 % faster; the
+// skewed training-shaped layer 2.5 %; at 96 rows 128-row tiles were still 15 % faster).
 int select_tile_m(const moe_dims &dm) {
     if (dm.tile_m) return dm.tile_m;
     const int64_t A = dm.T * dm.k;
     const int64_t avg = A / dm.E;          // mean rows per expert
-    if (dm.T <= 16 || avg <= 16) return 16;
-    if (dm.T <= 32 || avg <= 32) return 32;
-    if (dm.T <= 64 || avg <= 96) return 64;
-    if (avg < 1024) return 128;
-    return 256;
+    if (avg >= 128) return 256;
+    const int64_t want = std::min<int64_t>(dm.T, (3 * A + 2 * dm.E - 1) / (2 * dm.E));
+    if (want <= 16) return 16;
+    if (want <= 32) return 32;
+    if (want <= 64) return 64;
+    return 128;
 }
 
 // Token tiles of any routing of A rows: sum over the active experts of ceil(c_e / tile_m)
