@@ -335,9 +335,9 @@ moe_status moe_shared_ffn(const moe_dims *dims, int32_t ranks, int32_t inter_sha
  * gate/up GEMM, between the two GEMMs and after the down GEMM (for timing). A bf16 layer
  * with at most 16 expert rows (T*k <= 16), d/16 >= 256 and inter a multiple of 768 runs
  * the down GEMM and the plain combine as one launch (same outputs, y included); the third
- * event then follows that launch. When such a layer also has T = 1, E <= 128, the plain
+ * event then follows that launch. When such a layer also has T <= 2, E <= 128, the plain
  * softmax router (router NULL or softmax, no hash table), no placement map and x_perm NULL,
- * the gate/up launch routes the token itself (every output as from the separate routing
+ * the gate/up launch routes the tokens itself (every output as from the separate routing
  * steps, bit for bit), so the first two events bracket routing and gate/up together.
  * Events recorded between the launches delay each following launch by a few
  * microseconds; decode-sized steps are best timed without them.

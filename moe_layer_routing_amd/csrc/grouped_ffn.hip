@@ -638,48 +638,61 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
                                                               gu_out);
 }
 
-// One-token decode step with the plain softmax router: the gate/up launch routes the token
-// itself. Every block forms the E router logits from the K-chain partials (chain order, then
-// the bias: the routing tail's sums). The last block runs the tail's softmax + top-k +
-// renormalisation routine on them ("0 train-infer mismatch ...", "The router: matching
-// expert ids and weights") and stores every output of the routing tail for T = 1 (logits,
-// ids and weights, lse, the probability mass 0 + q p_e, counts, offsets, perm / inv,
-// weighted counts, tile list, error bits); it computes no GEMM tile. The GEMM blocks run only
-// that routine's selection rounds on the same keys (select_row4), so they hold the same k
-// ids. Token tile mt is the mt-th smallest selected id (the stable counting sort puts the
-// k rows in expert order, one 16-row tile each, row mt), and block (mt, ft) computes
-// feature tile ft of it. The tail's launch and its boundary leave the step: the partials
-// come straight from the logit-chain launch before this one.
-template <class C, int NV>
+// Decode steps of one or two tokens with the plain softmax router: the gate/up launch routes
+// the tokens itself. Every block forms the T x E router logits from the K-chain partials
+// (chain order, then the bias: the routing tail's sums). The last block runs the tail's
+// softmax + top-k + renormalisation routine on them ("0 train-infer mismatch ...", "The
+// router: matching expert ids and weights") and stores every output of the routing tail
+// (logits, ids and weights, lse, probability mass, counts, offsets, perm / inv, weighted
+// counts, tile list, error bits); it computes no GEMM tile. The GEMM blocks run only that
+// routine's selection rounds on the same keys (select_row4), so they hold the same ids, and
+// form in LDS the stable counting sort of the T k assignments by expert ("RoutePack ...",
+// Sec. 2.1; at most 16 rows, so every active expert is one 16-row tile, in expert order).
+// Block (mt, ft) computes feature tile ft of the mt-th active expert, gathering its rows'
+// tokens through that LDS permutation; blocks past the active experts exit. The tail's
+// launch and its boundary leave the step: the partials come straight from the logit-chain
+// launch before this one.
+constexpr int kSrMaxT = 2;                 // tokens per self-routing launch
+constexpr int kSrMaxA = kSrMaxT * kMaxK;   // their assignments
+
+template <class C, int NV, int MT>   // MT: the most tokens the instantiation takes (1 or 2)
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_kernel(
     const uint8_t *__restrict__ x, const uint8_t *__restrict__ w13, void *__restrict__ h,
-    int K, int N, int nft, int E, int k, DecodeRoute r, float *__restrict__ gu_out) {
+    int K, int N, int nft, int T, int E, int k, int cap, DecodeRoute r,
+    float *__restrict__ gu_out) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NS * ((C::BW + C::BT) / 8) * 1024];
-    __shared__ float lgl[kMaxE / 2];
-    __shared__ float selw[kMaxK];
-    __shared__ int32_t sel[kMaxK], sorted[kMaxK];
+    static_assert(MT >= 1 && MT <= kSrMaxT, "one or two tokens");
+    __shared__ float lgl[MT * kMaxE / 2];
+    __shared__ float mp[MT][kMaxE / 2];          // q p per token (routing block)
+    __shared__ float selw[MT * kMaxK];
+    __shared__ int32_t sel[MT * kMaxK], lperm[MT * kMaxK], first[MT * kMaxK], tinfo[4];
     const int tid = threadIdx.x;
+    const int A = T * k, TE = T * E;
     const bool router = blockIdx.x == gridDim.x - 1;   // the block that writes the routing
-    for (int e = tid; e < E; e += C::kThreads) {
-        float p[kLogitChains];
+    for (int t = 0; t < (MT == 1 ? 1 : T); ++t) {
+        for (int e = tid; e < E; e += C::kThreads) {
+            const int i = t * E + e;
+            float p[kLogitChains];
 #pragma unroll
-        for (int c = 0; c < kLogitChains; ++c) p[c] = r.part[c * E + e];
-        float v = p[0];
+            for (int c = 0; c < kLogitChains; ++c) p[c] = r.part[c * TE + i];
+            float v = p[0];
 #pragma unroll
-        for (int c = 1; c < kLogitChains; ++c) v = v + p[c];
-        const float l = r.bias ? v + r.bias[e] : v;
-        lgl[e] = l;
-        if (router) r.logits[e] = l;
+            for (int c = 1; c < kLogitChains; ++c) v = v + p[c];
+            const float l = r.bias ? v + r.bias[e] : v;
+            lgl[i] = l;
+            if (router) r.logits[i] = l;
+        }
     }
     lds_barrier();
-    if (router) {
+    if (MT == 1 && router) {   // one token: the k ids are distinct, row j of the sort is id j's rank
         if (tid < kWave) {
             float qp[kRowVals];
             int err = 0;
             route_rows4<NV>(lgl, r.q, 0, 1, E, k, sel, selw, nullptr, qp, err, r.lse);
             wave_raise(err, r.d_err);
             if (r.prob_mass && tid < 16) {
+                // the tail's sum over one token reduces to 0 + q p (the other rows add zeros)
 #pragma unroll
                 for (int i = 0; i < NV; ++i)
                     if (tid + 16 * i < E) r.prob_mass[tid + 16 * i] = 0.f + qp[i];
@@ -717,23 +730,134 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
         }
         return;
     }
+    if (router) {
+        if (tid < kWave) {
+            float qp[kRowVals];
+            int err = 0;
+            route_rows4<NV>(lgl, r.q, 0, T, E, k, sel, selw, nullptr, qp, err, r.lse);
+            wave_raise(err, r.d_err);
+            const int row = tid >> 4, c = tid & 15;
+            if (row < T) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (c + 16 * i < E) mp[row][c + 16 * i] = qp[i];
+            }
+        }
+        lds_barrier();
+        if (tid < A) {   // assignment a = t k + j: its place in the stable sort by expert
+            const int ea = sel[tid];
+            int before = 0, same = 0;
+            for (int b = 0; b < A; ++b) {
+                before += sel[b] < ea;
+                same += (sel[b] == ea) & (b < tid);
+            }
+            r.topk_idx[tid] = ea;
+            r.topk_w[tid] = selw[tid];
+            r.perm[before + same] = tid;
+            r.inv[tid] = before + same;
+            first[tid] = same == 0;   // the expert's first assignment
+        }
+        if (tid == 0) r.offsets[E] = A;
+        lds_barrier();
+        for (int e = tid; e < E; e += C::kThreads) {
+            int before = 0, cnt = 0, tile = 0;   // tile: active experts below e
+            uint64_t wsum = 0;
+            for (int b = 0; b < A; ++b) {
+                const int eb = sel[b];
+                before += eb < e;
+                tile += first[b] & (eb < e);
+                if (eb == e) {
+                    ++cnt;
+                    if (r.q) wsum += (uint64_t)(uint32_t)r.q[b / k];
+                }
+            }
+            r.counts[e] = cnt;
+            r.offsets[e] = before;
+            if (r.weighted_counts) r.weighted_counts[e] = r.q ? (int64_t)wsum : (int64_t)cnt;
+            if (r.prob_mass) {
+                // the tail's sum for a batch of at most 4 tokens: its first wave's four rows,
+                // then the zero sums of the other waves and groups
+                float m = 0.f + mp[0][e];
+                m = m + (MT > 1 && T > 1 ? mp[MT - 1][e] : 0.f);
+                m = m + 0.f;
+                m = m + 0.f;
+                float v = m;
+                v = v + 0.f;
+                v = v + 0.f;
+                v = v + 0.f;
+                r.prob_mass[e] = (v + 0.f) + (0.f + 0.f);
+            }
+            if (cnt) {
+                int32_t *d = r.tiles + 1 + 3 * tile;
+                d[0] = e;
+                d[1] = before;
+                d[2] = cnt;
+            }
+            if (e == E - 1) r.tiles[0] = tile + (cnt ? 1 : 0);
+        }
+        return;
+    }
     // the GEMM blocks need the ids only: the selection rounds without the softmax
     if (tid < kWave) {
-        const int e = select_row4<NV>(lgl, E, k);
-        if (tid < k) sel[tid] = e;
-    }
-    lds_barrier();
-    if (tid < k) {
-        const int ej = sel[tid];
-        int rank = 0;
-        for (int i = 0; i < k; ++i) rank += sel[i] < ej;
-        sorted[rank] = ej;
+        if constexpr (MT == 1) {
+            const int e = select_row4<NV>(lgl, E, k);
+            if (tid < k) sel[tid] = e;
+        } else {   // row t of the wave selects token t's experts
+            const int row = tid >> 4, c = tid & 15;
+            const int e = select_row4<NV>(lgl + min(row, T - 1) * E, E, k);
+            if (row < T && c < k) sel[row * k + c] = e;
+        }
     }
     lds_barrier();
     int mt, ft;
-    block_tile(k, nft, mt, ft);   // blocks 0 .. k nft - 1 are the GEMM's
+    block_tile(cap, nft, mt, ft);   // blocks 0 .. cap nft - 1 are the GEMM's
+    if constexpr (MT == 1) {
+        // one token: k distinct experts, tile mt = the mt-th smallest id, row mt = token 0
+        if (tid < k) {
+            const int ej = sel[tid];
+            int rank = 0;
+            for (int i = 0; i < k; ++i) rank += sel[i] < ej;
+            lperm[rank] = ej;
+        }
+        lds_barrier();
+        dma128_tile<true, C::BW, C::BT, C::WF, C::WT, C::NS, false, 0>(
+            ring, x, w13, h, K, N, lperm[mt], mt, 1, ft, nullptr, 1, 1, nullptr, gu_out);
+        return;
+    }
+    if (tid < A) {
+        const int ea = sel[tid];
+        int before = 0, same = 0;
+        for (int b = 0; b < A; ++b) {
+            before += sel[b] < ea;
+            same += (sel[b] == ea) & (b < tid);
+        }
+        lperm[before + same] = tid;
+        first[tid] = same == 0;
+    }
+    lds_barrier();
+    if (tid < A && first[tid]) {   // the active experts in id order: tile mt is this block's
+        const int ea = sel[tid];
+        int rank = 0, before = 0, cnt = 0;
+        for (int b = 0; b < A; ++b) {
+            rank += first[b] & (sel[b] < ea);
+            before += sel[b] < ea;
+            cnt += sel[b] == ea;
+        }
+        if (rank == mt) {
+            tinfo[0] = ea;
+            tinfo[1] = before;
+            tinfo[2] = cnt;
+        }
+    }
+    if (tid == 0) {
+        int n = 0;
+        for (int b = 0; b < A; ++b) n += first[b];
+        tinfo[3] = n;
+    }
+    lds_barrier();
+    if (mt >= tinfo[3]) return;   // fewer active experts than the grid allows for
     dma128_tile<true, C::BW, C::BT, C::WF, C::WT, C::NS, false, 0>(
-        ring, x, w13, h, K, N, sorted[mt], mt, 1, ft, nullptr, 1, 1, nullptr, gu_out);
+        ring, x, w13, h, K, N, tinfo[0], tinfo[1], tinfo[2], ft, lperm, k, T, nullptr, gu_out);
 }
 
 // ------------------------------------------------------------------------------------
@@ -949,6 +1073,10 @@ using DOWN_CFG16 = MOE_FFN_DOWN_CFG16;
 #define MOE_SELF_ROUTE_CFG Dma128Cfg<32, 16, 1, 1, 6>
 #endif
 using SELF_ROUTE_CFG = MOE_SELF_ROUTE_CFG;
+#ifndef MOE_SELF_ROUTE_CFG2
+#define MOE_SELF_ROUTE_CFG2 Dma128Cfg<64, 16, 2, 1, 5, 2>
+#endif
+using SELF_ROUTE_CFG2 = MOE_SELF_ROUTE_CFG2;   // two tokens: the 16-row gate/up shape
 #ifndef MOE_FFN_CFG32
 #define MOE_FFN_CFG32 Dma128Cfg<64, 32, 2, 1, 4, 2>
 #endif
@@ -1130,26 +1258,38 @@ hipError_t launch_grouped_ffn(const moe_dims &dm, const void *x_perm, const int3
 }
 
 bool decode_self_route_ok(const moe_dims &dm) {
-    return dm.dtype == MOE_BF16 && dm.T == 1 && dm.E >= dm.k && dm.E <= kMaxE / 2 &&
-           dm.k >= 1 && dm.k <= kMaxK && select_tile_m(dm) == 16;
+    return dm.dtype == MOE_BF16 && dm.T >= 1 && dm.T <= kSrMaxT && dm.T * dm.k <= 16 &&
+           dm.E >= dm.k && dm.E <= kMaxE / 2 && dm.k >= 1 && dm.k <= kMaxK &&
+           select_tile_m(dm) == 16;
 }
 
 hipError_t launch_decode_self_route(const moe_dims &dm, const DecodeRoute &r, const void *x,
                                     const void *w13, void *h, float *gu_out,
                                     void *const *prof_events, hipStream_t s) {
     if (!decode_self_route_ok(dm)) return hipErrorInvalidValue;
-    using C = SELF_ROUTE_CFG;
-    const int nft = (dm.inter + C::BW / 2 - 1) / (C::BW / 2);
     if (prof_events && hipEventRecord(static_cast<hipEvent_t>(prof_events[0]), s) != hipSuccess)
         return hipErrorInvalidValue;
-    auto go = [&](auto nv) {
-        gate_up_self_route_kernel<C, decltype(nv)::value>
-            <<<dim3((unsigned)(dm.k * nft + 1)), dim3(C::kThreads), 0, s>>>(
+    // at most one 16-row tile per active expert: min(E, T k) tiles
+    const int cap = (int)std::min<int64_t>(dm.E, dm.T * dm.k);
+    auto go = [&](auto nv, auto cfg, auto mt) {
+        using C = decltype(cfg);
+        const int nft = (dm.inter + C::BW / 2 - 1) / (C::BW / 2);
+        gate_up_self_route_kernel<C, decltype(nv)::value, decltype(mt)::value>
+            <<<dim3((unsigned)(cap * nft + 1)), dim3(C::kThreads), 0, s>>>(
                 static_cast<const uint8_t *>(x), static_cast<const uint8_t *>(w13), h, dm.d,
-                dm.inter, nft, dm.E, dm.k, r, gu_out);
+                dm.inter, nft, (int)dm.T, dm.E, dm.k, cap, r, gu_out);
     };
-    if (dm.E <= 64) go(std::integral_constant<int, 4>{});
-    else go(std::integral_constant<int, 8>{});
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    using NV4 = std::integral_constant<int, 4>;
+    using NV8 = std::integral_constant<int, 8>;
+    if (dm.T == 1) {
+        if (dm.E <= 64) go(NV4{}, SELF_ROUTE_CFG{}, One{});
+        else go(NV8{}, SELF_ROUTE_CFG{}, One{});
+    } else {
+        if (dm.E <= 64) go(NV4{}, SELF_ROUTE_CFG2{}, Two{});
+        else go(NV8{}, SELF_ROUTE_CFG2{}, Two{});
+    }
     if (prof_events && hipEventRecord(static_cast<hipEvent_t>(prof_events[1]), s) != hipSuccess)
         return hipErrorInvalidValue;
     return hipGetLastError();

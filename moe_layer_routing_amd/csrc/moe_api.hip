@@ -415,7 +415,8 @@ static moe_status forward_impl(const moe_dims *dims, const moe_forward_args *a, 
         if (chains) {
             e = launch_router_logit_chains(*dims, a->x, a->w_router, ws.logit_part, s);
             if (e != hipSuccess) return MOE_E_LAUNCH;
-            // one token, plain softmax router: the gate/up launch routes it (no tail launch)
+            // one or two tokens, plain softmax router: the gate/up launch routes them (no
+            // tail launch)
             if (dc && ro.plain() && !a->slot_of_expert && !a->x_perm &&
                 decode_self_route_ok(*dims)) {
                 DecodeRoute r;

@@ -262,12 +262,13 @@ hipError_t launch_down_combine_small(const moe_dims &dm, const void *h, const vo
                                      const int32_t *tiles, const int32_t *inv,
                                      const float *topk_w, float scale, void *out,
                                      void *const *prof_events, hipStream_t s);
-// One-token bf16 decode step with the plain softmax router (T = 1, E <= 128, 16-row tiles):
-// the gate/up launch (gathered from x, records prof_events[0] and [1] around it) forms the
-// logits from the logit-chain partials and routes the token in every block, with the
-// routing tail's arithmetic; block 0 writes every output launch_small_tail writes for
-// T = 1 without a placement map (pointers as there; prob_mass, weighted_counts, lse and q
-// may be null). The tile list it writes serves the down GEMM launch after it.
+// Decode steps of one or two tokens, bf16, plain softmax router (T <= 2, T k <= 16,
+// E <= 128, 16-row tiles): the gate/up launch (gathered from x, records prof_events[0] and
+// [1] around it) forms the logits from the logit-chain partials and routes the tokens in
+// every block, with the routing tail's arithmetic; its last block writes every output
+// launch_small_tail writes for such a batch without a placement map (pointers as there;
+// prob_mass, weighted_counts, lse and q may be null). The tile list it writes serves the
+// down GEMM launch after it.
 struct DecodeRoute {
     const float *part;   // [kLogitChains][E] chain partials
     const float *bias;   // [E] or null

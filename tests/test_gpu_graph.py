@@ -27,7 +27,8 @@ OUTS = ("out", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "h", "y
 @pytest.mark.parametrize("T,mode,d", [(1, "router", 256), (48, "router", 256),
                                       (700, "router", 256), (300, "replay", 256),
                                       # d/16 >= 256: the one-launch down GEMM + combine
-                                      (1, "router", 4096), (2, "replay", 4096)])
+                                      (1, "router", 4096), (2, "router", 4096),
+                                      (2, "replay", 4096)])
 def test_graph_replay_matches_eager(T, mode, d):
     E, I = (32, 128) if d == 256 else (16, 768)
     L = W.make_layer(T=T, d=d, E=E, k=8, I=I, dtype="bf16", mode=mode, seed=T,

@@ -183,10 +183,15 @@ def test_decode_down_combine_launch_matches_steps(case):
 
 
 SR_CASES = [
-    dict(E=16, k=8, I=768, mult=True, scale=None, lse=True),
-    dict(E=12, k=3, I=1536, mult=False, scale=2.5, lse=False),
-    dict(E=8, k=8, I=768, mult=True, scale=None, lse=False),     # every expert selected
-    dict(E=33, k=1, I=768, mult=True, scale=0.5, lse=True),
+    dict(T=1, E=16, k=8, I=768, mult=True, scale=None, lse=True),
+    dict(T=1, E=12, k=3, I=1536, mult=False, scale=2.5, lse=False),
+    dict(T=1, E=8, k=8, I=768, mult=True, scale=None, lse=False),     # every expert selected
+    dict(T=1, E=33, k=1, I=768, mult=True, scale=0.5, lse=True),
+    dict(T=2, E=16, k=8, I=768, mult=True, scale=None, lse=True),     # 16 rows
+    dict(T=2, E=12, k=3, I=1536, mult=True, scale=2.5, lse=False),
+    dict(T=2, E=8, k=8, I=768, mult=False, scale=None, lse=True),     # 8 tiles of 2 rows
+    dict(T=2, E=33, k=1, I=768, mult=True, scale=0.5, lse=False),
+    dict(T=2, E=16, k=8, I=768, mult=True, scale=None, lse=False, dup=True),  # same token twice
 ]
 SR_OUTS = ("logits", "topk_idx", "topk_w", "prob_mass", "counts", "offsets", "perm", "inv",
            "weighted_counts", "gu", "h", "y", "out", "d_err")
@@ -203,8 +208,10 @@ def _decode_one(L, inp, fused, mult, scale, lse):
         b["token_mult"] = inp["token_mult"]
     if fused:
         del b["x_perm"]
-    b["gu"] = torch.empty((L.k, 2 * L.I), dtype=torch.float32, device="cuda")
-    lse_t = torch.full((1,), 7.0, dtype=torch.float32, device="cuda") if lse else None
+    # the saved pre-activations: one FP32 row of 2 I values per assignment (T k rows)
+    b["gu"] = torch.empty((L.T * L.k, 2 * L.I), dtype=torch.float32, device="cuda")
+    assert b["gu"].shape[0] == b["h"].shape[0]
+    lse_t = torch.full((L.T,), 7.0, dtype=torch.float32, device="cuda") if lse else None
     M.forward(dims, b, M.alloc_workspace(dims), routed_scale=scale or 0.0,
               router=dict(score="softmax", lse=lse_t) if lse else None)
     torch.cuda.synchronize()
@@ -212,16 +219,19 @@ def _decode_one(L, inp, fused, mult, scale, lse):
 
 
 @pytest.mark.parametrize("case", SR_CASES,
-                         ids=lambda c: f"E{c['E']}_k{c['k']}_I{c['I']}_q{int(c['mult'])}")
+                         ids=lambda c: (f"T{c['T']}_E{c['E']}_k{c['k']}_I{c['I']}_q{int(c['mult'])}"
+                                        + ("_dup" if c.get("dup") else "")))
 def test_decode_self_route_matches_tail(case):
-    """T = 1, plain softmax router, gather fused (the decode step's launch shape): the
-    gate/up launch forms the logits from the chain partials and selects the experts in
-    every block. Every output is bitwise the routing-tail path's (tail launch, gather,
-    gate/up from x_perm), the routing outputs the multi-kernel steps', and the oracle
-    agrees on the GPU logits."""
-    L = W.make_layer(T=1, d=4096, E=case["E"], k=case["k"], I=case["I"], dtype="bf16",
-                     mode="router", seed=90 + case["E"] + case["k"], bias="zipf")
-    L.token_mult = np.array([3], dtype=np.int32)
+    """One or two tokens, plain softmax router, gather fused (the decode step's launch
+    shape): the gate/up launch forms the logits from the chain partials and selects the
+    experts in every block. Every output is bitwise the routing-tail path's (tail launch,
+    gather, gate/up from x_perm), the routing outputs the multi-kernel steps', and the
+    oracle agrees on the GPU logits."""
+    L = W.make_layer(T=case["T"], d=4096, E=case["E"], k=case["k"], I=case["I"], dtype="bf16",
+                     mode="router", seed=90 + case["E"] + case["k"] + case["T"], bias="zipf")
+    if case.get("dup"):
+        L.x = np.ascontiguousarray(np.repeat(L.x[:1], L.T, axis=0))
+    L.token_mult = np.array([3, 5][:L.T], dtype=np.int32)
     inp = upload(L)
     args = (case["mult"], case["scale"], case["lse"])
     ref, lse_r = _decode_one(L, inp, False, *args)
@@ -243,7 +253,8 @@ def test_decode_self_route_matches_tail(case):
     assert_close(host(got["topk_w"]), w_o, "f32", "topk_w")
     assert_close(host(got["prob_mass"]), mass_o, "f32", "prob_mass")
     L.routed_scale = case["scale"] or 1.0
-    _, _, rout = oracle.forward_tokens(L, [0], host(got["topk_idx"]), host(got["topk_w"]))
+    _, _, rout = oracle.forward_tokens(L, list(range(L.T)), host(got["topk_idx"]),
+                                       host(got["topk_w"]))
     assert_close(as_f32(host(got["out"]), "bf16"), as_f32(rout, "bf16"), "bf16", "out")
 
 
