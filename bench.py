@@ -584,14 +584,14 @@ def upload(L, dev):
                                            "w13", "w2", "token_mult", "cu_seqlens")}
 
 
-def decode_sweep(args):
+def decode_rows(Ts, steps, warmup, tile_m=0):
     """Decode-shaped layer: one timed moe_forward per batch size T, each after a read of
     another 512 MB buffer so that the expert weights come from HBM (a read evicts
     them from L2 and the 256 MB memory-attached cache without leaving dirty lines whose
     write-back would be charged to the timed step), reported in tokens/s and in
     effective HBM GB/s = algorithmic bytes / time, where the algorithmic bytes are the
     active experts' w13 and w2 (read once), the router weights, x and out, and the
-    routing outputs."""
+    routing outputs. Returns (rows, layer)."""
     import torch
 
     import moe_layer_routing_amd as M
@@ -604,22 +604,21 @@ def decode_sweep(args):
     scrub = torch.ones(128 << 20, dtype=torch.int32, device=dev)      # 512 MB
     hip = HipEvents()
     stream = torch.cuda.current_stream()
-    Ts = [int(t) for t in args.decode_t.split(",")]
     rows = []
     for T in Ts:
-        dims = M.make_dims(T, L.d, L.E, L.k, L.I, M.MOE_BF16, args.tile_m)
+        dims = M.make_dims(T, L.d, L.E, L.k, L.I, M.MOE_BF16, tile_m)
         b = M.alloc_forward_buffers(dims, dev, router=True)
         del b["x_perm"]
         b.update(x=inp["x"][:T].contiguous(), w_router=inp["w_router"], w13=inp["w13"],
                  w2=inp["w2"])
         ws = M.alloc_workspace(dims, dev)
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             M.forward(dims, b, ws)
         # the step as a caller runs it (events only around it), then the same step with the
         # library's profiling events between its launches, for the gate/up launch's duration
         # (each event recorded inside the step delays the launch after it by a few us)
         times, itimes, t13 = [], [], []
-        for _ in range(args.steps):
+        for _ in range(steps):
             scrub.sum()
             ev = hip.create(2)
             hip.record(ev[0], stream.cuda_stream)
@@ -628,7 +627,7 @@ def decode_sweep(args):
             torch.cuda.synchronize()
             times.append(hip.ms(ev[0], ev[1]))
             hip.destroy(ev)
-        for _ in range(args.steps):
+        for _ in range(steps):
             scrub.sum()
             ev = hip.create(5)
             hip.record(ev[0], stream.cuda_stream)
@@ -649,7 +648,7 @@ def decode_sweep(args):
         with torch.cuda.graph(graph):
             M.forward(dims, b, ws)
         gtimes = []
-        for _ in range(args.steps):
+        for _ in range(steps):
             scrub.sum()
             ev = hip.create(2)
             hip.record(ev[0], stream.cuda_stream)
@@ -677,6 +676,15 @@ def decode_sweep(args):
                      "gate_up_ms": round(g_ms, 4), "gate_up_bytes": g_bytes,
                      "gate_up_gbs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1)})
         rows[-1]["graph_hbm_gbs"] = round(nbytes / (gr_ms * 1e-3) / 1e9, 1)
+    del scrub
+    return rows, L
+
+
+def decode_sweep(args):
+    """The decode-shaped sweep as its own JSON line (bench.py --config c5)."""
+    rows, L = decode_rows([int(t) for t in args.decode_t.split(",")], args.steps, args.warmup,
+                          args.tile_m)
+    dev = "cuda:0"
     top = rows[-1]
     rec = {
         "metric": METRIC + " (decode-shaped layer, HBM GB/s)",
@@ -862,9 +870,10 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS),
                     help="headline workload (default: the packed-microbatch layer, the "
                          "largest that the metric is quoted on)")
-    ap.add_argument("--extra", default="c2,c4",
+    ap.add_argument("--extra", default="c2,c4,c5",
                     help="further workloads timed in the same run and reported under "
-                         "'other_configs' (comma list, '' for none)")
+                         "'other_configs' (comma list, '' for none; c5: the decode-shaped "
+                         "layer at T = 1 and 64, under 'decode')")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens of the workload the CPU oracle runs (0 = skip)")
     ap.add_argument("--tile-m", type=int, default=0)
@@ -900,11 +909,15 @@ def main():
     stream = torch.cuda.current_stream()
     head = run_layer(args.config, args, hip, not args.no_reports, args.cpu_sample)
     extra = {}
+    decode = None
     if not args.no_reports:
         head["ep_share"] = ep_share_report(args.steps, hip, stream)
         log("expert-parallel share done")
         for cfg in [c for c in args.extra.split(",") if c and c != args.config]:
             if cfg == "c5":
+                rows, _ = decode_rows([1, 64], min(args.steps, 20), min(args.warmup, 5))
+                decode = {"workload": WORKLOADS["c5"], "sweep": rows}
+                log("decode-shaped layer done")
                 continue
             r = run_layer(cfg, args, hip, reports=(cfg == "c2"), cpu_sample=0)
             extra[cfg] = {n: r[n] for n in ("tokens_per_s", "step_ms", "grouped_gemm",
@@ -939,6 +952,7 @@ def main():
         "backward": head.get("backward"),
         "ep_share": head.get("ep_share"),
         "other_configs": extra or None,
+        "decode": decode,
         "wall_s_timed": head["wall_s_timed"],
         "cpu_baseline": head.get("cpu_baseline"),
     }
