@@ -775,8 +775,9 @@ __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE))) void gate_up_self_route_ker
             r.offsets[e] = before;
             if (r.weighted_counts) r.weighted_counts[e] = r.q ? (int64_t)wsum : (int64_t)cnt;
             if (r.prob_mass) {
-                // the tail's sum for a batch of at most 4 tokens: its first wave's four rows,
-                // then the zero sums of the other waves and groups
+                // the tail's sum for a batch of at most two tokens: its first wave's four
+                // rows (rows past the batch add zeros), then the other waves' and groups'
+                // zero sums
                 float m = 0.f + mp[0][e];
                 m = m + (MT > 1 && T > 1 ? mp[MT - 1][e] : 0.f);
                 m = m + 0.f;
