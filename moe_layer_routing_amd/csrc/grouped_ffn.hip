@@ -652,8 +652,7 @@ __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void grouped_gemm_dma128_kernel(
 // tokens through that LDS permutation; blocks past the active experts exit. The tail's
 // launch and its boundary leave the step: the partials come straight from the logit-chain
 // launch before this one.
-constexpr int kSrMaxT = 2;                 // tokens per self-routing launch
-constexpr int kSrMaxA = kSrMaxT * kMaxK;   // their assignments
+constexpr int kSrMaxT = 2;   // tokens per self-routing launch
 
 template <class C, int NV, int MT>   // MT: the most tokens the instantiation takes (1 or 2)
 __global__ __launch_bounds__(C::kThreads)
