@@ -276,3 +276,26 @@ def test_decode_self_route_nonfinite_logit():
     for n in ("logits", "topk_w", "prob_mass", "out"):
         np.testing.assert_array_equal(host(got[n]).view(np.uint8), host(ref[n]).view(np.uint8),
                                       err_msg=n)
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_self_route_optional_outputs_absent(T):
+    """The self-routing launch with logits, probability mass and weighted counts not
+    requested (NULL; the logits then go to the workspace): the ids, weights, permutation
+    and output rows are bitwise those of the call that requests everything."""
+    L = W.make_layer(T=T, d=4096, E=64, k=8, I=768, dtype="bf16", mode="router",
+                     seed=120 + T, bias="zipf")
+    L.token_mult = np.array([2, 7][:T], dtype=np.int32)
+    inp = upload(L)
+    full, _ = _decode_one(L, inp, True, True, None, False)
+    dims = dims_of(L)
+    b = M.alloc_forward_buffers(dims, "cuda", router=True, weighted=False)
+    for n in ("x", "w13", "w2", "w_router", "logit_bias", "token_mult"):
+        b[n] = inp[n]
+    for n in ("x_perm", "logits", "prob_mass"):
+        del b[n]
+    M.forward(dims, b, M.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    assert int(b["d_err"].item()) == 0
+    for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "h", "y", "out"):
+        assert host(b[n]).tobytes() == host(full[n]).tobytes(), n
