@@ -163,6 +163,11 @@ def test_c5_batch_invariance():
         assert idx.tobytes() == ref_idx[t0:t0 + T].tobytes(), (t0, T)
         assert w.tobytes() == ref_w[t0:t0 + T].tobytes(), (t0, T)
         assert host(b1["logits"]).tobytes() == host(b64["logits"])[t0:t0 + T].tobytes()
+        # every routing output of the self-routing launch (E = 128: eight logits per lane)
+        # against the routing tail's for the same rows
+        _, _, _, bt = run(rows, fused=False)
+        for n in ("counts", "offsets", "perm", "inv", "prob_mass", "h", "y"):
+            assert host(b1[n]).tobytes() == host(bt[n]).tobytes(), (t0, T, n)
     out, idx, _, _ = run(pool[::-1])
     assert out.tobytes() == ref_out[::-1].tobytes()
     for tm in (16, 32, 64, 128, 256):
