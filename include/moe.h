@@ -94,6 +94,14 @@ typedef struct moe_dims {
  * workspace holds small per-block partials and tile lists, never a full activation. */
 size_t moe_workspace_size(const moe_dims *dims);
 
+/* Token-tile height (rows of the permuted activation per GEMM block) that every grouped
+ * GEMM of `dims` uses: dims->tile_m when it is nonzero, else the automatic choice. The
+ * automatic choice is 256 from 128 mean rows per expert (T*k/E, rounded down) on; below
+ * that it is the smallest of 16, 32, 64, 128 that holds min(T, ceil(1.5 T*k/E)) rows, so
+ * that most active experts take a single token tile. Results do not depend on it (launch
+ * shape only). Pure host function; returns 0 for invalid dims. */
+int32_t moe_tile_height(const moe_dims *dims);
+
 /* Human-readable name of a status code (static string). */
 const char *moe_status_string(moe_status s);
 

@@ -80,6 +80,7 @@ class BackwardArgs(ctypes.Structure):
 # exported symbols and their signatures (argument types after the dims pointer)
 _SIGS = {
     "moe_workspace_size": ([ctypes.POINTER(Dims)], ctypes.c_size_t),
+    "moe_tile_height": ([ctypes.POINTER(Dims)], ctypes.c_int32),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_version": ([], ctypes.c_int),
     "moe_route": ([ctypes.POINTER(Dims)] + [_P] * 9 + [_P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -166,6 +167,11 @@ def make_dims(T: int, d: int, E: int, k: int, inter: int, dtype: int, tile_m: in
 
 def workspace_size(dims: Dims) -> int:
     return int(lib().moe_workspace_size(ctypes.byref(dims)))
+
+
+def tile_height(dims: Dims) -> int:
+    """Token-tile height of the grouped GEMMs for dims (0 for invalid dims)."""
+    return int(lib().moe_tile_height(ctypes.byref(dims)))
 
 
 def alloc_workspace(dims: Dims, device="cuda") -> torch.Tensor:

@@ -80,6 +80,11 @@ size_t moe_workspace_size(const moe_dims *dims) {
     return carve_workspace(*dims, nullptr).total;
 }
 
+int32_t moe_tile_height(const moe_dims *dims) {
+    if (!dims_ok(dims) || !dtype_ok(dims)) return 0;
+    return select_tile_m(*dims);
+}
+
 static moe_status check_common(const moe_dims *dims) {
     if (!dims) return MOE_E_NULLPTR;
     if (!dtype_ok(dims)) return MOE_E_DTYPE;

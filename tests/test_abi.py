@@ -77,6 +77,33 @@ def test_workspace_size(M):
     assert M.workspace_size(M.make_dims(0, 128, 8, 2, 128, M.MOE_F32)) > 0
 
 
+def test_tile_height(M):
+    """The grouped GEMMs' token-tile height: 256 from 128 mean rows per expert on, else the
+    smallest of 16/32/64/128 holding min(T, ceil(1.5 * mean rows)); a nonzero tile_m wins."""
+    cases = [  # (T, E, k, tile_m, expected) - mean rows T*k/E, want = min(T, ceil(1.5 mean))
+        (16384, 128, 8, 0, 256),   # mean 1024
+        (2048, 128, 8, 0, 256),    # mean exactly 128
+        (2047, 128, 8, 0, 128),    # mean 127.9 -> want 192, above 128 but not yet 256
+        (1024, 128, 8, 0, 128),    # mean 64 -> want 96
+        (512, 128, 8, 0, 64),      # mean 32 -> want 48
+        (256, 128, 8, 0, 32),      # mean 16 -> want 24
+        (64, 128, 8, 0, 16),       # mean 4 -> want 6
+        (1, 128, 8, 0, 16),        # one token
+        (0, 128, 8, 0, 16),        # empty batch
+        (32, 3, 1, 0, 16),         # want exactly 16
+        (33, 3, 1, 0, 32),         # want 16.5 -> 17
+        (16, 8, 8, 0, 16),         # want 24 capped at T = 16 (no expert has more than T rows)
+        (20, 8, 8, 0, 32),         # want 30 capped at T = 20
+        (4096, 64, 8, 0, 256),     # mean 512
+        (4096, 64, 8, 64, 64),     # forced
+        (1, 128, 8, 256, 256),     # forced
+    ]
+    for T, E, k, tm, want in cases:
+        assert M.tile_height(M.make_dims(T, 256, E, k, 256, M.MOE_BF16, tm)) == want, (T, E, k, tm)
+    assert M.tile_height(M.make_dims(10, 128, 8, 2, 128, M.MOE_BF16, 48)) == 0
+    assert M.tile_height(M.make_dims(10, 128, 8, 2, 128, 7)) == 0
+
+
 def test_status_strings(M):
     L = M.lib()
     for s in range(7):
