@@ -192,6 +192,11 @@ SR_CASES = [
     dict(T=2, E=8, k=8, I=768, mult=False, scale=None, lse=True),     # 8 tiles of 2 rows
     dict(T=2, E=33, k=1, I=768, mult=True, scale=0.5, lse=False),
     dict(T=2, E=16, k=8, I=768, mult=True, scale=None, lse=False, dup=True),  # same token twice
+    # 8 logits per lane with a partly empty last group; short K (2 or 4 ring stages, 4 or 8
+    # of the 16 logit chains empty)
+    dict(T=1, E=100, k=6, I=128, d=128, mult=True, scale=None, lse=True),
+    dict(T=2, E=100, k=8, I=256, d=128, mult=True, scale=2.5, lse=False),
+    dict(T=2, E=65, k=2, I=128, d=256, mult=False, scale=None, lse=True),
 ]
 SR_OUTS = ("logits", "topk_idx", "topk_w", "prob_mass", "counts", "offsets", "perm", "inv",
            "weighted_counts", "gu", "h", "y", "out", "d_err")
@@ -220,6 +225,7 @@ def _decode_one(L, inp, fused, mult, scale, lse):
 
 @pytest.mark.parametrize("case", SR_CASES,
                          ids=lambda c: (f"T{c['T']}_E{c['E']}_k{c['k']}_I{c['I']}_q{int(c['mult'])}"
+                                        + (f"_d{c['d']}" if "d" in c else "")
                                         + ("_dup" if c.get("dup") else "")))
 def test_decode_self_route_matches_tail(case):
     """One or two tokens, plain softmax router, gather fused (the decode step's launch
@@ -227,8 +233,9 @@ def test_decode_self_route_matches_tail(case):
     experts in every block. Every output is bitwise the routing-tail path's (tail launch,
     gather, gate/up from x_perm), the routing outputs the multi-kernel steps', and the
     oracle agrees on the GPU logits."""
-    L = W.make_layer(T=case["T"], d=4096, E=case["E"], k=case["k"], I=case["I"], dtype="bf16",
-                     mode="router", seed=90 + case["E"] + case["k"] + case["T"], bias="zipf")
+    L = W.make_layer(T=case["T"], d=case.get("d", 4096), E=case["E"], k=case["k"], I=case["I"],
+                     dtype="bf16", mode="router", seed=90 + case["E"] + case["k"] + case["T"],
+                     bias="zipf")
     if case.get("dup"):
         L.x = np.ascontiguousarray(np.repeat(L.x[:1], L.T, axis=0))
     L.token_mult = np.array([3, 5][:L.T], dtype=np.int32)
