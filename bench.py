@@ -825,7 +825,8 @@ def run_layer(cfg: str, args, hip, reports: bool, cpu_sample: int):
                     "p10": round(float(np.percentile(step_ms, 10)), 5),
                     "p90": round(float(np.percentile(step_ms, 90)), 5)},
         "config": {"workload": WORKLOADS[cfg], "name": cfg, "T": L.T, "d": L.d, "E": L.E,
-                   "k": L.k, "inter": L.I, "mode": L.mode, "tile_m": args.tile_m or "auto"},
+                   "k": L.k, "inter": L.I, "mode": L.mode, "tile_m": args.tile_m or "auto",
+                   "tile_height": M.tile_height(dims)},
         "dtype": "bf16" if L.dtype == "bf16" else "f32",
         "roofline": {
             "kernel": "grouped_gemm_dma128_kernel<gate/up + SwiGLU, fused gather>",
